@@ -1,0 +1,211 @@
+"""Decode throughput of the persistent megakernel on one MI355X.
+
+A step is one full decode step (embedding through greedy argmax) of the workload's model on a
+batch of synthetic input, greedy ids chained on the device. Prints ONE JSON line with
+tokens/s, the achieved HBM rate of the megakernel against MI355X's 8 TB/s, the unfused
+ablation measured in the same run, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 64] [--warmup 3] [--workload llama2_7b]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kv_bytes_step(cfg, ctx):
+    return cfg.batch * cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim * 2 * ctx
+
+
+def time_path(cfg, weights, kv_host, path, steps, warmup):
+    """Returns (ms per step from events around the whole timed region, per-launch durations ms,
+    model info)."""
+    import torch
+    from persistent_decode_megakernel_amd import synth
+    from persistent_decode_megakernel_amd.model import Model
+
+    max_seq = cfg.prefill + max(steps, warmup) + 1
+    t0 = time.time()
+    model = Model(cfg, weights, path=path, max_seq=max_seq)
+    info = model.info()
+    kv = model.kv(cfg.batch, max_seq)
+    kv.tensor.copy_(kv_host[..., :max_seq, :].to(kv.tensor.device))
+    log(f"[bench] {path}: model ready in {time.time() - t0:.1f}s "
+        f"({info.n_tasks} tasks on {info.n_cu} CUs, {info.launches_per_step} launches/step)")
+    first = synth.make_tokens(cfg, 0)[:, 0].to(torch.int32).cuda()
+    tok = torch.empty_like(first)
+    stream = torch.cuda.current_stream()
+    # warmup (positions P .. P+W-1), then the timed region restarts at P
+    tok.copy_(first)
+    for i in range(warmup):
+        model.step(kv, tok, cfg.prefill + i, next_out=tok)
+    model.sync()
+    torch.cuda.synchronize()
+    tok.copy_(first)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        model.step(kv, tok, cfg.prefill + i, next_out=tok)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    model.sync()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    total = ev[0].elapsed_time(ev[steps])
+    ids = tok.cpu().tolist()
+    kv.close()
+    model.close()
+    del kv, model
+    torch.cuda.empty_cache()
+    return total / steps, per, info, ids
+
+
+def cpu_baseline(cfg, weights, kv_host, sample_layers):
+    """The oracle on a bounded sample: one decode step of a model truncated to its first
+    `sample_layers` layers (plus final norm and LM head); per-layer time scaled to all layers."""
+    import numpy as np
+    import oracle
+    from persistent_decode_megakernel_amd import synth
+
+    params, wn = synth.oracle_inputs(weights)
+    k = min(sample_layers, cfg.n_layers)
+    pos = cfg.prefill
+    kv = synth.bf16_to_numpy_bits(kv_host[:k, ..., :pos + 1, :]).copy()
+    tok = synth.make_tokens(cfg, 0)[:, 0].numpy()
+    # head-only model: 0 layers -> time of embedding + final norm + LM head
+    p0 = dict(params, n_layers=0)
+    w0 = dict(wn, layers=[])
+    dec0 = oracle.Decoder(p0, w0, cache_bytes=0)
+    t = time.perf_counter()
+    dec0.step(kv[:0], tok, pos)
+    t_head = time.perf_counter() - t
+    pk = dict(params, n_layers=k)
+    wk = dict(wn, layers=wn["layers"][:k])
+    deck = oracle.Decoder(pk, wk, cache_bytes=0)
+    t = time.perf_counter()
+    deck.step(kv, tok, pos)
+    t_k = time.perf_counter() - t
+    t_step = t_head + (t_k - t_head) * cfg.n_layers / k
+    cores = len(os.sched_getaffinity(0))
+    threads = cores
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            threads = int(info[0].get("num_threads", cores))
+    except Exception:
+        pass
+    return {
+        "value": cfg.batch / t_step,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"one decode step at position {pos} of the same model truncated to its first "
+                   f"{k} of {cfg.n_layers} layers plus final norm and LM head "
+                   f"({t_k:.1f}s; head alone {t_head:.2f}s), per-layer time scaled to "
+                   f"{cfg.n_layers} layers; float64 numpy; host has {cores} cores"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama2_7b")
+    ap.add_argument("--no-ablation", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-layers", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the decode "
+              "step runs on a single MI355X; multi-GPU sharding is a design note, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from persistent_decode_megakernel_amd import _lib, synth
+
+    _lib.load()
+    torch.cuda.set_device(0)
+    cfg = synth.get_config(args.workload)
+    steps, warmup = args.steps, args.warmup
+    t0 = time.time()
+    weights = synth.make_weights(cfg, 0, threads=16)
+    max_seq = cfg.prefill + max(steps, warmup) + 1
+    kv_host = synth.make_kv(cfg, max_seq, 0, threads=16)
+    log(f"[bench] synthetic {cfg.name} generated in {time.time() - t0:.1f}s")
+
+    ms, per, info, ids = time_path(cfg, weights, kv_host, "megakernel", steps, warmup)
+    weight_bytes = info.weight_bytes + 2 * cfg.hidden * cfg.batch  # + embedding rows
+    ctxs = [cfg.prefill + i + 1 for i in range(steps)]
+    step_bytes = [weight_bytes + kv_bytes_step(cfg, c) for c in ctxs]
+    avg_bytes = sum(step_bytes) / steps
+    avg_launch_ms = sum(per) / steps  # one launch per step
+    achieved = avg_bytes / (avg_launch_ms * 1e-3) / 1e9
+    value = cfg.batch * steps / (ms * steps * 1e-3)
+    out = {
+        "metric": "decode tokens/s at batch 1 + achieved HBM GB/s as % of 8 TB/s peak",
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.wtype == "bf16" else "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.n_layers} layers, hidden {cfg.hidden}, "
+                        f"{cfg.n_heads}/{cfg.n_kv_heads} heads, head_dim {cfg.head_dim}, "
+                        f"FFN {cfg.ffn}, vocab {cfg.vocab}, random-init {cfg.wtype} weights",
+            "batch": cfg.batch,
+            "kv_prefill": cfg.prefill,
+            "positions": f"{cfg.prefill}..{cfg.prefill + steps - 1}",
+            "path": "megakernel (1 persistent launch per step)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "algorithmic_bytes_per_step": int(avg_bytes),
+        "launches_per_step": info.launches_per_step,
+        "step_ms_p10_p50_p90": [round(sorted(per)[int(q * (steps - 1))], 4) for q in (0.1, 0.5, 0.9)],
+    }
+    if not args.no_ablation:
+        ms_u, per_u, info_u, ids_u = time_path(cfg, weights, kv_host, "unfused", steps, warmup)
+        out["ablation_unfused"] = {
+            "ms_per_step": round(ms_u, 4),
+            "tokens_per_s": round(cfg.batch / (ms_u * 1e-3), 2),
+            "launches_per_step": info_u.launches_per_step,
+            "hbm_gbs": round(avg_bytes / (ms_u * 1e-3) / 1e9, 1),
+            "same_final_ids": ids_u == ids,
+            "megakernel_speedup": round(ms_u / ms, 3),
+        }
+    if not args.no_cpu_baseline:
+        t = time.time()
+        out["cpu_baseline"] = cpu_baseline(cfg, weights, kv_host, args.cpu_sample_layers)
+        log(f"[bench] cpu baseline took {time.time() - t:.1f}s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

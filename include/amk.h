@@ -1,0 +1,187 @@
+/*
+ * amk.h - C ABI of the persistent decode megakernel library (libamk.so) for AMD MI355X (gfx950).
+ *
+ * One call of amk_decode_step runs one autoregressive decode step of a Llama-style decoder
+ * (RMSNorm, QKV projection, RoPE, grouped-query attention over a bf16 KV cache, O projection,
+ * SwiGLU MLP, final norm, LM head, greedy argmax).
+ *
+ * Source of the operation: the Ada-MK technical summary (gist.science, "Methodology": a decode
+ * step of the Transformer decoder plus LM head fused into one persistent kernel whose execution
+ * order is searched offline and solidified, "Phase I"; warp-specialised execution, "Phase II")
+ * and the AutoMegaKernel abstract (page 5 of the set: a HuggingFace Llama-family model compiled
+ * into one persistent kernel, a frozen schedule IR checked statically for deadlock and races
+ * before launch, int8 W8A16 weights, greedy decoding).
+ *
+ * Conventions for every entry point:
+ *   - every function returns amk_status; no C++ exception crosses this boundary;
+ *   - argument errors are reported synchronously, before anything is launched;
+ *   - on failure amk_last_error() returns a message for the calling thread;
+ *   - "device" pointers are HIP device memory of the current device; "host" pointers are
+ *     ordinary process memory; `stream` is a hipStream_t passed as void* (NULL = default stream).
+ * Threading: a model may be used from one thread (or serialised by the caller) at a time.
+ */
+#ifndef AMK_H
+#define AMK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AMK_OK = 0,
+  AMK_E_INVALID = 1,            /* bad argument or shape */
+  AMK_E_UNSUPPORTED = 2,        /* valid request this build does not implement */
+  AMK_E_OOM = 3,                /* device or host allocation failed */
+  AMK_E_SCHEDULE_REJECTED = 4,  /* the schedule failed static validation; nothing launched */
+  AMK_E_HIP = 5,                /* a HIP runtime call failed (message carries its text) */
+  AMK_E_CAPACITY = 6,           /* position or batch beyond what was allocated */
+  AMK_E_DEVICE_TIMEOUT = 7,     /* a device-side dependency wait exceeded its bound */
+  AMK_E_DEVICE_FAULT = 8        /* the device flagged bad data (e.g. token id out of range) */
+} amk_status;
+
+typedef enum { AMK_WT_BF16 = 0, AMK_WT_INT8 = 1 } amk_wtype;
+
+typedef enum {
+  AMK_PATH_MEGAKERNEL = 0,  /* one persistent launch per step, frozen per-CU task tables */
+  AMK_PATH_UNFUSED = 1      /* ablation: one kernel launch per operator (1 + 10 L + 3 per step) */
+} amk_path;
+
+/* Model shape. hidden = n_heads * head_dim; n_heads % n_kv_heads == 0; head_dim even and a
+ * multiple of 8; hidden and ffn multiples of 8; 1 <= max_batch <= 8. */
+typedef struct {
+  int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab;
+  float rms_eps, rope_theta;
+  int32_t tied_lm_head; /* 1: the LM head is the embedding matrix */
+  int32_t wtype;        /* amk_wtype of the 7 layer matrices and the (untied) LM head */
+  int32_t max_batch;    /* largest batch a decode step will be called with */
+  int32_t max_seq;      /* largest position + 1 the model will be asked to decode */
+} amk_config;
+
+/* Per-layer weights: device pointers, [out, in] row-major. bf16 matrices hold bfloat16 bit
+ * patterns; int8 matrices hold int8 values with one float32 scale per output row (s* arrays,
+ * NULL for bf16). Norm gains are bfloat16 [hidden]. */
+typedef struct {
+  const void *wq, *wk, *wv, *wo, *wg, *wu, *wd;
+  const float *sq, *sk, *sv, *so, *sg, *su, *sd;
+  const void *attn_norm, *mlp_norm;
+} amk_layer_weights;
+
+/* embed: bf16 [vocab, hidden]; final_norm: bf16 [hidden]; lm_head: [vocab, hidden] (bf16, or int8
+ * with lm_head_scale [vocab]) or NULL when tied. `layers` is a HOST array of n_layers entries. */
+typedef struct {
+  const void *embed, *final_norm, *lm_head;
+  const float *lm_head_scale;
+  const amk_layer_weights *layers;
+} amk_weights;
+
+/* Schedule-search parameters (host only). Zero fields select the builder's default. */
+typedef struct {
+  int32_t attn_blocks;   /* KV blocks per KV head (split-KV); 0 = auto */
+  int32_t min_block;     /* smallest KV block (positions) the auto choice may produce; 0 = 64 */
+  int32_t placement;     /* 0 = XCD-blocked (tiles of one KV group on one XCD), 1 = round-robin */
+  int32_t rotate;        /* phase-to-phase CU rotation of tile placement (0 = none) */
+  int32_t ctx_hint;      /* context length the cost model assumes (0 = max_seq) */
+  int32_t min_tile_kb;   /* smallest weight tile (KiB) a GEMV is cut into; 0 = 4 */
+  int32_t search;        /* 1: exhaustive search over the free fields above; 0: take them as is */
+} amk_sched_params;
+
+/* Cost model used by the schedule search (host only). Zero fields select defaults. */
+typedef struct {
+  double cu_stream_gbs;  /* sustained HBM read rate of one CU when all CUs stream, GB/s */
+  double hop_us;         /* latency from a producer's flag release to a consumer's start, us */
+  double task_us;        /* fixed cost of one task (wait, staging, epilogue), us */
+  double l2_gbs;         /* per-CU rate for re-read activation data (L2 / MALL), GB/s */
+} amk_cost_model;
+
+typedef struct {
+  int32_t n_cu;              /* compute units the schedule targets (grid size) */
+  int32_t n_tasks;           /* tasks per step */
+  int32_t launches_per_step; /* kernel launches one amk_decode_step issues */
+  int32_t lds_bytes;         /* LDS per workgroup of the megakernel */
+  int32_t attn_blocks;       /* KV blocks per KV head */
+  int32_t path;              /* amk_path */
+  uint64_t weight_bytes;     /* algorithmic weight bytes read per step (matrices, gains, scales) */
+  double predicted_us;       /* cost-model makespan of the frozen schedule at ctx_hint */
+} amk_model_info;
+
+typedef struct amk_model amk_model;
+typedef struct amk_kv amk_kv;
+
+/* Create a model on the current device. Weights are BORROWED for the duration of the call: the
+ * library repacks them into its own buffers (tile-major row order) and synchronises `stream`
+ * before returning, so the caller may free them afterwards. schedule_blob (host, may be NULL)
+ * is a frozen schedule from amk_schedule_build; NULL builds one with default parameters. The
+ * schedule is validated before anything is launched (AMK_E_SCHEDULE_REJECTED on failure). */
+amk_status amk_model_create(const amk_config *cfg, const amk_weights *weights, int32_t path,
+                            const void *schedule_blob, size_t blob_bytes, void *stream,
+                            amk_model **out);
+
+/* Bytes of a KV cache for `batch` sequences of `max_seq` positions:
+ * layout [n_layers][2 (K, V)][batch][n_kv_heads][max_seq][head_dim] bfloat16, K post-RoPE. */
+amk_status amk_kv_bytes(const amk_model *m, int32_t batch, int32_t max_seq, size_t *bytes);
+
+/* Attach a KV cache. d_buf == NULL: the library allocates (zeroed) and owns the memory;
+ * otherwise d_buf is caller-owned device memory of at least amk_kv_bytes bytes, borrowed
+ * until amk_kv_free. max_seq must not exceed the model's max_seq. */
+amk_status amk_kv_alloc(amk_model *m, int32_t batch, int32_t max_seq, void *d_buf,
+                        size_t buf_bytes, amk_kv **out);
+
+/* Device pointer of the cache (for the caller to prefill or inspect). */
+amk_status amk_kv_data(const amk_kv *kv, void **d_ptr);
+
+/* One decode step, asynchronous on `stream`. d_tokens: device int32 [batch], the token of each
+ * sequence at position `pos`. Writes K/V at slot `pos`, attends over [0, pos], writes d_next
+ * (device int32 [batch], greedy argmax, lowest index on ties) and, when d_logits != NULL,
+ * d_logits (device float32 [batch, vocab]). d_next may alias the next call's d_tokens. Calls on
+ * one model must be stream-ordered (scratch is reused). Device-side errors (dependency timeout,
+ * token out of range) are recorded on the device and reported by amk_sync. */
+amk_status amk_decode_step(amk_model *m, amk_kv *kv, const int32_t *d_tokens, int32_t pos,
+                           int32_t batch, float *d_logits, int32_t *d_next, void *stream);
+
+/* Synchronise `stream` and report a device-side error recorded by earlier steps (and clear it). */
+amk_status amk_sync(amk_model *m, void *stream);
+
+amk_status amk_model_get_info(const amk_model *m, amk_model_info *out);
+
+/* Copy of the model's frozen schedule blob (host memory, release with amk_blob_free). */
+amk_status amk_model_get_schedule(const amk_model *m, void **blob, size_t *bytes);
+
+amk_status amk_kv_free(amk_kv *kv);
+amk_status amk_destroy(amk_model *m);
+
+/* Message of the last failure on the calling thread ("" if none). Valid until the next call. */
+const char *amk_last_error(void);
+
+/* ---- host-only schedule layer (no GPU needed) ------------------------------------------- */
+
+/* Decompose the decoder into tile tasks, search placement/tiling against `cost` (NULL: default
+ * model) and serialise the best schedule for `n_cu` compute units and `batch`. `params` may be
+ * NULL. The result (host memory) is released with amk_blob_free. */
+amk_status amk_schedule_build(const amk_config *cfg, int32_t batch, int32_t n_cu,
+                              const amk_sched_params *params, const amk_cost_model *cost,
+                              void **blob, size_t *bytes);
+
+/* Static check of a schedule blob: structure, acyclicity of the dependency graph (with per-CU
+ * program order), race freedom and read coverage of every step-local buffer, resource limits.
+ * AMK_OK if safe, AMK_E_SCHEDULE_REJECTED otherwise; report (may be NULL) receives a
+ * NUL-terminated text of at most report_cap bytes. */
+amk_status amk_schedule_validate(const void *blob, size_t bytes, char *report, size_t report_cap);
+
+/* Dynamic cross-check: executes the schedule on the host under several interleavings with
+ * monotone flags and shadow memory; reports deadlock or a stale read. Same return convention. */
+amk_status amk_schedule_simulate(const void *blob, size_t bytes, char *report, size_t report_cap);
+
+/* Cost-model makespan (us) of a schedule at context length ctx. */
+amk_status amk_schedule_predict(const void *blob, size_t bytes, const amk_cost_model *cost,
+                                int32_t ctx, double *makespan_us);
+
+void amk_blob_free(void *blob);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AMK_H */

@@ -1,0 +1,638 @@
+// Device-side task bodies shared by the persistent megakernel and the unfused ablation kernels.
+// gfx950 only: wave64, 16 waves per workgroup in the megakernel.
+//
+// Numerics: weights are bf16 (or int8 with per-row fp32 scales) and are converted exactly to
+// fp32; activations, accumulations, norms, softmax and residuals are fp32. Appended K/V rows are
+// rounded to bf16 (round to nearest even). Every reduction runs in a fixed order, so results do
+// not depend on which CU ran a tile or when.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../sched/layout.h"
+
+namespace amk {
+
+struct DevLayer {
+  const void *qkv, *o, *gu, *dn;           // packed weights (bf16 bits or int8)
+  const float *s_qkv, *s_o, *s_gu, *s_dn;  // per-row scales (int8) or null
+  const uint16_t *attn_norm, *mlp_norm;
+};
+
+struct DevModel {
+  int32_t L, d, nq, nkv, hd, F, V, qkvr, qd, qpg;
+  int32_t wtype, tied, max_batch, max_seq;
+  int32_t nblk, n_lm;
+  float eps, attn_scale;
+  const DevLayer *layers;
+  const uint16_t *embed, *final_norm;
+  const void *lm;
+  const float *lm_scale;
+  const float2 *rope;  // [max_seq][hd/2] (cos, sin) of pos * theta^(-2j/hd)
+  float *h;            // [2L+1][B][d] residual stream (slot 0 unused: the embedding row)
+  float *q;            // [L][B][qd]
+  float *part;         // [L][B][nq][nblk][hd+2]
+  float *a;            // [L][B][F]
+  float *logits;       // [B][V] used when the caller passes no logits buffer
+  float2 *amax;        // [n_lm][B] (value, index bits)
+  uint32_t *flags;     // [n_tasks]
+  uint32_t *err;       // [0] status, [1] abort, [2] task, [3] detail
+  const Task *tasks;
+  const uint32_t *offsets;
+  // unfused-path scratch
+  float *xn;    // [B][max(d, qd, F)]
+  float *y;     // [B][max(qkvr, 2F, V, d)]
+  float *o;     // [B][qd]
+  uint64_t timeout_ticks;  // bound of one dependency wait (s_memrealtime ticks, 100 MHz)
+};
+
+struct StepArgs {
+  const int32_t *tokens;
+  float *logits;
+  int32_t *next;
+  uint16_t *kv;
+  int32_t kv_batch, kv_max_seq;
+  int32_t pos, batch;
+  uint32_t epoch;
+};
+
+constexpr uint32_t ERR_TIMEOUT = 7;
+constexpr uint32_t ERR_TOKEN = 8;
+
+// ------------------------------------------------------------------------------------------
+// small helpers
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// round to nearest even (inputs are finite)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+__device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
+
+// butterfly sum over the 64 lanes; every lane receives the total
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// sum over the threads of a workgroup of nw waves; red = LDS scratch of >= nw floats.
+// Every thread receives the total (fixed order: waves summed 0..nw-1).
+__device__ __forceinline__ float block_sum(float v, float *red, int nw) {
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane_id() == 0) red[wave_id()] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int w = 0; w < nw; ++w) t += red[w];
+  return t;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+__device__ __forceinline__ float dot8_bf16(const uint4 w, const float *x) {
+  const float4 x0 = *reinterpret_cast<const float4 *>(x);
+  const float4 x1 = *reinterpret_cast<const float4 *>(x + 4);
+  float a = bf_lo(w.x) * x0.x;
+  float b = bf_hi(w.x) * x0.y;
+  a = fmaf(bf_lo(w.y), x0.z, a);
+  b = fmaf(bf_hi(w.y), x0.w, b);
+  a = fmaf(bf_lo(w.z), x1.x, a);
+  b = fmaf(bf_hi(w.z), x1.y, b);
+  a = fmaf(bf_lo(w.w), x1.z, a);
+  b = fmaf(bf_hi(w.w), x1.w, b);
+  return a + b;
+}
+
+// 16 int8 weights (two's complement) dotted with 16 floats.
+__device__ __forceinline__ float dot16_i8(const uint4 w, const float *x) {
+  float a = 0.f, b = 0.f;
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 xv = *reinterpret_cast<const float4 *>(x + 4 * i);
+    const int32_t v = (int32_t)ws[i];
+    a = fmaf((float)((v << 24) >> 24), xv.x, a);
+    b = fmaf((float)((v << 16) >> 24), xv.y, b);
+    a = fmaf((float)((v << 8) >> 24), xv.z, a);
+    b = fmaf((float)(v >> 24), xv.w, b);
+  }
+  return a + b;
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const uint4 *p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ------------------------------------------------------------------------------------------
+// dependency flags
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t flag_load(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void record_error(uint32_t *err, uint32_t code, uint32_t task,
+                                             uint32_t detail) {
+  uint32_t expected = 0;
+  if (__hip_atomic_compare_exchange_strong(&err[0], &expected, code, __ATOMIC_RELAXED,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+    __hip_atomic_store(&err[2], task, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&err[3], detail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Called by one whole wave. Spins until flags[lo..hi) all reached `epoch`, then performs an
+// agent-scope acquire. Returns false (after recording the error and raising the abort flag)
+// when the wait exceeds the timeout or another workgroup has aborted.
+__device__ bool wait_range(const DevModel &m, uint32_t lo, uint32_t hi, uint32_t epoch,
+                           uint32_t task) {
+  const int lane = lane_id();
+  uint64_t t0 = 0;
+  for (uint32_t base = lo; base < hi; base += 64) {
+    const uint32_t idx = base + (uint32_t)lane;
+    uint32_t spins = 0;
+    while (true) {
+      bool ok = idx >= hi || (int32_t)(flag_load(&m.flags[idx]) - epoch) >= 0;
+      if (__all(ok)) break;
+      if (spins == 0) t0 = wall_clock64();
+      ++spins;
+      if ((spins & 15) == 0) {
+        if (flag_load(&m.err[1]) != 0) return false;
+        if (wall_clock64() - t0 > m.timeout_ticks) {
+          if (lane == 0) {
+            record_error(m.err, ERR_TIMEOUT, task, idx);
+            __hip_atomic_store(&m.err[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          return false;
+        }
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return true;
+}
+
+// ------------------------------------------------------------------------------------------
+// GEMV core: ys[r - r0] = sum_k W[r, k] * xs[k] for r in [r0, r1), one wave per row in turn.
+// W row-major [rows, K]; xs in LDS (K floats). Rows are dealt to waves round-robin. The K loop
+// issues U 16-byte loads per lane before consuming them.
+// ------------------------------------------------------------------------------------------
+template <int U>
+__device__ __forceinline__ float row_dot_bf16(const uint16_t *__restrict__ W, int64_t row, int K,
+                                              const float *xs) {
+  const uint4 *wr = reinterpret_cast<const uint4 *>(W + row * (int64_t)K);
+  const int n16 = K >> 3;
+  const int lane = lane_id();
+  float acc = 0.f;
+  for (int u0 = 0; u0 < n16; u0 += 64 * U) {
+    uint4 w[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int u = u0 + j * 64 + lane;
+      w[j] = (u < n16) ? load_nt(wr + u) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int u = u0 + j * 64 + lane;
+      if (u < n16) acc += dot8_bf16(w[j], xs + 8 * u);
+    }
+  }
+  return wave_sum(acc);
+}
+
+template <int U>
+__device__ __forceinline__ float row_dot_i8(const int8_t *__restrict__ W, int64_t row, int K,
+                                            const float *xs) {
+  const uint4 *wr = reinterpret_cast<const uint4 *>(W + row * (int64_t)K);
+  const int n16 = K >> 4;
+  const int lane = lane_id();
+  float acc = 0.f;
+  for (int u0 = 0; u0 < n16; u0 += 64 * U) {
+    uint4 w[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int u = u0 + j * 64 + lane;
+      w[j] = (u < n16) ? load_nt(wr + u) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int u = u0 + j * 64 + lane;
+      if (u < n16) acc += dot16_i8(w[j], xs + 16 * u);
+    }
+  }
+  return wave_sum(acc);
+}
+
+// rows [r0, r1) of a matrix for B staged vectors (xs + b*K); ys[b*(r1-r0) + r - r0].
+// WT = 0: bf16 weights; WT = 1: int8 weights times scale[r].
+template <int WT>
+__device__ void gemv_rows(const void *W, const float *scale, int K, int r0, int r1,
+                          const float *xs, float *ys, int B, int nw) {
+  const int n = r1 - r0;
+  for (int i = wave_id(); i < n; i += nw) {
+    const int64_t r = r0 + i;
+    for (int b = 0; b < B; ++b) {
+      float v;
+      if constexpr (WT == 1)
+        v = row_dot_i8<4>(static_cast<const int8_t *>(W), r, K, xs + (int64_t)b * K) * scale[r];
+      else
+        v = row_dot_bf16<8>(static_cast<const uint16_t *>(W), r, K, xs + (int64_t)b * K);
+      if (lane_id() == 0) ys[b * n + i] = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// input staging (LDS)
+// ------------------------------------------------------------------------------------------
+// token of sequence b, validated (an out-of-range id is recorded as a device error and read as 0)
+__device__ __forceinline__ int32_t token_of(const DevModel &m, const StepArgs &s, int b) {
+  int32_t t = s.tokens[b];
+  if (t < 0 || t >= m.V) {
+    if (threadIdx.x == 0) record_error(m.err, ERR_TOKEN, 0xffffffffu, (uint32_t)t);
+    t = 0;
+  }
+  return t;
+}
+
+// xs[b][i] = rmsnorm(src_b)[i] * gain[i]. src = h slot `slot` or, for slot 0, the embedding row.
+__device__ void stage_norm(const DevModel &m, const StepArgs &s, int slot, const uint16_t *gain,
+                           float *xs, float *red, int nw) {
+  const int d = m.d;
+  for (int b = 0; b < s.batch; ++b) {
+    float *x = xs + (int64_t)b * d;
+    float ss = 0.f;
+    if (slot == 0) {
+      const uint16_t *e = m.embed + (int64_t)token_of(m, s, b) * d;
+      for (int i = threadIdx.x; i < d; i += nw * 64) {
+        float v = bf16_to_f32(e[i]);
+        x[i] = v;
+        ss += v * v;
+      }
+    } else {
+      const float *src = m.h + ((int64_t)slot * m.max_batch + b) * d;
+      for (int i = threadIdx.x; i < d; i += nw * 64) {
+        float v = src[i];
+        x[i] = v;
+        ss += v * v;
+      }
+    }
+    const float tot = block_sum(ss, red, nw);
+    const float inv = 1.0f / sqrtf(tot / (float)d + m.eps);
+    for (int i = threadIdx.x; i < d; i += nw * 64) x[i] = x[i] * inv * bf16_to_f32(gain[i]);
+  }
+  __syncthreads();
+}
+
+// xs[b][h*hd + j] = attention output of head h, merged over the KV blocks (log-sum-exp).
+__device__ void stage_combine(const DevModel &m, const StepArgs &s, int l, float *xs, int nw) {
+  const int hd = m.hd, nblk = m.nblk, qd = m.qd;
+  for (int b = 0; b < s.batch; ++b) {
+    const float *pb = m.part + (((int64_t)l * m.max_batch + b) * m.nq) * nblk * (hd + 2);
+    for (int e = threadIdx.x; e < qd; e += nw * 64) {
+      const int h = e / hd, j = e - h * hd;
+      const float *ph = pb + (int64_t)h * nblk * (hd + 2);
+      float M = -INFINITY;
+      for (int k = 0; k < nblk; ++k) M = fmaxf(M, ph[k * (hd + 2) + hd]);
+      float num = 0.f, den = 0.f;
+      for (int k = 0; k < nblk; ++k) {
+        const float *p = ph + k * (hd + 2);
+        const float w = __expf(p[hd] - M);  // empty blocks carry m = -inf -> weight 0
+        num = fmaf(w, p[j], num);
+        den = fmaf(w, p[hd + 1], den);
+      }
+      xs[(int64_t)b * qd + e] = num / den;
+    }
+  }
+  __syncthreads();
+}
+
+__device__ void stage_plain(const float *src, int64_t src_stride, int K, int B, float *xs, int nw) {
+  for (int b = 0; b < B; ++b)
+    for (int i = threadIdx.x; i < K; i += nw * 64) xs[(int64_t)b * K + i] = src[b * src_stride + i];
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------------------------------
+// epilogues (ys in LDS, n = r1 - r0 rows per batch row)
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ int64_t kv_index(const DevModel &m, const StepArgs &s, int l, int kvi,
+                                            int b, int g, int p, int dim) {
+  return (((((int64_t)l * 2 + kvi) * s.kv_batch + b) * m.nkv + g) * s.kv_max_seq + p) *
+             (int64_t)m.hd + dim;
+}
+
+// QKV rows: RoPE on pairs of rotary rows, q -> q buffer (fp32), k/v -> KV cache slot pos (bf16).
+__device__ void epi_qkv(const DevModel &m, const StepArgs &s, int l, int r0, int r1,
+                        const float *ys, int nw) {
+  const int n = r1 - r0, hd = m.hd, half = hd / 2;
+  const float2 *cs = m.rope + (int64_t)s.pos * half;
+  for (int b = 0; b < s.batch; ++b) {
+    for (int pi = threadIdx.x; pi < n / 2; pi += nw * 64) {
+      const int r = r0 + 2 * pi;
+      const QkvRow q0 = qkv_decode(r, m.nq, m.nkv, hd);
+      const QkvRow q1 = qkv_decode(r + 1, m.nq, m.nkv, hd);
+      float v0 = ys[b * n + 2 * pi], v1 = ys[b * n + 2 * pi + 1];
+      if (q0.kind != KIND_V) {  // rotary pair (dim j, dim j + hd/2)
+        const float2 c = cs[q0.dim];
+        const float a = v0, bb = v1;
+        v0 = a * c.x - bb * c.y;
+        v1 = bb * c.x + a * c.y;
+      }
+      if (q0.kind == KIND_Q) {
+        float *qb = m.q + ((int64_t)l * m.max_batch + b) * m.qd;
+        qb[q0.head * hd + q0.dim] = v0;
+        qb[q1.head * hd + q1.dim] = v1;
+      } else {
+        const int kvi = (q0.kind == KIND_K) ? 0 : 1;
+        s.kv[kv_index(m, s, l, kvi, b, q0.head, s.pos, q0.dim)] = f32_to_bf16(v0);
+        s.kv[kv_index(m, s, l, kvi, b, q1.head, s.pos, q1.dim)] = f32_to_bf16(v1);
+      }
+    }
+  }
+}
+
+// out[b][r] = res[b][r] + ys (res slot 0 = the embedding row of the token)
+__device__ void epi_residual(const DevModel &m, const StepArgs &s, int res_slot, int out_slot,
+                             int r0, int r1, const float *ys, int nw) {
+  const int n = r1 - r0, d = m.d;
+  for (int b = 0; b < s.batch; ++b) {
+    float *out = m.h + ((int64_t)out_slot * m.max_batch + b) * d;
+    const float *res = m.h + ((int64_t)res_slot * m.max_batch + b) * d;
+    const uint16_t *e = (res_slot == 0) ? m.embed + (int64_t)token_of(m, s, b) * d : nullptr;
+    for (int i = threadIdx.x; i < n; i += nw * 64) {
+      const int r = r0 + i;
+      const float base = e ? bf16_to_f32(e[r]) : res[r];
+      out[r] = base + ys[b * n + i];
+    }
+  }
+}
+
+__device__ void epi_swiglu(const DevModel &m, const StepArgs &s, int l, int r0, int r1,
+                           const float *ys, int nw) {
+  const int n = r1 - r0;
+  for (int b = 0; b < s.batch; ++b) {
+    float *a = m.a + ((int64_t)l * m.max_batch + b) * m.F;
+    for (int i = threadIdx.x; i < n / 2; i += nw * 64)
+      a[r0 / 2 + i] = silu(ys[b * n + 2 * i]) * ys[b * n + 2 * i + 1];
+  }
+}
+
+// logits rows + (max, lowest index of max) of this tile into amax[slot][b]
+__device__ void epi_logits(const DevModel &m, const StepArgs &s, int r0, int r1, int slot,
+                           const float *ys, float *red, int nw) {
+  const int n = r1 - r0;
+  float *lg = s.logits ? s.logits : m.logits;
+  for (int b = 0; b < s.batch; ++b) {
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int i = threadIdx.x; i < n; i += nw * 64) {
+      const float v = ys[b * n + i];
+      lg[(int64_t)b * m.V + r0 + i] = v;
+      if (v > best) { best = v; bi = r0 + i; }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(best, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+    }
+    __syncthreads();
+    if (lane_id() == 0) {
+      red[2 * wave_id()] = best;
+      red[2 * wave_id() + 1] = __int_as_float(bi);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float bv = red[0];
+      int bj = __float_as_int(red[1]);
+      for (int w = 1; w < nw; ++w) {
+        const float v = red[2 * w];
+        const int j = __float_as_int(red[2 * w + 1]);
+        if (v > bv || (v == bv && j < bj)) { bv = v; bj = j; }
+      }
+      m.amax[(int64_t)slot * m.max_batch + b] = make_float2(bv, __int_as_float(bj));
+    }
+  }
+}
+
+// next[b] = argmax over the LM tiles' partials (value desc, index asc); one wave.
+__device__ void argmax_combine(const DevModel &m, const StepArgs &s, int n_slots) {
+  if (wave_id() != 0) return;
+  for (int b = 0; b < s.batch; ++b) {
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int k = lane_id(); k < n_slots; k += 64) {
+      const float2 p = m.amax[(int64_t)k * m.max_batch + b];
+      const int j = __float_as_int(p.y);
+      if (p.x > best || (p.x == best && j < bi)) { best = p.x; bi = j; }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(best, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+    }
+    if (lane_id() == 0) s.next[b] = (bi == 0x7fffffff) ? 0 : bi;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// attention partial for (layer l, kv group g, KV block blk) over positions [lo, hi) of ctx.
+// LDS: q [qpg][hd] | scores [qpg][kAttnRowsPerChunk] | acc [nw][qpg*hd] | stats.
+// Lane layout: LPR = hd/8 lanes per KV row (8 dims each), 64/LPR rows per wave per load.
+// ------------------------------------------------------------------------------------------
+template <int HD, int QMAX>
+__device__ void attn_block(const DevModel &m, const StepArgs &s, int l, int g, int blk,
+                           int h0, int qn, float *lds, float *red) {
+  constexpr int NW = kWaves;
+  constexpr int LPR = HD / 8;
+  constexpr int RPW = 64 / LPR;  // rows per wave per load
+  constexpr int ROWS_PER_ITER = NW * RPW;
+  constexpr int NIT = kAttnRowsPerChunk / ROWS_PER_ITER;
+  static_assert(NIT * ROWS_PER_ITER == kAttnRowsPerChunk, "chunk must be whole iterations");
+  // heads [h0, h0 + qn) of the group (qn <= QMAX), i.e. query heads g*qpg + h0 + i
+  const int qpg = qn, nq = m.nq, nblk = m.nblk;
+  const int lane = lane_id(), wave = wave_id();
+  const int sub = lane % LPR, rs = lane / LPR;
+  int lo, hi;
+  attn_block_range(s.pos + 1, nblk, blk, &lo, &hi);
+  float *qs = lds;                             // [qpg][HD]
+  float *sc = qs + qpg * HD;                   // [qpg][chunk]
+  float *accw = sc + qpg * kAttnRowsPerChunk;  // [NW][qpg*HD]
+  for (int b = 0; b < s.batch; ++b) {
+    const float *qsrc = m.q + ((int64_t)l * m.max_batch + b) * m.qd + ((int64_t)g * m.qpg + h0) * HD;
+    for (int i = threadIdx.x; i < qpg * HD; i += NW * 64) qs[i] = qsrc[i] * m.attn_scale;
+    __syncthreads();
+    float *pout = m.part + ((((int64_t)l * m.max_batch + b) * nq + (int64_t)g * m.qpg + h0) * nblk + blk) * (HD + 2);
+    if (hi <= lo) {
+      for (int i = threadIdx.x; i < qpg * (HD + 2); i += NW * 64) {
+        const int h = i / (HD + 2), e = i - h * (HD + 2);
+        pout[(int64_t)h * nblk * (HD + 2) + e] = (e == HD) ? -INFINITY : 0.f;
+      }
+      __syncthreads();
+      continue;
+    }
+    const uint16_t *Kb = s.kv + kv_index(m, s, l, 0, b, g, 0, 0);
+    const uint16_t *Vb = s.kv + kv_index(m, s, l, 1, b, g, 0, 0);
+    float acc[QMAX][8];
+    float lsum[QMAX];
+    float mrun[QMAX];
+#pragma unroll
+    for (int h = 0; h < QMAX; ++h) {
+      lsum[h] = 0.f;
+      mrun[h] = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    }
+    for (int c0 = lo; c0 < hi; c0 += kAttnRowsPerChunk) {
+      const int c1 = min(hi, c0 + kAttnRowsPerChunk);
+      uint4 kr[NIT], vr[NIT];
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int j = c0 + it * ROWS_PER_ITER + wave * RPW + rs;
+        const bool ok = j < c1;
+        kr[it] = ok ? *reinterpret_cast<const uint4 *>(Kb + (int64_t)j * HD + sub * 8) : make_uint4(0, 0, 0, 0);
+        vr[it] = ok ? *reinterpret_cast<const uint4 *>(Vb + (int64_t)j * HD + sub * 8) : make_uint4(0, 0, 0, 0);
+      }
+      // scores of this lane's rows, reduced over the LPR lanes of a row
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int j = c0 + it * ROWS_PER_ITER + wave * RPW + rs;
+#pragma unroll
+        for (int h = 0; h < QMAX; ++h) {
+          if (h < qpg) {
+            float p = dot8_bf16(kr[it], qs + h * HD + sub * 8);
+#pragma unroll
+            for (int o = LPR / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o, 64);
+            if (j < c1 && sub == 0) sc[h * kAttnRowsPerChunk + (j - c0)] = p;
+          }
+        }
+      }
+      __syncthreads();
+      // chunk max per head (wave h), published in red[h]
+      const int n = c1 - c0;
+      if (wave < qpg) {
+        float mx = -INFINITY;
+        for (int i = lane; i < n; i += 64) mx = fmaxf(mx, sc[wave * kAttnRowsPerChunk + i]);
+        mx = wave_max(mx);
+        if (lane == 0) red[wave] = mx;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int h = 0; h < QMAX; ++h) {
+        if (h < qpg) {
+          const float mnew = fmaxf(mrun[h], red[h]);
+          const float f = __expf(mrun[h] - mnew);
+          lsum[h] *= f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] *= f;
+          mrun[h] = mnew;
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int j = c0 + it * ROWS_PER_ITER + wave * RPW + rs;
+        if (j < c1) {
+          const uint4 v = vr[it];
+          const float vv[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
+                               bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
+#pragma unroll
+          for (int h = 0; h < QMAX; ++h) {
+            if (h < qpg) {
+              const float p = __expf(sc[h * kAttnRowsPerChunk + (j - c0)] - mrun[h]);
+              if (sub == 0) lsum[h] += p;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vv[e], acc[h][e]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+    // reduce acc over the row slots of the wave (lanes with equal sub), then over waves
+#pragma unroll
+    for (int h = 0; h < QMAX; ++h) {
+      if (h < qpg) {
+#pragma unroll
+        for (int o = LPR; o < 64; o <<= 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, 64);
+          lsum[h] += __shfl_xor(lsum[h], o, 64);
+        }
+#pragma unroll
+        for (int o = 1; o < LPR; o <<= 1) lsum[h] += __shfl_xor(lsum[h], o, 64);
+        if (rs == 0) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) accw[(int64_t)wave * qpg * HD + h * HD + sub * 8 + e] = acc[h][e];
+        }
+        if (lane == 0) red[16 + wave * 8 + h] = lsum[h];
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < qpg * HD; i += NW * 64) {
+      float t = 0.f;
+      for (int w = 0; w < NW; ++w) t += accw[(int64_t)w * qpg * HD + i];
+      const int h = i / HD, e = i - h * HD;
+      pout[(int64_t)h * nblk * (HD + 2) + e] = t;
+    }
+    if (threadIdx.x < qpg) {
+      const int h = threadIdx.x;
+      float t = 0.f;
+      for (int w = 0; w < NW; ++w) t += red[16 + w * 8 + h];
+      float mh = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < QMAX; ++k)
+        if (k == h) mh = mrun[k];
+      pout[(int64_t)h * nblk * (HD + 2) + HD] = mh;
+      pout[(int64_t)h * nblk * (HD + 2) + HD + 1] = t;
+    }
+    __syncthreads();
+  }
+}
+
+// Attention tasks always run with kWaves waves (1024 threads). A group of more query heads than
+// QMAX is processed QMAX heads at a time (the KV block is re-read from cache for each pass).
+template <int HD, int QMAX>
+__device__ __forceinline__ void attn_task(const DevModel &m, const StepArgs &s, int l, int g,
+                                          int blk, float *lds, float *red) {
+  for (int h0 = 0; h0 < m.qpg; h0 += QMAX)
+    attn_block<HD, QMAX>(m, s, l, g, blk, h0, min(QMAX, m.qpg - h0), lds, red);
+}
+
+// ------------------------------------------------------------------------------------------
+// weights of a GEMV matrix
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ void gemv_matrix(const DevModel &m, int mat, int l, const void **W,
+                                            const float **scale, int *K, int *wtype) {
+  *wtype = m.wtype;
+  switch (mat) {
+    case M_QKV: *W = m.layers[l].qkv; *scale = m.layers[l].s_qkv; *K = m.d; break;
+    case M_O: *W = m.layers[l].o; *scale = m.layers[l].s_o; *K = m.qd; break;
+    case M_GU: *W = m.layers[l].gu; *scale = m.layers[l].s_gu; *K = m.d; break;
+    case M_D: *W = m.layers[l].dn; *scale = m.layers[l].s_dn; *K = m.F; break;
+    default:
+      *W = m.lm;
+      *scale = m.lm_scale;
+      *K = m.d;
+      if (m.tied) *wtype = 0;
+      break;
+  }
+}
+
+}  // namespace amk

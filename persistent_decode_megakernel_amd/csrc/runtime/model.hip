@@ -1,0 +1,658 @@
+// Runtime behind the C ABI: model creation (weight repacking, schedule build/validation, device
+// tables), KV caches, and the per-step launch of the megakernel or the unfused ablation.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <stdexcept>
+#include <string>
+#include <vector>
+
+#include "../kernels/device.h"
+#include "../sched/sched_internal.h"
+#include "errors.h"
+
+using namespace amk;
+
+// kernels defined in the other translation units
+#define AMK_DECL_MK(WT, HD, Q) \
+  extern "C" __global__ void amk_megakernel_w##WT##_h##HD##_q##Q(const DevModel *, StepArgs);
+AMK_DECL_MK(0, 64, 1)
+AMK_DECL_MK(0, 64, 2)
+AMK_DECL_MK(0, 64, 4)
+AMK_DECL_MK(0, 128, 1)
+AMK_DECL_MK(0, 128, 2)
+AMK_DECL_MK(0, 128, 4)
+AMK_DECL_MK(1, 64, 1)
+AMK_DECL_MK(1, 64, 2)
+AMK_DECL_MK(1, 64, 4)
+AMK_DECL_MK(1, 128, 1)
+AMK_DECL_MK(1, 128, 2)
+AMK_DECL_MK(1, 128, 4)
+extern "C" __global__ void amk_uf_embed(const DevModel *, StepArgs);
+extern "C" __global__ void amk_uf_rmsnorm(const DevModel *, const float *, const uint16_t *, float *);
+#define AMK_DECL_UG(WT, MODE)                                                                  \
+  extern "C" __global__ void amk_uf_gemv_w##WT##_m##MODE(const DevModel *, StepArgs, const void *, \
+                                                         const float *, int, int, const float *,  \
+                                                         float *, const float *, float *);
+AMK_DECL_UG(0, 0)
+AMK_DECL_UG(0, 1)
+AMK_DECL_UG(0, 2)
+AMK_DECL_UG(1, 0)
+AMK_DECL_UG(1, 1)
+AMK_DECL_UG(1, 2)
+extern "C" __global__ void amk_uf_rope_kv(const DevModel *, StepArgs, int);
+#define AMK_DECL_UA(HD, Q) extern "C" __global__ void amk_uf_attn_h##HD##_q##Q(const DevModel *, StepArgs, int);
+AMK_DECL_UA(64, 1)
+AMK_DECL_UA(64, 2)
+AMK_DECL_UA(64, 4)
+AMK_DECL_UA(128, 1)
+AMK_DECL_UA(128, 2)
+AMK_DECL_UA(128, 4)
+extern "C" __global__ void amk_uf_combine(const DevModel *, int);
+extern "C" __global__ void amk_uf_swiglu(const DevModel *, int, int);
+extern "C" __global__ void amk_uf_argmax(const DevModel *, StepArgs, int);
+
+// row gather used for repacking: dst row pairs[i].x <- src row pairs[i].y (4-byte words)
+extern "C" __global__ void __launch_bounds__(256)
+amk_gather_rows(uint32_t *dst, const uint32_t *src, const int2 *pairs, int n, int row_words) {
+  for (int i = blockIdx.x; i < n; i += gridDim.x) {
+    const int2 p = pairs[i];
+    const uint32_t *s = src + (int64_t)p.y * row_words;
+    uint32_t *d = dst + (int64_t)p.x * row_words;
+    for (int k = threadIdx.x; k < row_words; k += 256) d[k] = s[k];
+  }
+}
+
+namespace {
+
+constexpr int kUfRowsPerBlock = 32;  // must match the unfused GEMV kernels
+constexpr int kUfThreads = 8 * 64;
+
+struct HipError : std::runtime_error {
+  explicit HipError(const std::string &m) : std::runtime_error(m) {}
+};
+
+void hip_check(hipError_t e, const char *what) {
+  if (e != hipSuccess) throw HipError(std::string(what) + ": " + hipGetErrorString(e));
+}
+
+using MkFn = void (*)(const DevModel *, StepArgs);
+
+MkFn pick_megakernel(int wt, int hd, int qmax) {
+#define AMK_P(WT, HD, Q) \
+  if (wt == WT && hd == HD && qmax == Q) return amk_megakernel_w##WT##_h##HD##_q##Q;
+  AMK_P(0, 64, 1) AMK_P(0, 64, 2) AMK_P(0, 64, 4) AMK_P(0, 128, 1) AMK_P(0, 128, 2) AMK_P(0, 128, 4)
+  AMK_P(1, 64, 1) AMK_P(1, 64, 2) AMK_P(1, 64, 4) AMK_P(1, 128, 1) AMK_P(1, 128, 2) AMK_P(1, 128, 4)
+#undef AMK_P
+  return nullptr;
+}
+
+using UaFn = void (*)(const DevModel *, StepArgs, int);
+UaFn pick_uf_attn(int hd, int qmax) {
+#define AMK_P(HD, Q) \
+  if (hd == HD && qmax == Q) return amk_uf_attn_h##HD##_q##Q;
+  AMK_P(64, 1) AMK_P(64, 2) AMK_P(64, 4) AMK_P(128, 1) AMK_P(128, 2) AMK_P(128, 4)
+#undef AMK_P
+  return nullptr;
+}
+
+using UgFn = void (*)(const DevModel *, StepArgs, const void *, const float *, int, int,
+                      const float *, float *, const float *, float *);
+UgFn pick_uf_gemv(int wt, int mode) {
+  static const UgFn t[2][3] = {{amk_uf_gemv_w0_m0, amk_uf_gemv_w0_m1, amk_uf_gemv_w0_m2},
+                               {amk_uf_gemv_w1_m0, amk_uf_gemv_w1_m1, amk_uf_gemv_w1_m2}};
+  return t[wt][mode];
+}
+
+int qmax_for(int qpg) { return qpg <= 1 ? 1 : (qpg <= 2 ? 2 : 4); }
+
+}  // namespace
+
+struct amk_model {
+  amk_config cfg{};
+  int32_t path = 0;
+  int device = 0;
+  int n_cu = 0;
+  Schedule sched;
+  std::vector<uint8_t> blob;
+  std::vector<void *> allocs;
+  DevModel dm{};
+  DevModel *d_dm = nullptr;
+  std::vector<DevLayer> layers;
+  uint32_t epoch = 0;
+  uint32_t lds_bytes = 0;
+  uint32_t uf_attn_lds = 0;
+  uint64_t weight_bytes = 0;
+  int n_lm_uf = 0;
+  MkFn mk = nullptr;
+  UaFn uf_attn = nullptr;
+  uint32_t *h_err = nullptr;  // pinned copy of the device error words
+  hipEvent_t err_event = nullptr;
+  bool err_pending = false;
+
+  template <typename T>
+  T *dalloc(size_t count) {
+    void *p = nullptr;
+    size_t bytes = count * sizeof(T);
+    if (bytes == 0) bytes = 16;
+    hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) throw std::bad_alloc();
+    allocs.push_back(p);
+    return static_cast<T *>(p);
+  }
+};
+
+struct amk_kv {
+  amk_model *m = nullptr;
+  void *data = nullptr;
+  bool owned = false;
+  int32_t batch = 0, max_seq = 0;
+  size_t bytes = 0;
+};
+
+namespace {
+
+void free_model(amk_model *m) {
+  if (!m) return;
+  for (void *p : m->allocs) (void)hipFree(p);
+  if (m->h_err) (void)hipHostFree(m->h_err);
+  if (m->err_event) (void)hipEventDestroy(m->err_event);
+  delete m;
+}
+
+void gather(amk_model *m, void *dst, const void *src, const std::vector<int2> &pairs,
+            size_t row_bytes, hipStream_t st) {
+  if (pairs.empty()) return;
+  if (row_bytes % 4) throw std::runtime_error("row size not a multiple of 4 bytes");
+  int2 *d_pairs = nullptr;
+  hip_check(hipMalloc(&d_pairs, pairs.size() * sizeof(int2)), "hipMalloc");
+  hipError_t e = hipMemcpyAsync(d_pairs, pairs.data(), pairs.size() * sizeof(int2),
+                                hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) {
+    int blocks = (int)std::min<size_t>(pairs.size(), 65535);
+    hipLaunchKernelGGL(amk_gather_rows, dim3(blocks), dim3(256), 0, st, (uint32_t *)dst,
+                       (const uint32_t *)src, (const int2 *)d_pairs, (int)pairs.size(),
+                       (int)(row_bytes / 4));
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  (void)hipFree(d_pairs);
+  hip_check(e, "repack");
+  (void)m;
+}
+
+void copy_d2d(void *dst, const void *src, size_t bytes, hipStream_t st) {
+  hip_check(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st), "hipMemcpyAsync");
+}
+
+amk_status map_device_error(uint32_t code, uint32_t task, uint32_t detail) {
+  if (code == ERR_TIMEOUT)
+    return set_error(AMK_E_DEVICE_TIMEOUT, "device dependency wait timed out (task " +
+                                               std::to_string(task) + " waiting on task " +
+                                               std::to_string(detail) + ")");
+  if (code == ERR_TOKEN)
+    return set_error(AMK_E_DEVICE_FAULT,
+                     "token id out of range: " + std::to_string((int32_t)detail));
+  return set_error(AMK_E_DEVICE_FAULT, "device error code " + std::to_string(code));
+}
+
+// reset device error words, flags and the epoch after a device-side failure
+void reset_device_state(amk_model *m, hipStream_t st) {
+  (void)hipMemsetAsync(m->dm.err, 0, 4 * sizeof(uint32_t), st);
+  (void)hipMemsetAsync(m->dm.flags, 0, sizeof(uint32_t) * std::max<uint32_t>(1, m->sched.hdr.n_tasks), st);
+  (void)hipStreamSynchronize(st);
+  m->epoch = 0;
+  m->err_pending = false;
+}
+
+}  // namespace
+
+extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights *w, int32_t path,
+                                       const void *schedule_blob, size_t blob_bytes, void *stream,
+                                       amk_model **out) {
+  amk_model *m = nullptr;
+  try {
+    if (!cfg || !w || !out) return set_error(AMK_E_INVALID, "amk_model_create: null argument");
+    *out = nullptr;
+    std::string e;
+    if (!config_ok(*cfg, &e)) return set_error(AMK_E_INVALID, e);
+    if (path != AMK_PATH_MEGAKERNEL && path != AMK_PATH_UNFUSED)
+      return set_error(AMK_E_INVALID, "amk_model_create: unknown path");
+    if (cfg->head_dim != 64 && cfg->head_dim != 128)
+      return set_error(AMK_E_UNSUPPORTED, "head_dim must be 64 or 128");
+    if (cfg->wtype == AMK_WT_INT8 && (cfg->hidden % 16 || cfg->ffn % 16))
+      return set_error(AMK_E_UNSUPPORTED, "int8 weights need hidden and ffn multiples of 16");
+    if (!w->embed || !w->final_norm || !w->layers || (!cfg->tied_lm_head && !w->lm_head))
+      return set_error(AMK_E_INVALID, "amk_model_create: missing weight pointer");
+    const bool i8 = cfg->wtype == AMK_WT_INT8;
+    for (int l = 0; l < cfg->n_layers; ++l) {
+      const amk_layer_weights &lw = w->layers[l];
+      if (!lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.wg || !lw.wu || !lw.wd || !lw.attn_norm ||
+          !lw.mlp_norm)
+        return set_error(AMK_E_INVALID, "amk_model_create: missing layer weight pointer");
+      if (i8 && (!lw.sq || !lw.sk || !lw.sv || !lw.so || !lw.sg || !lw.su || !lw.sd))
+        return set_error(AMK_E_INVALID, "amk_model_create: int8 weights need scales");
+    }
+    if (i8 && !cfg->tied_lm_head && !w->lm_head_scale)
+      return set_error(AMK_E_INVALID, "amk_model_create: int8 LM head needs scales");
+
+    m = new amk_model();
+    m->cfg = *cfg;
+    m->path = path;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hip_check(hipGetDevice(&m->device), "hipGetDevice");
+    hipDeviceProp_t prop;
+    hip_check(hipGetDeviceProperties(&prop, m->device), "hipGetDeviceProperties");
+    m->n_cu = prop.multiProcessorCount;
+    int clock_khz = 0;
+    if (hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, m->device) != hipSuccess ||
+        clock_khz <= 0)
+      clock_khz = 100000;
+
+    // ---- schedule -------------------------------------------------------------------------
+    if (schedule_blob) {
+      if (!parse(schedule_blob, blob_bytes, &m->sched, &e)) {
+        free_model(m);
+        return set_error(AMK_E_SCHEDULE_REJECTED, e);
+      }
+      m->blob.assign((const uint8_t *)schedule_blob, (const uint8_t *)schedule_blob + blob_bytes);
+    } else {
+      void *b = nullptr;
+      size_t n = 0;
+      amk_status s2 = amk_schedule_build(cfg, cfg->max_batch, m->n_cu, nullptr, nullptr, &b, &n);
+      if (s2 != AMK_OK) {
+        free_model(m);
+        return s2;
+      }
+      m->blob.assign((uint8_t *)b, (uint8_t *)b + n);
+      amk_blob_free(b);
+      parse(m->blob.data(), m->blob.size(), &m->sched, &e);
+    }
+    std::string rep;
+    if (!validate_schedule(m->sched, &rep)) {
+      free_model(m);
+      return set_error(AMK_E_SCHEDULE_REJECTED, rep);
+    }
+    const BlobHeader &h = m->sched.hdr;
+    if (std::memcmp(&h.cfg, cfg, sizeof(BlobConfig)) != 0) {
+      free_model(m);
+      return set_error(AMK_E_SCHEDULE_REJECTED, "schedule was built for a different config");
+    }
+    if ((int32_t)h.batch != cfg->max_batch) {
+      free_model(m);
+      return set_error(AMK_E_SCHEDULE_REJECTED, "schedule batch differs from max_batch");
+    }
+    if (path == AMK_PATH_MEGAKERNEL && (int)h.n_cu != m->n_cu) {
+      free_model(m);
+      return set_error(AMK_E_SCHEDULE_REJECTED,
+                       "schedule targets " + std::to_string(h.n_cu) + " CUs, device has " +
+                           std::to_string(m->n_cu));
+    }
+    m->lds_bytes = h.lds_bytes;
+    if (m->lds_bytes > (uint32_t)prop.sharedMemPerBlock && prop.sharedMemPerBlock > 0) {
+      free_model(m);
+      return set_error(AMK_E_SCHEDULE_REJECTED, "schedule LDS exceeds the device limit");
+    }
+
+    // ---- weights --------------------------------------------------------------------------
+    const int L = cfg->n_layers, d = cfg->hidden, nq = cfg->n_heads, nkv = cfg->n_kv_heads,
+              hd = cfg->head_dim, F = cfg->ffn, V = cfg->vocab, B = cfg->max_batch;
+    const int qd = nq * hd, qkvr = qkv_rows(nq, nkv, hd);
+    const size_t wb = i8 ? 1 : 2;
+    DevModel &dm = m->dm;
+    dm.L = L; dm.d = d; dm.nq = nq; dm.nkv = nkv; dm.hd = hd; dm.F = F; dm.V = V;
+    dm.qkvr = qkvr; dm.qd = qd; dm.qpg = nq / nkv;
+    dm.wtype = cfg->wtype; dm.tied = cfg->tied_lm_head; dm.max_batch = B; dm.max_seq = cfg->max_seq;
+    dm.nblk = (int32_t)h.attn_blocks;
+    dm.n_lm = (int32_t)h.n_lm_tiles;
+    dm.eps = cfg->rms_eps;
+    dm.attn_scale = (float)(1.0 / std::sqrt((double)hd));
+    m->layers.resize(L);
+    m->weight_bytes = 0;
+    for (int l = 0; l < L; ++l) {
+      const amk_layer_weights &lw = w->layers[l];
+      DevLayer &dl = m->layers[l];
+      void *qkv = m->dalloc<uint8_t>((size_t)qkvr * d * wb);
+      void *gu = m->dalloc<uint8_t>((size_t)2 * F * d * wb);
+      void *o = m->dalloc<uint8_t>((size_t)d * qd * wb);
+      void *dn = m->dalloc<uint8_t>((size_t)d * F * wb);
+      std::vector<int2> pq, pk, pv, pg, pu;
+      for (int r = 0; r < qkvr; ++r) {
+        QkvRow q = qkv_decode(r, nq, nkv, hd);
+        int2 pr = make_int2(r, q.head * hd + q.dim);
+        (q.kind == KIND_Q ? pq : (q.kind == KIND_K ? pk : pv)).push_back(pr);
+      }
+      for (int i = 0; i < F; ++i) {
+        pg.push_back(make_int2(2 * i, i));
+        pu.push_back(make_int2(2 * i + 1, i));
+      }
+      gather(m, qkv, lw.wq, pq, d * wb, st);
+      gather(m, qkv, lw.wk, pk, d * wb, st);
+      gather(m, qkv, lw.wv, pv, d * wb, st);
+      gather(m, gu, lw.wg, pg, d * wb, st);
+      gather(m, gu, lw.wu, pu, d * wb, st);
+      copy_d2d(o, lw.wo, (size_t)d * qd * wb, st);
+      copy_d2d(dn, lw.wd, (size_t)d * F * wb, st);
+      dl.qkv = qkv; dl.gu = gu; dl.o = o; dl.dn = dn;
+      dl.s_qkv = dl.s_gu = dl.s_o = dl.s_dn = nullptr;
+      if (i8) {
+        float *sqkv = m->dalloc<float>(qkvr), *sgu = m->dalloc<float>(2 * F);
+        float *so = m->dalloc<float>(d), *sdn = m->dalloc<float>(d);
+        gather(m, sqkv, lw.sq, pq, 4, st);
+        gather(m, sqkv, lw.sk, pk, 4, st);
+        gather(m, sqkv, lw.sv, pv, 4, st);
+        gather(m, sgu, lw.sg, pg, 4, st);
+        gather(m, sgu, lw.su, pu, 4, st);
+        copy_d2d(so, lw.so, (size_t)d * 4, st);
+        copy_d2d(sdn, lw.sd, (size_t)d * 4, st);
+        dl.s_qkv = sqkv; dl.s_gu = sgu; dl.s_o = so; dl.s_dn = sdn;
+        m->weight_bytes += 4ull * (qkvr + 2 * F + 2 * d);
+      }
+      uint16_t *an = m->dalloc<uint16_t>(d), *mn = m->dalloc<uint16_t>(d);
+      copy_d2d(an, lw.attn_norm, (size_t)d * 2, st);
+      copy_d2d(mn, lw.mlp_norm, (size_t)d * 2, st);
+      dl.attn_norm = an;
+      dl.mlp_norm = mn;
+      m->weight_bytes += wb * ((uint64_t)qkvr * d + 2ull * F * d + (uint64_t)d * qd + (uint64_t)d * F) + 4ull * d;
+    }
+    uint16_t *emb = m->dalloc<uint16_t>((size_t)V * d);
+    copy_d2d(emb, w->embed, (size_t)V * d * 2, st);
+    uint16_t *fn = m->dalloc<uint16_t>(d);
+    copy_d2d(fn, w->final_norm, (size_t)d * 2, st);
+    dm.embed = emb;
+    dm.final_norm = fn;
+    m->weight_bytes += 2ull * d;
+    if (cfg->tied_lm_head) {
+      dm.lm = emb;
+      dm.lm_scale = nullptr;
+      m->weight_bytes += 2ull * V * d;
+    } else {
+      void *lm = m->dalloc<uint8_t>((size_t)V * d * wb);
+      copy_d2d(lm, w->lm_head, (size_t)V * d * wb, st);
+      dm.lm = lm;
+      m->weight_bytes += wb * (uint64_t)V * d;
+      if (i8) {
+        float *ls = m->dalloc<float>(V);
+        copy_d2d(ls, w->lm_head_scale, (size_t)V * 4, st);
+        dm.lm_scale = ls;
+        m->weight_bytes += 4ull * V;
+      }
+    }
+    DevLayer *d_layers = m->dalloc<DevLayer>(L);
+    hip_check(hipMemcpyAsync(d_layers, m->layers.data(), sizeof(DevLayer) * L,
+                             hipMemcpyHostToDevice, st), "hipMemcpyAsync");
+    dm.layers = d_layers;
+
+    // ---- tables and scratch ----------------------------------------------------------------
+    std::vector<float2> rope((size_t)cfg->max_seq * (hd / 2));
+    for (int p = 0; p < cfg->max_seq; ++p)
+      for (int j = 0; j < hd / 2; ++j) {
+        const double ang = (double)p * std::pow((double)cfg->rope_theta, -2.0 * j / hd);
+        rope[(size_t)p * (hd / 2) + j] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+      }
+    float2 *d_rope = m->dalloc<float2>(rope.size());
+    hip_check(hipMemcpyAsync(d_rope, rope.data(), rope.size() * sizeof(float2),
+                             hipMemcpyHostToDevice, st), "hipMemcpyAsync");
+    dm.rope = d_rope;
+    const int nblk = dm.nblk;
+    dm.h = m->dalloc<float>((size_t)(2 * L + 1) * B * d);
+    dm.q = m->dalloc<float>((size_t)L * B * qd);
+    dm.part = m->dalloc<float>((size_t)L * B * nq * nblk * (hd + 2));
+    dm.a = m->dalloc<float>((size_t)L * B * F);
+    dm.logits = m->dalloc<float>((size_t)B * V);
+    m->n_lm_uf = (V + kUfRowsPerBlock - 1) / kUfRowsPerBlock;
+    dm.amax = m->dalloc<float2>((size_t)std::max<int>(m->n_lm_uf, dm.n_lm) * B);
+    dm.flags = m->dalloc<uint32_t>(std::max<uint32_t>(1, h.n_tasks));
+    dm.err = m->dalloc<uint32_t>(4);
+    const int kmax = std::max(std::max(d, qd), F);
+    dm.xn = m->dalloc<float>((size_t)B * kmax);
+    dm.y = m->dalloc<float>((size_t)B * std::max(std::max(qkvr, 2 * F), std::max(V, d)));
+    dm.o = m->dalloc<float>((size_t)B * qd);
+    hip_check(hipMemsetAsync(dm.flags, 0, sizeof(uint32_t) * std::max<uint32_t>(1, h.n_tasks), st), "hipMemsetAsync");
+    hip_check(hipMemsetAsync(dm.err, 0, 16, st), "hipMemsetAsync");
+    // task tables
+    std::vector<uint32_t> offs(h.n_cu + 1);
+    std::vector<Task> tasks;
+    tasks.reserve(h.n_tasks);
+    for (uint32_t c = 0; c < h.n_cu; ++c) {
+      offs[c] = (uint32_t)tasks.size();
+      for (const Task &t : m->sched.per_cu[c]) tasks.push_back(t);
+    }
+    offs[h.n_cu] = (uint32_t)tasks.size();
+    Task *d_tasks = m->dalloc<Task>(tasks.size());
+    uint32_t *d_offs = m->dalloc<uint32_t>(offs.size());
+    hip_check(hipMemcpyAsync(d_tasks, tasks.data(), tasks.size() * sizeof(Task),
+                             hipMemcpyHostToDevice, st), "hipMemcpyAsync");
+    hip_check(hipMemcpyAsync(d_offs, offs.data(), offs.size() * 4, hipMemcpyHostToDevice, st),
+              "hipMemcpyAsync");
+    dm.tasks = d_tasks;
+    dm.offsets = d_offs;
+    double wd_ms = 2000.0;
+    if (const char *env = std::getenv("AMK_WATCHDOG_MS")) wd_ms = std::atof(env);
+    dm.timeout_ticks = (uint64_t)(wd_ms * clock_khz);
+    m->d_dm = m->dalloc<DevModel>(1);
+    hip_check(hipMemcpyAsync(m->d_dm, &dm, sizeof dm, hipMemcpyHostToDevice, st), "hipMemcpyAsync");
+
+    const int qmax = qmax_for(dm.qpg);
+    m->mk = pick_megakernel(cfg->wtype, hd, qmax);
+    m->uf_attn = pick_uf_attn(hd, qmax);
+    if (!m->mk || !m->uf_attn) throw std::runtime_error("no kernel instance for this shape");
+    m->uf_attn_lds = 4u * (64 * 8 + (uint32_t)lds_attn_floats(1, qmax, hd));
+    if (path == AMK_PATH_MEGAKERNEL) {
+      hip_check(hipFuncSetAttribute((const void *)m->mk, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)m->lds_bytes), "hipFuncSetAttribute");
+      int per_cu = 0;
+      hip_check(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)m->mk, kThreads,
+                                                             m->lds_bytes), "occupancy");
+      if (per_cu < 1) throw std::runtime_error("megakernel workgroup does not fit on a CU");
+    } else {
+      const uint32_t gl = 4u * (64 * 8 + 8 * kUfRowsPerBlock + (uint32_t)(B * kmax));
+      for (int wt = 0; wt < 2; ++wt)
+        for (int mode = 0; mode < 3; ++mode)
+          hip_check(hipFuncSetAttribute((const void *)pick_uf_gemv(wt, mode),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)gl),
+                    "hipFuncSetAttribute");
+      hip_check(hipFuncSetAttribute((const void *)m->uf_attn,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)m->uf_attn_lds),
+                "hipFuncSetAttribute");
+    }
+    hip_check(hipHostMalloc((void **)&m->h_err, 16, hipHostMallocDefault), "hipHostMalloc");
+    std::memset(m->h_err, 0, 16);
+    hip_check(hipEventCreateWithFlags(&m->err_event, hipEventDisableTiming), "hipEventCreate");
+    hip_check(hipStreamSynchronize(st), "hipStreamSynchronize");
+    *out = m;
+    clear_error();
+    return AMK_OK;
+  } catch (const std::bad_alloc &) {
+    free_model(m);
+    return set_error(AMK_E_OOM, "amk_model_create: allocation failed");
+  } catch (const HipError &ex) {
+    free_model(m);
+    return set_error(AMK_E_HIP, ex.what());
+  } catch (const std::exception &ex) {
+    free_model(m);
+    return set_error(AMK_E_INVALID, std::string("amk_model_create: ") + ex.what());
+  }
+}
+
+extern "C" amk_status amk_kv_bytes(const amk_model *m, int32_t batch, int32_t max_seq, size_t *bytes) {
+  if (!m || !bytes) return set_error(AMK_E_INVALID, "amk_kv_bytes: null argument");
+  if (batch < 1 || batch > m->cfg.max_batch) return set_error(AMK_E_INVALID, "amk_kv_bytes: bad batch");
+  if (max_seq < 1 || max_seq > m->cfg.max_seq) return set_error(AMK_E_INVALID, "amk_kv_bytes: bad max_seq");
+  *bytes = (size_t)m->cfg.n_layers * 2 * batch * m->cfg.n_kv_heads * (size_t)max_seq * m->cfg.head_dim * 2;
+  clear_error();
+  return AMK_OK;
+}
+
+extern "C" amk_status amk_kv_alloc(amk_model *m, int32_t batch, int32_t max_seq, void *d_buf,
+                                   size_t buf_bytes, amk_kv **out) {
+  AMK_API_BEGIN
+  if (!out) return set_error(AMK_E_INVALID, "amk_kv_alloc: null output");
+  *out = nullptr;
+  size_t need = 0;
+  amk_status st = amk_kv_bytes(m, batch, max_seq, &need);
+  if (st != AMK_OK) return st;
+  amk_kv *kv = new amk_kv();
+  kv->m = m;
+  kv->batch = batch;
+  kv->max_seq = max_seq;
+  kv->bytes = need;
+  if (d_buf) {
+    if (buf_bytes < need) {
+      delete kv;
+      return set_error(AMK_E_CAPACITY, "amk_kv_alloc: buffer smaller than amk_kv_bytes");
+    }
+    kv->data = d_buf;
+  } else {
+    if (hipMalloc(&kv->data, need) != hipSuccess) {
+      delete kv;
+      return set_error(AMK_E_OOM, "amk_kv_alloc: device allocation failed");
+    }
+    kv->owned = true;
+    if (hipMemset(kv->data, 0, need) != hipSuccess) {
+      (void)hipFree(kv->data);
+      delete kv;
+      return set_error(AMK_E_HIP, "amk_kv_alloc: hipMemset failed");
+    }
+  }
+  *out = kv;
+  clear_error();
+  return AMK_OK;
+  AMK_API_END
+}
+
+extern "C" amk_status amk_kv_data(const amk_kv *kv, void **d_ptr) {
+  if (!kv || !d_ptr) return set_error(AMK_E_INVALID, "amk_kv_data: null argument");
+  *d_ptr = kv->data;
+  return AMK_OK;
+}
+
+extern "C" amk_status amk_kv_free(amk_kv *kv) {
+  if (!kv) return set_error(AMK_E_INVALID, "amk_kv_free: null argument");
+  if (kv->owned) (void)hipFree(kv->data);
+  delete kv;
+  return AMK_OK;
+}
+
+static void launch_unfused(amk_model *m, const StepArgs &s, hipStream_t st) {
+  const DevModel &dm = m->dm;
+  const DevModel *g = m->d_dm;
+  const int B = s.batch, L = dm.L, d = dm.d;
+  const int wt = dm.wtype;
+  const uint32_t gl = 4u * (64 * 8 + 8 * kUfRowsPerBlock + (uint32_t)(B * std::max(std::max(d, dm.qd), dm.F)));
+  auto grid = [](int rows) { return dim3((rows + kUfRowsPerBlock - 1) / kUfRowsPerBlock); };
+  float *h = dm.h;
+  auto hslot = [&](int slot) { return h + (size_t)slot * dm.max_batch * d; };
+  hipLaunchKernelGGL(amk_uf_embed, dim3((d + 255) / 256, B), dim3(256), 0, st, g, s);
+  for (int l = 0; l < L; ++l) {
+    const DevLayer &ly = m->layers[l];
+    hipLaunchKernelGGL(amk_uf_rmsnorm, dim3(B), dim3(1024), 0, st, g, (const float *)hslot(2 * l), ly.attn_norm, dm.xn);
+    hipLaunchKernelGGL(pick_uf_gemv(wt, 0), grid(dm.qkvr), dim3(kUfThreads), gl, st, g, s, ly.qkv, ly.s_qkv, d, dm.qkvr, (const float *)dm.xn, dm.y, (const float *)nullptr, (float *)nullptr);
+    hipLaunchKernelGGL(amk_uf_rope_kv, dim3((dm.qkvr / 2 + 255) / 256, B), dim3(256), 0, st, g, s, l);
+    hipLaunchKernelGGL(m->uf_attn, dim3(dm.nkv, dm.nblk), dim3(kThreads), m->uf_attn_lds, st, g, s, l);
+    hipLaunchKernelGGL(amk_uf_combine, dim3(dm.nq, B), dim3(128), 0, st, g, l);
+    hipLaunchKernelGGL(pick_uf_gemv(wt, 1), grid(d), dim3(kUfThreads), gl, st, g, s, ly.o, ly.s_o, dm.qd, d, (const float *)dm.o, (float *)nullptr, (const float *)hslot(2 * l), hslot(2 * l + 1));
+    hipLaunchKernelGGL(amk_uf_rmsnorm, dim3(B), dim3(1024), 0, st, g, (const float *)hslot(2 * l + 1), ly.mlp_norm, dm.xn);
+    hipLaunchKernelGGL(pick_uf_gemv(wt, 0), grid(2 * dm.F), dim3(kUfThreads), gl, st, g, s, ly.gu, ly.s_gu, d, 2 * dm.F, (const float *)dm.xn, dm.y, (const float *)nullptr, (float *)nullptr);
+    hipLaunchKernelGGL(amk_uf_swiglu, dim3(std::min(1024, (B * dm.F + 255) / 256)), dim3(256), 0, st, g, l, B);
+    hipLaunchKernelGGL(pick_uf_gemv(wt, 1), grid(d), dim3(kUfThreads), gl, st, g, s, ly.dn, ly.s_dn, dm.F, d, (const float *)(dm.a + (size_t)l * dm.max_batch * dm.F), (float *)nullptr, (const float *)hslot(2 * l + 1), hslot(2 * l + 2));
+  }
+  hipLaunchKernelGGL(amk_uf_rmsnorm, dim3(B), dim3(1024), 0, st, g, (const float *)hslot(2 * L), dm.final_norm, dm.xn);
+  const int lm_wt = dm.tied ? 0 : wt;
+  hipLaunchKernelGGL(pick_uf_gemv(lm_wt, 2), grid(dm.V), dim3(kUfThreads), gl, st, g, s, dm.lm, dm.lm_scale, d, dm.V, (const float *)dm.xn, (float *)nullptr, (const float *)nullptr, (float *)nullptr);
+  hipLaunchKernelGGL(amk_uf_argmax, dim3(1), dim3(64), 0, st, g, s, m->n_lm_uf);
+}
+
+extern "C" amk_status amk_decode_step(amk_model *m, amk_kv *kv, const int32_t *d_tokens,
+                                      int32_t pos, int32_t batch, float *d_logits,
+                                      int32_t *d_next, void *stream) {
+  AMK_API_BEGIN
+  if (!m || !kv || !d_tokens || !d_next) return set_error(AMK_E_INVALID, "amk_decode_step: null argument");
+  if (kv->m != m) return set_error(AMK_E_INVALID, "amk_decode_step: KV cache belongs to another model");
+  if (batch < 1 || batch > m->cfg.max_batch || batch > kv->batch)
+    return set_error(AMK_E_CAPACITY, "amk_decode_step: batch exceeds max_batch or the KV cache");
+  if (pos < 0 || pos >= kv->max_seq || pos >= m->cfg.max_seq)
+    return set_error(AMK_E_CAPACITY, "amk_decode_step: position beyond max_seq");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (m->epoch >= 0x7ffffff0u) {  // keep the signed flag comparison unambiguous
+    hip_check(hipMemsetAsync(m->dm.flags, 0, sizeof(uint32_t) * std::max<uint32_t>(1, m->sched.hdr.n_tasks), st), "hipMemsetAsync");
+    m->epoch = 0;
+  }
+  StepArgs s;
+  s.tokens = d_tokens;
+  s.logits = d_logits;
+  s.next = d_next;
+  s.kv = static_cast<uint16_t *>(kv->data);
+  s.kv_batch = kv->batch;
+  s.kv_max_seq = kv->max_seq;
+  s.pos = pos;
+  s.batch = batch;
+  s.epoch = ++m->epoch;
+  if (m->path == AMK_PATH_MEGAKERNEL) {
+    const DevModel *g = m->d_dm;
+    void *args[] = {(void *)&g, (void *)&s};
+    hipError_t e = hipLaunchCooperativeKernel((const void *)m->mk, dim3(m->n_cu), dim3(kThreads),
+                                              args, m->lds_bytes, st);
+    if (e != hipSuccess) return set_error(AMK_E_HIP, std::string("megakernel launch: ") + hipGetErrorString(e));
+  } else {
+    launch_unfused(m, s, st);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return set_error(AMK_E_HIP, std::string("unfused launch: ") + hipGetErrorString(e));
+  }
+  clear_error();
+  return AMK_OK;
+  AMK_API_END
+}
+
+extern "C" amk_status amk_sync(amk_model *m, void *stream) {
+  AMK_API_BEGIN
+  if (!m) return set_error(AMK_E_INVALID, "amk_sync: null model");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return set_error(AMK_E_HIP, std::string("amk_sync: ") + hipGetErrorString(e));
+  uint32_t err[4];
+  e = hipMemcpy(err, m->dm.err, 16, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return set_error(AMK_E_HIP, std::string("amk_sync: ") + hipGetErrorString(e));
+  m->err_pending = false;
+  if (err[0]) {
+    reset_device_state(m, st);
+    std::memset(m->h_err, 0, 16);
+    return map_device_error(err[0], err[2], err[3]);
+  }
+  clear_error();
+  return AMK_OK;
+  AMK_API_END
+}
+
+extern "C" amk_status amk_model_get_info(const amk_model *m, amk_model_info *out) {
+  if (!m || !out) return set_error(AMK_E_INVALID, "amk_model_get_info: null argument");
+  out->n_cu = m->n_cu;
+  out->n_tasks = (int32_t)m->sched.hdr.n_tasks;
+  out->launches_per_step = m->path == AMK_PATH_MEGAKERNEL ? 1 : 1 + 10 * m->cfg.n_layers + 3;
+  out->lds_bytes = (int32_t)m->lds_bytes;
+  out->attn_blocks = (int32_t)m->sched.hdr.attn_blocks;
+  out->path = m->path;
+  out->weight_bytes = m->weight_bytes;
+  out->predicted_us = m->sched.hdr.predicted_us;
+  return AMK_OK;
+}
+
+extern "C" amk_status amk_model_get_schedule(const amk_model *m, void **blob, size_t *bytes) {
+  if (!m || !blob || !bytes) return set_error(AMK_E_INVALID, "amk_model_get_schedule: null argument");
+  void *p = std::malloc(m->blob.size());
+  if (!p) return set_error(AMK_E_OOM, "amk_model_get_schedule: out of host memory");
+  std::memcpy(p, m->blob.data(), m->blob.size());
+  *blob = p;
+  *bytes = m->blob.size();
+  return AMK_OK;
+}
+
+extern "C" amk_status amk_destroy(amk_model *m) {
+  if (!m) return set_error(AMK_E_INVALID, "amk_destroy: null model");
+  (void)hipDeviceSynchronize();
+  free_model(m);
+  return AMK_OK;
+}

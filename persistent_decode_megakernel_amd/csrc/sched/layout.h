@@ -1,0 +1,140 @@
+// Packed weight-row layouts and the frozen schedule format, shared by the host-side schedule
+// layer, the runtime (repacking) and the device kernels.
+//
+// Packed QKV matrix (rows = (n_heads + 2 n_kv_heads) * head_dim, cols = hidden): KV-group major.
+// Group g holds, in order, the rows of its q heads, then of k head g, then of v head g. Inside
+// a rotary head (q or k) rows are pair-interleaved: packed row 2j is dimension j and packed row
+// 2j+1 is dimension j + head_dim/2, so any tile that starts and ends on an even row holds whole
+// RoPE pairs. V rows keep their natural order. Every row a KV group needs is therefore one
+// contiguous packed range, which lets attention tasks wait on a contiguous range of tiles.
+//
+// Packed gate/up matrix (rows = 2 ffn): row 2i is gate row i, row 2i+1 is up row i, so an
+// even-aligned tile can apply SwiGLU on its own outputs.
+#pragma once
+#include <stdint.h>
+
+#ifdef __HIPCC__
+#define AMK_HD __host__ __device__ __forceinline__
+#else
+#define AMK_HD inline
+#endif
+
+namespace amk {
+
+enum QkvKind : int32_t { KIND_Q = 0, KIND_K = 1, KIND_V = 2 };
+
+struct QkvRow {
+  int32_t kind;  // QkvKind
+  int32_t head;  // q head index (KIND_Q) or kv head index (KIND_K / KIND_V)
+  int32_t dim;   // dimension inside the head
+};
+
+AMK_HD int32_t qkv_group_rows(int32_t nq, int32_t nkv, int32_t hd) { return (nq / nkv + 2) * hd; }
+AMK_HD int32_t qkv_rows(int32_t nq, int32_t nkv, int32_t hd) { return (nq + 2 * nkv) * hd; }
+
+AMK_HD QkvRow qkv_decode(int32_t r, int32_t nq, int32_t nkv, int32_t hd) {
+  const int32_t qpg = nq / nkv;
+  const int32_t grows = (qpg + 2) * hd;
+  const int32_t g = r / grows;
+  const int32_t rem = r - g * grows;
+  const int32_t s = rem / hd;
+  const int32_t t = rem - s * hd;
+  QkvRow out;
+  if (s < qpg) {
+    out.kind = KIND_Q;
+    out.head = g * qpg + s;
+  } else {
+    out.kind = (s == qpg) ? KIND_K : KIND_V;
+    out.head = g;
+  }
+  out.dim = (out.kind == KIND_V) ? t : ((t & 1) ? (hd / 2 + t / 2) : (t / 2));
+  return out;
+}
+
+// Source row (in the caller's wq / wk / wv matrix) of packed QKV row r.
+AMK_HD int32_t qkv_source_row(int32_t r, int32_t nq, int32_t nkv, int32_t hd) {
+  QkvRow q = qkv_decode(r, nq, nkv, hd);
+  return q.head * hd + q.dim;
+}
+
+// ------------------------------------------------------------------------------------------
+// Frozen schedule format
+// ------------------------------------------------------------------------------------------
+constexpr uint32_t kBlobMagic = 0x534b4d41u;  // "AMKS"
+constexpr uint32_t kBlobVersion = 1;
+
+enum TaskType : uint8_t { T_GEMV = 1, T_ATTN = 2, T_ARGMAX = 3 };
+enum MatId : uint8_t { M_QKV = 0, M_O = 1, M_GU = 2, M_D = 3, M_LM = 4 };
+
+// One tile task. The device reads these with scalar loads; the order of a CU's tasks in the
+// blob is the order the CU executes them. A task may start once every task whose id lies in
+// [w0_lo, w0_hi) or [w1_lo, w1_hi) has published flag >= the step's epoch; on completion it
+// publishes flags[id] = epoch.
+struct Task {
+  uint8_t type;   // TaskType
+  uint8_t mat;    // MatId (T_GEMV)
+  uint16_t layer;
+  uint32_t id;
+  uint32_t a0, a1;  // T_GEMV: packed rows [a0, a1); T_ATTN: kv group a0, KV block a1
+  uint32_t w0_lo, w0_hi;
+  uint32_t w1_lo, w1_hi;
+  uint32_t aux0;  // T_GEMV + M_LM: argmax partial slot; T_ATTN: blocks per group; T_ARGMAX: slots
+  uint32_t aux1, aux2;  // T_GEMV: K range [aux1, aux2) (always the full row in this version)
+  uint32_t aux3;
+};
+static_assert(sizeof(Task) == 48, "task record is 48 bytes");
+
+struct BlobConfig {  // plain copy of amk_config (kept layout-stable inside the blob)
+  int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab;
+  float rms_eps, rope_theta;
+  int32_t tied_lm_head, wtype, max_batch, max_seq;
+};
+
+struct BlobHeader {
+  uint32_t magic, version;
+  uint32_t n_cu, n_tasks;
+  uint32_t batch, attn_blocks;
+  uint32_t n_lm_tiles, lds_bytes;
+  uint32_t ctx_hint, placement;
+  uint32_t offsets_off, tasks_off;  // byte offsets of uint32 offsets[n_cu+1] and Task[n_tasks]
+  uint32_t total_bytes, rotate;
+  BlobConfig cfg;
+  double predicted_us;
+};
+
+// Attention KV block b of nblk over a context of ctx positions: [lo, hi).
+AMK_HD void attn_block_range(int32_t ctx, int32_t nblk, int32_t b, int32_t *lo, int32_t *hi) {
+  *lo = (int32_t)(((int64_t)b * ctx) / nblk);
+  *hi = (int32_t)(((int64_t)(b + 1) * ctx) / nblk);
+}
+
+}  // namespace amk
+
+namespace amk {
+// LDS layout of the megakernel workgroup (bytes), shared by the builder (recorded in the blob,
+// checked by the validator) and the runtime (dynamic LDS at launch).
+//   xs : batch x max(hidden, n_heads*head_dim, ffn) float  -- staged GEMV input vector(s)
+//   ys : batch x max_tile_rows float                        -- GEMV tile outputs before epilogue
+//   red: 64 x 8 float                                       -- cross-wave reductions
+// Attention tasks reuse the xs region (q, scores, partial accumulators).
+constexpr int32_t kWaves = 16;
+constexpr int32_t kThreads = kWaves * 64;
+constexpr int32_t kAttnRowsPerChunk = 256;  // KV rows staged per attention chunk
+
+AMK_HD int32_t lds_xs_floats(int32_t batch, int32_t hidden, int32_t qdim, int32_t ffn) {
+  int32_t k = hidden > qdim ? hidden : qdim;
+  k = k > ffn ? k : ffn;
+  return batch * k;
+}
+AMK_HD int32_t lds_attn_floats(int32_t batch, int32_t qpg, int32_t hd) {
+  // q [B][qpg][hd] + scores [B][qpg][chunk] + partial acc [waves][B*qpg*hd]
+  return batch * qpg * hd + batch * qpg * kAttnRowsPerChunk + kWaves * batch * qpg * hd;
+}
+AMK_HD int32_t lds_bytes_for(int32_t batch, int32_t hidden, int32_t qdim, int32_t ffn,
+                             int32_t qpg, int32_t hd, int32_t max_tile_rows) {
+  int32_t a = lds_xs_floats(batch, hidden, qdim, ffn);
+  int32_t b = lds_attn_floats(batch, qpg, hd);
+  int32_t region = a > b ? a : b;
+  return 4 * (region + batch * max_tile_rows + 64 * 8);
+}
+}  // namespace amk

@@ -1,0 +1,67 @@
+// Host-side schedule layer: in-memory schedule, blob (de)serialisation, task footprints.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../../include/amk.h"
+#include "layout.h"
+
+namespace amk {
+
+// LDS the megakernel declares per workgroup (bytes); the validator checks it against the CU.
+constexpr uint32_t kMaxLdsBytes = 160 * 1024;
+
+struct Schedule {
+  BlobHeader hdr{};
+  std::vector<std::vector<Task>> per_cu;  // program order per CU
+
+  uint32_t n_tasks() const;
+};
+
+// Serialise / parse. parse() checks only framing (magic, version, sizes); validate() the rest.
+std::vector<uint8_t> serialize(const Schedule &s);
+bool parse(const void *blob, size_t bytes, Schedule *out, std::string *err);
+
+// Buffers whose contents a decode step produces (all other inputs are read-only for a step).
+enum BufId : int32_t {
+  BUF_H = 0,       // residual stream h[s], s = 0..2L: [B][d]; h[0] is the embedding gather
+  BUF_Q = 1,       // q after RoPE, per layer: [B][nq*hd]
+  BUF_KVNEW = 2,   // the KV cache slot being appended, per layer: [2][B][nkv][hd]
+  BUF_PART = 3,    // attention partials, per layer: [B][nq][nblk][hd+2]
+  BUF_A = 4,       // SwiGLU output, per layer: [B][F]
+  BUF_LOGITS = 5,  // [B][V]
+  BUF_AMAX = 6,    // argmax partials [slots][B]
+  BUF_NEXT = 7,    // [B]
+};
+
+struct Access {
+  int32_t buf;    // BufId
+  int32_t index;  // layer (BUF_Q/KVNEW/PART/A) or residual slot (BUF_H); 0 otherwise
+  int64_t lo, hi; // element range [lo, hi)
+  bool write;
+};
+
+// Read/write footprint of a task, derived from the task's own fields and the config. Reads of
+// the embedding row (h[0]), weights and KV history are not listed: nothing in a step writes them.
+// Returns false (and err) if the task's fields are malformed for the config.
+bool footprint(const BlobHeader &h, const Task &t, std::vector<Access> *acc, std::string *err);
+
+// Algorithmic HBM bytes a task streams (weights, scales, KV rows) at context length ctx, and the
+// activation bytes it re-reads from cache. Used by the cost model.
+void task_bytes(const BlobHeader &h, const Task &t, int32_t ctx, double *hbm, double *act);
+
+double predict_makespan(const Schedule &s, const amk_cost_model &cost, int32_t ctx);
+
+amk_cost_model default_cost_model();
+
+Schedule build_schedule(const amk_config &cfg, int32_t batch, int32_t n_cu,
+                        const amk_sched_params &p);
+
+bool validate_schedule(const Schedule &s, std::string *report);
+bool simulate_schedule(const Schedule &s, std::string *report, int32_t max_delay_runs);
+
+bool config_ok(const amk_config &c, std::string *err);
+
+}  // namespace amk

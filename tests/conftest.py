@@ -26,3 +26,13 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+@pytest.fixture(scope="session")
+def libamk():
+    """The in-tree libamk.so, built first if it is missing."""
+    from persistent_decode_megakernel_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from persistent_decode_megakernel_amd import build
+        build.build()
+    return _lib.load()

@@ -1,0 +1,108 @@
+"""Shared driver for GPU parity tests: runs the library and the CPU oracle side by side on the same
+seeded inputs (logits within 3e-2 max-abs; greedy ids equal wherever the oracle's top-2 margin
+exceeds 0.05)."""
+from __future__ import annotations
+
+import sys
+import time
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+import oracle
+from persistent_decode_megakernel_amd import synth
+from persistent_decode_megakernel_amd.model import Model
+
+LOGIT_TOL = 3e-2
+MARGIN = 0.05
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@dataclass
+class Report:
+    steps: int = 0
+    max_abs: float = 0.0
+    tokens_checked: int = 0
+    token_mismatch: List[tuple] = field(default_factory=list)
+    kv_max_rel: float = 0.0
+
+
+def bf16_close(gpu_bits: np.ndarray, ref_bits: np.ndarray) -> float:
+    """Largest |a - b| / max(|b|, 1e-3) between two bf16 arrays (a 1-ulp rounding flip is ~4e-3)."""
+    a = oracle.bf16_to_float(gpu_bits, np.float64)
+    b = oracle.bf16_to_float(ref_bits, np.float64)
+    return float(np.max(np.abs(a - b) / np.maximum(np.abs(b), 1e-3))) if a.size else 0.0
+
+
+def teacher_forced(cfg: synth.Config, path: str = "megakernel", seed: int = 0,
+                   n_calls: Optional[int] = None, random_gains: bool = False,
+                   oracle_dtype=np.float64, weights: Optional[synth.Weights] = None,
+                   first_pos: Optional[int] = None, check_kv: bool = True,
+                   model: Optional[Model] = None) -> Report:
+    """Feed the oracle's tokens (prompt ids, then the oracle's argmax) to both sides."""
+    t0 = time.time()
+    w = weights if weights is not None else synth.make_weights(cfg, seed, random_gains, threads=16)
+    params, wn = synth.oracle_inputs(w)
+    dec = oracle.Decoder(params, wn, dtype=oracle_dtype)
+    n = n_calls if n_calls is not None else cfg.n_calls
+    p0 = cfg.first_pos if first_pos is None else first_pos
+    max_seq = max(cfg.max_seq, p0 + n + 1)
+    kv_host = synth.make_kv(cfg, max_seq, seed, threads=16)
+    kv_np = synth.bf16_to_numpy_bits(kv_host).copy()
+    toks = synth.make_tokens(cfg, seed).numpy()  # [B, prompt or 1]
+    log(f"  [{cfg.name}/{path}] inputs ready in {time.time() - t0:.1f}s")
+    own = model is None
+    if own:
+        model = Model(cfg, w, path=path, max_seq=max_seq)
+    kv = model.kv(cfg.batch, max_seq)
+    kv.tensor.copy_(kv_host.to(kv.tensor.device))
+    rep = Report()
+    tok = toks[:, 0].astype(np.int64)
+    d_logits = torch.empty((cfg.batch, cfg.vocab), dtype=torch.float32, device="cuda")
+    for i in range(n):
+        pos = p0 + i
+        lo = dec.step(kv_np, tok, pos)
+        d_tok = torch.from_numpy(tok.astype(np.int32)).cuda()
+        nxt = model.step(kv, d_tok, pos, d_logits)
+        model.sync()
+        lg = d_logits.cpu().numpy().astype(np.float64)
+        err = float(np.max(np.abs(lg - lo)))
+        rep.max_abs = max(rep.max_abs, err)
+        ids_o = oracle.argmax_lowest(lo)
+        marg = oracle.top2_margin(lo)
+        ids_g = nxt.cpu().numpy()
+        for b in range(cfg.batch):
+            if marg[b] > MARGIN:
+                rep.tokens_checked += 1
+                if ids_g[b] != ids_o[b]:
+                    rep.token_mismatch.append((i, b, int(ids_g[b]), int(ids_o[b]), float(marg[b])))
+        rep.steps += 1
+        if cfg.prompt and i + 1 < cfg.prompt:
+            tok = toks[:, i + 1].astype(np.int64)
+        else:
+            tok = ids_o.astype(np.int64)
+        if (i + 1) % 8 == 0 or i == n - 1:
+            log(f"  [{cfg.name}/{path}] step {i + 1}/{n} max_abs {rep.max_abs:.2e} "
+                f"checked {rep.tokens_checked} mismatches {len(rep.token_mismatch)}")
+    if check_kv:
+        g = synth.bf16_to_numpy_bits(kv.tensor.cpu())
+        sl = (slice(None),) * 4 + (slice(p0, p0 + n),)
+        rep.kv_max_rel = bf16_close(g[sl], kv_np[sl])
+        # history untouched
+        assert np.array_equal(g[..., :p0, :], kv_np[..., :p0, :]), "KV history was modified"
+    kv.close()
+    if own:
+        model.close()
+    return rep
+
+
+def assert_parity(rep: Report):
+    assert rep.max_abs <= LOGIT_TOL, f"logits max-abs {rep.max_abs} > {LOGIT_TOL}"
+    assert not rep.token_mismatch, f"greedy ids differ at confident steps: {rep.token_mismatch[:5]}"
+    assert rep.kv_max_rel < 2e-2, f"appended KV rows differ: max rel {rep.kv_max_rel}"

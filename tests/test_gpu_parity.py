@@ -1,0 +1,90 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI (GPU only)."""
+import numpy as np
+import pytest
+import torch
+
+from persistent_decode_megakernel_amd import synth
+from persistent_decode_megakernel_amd.model import Model
+
+from gpu_helpers import assert_parity, log, teacher_forced
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("path", ["megakernel", "unfused"])
+def test_tiny_teacher_forced(path):
+    """Tiny config: 32 prompt ids fed one by one, then 16 greedy steps (47 calls), p = 0..46."""
+    rep = teacher_forced(synth.get_config("tiny"), path)
+    log(f"tiny/{path}: {rep}")
+    assert rep.steps == 47
+    assert_parity(rep)
+
+
+@pytest.mark.parametrize("path", ["megakernel", "unfused"])
+def test_tiny_random_gains(path):
+    """Norm gains 1 + N(0, 0.02): a kernel that ignored a gain would fail here."""
+    rep = teacher_forced(synth.get_config("tiny"), path, seed=1, n_calls=12, random_gains=True)
+    assert_parity(rep)
+
+
+def test_tiny_free_running_matches_oracle_until_low_margin():
+    import oracle
+    cfg = synth.get_config("tiny")
+    w = synth.make_weights(cfg, 2)
+    params, wn = synth.oracle_inputs(w)
+    dec = oracle.Decoder(params, wn)
+    kv_np = np.zeros((cfg.n_layers, 2, 1, cfg.n_kv_heads, cfg.max_seq, cfg.head_dim), np.uint16)
+    toks = synth.make_tokens(cfg, 2).numpy()[0]
+    model = Model(cfg, w)
+    kv = model.kv()
+    d_tok = torch.tensor([int(toks[0])], dtype=torch.int32, device="cuda")
+    gpu_ids, ora_ids, margins = [], [], []
+    tok = int(toks[0])
+    for i in range(cfg.n_calls):
+        lo = dec.step(kv_np, np.array([tok]), i)
+        nxt = model.step(kv, d_tok, i, next_out=None)
+        ora = int(oracle.argmax_lowest(lo)[0])
+        margins.append(float(oracle.top2_margin(lo)[0]))
+        if i + 1 < cfg.prompt:
+            tok = int(toks[i + 1])
+            d_tok = torch.tensor([tok], dtype=torch.int32, device="cuda")
+        else:
+            gpu_ids.append(int(nxt.item()))
+            ora_ids.append(ora)
+            tok = ora
+            d_tok = nxt  # on-device greedy chaining
+        model.sync()
+    gen_margins = margins[cfg.prompt - 1:]
+    for i, (g, o) in enumerate(zip(gpu_ids, ora_ids)):
+        if gen_margins[i] <= 0.05:
+            break
+        assert g == o, f"generated token {i}: gpu {g} oracle {o}"
+    kv.close()
+    model.close()
+
+
+def test_smollm2_135m_teacher_forced():
+    rep = teacher_forced(synth.get_config("smollm2_135m"), "megakernel", n_calls=8)
+    log(f"135m: {rep}")
+    assert_parity(rep)
+
+
+def test_tinyllama_1b_teacher_forced():
+    rep = teacher_forced(synth.get_config("tinyllama_1b"), "megakernel", n_calls=3,
+                         oracle_dtype=np.float32)
+    log(f"1.1b: {rep}")
+    assert_parity(rep)
+
+
+@pytest.mark.parametrize("pos", [0, 1, 5])
+def test_first_positions_and_empty_kv_blocks(pos):
+    """ctx = pos + 1 smaller than the number of KV blocks: most blocks are empty."""
+    cfg = synth.get_config("smollm2_135m").replace(prefill=pos)
+    rep = teacher_forced(cfg, "megakernel", n_calls=2, first_pos=pos)
+    assert_parity(rep)
+
+
+def test_last_position():
+    cfg = synth.get_config("tiny")
+    rep = teacher_forced(cfg.replace(prefill=40, prompt=0, steps=7), "megakernel", n_calls=7)
+    assert_parity(rep)

@@ -1,0 +1,149 @@
+"""Schedule layer (host only): real lowerings validate and simulate clean; adversarial mutants
+that the simulator finds unsafe are all rejected by the static validator (no false accepts)."""
+import random
+
+import numpy as np
+import pytest
+
+from persistent_decode_megakernel_amd import _lib, synth
+from persistent_decode_megakernel_amd import blob as B
+
+CONFIGS = ["tiny", "smollm2_135m", "tinyllama_1b", "llama2_7b", "llama2_7b_w8a16"]
+
+
+@pytest.mark.parametrize("name", CONFIGS)
+def test_real_lowerings_validate(libamk, name):
+    cfg = synth.get_config(name)
+    c = _lib.make_config(cfg)
+    for n_cu in (256, 304, 80):
+        blob = _lib.schedule_build(c, cfg.batch, n_cu)
+        st, rep = _lib.schedule_validate(blob)
+        assert st == _lib.AMK_OK, rep
+        b = B.Blob(blob)
+        assert b.hdr.n_cu == n_cu and b.n_tasks == b.hdr.n_tasks
+        ids = np.sort(b.all_tasks()["id"])
+        assert np.array_equal(ids, np.arange(b.n_tasks))
+        assert b.hdr.lds_bytes <= 160 * 1024
+
+
+def test_search_parameters_and_predict(libamk):
+    cfg = synth.get_config("llama2_7b")
+    c = _lib.make_config(cfg)
+    p = _lib.amk_sched_params(attn_blocks=4, placement=1, rotate=1, min_tile_kb=16, search=0)
+    blob = _lib.schedule_build(c, 1, 256, p)
+    b = B.Blob(blob)
+    assert b.hdr.attn_blocks == 4 and b.hdr.placement == 1
+    assert _lib.schedule_validate(blob)[0] == _lib.AMK_OK
+    t1 = _lib.schedule_predict(blob, 2049)
+    t2 = _lib.schedule_predict(blob, 4096)
+    assert 0 < t1 < t2  # longer context, more KV bytes
+    best = B.Blob(_lib.schedule_build(c, 1, 256))  # default: exhaustive search
+    assert best.hdr.predicted_us <= _lib.schedule_predict(blob, c.max_seq) + 1e-6
+
+
+def small_blobs():
+    out = []
+    for name, n_cu in (("tiny", 8), ("tiny", 13), ("smollm2_135m", 16)):
+        cfg = synth.get_config(name)
+        c = _lib.make_config(cfg)
+        if name == "smollm2_135m":
+            c.n_layers = 2
+        for p in (None, _lib.amk_sched_params(placement=1, rotate=1, search=0)):
+            out.append(_lib.schedule_build(c, 1, n_cu, p))
+    return out
+
+
+@pytest.mark.parametrize("idx", range(6))
+def test_simulator_accepts_real_lowerings(libamk, idx):
+    blob = small_blobs()[idx]
+    st, rep = _lib.schedule_simulate(blob)
+    assert st == _lib.AMK_OK, rep
+
+
+def mutate(b: B.Blob, rng: random.Random) -> str:
+    """Apply one random adversarial edit in place; return its kind."""
+    cus = [c for c in range(len(b.per_cu)) if len(b.per_cu[c])]
+    kind = rng.choice(["drop_wait", "shrink_wait", "shift_wait", "swap_same_cu", "move_cu",
+                       "dup_rows", "gap_rows", "self_wait", "wait_later_same_cu", "widen_wait",
+                       "reorder_cu", "bad_field"])
+    c = rng.choice(cus)
+    v = b.per_cu[c]
+    i = rng.randrange(len(v))
+    t = v[i]
+    if kind == "drop_wait":
+        t["w0_lo"] = t["w0_hi"] = 0
+    elif kind == "shrink_wait":
+        if t["w0_hi"] > t["w0_lo"]:
+            if rng.random() < 0.5:
+                t["w0_hi"] -= 1
+            else:
+                t["w0_lo"] += 1
+    elif kind == "shift_wait":
+        d = rng.choice([-2, -1, 1, 2])
+        t["w0_lo"] = max(0, int(t["w0_lo"]) + d)
+        t["w0_hi"] = max(int(t["w0_lo"]), int(t["w0_hi"]) + d)
+    elif kind == "widen_wait":
+        t["w0_hi"] = min(b.hdr.n_tasks, int(t["w0_hi"]) + rng.randint(1, 50))
+    elif kind == "swap_same_cu" and len(v) > 1:
+        j = rng.randrange(len(v))
+        v[[i, j]] = v[[j, i]]
+    elif kind == "reorder_cu" and len(v) > 2:
+        perm = list(range(len(v)))
+        rng.shuffle(perm)
+        b.per_cu[c] = v[perm]
+    elif kind == "move_cu":
+        c2 = rng.choice(range(len(b.per_cu)))
+        task = v[i].copy()
+        b.per_cu[c] = np.delete(v, i)
+        pos = rng.randrange(len(b.per_cu[c2]) + 1)
+        b.per_cu[c2] = np.insert(b.per_cu[c2], pos, task)
+    elif kind == "dup_rows" and t["type"] == B.T_GEMV:
+        t["a1"] = int(t["a1"]) + 2
+    elif kind == "gap_rows" and t["type"] == B.T_GEMV and t["a1"] - t["a0"] > 2:
+        t["a0"] = int(t["a0"]) + 2
+    elif kind == "self_wait":
+        t["w1_lo"], t["w1_hi"] = t["id"], t["id"] + 1
+    elif kind == "wait_later_same_cu" and i + 1 < len(v):
+        j = rng.randrange(i + 1, len(v))
+        t["w1_lo"], t["w1_hi"] = v[j]["id"], v[j]["id"] + 1
+    elif kind == "bad_field":
+        t["a1"] = 10 ** 6
+    return kind
+
+
+def test_adversarial_corpus_zero_false_accepts(libamk):
+    """Every mutant the dynamic simulator finds unsafe must be rejected by the validator; the
+    validator may also reject mutants that happen to be safe (conservative), which is counted."""
+    rng = random.Random(1234)
+    bases = small_blobs()
+    n_unsafe = n_safe = false_accepts = conservative = 0
+    for k in range(600):
+        b = B.Blob(rng.choice(bases))
+        kinds = [mutate(b, rng) for _ in range(rng.choice([1, 1, 2]))]
+        data = b.to_bytes()
+        sv, rv = _lib.schedule_validate(data)
+        ss, rs = _lib.schedule_simulate(data)
+        if ss != _lib.AMK_OK:
+            n_unsafe += 1
+            if sv == _lib.AMK_OK:
+                false_accepts += 1
+                print("FALSE ACCEPT", kinds, rs)
+        else:
+            n_safe += 1
+            if sv != _lib.AMK_OK:
+                conservative += 1
+    print(f"mutants: {n_unsafe} unsafe, {n_safe} safe, {conservative} safe-but-rejected")
+    assert false_accepts == 0
+    assert n_unsafe > 200
+
+
+def test_truncated_and_corrupt_blobs_rejected(libamk):
+    cfg = synth.get_config("tiny")
+    blob = _lib.schedule_build(_lib.make_config(cfg), 1, 8)
+    assert _lib.schedule_validate(blob[:100])[0] == _lib.AMK_E_SCHEDULE_REJECTED
+    bad = bytearray(blob)
+    bad[0] ^= 0xFF
+    assert _lib.schedule_validate(bytes(bad))[0] == _lib.AMK_E_SCHEDULE_REJECTED
+    b = B.Blob(blob)
+    b.hdr.lds_bytes = 200 * 1024
+    assert _lib.schedule_validate(b.to_bytes())[0] == _lib.AMK_E_SCHEDULE_REJECTED
