@@ -34,10 +34,19 @@ class Report:
 
 
 def bf16_close(gpu_bits: np.ndarray, ref_bits: np.ndarray) -> float:
-    """Largest |a - b| / max(|b|, 1e-3) between two bf16 arrays (a 1-ulp rounding flip is ~4e-3)."""
+    """Largest |a - b| / (2 ulp_bf16(|b|) + 1e-3) over two bf16 arrays; <= 1 passes.
+
+    Appended K/V rows are bf16 roundings of fp32 (device) and fp64 (oracle) values. Through a
+    deep random network fp32 rounding is amplified (the oracle's own fp32 mode differs from its
+    fp64 mode by one bf16 ulp on ~5% of appended elements), so the bound allows 2 ulps plus a
+    small absolute floor rather than bit equality."""
     a = oracle.bf16_to_float(gpu_bits, np.float64)
     b = oracle.bf16_to_float(ref_bits, np.float64)
-    return float(np.max(np.abs(a - b) / np.maximum(np.abs(b), 1e-3))) if a.size else 0.0
+    if not a.size:
+        return 0.0
+    mag = np.maximum(np.abs(b), 1e-30)
+    ulp = np.exp2(np.floor(np.log2(mag)) - 7)
+    return float(np.max(np.abs(a - b) / (2 * ulp + 1e-3)))
 
 
 def teacher_forced(cfg: synth.Config, path: str = "megakernel", seed: int = 0,
@@ -105,4 +114,4 @@ def teacher_forced(cfg: synth.Config, path: str = "megakernel", seed: int = 0,
 def assert_parity(rep: Report):
     assert rep.max_abs <= LOGIT_TOL, f"logits max-abs {rep.max_abs} > {LOGIT_TOL}"
     assert not rep.token_mismatch, f"greedy ids differ at confident steps: {rep.token_mismatch[:5]}"
-    assert rep.kv_max_rel < 2e-2, f"appended KV rows differ: max rel {rep.kv_max_rel}"
+    assert rep.kv_max_rel <= 1.0, f"appended KV rows differ beyond 2 bf16 ulps: {rep.kv_max_rel}"
