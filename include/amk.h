@@ -146,6 +146,12 @@ amk_status amk_sync(amk_model *m, void *stream);
 
 amk_status amk_model_get_info(const amk_model *m, amk_model_info *out);
 
+/* Task trace of the megakernel (profiling). d_trace: device buffer of at least
+ * 8 * (4 * n_tasks + n_cu) bytes, caller-owned; NULL turns tracing off. While on, every step
+ * writes, per task id, four 100 MHz wall-clock stamps (start of wait, wait done, input staged,
+ * end) and, after them, the XCC id of each workgroup. Synchronises the device. */
+amk_status amk_trace_enable(amk_model *m, uint64_t *d_trace, size_t bytes);
+
 /* Copy of the model's frozen schedule blob (host memory, release with amk_blob_free). */
 amk_status amk_model_get_schedule(const amk_model *m, void **blob, size_t *bytes);
 

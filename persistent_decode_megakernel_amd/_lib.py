@@ -79,6 +79,7 @@ SIGNATURES = {
                                   C.c_void_p, C.c_void_p, C.c_void_p]),
     "amk_sync": (C.c_int, [C.c_void_p, C.c_void_p]),
     "amk_model_get_info": (C.c_int, [C.c_void_p, C.POINTER(amk_model_info)]),
+    "amk_trace_enable": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t]),
     "amk_model_get_schedule": (C.c_int, [C.c_void_p, C.POINTER(C.c_void_p),
                                          C.POINTER(C.c_size_t)]),
     "amk_kv_free": (C.c_int, [C.c_void_p]),
@@ -108,7 +109,7 @@ def load(path: Optional[str] = None) -> C.CDLL:
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("AMK_LIB_PATH") or LIB_PATH
     if not os.path.exists(p):
         raise FileNotFoundError(
             f"{p} is missing: build it with persistent_decode_megakernel_amd.build (hipcc, gfx950)")

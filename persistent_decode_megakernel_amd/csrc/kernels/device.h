@@ -1,5 +1,5 @@
 // Device-side task bodies shared by the persistent megakernel and the unfused ablation kernels.
-// gfx950 only: wave64, 16 waves per workgroup in the megakernel.
+// gfx950 only: wave64, kWaves (8) waves per workgroup in the megakernel.
 //
 // Numerics: weights are bf16 (or int8 with per-row fp32 scales) and are converted exactly to
 // fp32; activations, accumulations, norms, softmax and residuals are fp32. Appended K/V rows are
@@ -23,6 +23,7 @@ struct DevModel {
   int32_t L, d, nq, nkv, hd, F, V, qkvr, qd, qpg;
   int32_t wtype, tied, max_batch, max_seq;
   int32_t nblk, n_lm;
+  uint32_t n_tasks;
   float eps, attn_scale;
   const DevLayer *layers;
   const uint16_t *embed, *final_norm;
@@ -44,6 +45,7 @@ struct DevModel {
   float *y;     // [B][max(qkvr, 2F, V, d)]
   float *o;     // [B][qd]
   uint64_t timeout_ticks;  // bound of one dependency wait (s_memrealtime ticks, 100 MHz)
+  uint64_t *trace;         // optional: [n_tasks][4] timestamps, then [n_cu] XCC ids; null = off
 };
 
 struct StepArgs {
@@ -132,9 +134,49 @@ __device__ __forceinline__ float dot16_i8(const uint4 w, const float *x) {
   return a + b;
 }
 
+// Global-memory accesses. Pointers held in DevModel are generic (flat) to the compiler; flat
+// accesses count against both vmcnt and lgkmcnt, so every LDS access would also wait for all
+// outstanding global loads. Casting to the global address space keeps the two counters apart.
+#define AMK_GAS __attribute__((address_space(1)))
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ const AMK_GAS T *gptr(const T *p) {
+  return (const AMK_GAS T *)p;
+}
+template <typename T>
+__device__ __forceinline__ AMK_GAS T *gptr(T *p) {
+  return (AMK_GAS T *)p;
+}
+template <typename T>
+__device__ __forceinline__ T gld(const T *p) { return *gptr(p); }
+template <typename T>
+__device__ __forceinline__ void gst(T *p, T v) { *gptr(p) = v; }
+// Device-coherent accesses for data that another CU reads or wrote within the same launch
+// (residual stream, q, the appended KV row, attention partials, SwiGLU output, argmax partials).
+// They are device-scope ("sc1") loads and stores: they do not hit a possibly stale copy in
+// another XCD's L2 and stores write through, so a producer only has to wait for its own stores
+// to complete before publishing its flag, and a consumer needs no cache invalidation after
+// observing it. This replaces whole-L2 writeback/invalidate fences at every dependency.
+template <typename T>
+__device__ __forceinline__ T cld(const T *p) {
+  return __hip_atomic_load(gptr(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void cst(T *p, T v) {
+  __hip_atomic_store(gptr(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float cldf(const float *p) {
+  return __uint_as_float(cld(reinterpret_cast<const uint32_t *>(p)));
+}
+__device__ __forceinline__ void cstf(float *p, float v) {
+  cst(reinterpret_cast<uint32_t *>(p), __float_as_uint(v));
+}
 __device__ __forceinline__ uint4 load_nt(const uint4 *p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  const u32x4_t v = __builtin_nontemporal_load((const AMK_GAS u32x4_t *)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 gld4(const uint4 *p) {
+  const u32x4_t v = *(const AMK_GAS u32x4_t *)p;
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -155,8 +197,7 @@ __device__ __forceinline__ void record_error(uint32_t *err, uint32_t code, uint3
   }
 }
 
-// Called by one whole wave. Spins until flags[lo..hi) all reached `epoch`, then performs an
-// agent-scope acquire. Returns false (after recording the error and raising the abort flag)
+// Called by one whole wave. Spins until flags[lo..hi) all reached `epoch`. Returns false (after recording the error and raising the abort flag)
 // when the wait exceeds the timeout or another workgroup has aborted.
 __device__ bool wait_range(const DevModel &m, uint32_t lo, uint32_t hi, uint32_t epoch,
                            uint32_t task) {
@@ -183,8 +224,24 @@ __device__ bool wait_range(const DevModel &m, uint32_t lo, uint32_t hi, uint32_t
       __builtin_amdgcn_s_sleep(1);
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // No acquire fence: everything a task reads that was produced in this launch is read with
+  // device-coherent loads (cld), ordered after the flag observation.
   return true;
+}
+
+// Dependency wait of a task: wave 0 spins on the task's flag ranges, then the workgroup meets at
+// a barrier. Returns false on every thread when the wait timed out or the step was aborted.
+__device__ __forceinline__ bool wait_task(const DevModel &m, const Task &t, uint32_t epoch,
+                                          int *abort_slot) {
+  if (wave_id() == 0) {
+    bool ok = true;
+    if (t.w0_hi > t.w0_lo) ok = wait_range(m, t.w0_lo, t.w0_hi, epoch, t.id);
+    if (ok && t.w1_hi > t.w1_lo) ok = wait_range(m, t.w1_lo, t.w1_hi, epoch, t.id);
+    if (lane_id() == 0) *abort_slot = ok ? 0 : 1;
+  }
+  __syncthreads();
+  if (m.trace && threadIdx.x == 0) m.trace[(uint64_t)t.id * 4 + 1] = wall_clock64();
+  return *abort_slot == 0;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -249,7 +306,7 @@ __device__ void gemv_rows(const void *W, const float *scale, int K, int r0, int 
     for (int b = 0; b < B; ++b) {
       float v;
       if constexpr (WT == 1)
-        v = row_dot_i8<4>(static_cast<const int8_t *>(W), r, K, xs + (int64_t)b * K) * scale[r];
+        v = row_dot_i8<4>(static_cast<const int8_t *>(W), r, K, xs + (int64_t)b * K) * gld(&scale[r]);
       else
         v = row_dot_bf16<8>(static_cast<const uint16_t *>(W), r, K, xs + (int64_t)b * K);
       if (lane_id() == 0) ys[b * n + i] = v;
@@ -258,11 +315,109 @@ __device__ void gemv_rows(const void *W, const float *scale, int K, int r0, int 
 }
 
 // ------------------------------------------------------------------------------------------
+// Batch-1 GEMV as a per-wave stream of 8 KB chunks (64 lanes x 8 units of 16 bytes). A wave owns
+// rows r0 + wave, r0 + wave + nw, ...; each row is nch chunks. Two register buffers alternate so
+// one chunk is always in flight while the other is consumed, and the first chunk can be issued
+// before the task's dependency wait (weights never depend on the step's activations).
+// WT = 0: bf16 (8 weights per unit); WT = 1: int8 (16 weights per unit, times scale[row]).
+// ------------------------------------------------------------------------------------------
+constexpr int kChunkUnits = 8;
+
+template <int WT>
+struct GemvStream {
+  const uint8_t *W;
+  int K, r0, r1, nw, n16, nch, S;
+  int wave, lane;
+
+  __device__ __forceinline__ void init(const void *w, int k, int a, int b, int nwaves) {
+    constexpr int EPU = WT ? 16 : 8;
+    W = static_cast<const uint8_t *>(w);
+    K = k;
+    r0 = a;
+    r1 = b;
+    nw = nwaves;
+    wave = __builtin_amdgcn_readfirstlane(wave_id());  // uniform: keeps the loop scalar
+    lane = lane_id();
+    n16 = K / EPU;
+    nch = (n16 + 64 * kChunkUnits - 1) / (64 * kChunkUnits);
+    const int n = r1 - r0;
+    const int rows_w = (n > wave) ? (n - wave + nw - 1) / nw : 0;
+    S = rows_w * nch;
+  }
+  __device__ __forceinline__ int row_of(int s) const { return r0 + wave + (s / nch) * nw; }
+  // Loads are unconditional (the ragged tail re-reads the row's last unit and is discarded in
+  // consume): a per-lane branch here would make the compiler wait for every outstanding load
+  // before each use, which serialises the two buffers.
+  __device__ __forceinline__ void load(uint4 (&buf)[kChunkUnits], int s) const {
+    const int row = row_of(s), c = s % nch;
+    const uint4 *rp = reinterpret_cast<const uint4 *>(W + (int64_t)row * K * (WT ? 1 : 2));
+    const int base = c * 64 * kChunkUnits + lane;
+#pragma unroll
+    for (int j = 0; j < kChunkUnits; ++j) buf[j] = load_nt(rp + min(base + j * 64, n16 - 1));
+  }
+  // accumulate chunk s; at the end of a row reduce over the wave and store ys[row - r0]
+  __device__ __forceinline__ void consume(const uint4 (&buf)[kChunkUnits], int s, float &acc,
+                                          const float *xs, float *ys, const float *scale) const {
+    constexpr int EPU = WT ? 16 : 8;
+    const int c = s % nch;
+    const int base = c * 64 * kChunkUnits + lane;
+#pragma unroll
+    for (int j = 0; j < kChunkUnits; ++j) {
+      const int u = base + j * 64;
+      const float *xp = xs + EPU * min(u, n16 - 1);
+      float d;
+      if constexpr (WT == 1)
+        d = dot16_i8(buf[j], xp);
+      else
+        d = dot8_bf16(buf[j], xp);
+      acc += (u < n16) ? d : 0.f;
+    }
+    if (c == nch - 1) {
+      const int row = row_of(s);
+      float v = wave_sum(acc);
+      if constexpr (WT == 1) v *= gld(&scale[row]);
+      if (lane == 0) ys[row - r0] = v;
+      acc = 0.f;
+    }
+  }
+  // Run the stream. P holds chunk 0, loaded before the task's dependency wait and complete by
+  // now. It is consumed before the steady-state loop, which then starts (and loops back) with
+  // exactly one buffer of loads in flight: the compiler's wait-count tracking stays exact across
+  // the back edge only when entry and back edge carry the same pending loads.
+  __device__ __forceinline__ void run(const uint4 (&P)[kChunkUnits], const float *xs, float *ys,
+                                      const float *scale) const {
+    if (S == 0) return;
+    float acc = 0.f;
+    if (S == 1) {
+      consume(P, 0, acc, xs, ys, scale);
+      return;
+    }
+    uint4 A[kChunkUnits], Bf[kChunkUnits];
+    load(A, 1);
+    consume(P, 0, acc, xs, ys, scale);
+    int s = 1;
+    for (; s + 2 < S; s += 2) {
+      load(Bf, s + 1);
+      consume(A, s, acc, xs, ys, scale);
+      load(A, s + 2);
+      consume(Bf, s + 1, acc, xs, ys, scale);
+    }
+    if (s + 1 < S) {
+      load(Bf, s + 1);
+      consume(A, s, acc, xs, ys, scale);
+      consume(Bf, s + 1, acc, xs, ys, scale);
+    } else {
+      consume(A, s, acc, xs, ys, scale);
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------------------
 // input staging (LDS)
 // ------------------------------------------------------------------------------------------
 // token of sequence b, validated (an out-of-range id is recorded as a device error and read as 0)
 __device__ __forceinline__ int32_t token_of(const DevModel &m, const StepArgs &s, int b) {
-  int32_t t = s.tokens[b];
+  int32_t t = gld(&s.tokens[b]);
   if (t < 0 || t >= m.V) {
     if (threadIdx.x == 0) record_error(m.err, ERR_TOKEN, 0xffffffffu, (uint32_t)t);
     t = 0;
@@ -280,51 +435,64 @@ __device__ void stage_norm(const DevModel &m, const StepArgs &s, int slot, const
     if (slot == 0) {
       const uint16_t *e = m.embed + (int64_t)token_of(m, s, b) * d;
       for (int i = threadIdx.x; i < d; i += nw * 64) {
-        float v = bf16_to_f32(e[i]);
+        float v = bf16_to_f32(gld(&e[i]));
         x[i] = v;
         ss += v * v;
       }
     } else {
       const float *src = m.h + ((int64_t)slot * m.max_batch + b) * d;
       for (int i = threadIdx.x; i < d; i += nw * 64) {
-        float v = src[i];
+        float v = cldf(&src[i]);
         x[i] = v;
         ss += v * v;
       }
     }
     const float tot = block_sum(ss, red, nw);
     const float inv = 1.0f / sqrtf(tot / (float)d + m.eps);
-    for (int i = threadIdx.x; i < d; i += nw * 64) x[i] = x[i] * inv * bf16_to_f32(gain[i]);
+    for (int i = threadIdx.x; i < d; i += nw * 64) x[i] = x[i] * inv * bf16_to_f32(gld(&gain[i]));
   }
   __syncthreads();
 }
 
-// xs[b][h*hd + j] = attention output of head h, merged over the KV blocks (log-sum-exp).
-__device__ void stage_combine(const DevModel &m, const StepArgs &s, int l, float *xs, int nw) {
-  const int hd = m.hd, nblk = m.nblk, qd = m.qd;
+// xs[b][h*hd + j] = attention output of head h, merged over the KV blocks (log-sum-exp):
+// o = sum_k e^{m_k - M} acc_k / sum_k e^{m_k - M} l_k with M = max_k m_k. Two rounds: one thread
+// per head computes the block weights w_k = e^{m_k - M} / sum e^{m - M} l into LDS (wts, >= nq*nblk
+// floats), then every output element sums its nblk weighted accumulators (independent loads).
+__device__ void stage_combine(const DevModel &m, const StepArgs &s, int l, float *xs, float *wts,
+                              int nw) {
+  const int hd = m.hd, nblk = m.nblk, qd = m.qd, nq = m.nq;
   for (int b = 0; b < s.batch; ++b) {
-    const float *pb = m.part + (((int64_t)l * m.max_batch + b) * m.nq) * nblk * (hd + 2);
-    for (int e = threadIdx.x; e < qd; e += nw * 64) {
-      const int h = e / hd, j = e - h * hd;
+    const float *pb = m.part + (((int64_t)l * m.max_batch + b) * nq) * nblk * (hd + 2);
+    for (int h = threadIdx.x; h < nq; h += nw * 64) {
       const float *ph = pb + (int64_t)h * nblk * (hd + 2);
       float M = -INFINITY;
-      for (int k = 0; k < nblk; ++k) M = fmaxf(M, ph[k * (hd + 2) + hd]);
-      float num = 0.f, den = 0.f;
+      for (int k = 0; k < nblk; ++k) M = fmaxf(M, cldf(&ph[k * (hd + 2) + hd]));
+      float den = 0.f;
       for (int k = 0; k < nblk; ++k) {
-        const float *p = ph + k * (hd + 2);
-        const float w = __expf(p[hd] - M);  // empty blocks carry m = -inf -> weight 0
-        num = fmaf(w, p[j], num);
-        den = fmaf(w, p[hd + 1], den);
+        const float w = __expf(cldf(&ph[k * (hd + 2) + hd]) - M);  // empty blocks: m = -inf -> 0
+        wts[h * nblk + k] = w;
+        den = fmaf(w, cldf(&ph[k * (hd + 2) + hd + 1]), den);
       }
-      xs[(int64_t)b * qd + e] = num / den;
+      const float inv = 1.0f / den;
+      for (int k = 0; k < nblk; ++k) wts[h * nblk + k] *= inv;
     }
+    __syncthreads();
+    for (int e = threadIdx.x; e < qd; e += nw * 64) {
+      const int h = e / hd, j = e - h * hd;
+      const float *ph = pb + (int64_t)h * nblk * (hd + 2) + j;
+      const float *wh = wts + h * nblk;
+      float acc = 0.f;
+#pragma unroll 8
+      for (int k = 0; k < nblk; ++k) acc = fmaf(wh[k], cldf(&ph[k * (hd + 2)]), acc);
+      xs[(int64_t)b * qd + e] = acc;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 }
 
 __device__ void stage_plain(const float *src, int64_t src_stride, int K, int B, float *xs, int nw) {
   for (int b = 0; b < B; ++b)
-    for (int i = threadIdx.x; i < K; i += nw * 64) xs[(int64_t)b * K + i] = src[b * src_stride + i];
+    for (int i = threadIdx.x; i < K; i += nw * 64) xs[(int64_t)b * K + i] = cldf(&src[b * src_stride + i]);
   __syncthreads();
 }
 
@@ -356,12 +524,12 @@ __device__ void epi_qkv(const DevModel &m, const StepArgs &s, int l, int r0, int
       }
       if (q0.kind == KIND_Q) {
         float *qb = m.q + ((int64_t)l * m.max_batch + b) * m.qd;
-        qb[q0.head * hd + q0.dim] = v0;
-        qb[q1.head * hd + q1.dim] = v1;
+        cstf(&qb[q0.head * hd + q0.dim], v0);
+        cstf(&qb[q1.head * hd + q1.dim], v1);
       } else {
         const int kvi = (q0.kind == KIND_K) ? 0 : 1;
-        s.kv[kv_index(m, s, l, kvi, b, q0.head, s.pos, q0.dim)] = f32_to_bf16(v0);
-        s.kv[kv_index(m, s, l, kvi, b, q1.head, s.pos, q1.dim)] = f32_to_bf16(v1);
+        cst(&s.kv[kv_index(m, s, l, kvi, b, q0.head, s.pos, q0.dim)], f32_to_bf16(v0));
+        cst(&s.kv[kv_index(m, s, l, kvi, b, q1.head, s.pos, q1.dim)], f32_to_bf16(v1));
       }
     }
   }
@@ -377,8 +545,8 @@ __device__ void epi_residual(const DevModel &m, const StepArgs &s, int res_slot,
     const uint16_t *e = (res_slot == 0) ? m.embed + (int64_t)token_of(m, s, b) * d : nullptr;
     for (int i = threadIdx.x; i < n; i += nw * 64) {
       const int r = r0 + i;
-      const float base = e ? bf16_to_f32(e[r]) : res[r];
-      out[r] = base + ys[b * n + i];
+      const float base = e ? bf16_to_f32(gld(&e[r])) : cldf(&res[r]);
+      cstf(&out[r], base + ys[b * n + i]);
     }
   }
 }
@@ -389,7 +557,7 @@ __device__ void epi_swiglu(const DevModel &m, const StepArgs &s, int l, int r0, 
   for (int b = 0; b < s.batch; ++b) {
     float *a = m.a + ((int64_t)l * m.max_batch + b) * m.F;
     for (int i = threadIdx.x; i < n / 2; i += nw * 64)
-      a[r0 / 2 + i] = silu(ys[b * n + 2 * i]) * ys[b * n + 2 * i + 1];
+      cstf(&a[r0 / 2 + i], silu(ys[b * n + 2 * i]) * ys[b * n + 2 * i + 1]);
   }
 }
 
@@ -403,7 +571,7 @@ __device__ void epi_logits(const DevModel &m, const StepArgs &s, int r0, int r1,
     int bi = 0x7fffffff;
     for (int i = threadIdx.x; i < n; i += nw * 64) {
       const float v = ys[b * n + i];
-      lg[(int64_t)b * m.V + r0 + i] = v;
+      gst(&lg[(int64_t)b * m.V + r0 + i], v);
       if (v > best) { best = v; bi = r0 + i; }
     }
 #pragma unroll
@@ -426,7 +594,8 @@ __device__ void epi_logits(const DevModel &m, const StepArgs &s, int r0, int r1,
         const int j = __float_as_int(red[2 * w + 1]);
         if (v > bv || (v == bv && j < bj)) { bv = v; bj = j; }
       }
-      m.amax[(int64_t)slot * m.max_batch + b] = make_float2(bv, __int_as_float(bj));
+      cst(reinterpret_cast<uint64_t *>(&m.amax[(int64_t)slot * m.max_batch + b]),
+          (uint64_t)__float_as_uint(bv) | ((uint64_t)(uint32_t)bj << 32));
     }
   }
 }
@@ -438,9 +607,10 @@ __device__ void argmax_combine(const DevModel &m, const StepArgs &s, int n_slots
     float best = -INFINITY;
     int bi = 0x7fffffff;
     for (int k = lane_id(); k < n_slots; k += 64) {
-      const float2 p = m.amax[(int64_t)k * m.max_batch + b];
-      const int j = __float_as_int(p.y);
-      if (p.x > best || (p.x == best && j < bi)) { best = p.x; bi = j; }
+      const uint64_t p = cld(reinterpret_cast<const uint64_t *>(&m.amax[(int64_t)k * m.max_batch + b]));
+      const float v = __uint_as_float((uint32_t)p);
+      const int j = (int)(uint32_t)(p >> 32);
+      if (v > best || (v == best && j < bi)) { best = v; bi = j; }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -448,7 +618,7 @@ __device__ void argmax_combine(const DevModel &m, const StepArgs &s, int n_slots
       const int oi = __shfl_xor(bi, o, 64);
       if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
     }
-    if (lane_id() == 0) s.next[b] = (bi == 0x7fffffff) ? 0 : bi;
+    if (lane_id() == 0) gst(&s.next[b], (bi == 0x7fffffff) ? 0 : bi);
   }
 }
 
@@ -458,38 +628,57 @@ __device__ void argmax_combine(const DevModel &m, const StepArgs &s, int n_slots
 // Lane layout: LPR = hd/8 lanes per KV row (8 dims each), 64/LPR rows per wave per load.
 // ------------------------------------------------------------------------------------------
 template <int HD, int QMAX>
-__device__ void attn_block(const DevModel &m, const StepArgs &s, int l, int g, int blk,
-                           int h0, int qn, float *lds, float *red) {
+__device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, int blk,
+                           int h0, int qn, float *lds, float *red, const Task *wait_for,
+                           int *abort_slot) {
+  // heads [h0, h0 + qn) of the group (qn <= QMAX), i.e. query heads g*qpg + h0 + i.
+  // When wait_for is set, the first chunk of KV history (rows written by earlier steps) is
+  // loaded before the dependency wait; only the row at `pos`, appended by this step's QKV tiles,
+  // is read after it.
   constexpr int NW = kWaves;
   constexpr int LPR = HD / 8;
   constexpr int RPW = 64 / LPR;  // rows per wave per load
   constexpr int ROWS_PER_ITER = NW * RPW;
   constexpr int NIT = kAttnRowsPerChunk / ROWS_PER_ITER;
   static_assert(NIT * ROWS_PER_ITER == kAttnRowsPerChunk, "chunk must be whole iterations");
-  // heads [h0, h0 + qn) of the group (qn <= QMAX), i.e. query heads g*qpg + h0 + i
   const int qpg = qn, nq = m.nq, nblk = m.nblk;
   const int lane = lane_id(), wave = wave_id();
   const int sub = lane % LPR, rs = lane / LPR;
+  const int pos = s.pos;
   int lo, hi;
-  attn_block_range(s.pos + 1, nblk, blk, &lo, &hi);
+  attn_block_range(pos + 1, nblk, blk, &lo, &hi);
   float *qs = lds;                             // [qpg][HD]
   float *sc = qs + qpg * HD;                   // [qpg][chunk]
   float *accw = sc + qpg * kAttnRowsPerChunk;  // [NW][qpg*HD]
   for (int b = 0; b < s.batch; ++b) {
+    const uint16_t *Kb = s.kv + kv_index(m, s, l, 0, b, g, 0, 0);
+    const uint16_t *Vb = s.kv + kv_index(m, s, l, 1, b, g, 0, 0);
+    uint4 kr[NIT], vr[NIT];
+    {
+      const int c1 = min(hi, lo + kAttnRowsPerChunk);
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int j = lo + it * ROWS_PER_ITER + wave * RPW + rs;
+        const bool ok = j < c1 && j != pos;
+        kr[it] = ok ? gld4(reinterpret_cast<const uint4 *>(Kb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
+        vr[it] = ok ? gld4(reinterpret_cast<const uint4 *>(Vb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
+      }
+    }
+    if (wait_for && b == 0) {
+      if (!wait_task(m, *wait_for, s.epoch, abort_slot)) return false;
+    }
     const float *qsrc = m.q + ((int64_t)l * m.max_batch + b) * m.qd + ((int64_t)g * m.qpg + h0) * HD;
-    for (int i = threadIdx.x; i < qpg * HD; i += NW * 64) qs[i] = qsrc[i] * m.attn_scale;
+    for (int i = threadIdx.x; i < qpg * HD; i += NW * 64) qs[i] = cldf(&qsrc[i]) * m.attn_scale;
     __syncthreads();
     float *pout = m.part + ((((int64_t)l * m.max_batch + b) * nq + (int64_t)g * m.qpg + h0) * nblk + blk) * (HD + 2);
     if (hi <= lo) {
       for (int i = threadIdx.x; i < qpg * (HD + 2); i += NW * 64) {
         const int h = i / (HD + 2), e = i - h * (HD + 2);
-        pout[(int64_t)h * nblk * (HD + 2) + e] = (e == HD) ? -INFINITY : 0.f;
+        cstf(&pout[(int64_t)h * nblk * (HD + 2) + e], (e == HD) ? -INFINITY : 0.f);
       }
       __syncthreads();
       continue;
     }
-    const uint16_t *Kb = s.kv + kv_index(m, s, l, 0, b, g, 0, 0);
-    const uint16_t *Vb = s.kv + kv_index(m, s, l, 1, b, g, 0, 0);
     float acc[QMAX][8];
     float lsum[QMAX];
     float mrun[QMAX];
@@ -502,13 +691,26 @@ __device__ void attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
     }
     for (int c0 = lo; c0 < hi; c0 += kAttnRowsPerChunk) {
       const int c1 = min(hi, c0 + kAttnRowsPerChunk);
-      uint4 kr[NIT], vr[NIT];
+      if (c0 == lo) {
+        // the row appended by this step (visible after the wait)
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int j = c0 + it * ROWS_PER_ITER + wave * RPW + rs;
-        const bool ok = j < c1;
-        kr[it] = ok ? *reinterpret_cast<const uint4 *>(Kb + (int64_t)j * HD + sub * 8) : make_uint4(0, 0, 0, 0);
-        vr[it] = ok ? *reinterpret_cast<const uint4 *>(Vb + (int64_t)j * HD + sub * 8) : make_uint4(0, 0, 0, 0);
+        for (int it = 0; it < NIT; ++it) {
+          const int j = c0 + it * ROWS_PER_ITER + wave * RPW + rs;
+          if (j == pos && j < c1) {  // written by this step: device-coherent loads
+            const uint32_t *kp = reinterpret_cast<const uint32_t *>(Kb + (int64_t)j * HD + sub * 8);
+            const uint32_t *vp = reinterpret_cast<const uint32_t *>(Vb + (int64_t)j * HD + sub * 8);
+            kr[it] = make_uint4(cld(kp), cld(kp + 1), cld(kp + 2), cld(kp + 3));
+            vr[it] = make_uint4(cld(vp), cld(vp + 1), cld(vp + 2), cld(vp + 3));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int j = c0 + it * ROWS_PER_ITER + wave * RPW + rs;
+          const bool ok = j < c1;
+          kr[it] = ok ? gld4(reinterpret_cast<const uint4 *>(Kb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
+          vr[it] = ok ? gld4(reinterpret_cast<const uint4 *>(Vb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
+        }
       }
       // scores of this lane's rows, reduced over the LPR lanes of a row
 #pragma unroll
@@ -589,7 +791,7 @@ __device__ void attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
       float t = 0.f;
       for (int w = 0; w < NW; ++w) t += accw[(int64_t)w * qpg * HD + i];
       const int h = i / HD, e = i - h * HD;
-      pout[(int64_t)h * nblk * (HD + 2) + e] = t;
+      cstf(&pout[(int64_t)h * nblk * (HD + 2) + e], t);
     }
     if (threadIdx.x < qpg) {
       const int h = threadIdx.x;
@@ -599,20 +801,26 @@ __device__ void attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
 #pragma unroll
       for (int k = 0; k < QMAX; ++k)
         if (k == h) mh = mrun[k];
-      pout[(int64_t)h * nblk * (HD + 2) + HD] = mh;
-      pout[(int64_t)h * nblk * (HD + 2) + HD + 1] = t;
+      cstf(&pout[(int64_t)h * nblk * (HD + 2) + HD], mh);
+      cstf(&pout[(int64_t)h * nblk * (HD + 2) + HD + 1], t);
     }
     __syncthreads();
   }
+  return true;
 }
 
-// Attention tasks always run with kWaves waves (1024 threads). A group of more query heads than
+// Attention tasks always run with kWaves waves (kThreads threads). A group of more query heads than
 // QMAX is processed QMAX heads at a time (the KV block is re-read from cache for each pass).
+// wait_for (megakernel) is waited on inside the first pass, after the KV-history prefetch.
 template <int HD, int QMAX>
-__device__ __forceinline__ void attn_task(const DevModel &m, const StepArgs &s, int l, int g,
-                                          int blk, float *lds, float *red) {
+__device__ __forceinline__ bool attn_task(const DevModel &m, const StepArgs &s, int l, int g,
+                                          int blk, float *lds, float *red, const Task *wait_for,
+                                          int *abort_slot) {
   for (int h0 = 0; h0 < m.qpg; h0 += QMAX)
-    attn_block<HD, QMAX>(m, s, l, g, blk, h0, min(QMAX, m.qpg - h0), lds, red);
+    if (!attn_block<HD, QMAX>(m, s, l, g, blk, h0, min(QMAX, m.qpg - h0), lds, red,
+                              h0 == 0 ? wait_for : nullptr, abort_slot))
+      return false;
+  return true;
 }
 
 // ------------------------------------------------------------------------------------------

@@ -3,9 +3,9 @@
 // Ada-MK technical summary ("Methodology", Phase I and II): the whole decode step runs as one
 // persistent kernel whose execution order was fixed offline and serialised, so the device makes
 // no decision about what to run where. Each workgroup reads its own list of tile tasks; before a
-// task it waits (one wave spinning on agent-scope flags, then an acquire), runs the task body
-// with all 16 waves, and publishes its own flag with an agent-scope release. Dependencies between
-// CUs are point-to-point flags; there is no grid-wide barrier.
+// task it waits (one wave spinning on device-scope flags), runs the task body with all of its
+// waves, and publishes its own flag once its stores have completed. Dependencies between CUs are
+// point-to-point flags; there is no grid-wide barrier.
 //
 // The kernel is instantiated per (weight type, head_dim, query heads per pass) so that each
 // instance carries a single GEMV and a single attention body.
@@ -15,27 +15,37 @@
 
 namespace amk {
 
+// GEMV tile task: the first weight chunk of every wave is issued before the dependency wait, the
+// input vector is staged (RMSNorm / attention combine / plain copy) after it, then the row stream
+// runs double-buffered and the epilogue writes the tile's outputs.
 template <int WT>
-__device__ __forceinline__ void run_gemv_task(const DevModel &m, const StepArgs &s, const Task &t,
-                                              float *xs, float *ys, float *red) {
+__device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, const Task &t,
+                                          float *xs, float *ys, float *red, int *abort_slot) {
   constexpr int NW = kWaves;
   const int l = t.layer;
   const void *W;
   const float *scale;
   int K, wtype;
   gemv_matrix(m, t.mat, l, &W, &scale, &K, &wtype);
+  const int r0 = (int)t.a0, r1 = (int)t.a1;
+  const bool b1 = s.batch == 1;
+  GemvStream<WT> st;
+  uint4 P[kChunkUnits];
+  st.init(W, K, r0, r1, NW);
+  if (b1 && st.S > 0) st.load(P, 0);
+  if (!wait_task(m, t, s.epoch, abort_slot)) return false;
   switch (t.mat) {
     case M_QKV: stage_norm(m, s, 2 * l, m.layers[l].attn_norm, xs, red, NW); break;
-    case M_O: stage_combine(m, s, l, xs, NW); break;
+    case M_O: stage_combine(m, s, l, xs, red, NW); break;
     case M_GU: stage_norm(m, s, 2 * l + 1, m.layers[l].mlp_norm, xs, red, NW); break;
     case M_D: stage_plain(m.a + (int64_t)l * m.max_batch * m.F, m.F, m.F, s.batch, xs, NW); break;
     default: stage_norm(m, s, 2 * m.L, m.final_norm, xs, red, NW); break;
   }
-  const int r0 = (int)t.a0, r1 = (int)t.a1;
-  if (WT == 1 && wtype == 1)
-    gemv_rows<1>(W, scale, K, r0, r1, xs, ys, s.batch, NW);
+  if (m.trace && threadIdx.x == 0) m.trace[(uint64_t)t.id * 4 + 2] = wall_clock64();
+  if (b1)
+    st.run(P, xs, ys, scale);
   else
-    gemv_rows<0>(W, scale, K, r0, r1, xs, ys, s.batch, NW);
+    gemv_rows<WT>(W, scale, K, r0, r1, xs, ys, s.batch, NW);
   __syncthreads();
   switch (t.mat) {
     case M_QKV: epi_qkv(m, s, l, r0, r1, ys, NW); break;
@@ -44,6 +54,7 @@ __device__ __forceinline__ void run_gemv_task(const DevModel &m, const StepArgs 
     case M_D: epi_residual(m, s, 2 * l + 1, 2 * l + 2, r0, r1, ys, NW); break;
     default: epi_logits(m, s, r0, r1, (int)t.aux0, ys, red, NW); break;
   }
+  return true;
 }
 
 template <int WT, int HD, int QMAX>
@@ -52,29 +63,38 @@ __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArg
   const int32_t xa = lds_xs_floats(m.max_batch, m.d, m.qd, m.F);
   const int32_t xb = lds_attn_floats(m.max_batch, m.qpg, m.hd);
   float *xs = lds;
-  float *red = lds + (xa > xb ? xa : xb);  // 64 * 8 floats
-  float *ys = red + 64 * 8;                // batch * max_tile_rows floats
+  float *red = lds + (xa > xb ? xa : xb);  // kRedFloats floats
+  float *ys = red + kRedFloats;            // batch * max_tile_rows floats
   __shared__ int abort_flag;
   const uint32_t t0 = m.offsets[blockIdx.x], t1 = m.offsets[blockIdx.x + 1];
+  uint64_t *const trace = m.trace;
+  if (trace && threadIdx.x == 0) {
+    // XCC (XCD) that runs this workgroup: HW_REG_XCC_ID, bits [3:0]
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20);
+    trace[(uint64_t)m.n_tasks * 4 + blockIdx.x] = xcc;
+  }
   for (uint32_t ti = t0; ti < t1; ++ti) {
     const Task t = m.tasks[ti];
-    if (wave_id() == 0) {
-      bool ok = true;
-      if (t.w0_hi > t.w0_lo) ok = wait_range(m, t.w0_lo, t.w0_hi, s.epoch, t.id);
-      if (ok && t.w1_hi > t.w1_lo) ok = wait_range(m, t.w1_lo, t.w1_hi, s.epoch, t.id);
-      if (lane_id() == 0) abort_flag = ok ? 0 : 1;
+    if (trace && threadIdx.x == 0) trace[(uint64_t)t.id * 4 + 0] = wall_clock64();
+    bool ok;
+    if (t.type == T_GEMV) {
+      ok = gemv_task<WT>(m, s, t, xs, ys, red, &abort_flag);
+    } else if (t.type == T_ATTN) {
+      ok = attn_task<HD, QMAX>(m, s, t.layer, (int)t.a0, (int)t.a1, xs, red, &t, &abort_flag);
+    } else {
+      ok = wait_task(m, t, s.epoch, &abort_flag);
+      if (ok) argmax_combine(m, s, (int)t.aux0);
     }
+    if (!ok) return;
+    // Publish: every wave waits for its own (device-coherent) stores to complete, the workgroup
+    // meets, then one thread stores the flag. Data that crosses CUs is written with device-scope
+    // stores, so no L2 writeback is needed before the flag.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (abort_flag) return;
-    if (t.type == T_GEMV)
-      run_gemv_task<WT>(m, s, t, xs, ys, red);
-    else if (t.type == T_ATTN)
-      attn_task<HD, QMAX>(m, s, t.layer, (int)t.a0, (int)t.a1, xs, red);
-    else
-      argmax_combine(m, s, (int)t.aux0);
-    __syncthreads();
-    if (threadIdx.x == 0)
-      __hip_atomic_store(&m.flags[t.id], s.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+      if (trace) trace[(uint64_t)t.id * 4 + 3] = wall_clock64();
+      __hip_atomic_store(&m.flags[t.id], s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 

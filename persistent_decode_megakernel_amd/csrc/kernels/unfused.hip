@@ -112,7 +112,7 @@ __device__ void uf_attn(const DevModel &m, const StepArgs &s, int l) {
   extern __shared__ float lds[];
   float *red = lds;
   float *work = lds + 64 * 8;
-  attn_task<HD, QMAX>(m, s, l, blockIdx.x, blockIdx.y, work, red);
+  attn_task<HD, QMAX>(m, s, l, blockIdx.x, blockIdx.y, work, red, nullptr, nullptr);
 }
 
 #define AMK_UF_ATTN(HD, Q)                                                                   \

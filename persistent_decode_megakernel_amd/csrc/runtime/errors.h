@@ -3,7 +3,7 @@
 #pragma once
 #include <string>
 
-#include "../../../include/amk.h"
+#include "amk.h"
 
 namespace amk {
 amk_status set_error(amk_status st, const std::string &msg);

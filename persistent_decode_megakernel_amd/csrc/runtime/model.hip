@@ -308,6 +308,8 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     dm.wtype = cfg->wtype; dm.tied = cfg->tied_lm_head; dm.max_batch = B; dm.max_seq = cfg->max_seq;
     dm.nblk = (int32_t)h.attn_blocks;
     dm.n_lm = (int32_t)h.n_lm_tiles;
+    dm.n_tasks = h.n_tasks;
+    dm.trace = nullptr;
     dm.eps = cfg->rms_eps;
     dm.attn_scale = (float)(1.0 / std::sqrt((double)hd));
     m->layers.resize(L);
@@ -622,6 +624,21 @@ extern "C" amk_status amk_sync(amk_model *m, void *stream) {
     std::memset(m->h_err, 0, 16);
     return map_device_error(err[0], err[2], err[3]);
   }
+  clear_error();
+  return AMK_OK;
+  AMK_API_END
+}
+
+extern "C" amk_status amk_trace_enable(amk_model *m, uint64_t *d_trace, size_t bytes) {
+  AMK_API_BEGIN
+  if (!m) return set_error(AMK_E_INVALID, "amk_trace_enable: null model");
+  const size_t need = 8ull * (4ull * m->sched.hdr.n_tasks + (size_t)m->n_cu);
+  if (d_trace && bytes < need)
+    return set_error(AMK_E_CAPACITY, "amk_trace_enable: buffer needs " + std::to_string(need) + " bytes");
+  (void)hipDeviceSynchronize();
+  m->dm.trace = d_trace;
+  hipError_t e = hipMemcpy(m->d_dm, &m->dm, sizeof(DevModel), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return set_error(AMK_E_HIP, std::string("amk_trace_enable: ") + hipGetErrorString(e));
   clear_error();
   return AMK_OK;
   AMK_API_END

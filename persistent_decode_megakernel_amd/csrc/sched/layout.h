@@ -115,11 +115,12 @@ namespace amk {
 // checked by the validator) and the runtime (dynamic LDS at launch).
 //   xs : batch x max(hidden, n_heads*head_dim, ffn) float  -- staged GEMV input vector(s)
 //   ys : batch x max_tile_rows float                        -- GEMV tile outputs before epilogue
-//   red: 64 x 8 float                                       -- cross-wave reductions
+//   red: kRedFloats float                                   -- reductions, combine weights
 // Attention tasks reuse the xs region (q, scores, partial accumulators).
-constexpr int32_t kWaves = 16;
+constexpr int32_t kWaves = 8;
 constexpr int32_t kThreads = kWaves * 64;
 constexpr int32_t kAttnRowsPerChunk = 256;  // KV rows staged per attention chunk
+constexpr int32_t kRedFloats = 2048;        // reduction scratch; holds n_heads x blocks weights
 
 AMK_HD int32_t lds_xs_floats(int32_t batch, int32_t hidden, int32_t qdim, int32_t ffn) {
   int32_t k = hidden > qdim ? hidden : qdim;
@@ -135,6 +136,6 @@ AMK_HD int32_t lds_bytes_for(int32_t batch, int32_t hidden, int32_t qdim, int32_
   int32_t a = lds_xs_floats(batch, hidden, qdim, ffn);
   int32_t b = lds_attn_floats(batch, qpg, hd);
   int32_t region = a > b ? a : b;
-  return 4 * (region + batch * max_tile_rows + 64 * 8);
+  return 4 * (region + batch * max_tile_rows + kRedFloats);
 }
 }  // namespace amk

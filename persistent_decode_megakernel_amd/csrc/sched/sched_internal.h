@@ -5,7 +5,7 @@
 #include <string>
 #include <vector>
 
-#include "../../../include/amk.h"
+#include "amk.h"
 #include "layout.h"
 
 namespace amk {

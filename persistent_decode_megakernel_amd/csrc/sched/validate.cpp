@@ -223,6 +223,8 @@ bool validate_schedule(const Schedule &s, std::string *report) {
   if (h.batch < 1 || (int32_t)h.batch > cfg.max_batch) return fail("batch outside [1, max_batch]");
   if (h.attn_blocks < 1) return fail("attn_blocks must be >= 1");
   if (h.n_lm_tiles < 1) return fail("no LM tiles");
+  if ((int64_t)cfg.n_heads * h.attn_blocks > kRedFloats)
+    return fail("n_heads x attn_blocks exceeds the combine scratch");
   if (s.per_cu.size() != h.n_cu) return fail("CU table size mismatch");
   if (h.lds_bytes > kMaxLdsBytes) return fail(fmt("LDS %lld bytes exceeds %lld", h.lds_bytes, kMaxLdsBytes));
   const uint32_t n = s.n_tasks();

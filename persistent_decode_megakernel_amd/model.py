@@ -120,6 +120,15 @@ class Model:
         finally:
             self.lib.amk_blob_free(b)
 
+    def enable_trace(self) -> torch.Tensor:
+        """Turn on the megakernel's task trace; returns the device buffer it fills each step."""
+        inf = self.info()
+        buf = torch.zeros(4 * inf.n_tasks + inf.n_cu, dtype=torch.int64, device=self.device)
+        _lib.check(self.lib.amk_trace_enable(self.handle, C.c_void_p(buf.data_ptr()),
+                                             buf.numel() * 8), "amk_trace_enable")
+        self._trace = buf
+        return buf
+
     def kv(self, batch: Optional[int] = None, max_seq: Optional[int] = None) -> KVCache:
         return KVCache(self, batch or self.max_batch, max_seq or self.max_seq)
 
