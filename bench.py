@@ -72,6 +72,20 @@ def time_path(cfg, weights, kv_host, path, steps, warmup):
     return total / steps, per, info, ids
 
 
+def profiled_traffic(cfg, kernel_name):
+    """Per-launch HBM bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from the committed
+    rocprofv3 summary of this workload, or None when the kernel sources changed since."""
+    from persistent_decode_megakernel_amd import profile_summary
+    path = os.path.join(ROOT, "profiles", f"megakernel_{cfg.name}_b{cfg.batch}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel") != kernel_name or rec.get("source_hash") != profile_summary.source_hash():
+        return None
+    return float(rec["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(cfg, weights, kv_host, sample_layers):
     """The oracle on a bounded sample: one decode step of a model truncated to its first
     `sample_layers` layers (plus final norm and LM head); per-layer time scaled to all layers."""
@@ -127,7 +141,10 @@ def main():
     ap.add_argument("--workload", default="llama2_7b")
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-layers", type=int, default=2)
+    ap.add_argument("--cpu-sample-layers", type=int, default=4)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device-to-device copy of this many MiB first (a kernel of "
+                         "known traffic for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the decode "
@@ -142,6 +159,15 @@ def main():
     torch.cuda.set_device(0)
     cfg = synth.get_config(args.workload)
     steps, warmup = args.steps, args.warmup
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {n} bytes read, {n} bytes written")
+        del src, dst
     t0 = time.time()
     weights = synth.make_weights(cfg, 0, threads=16)
     max_seq = cfg.prefill + max(steps, warmup) + 1
@@ -149,6 +175,9 @@ def main():
     log(f"[bench] synthetic {cfg.name} generated in {time.time() - t0:.1f}s")
 
     ms, per, info, ids = time_path(cfg, weights, kv_host, "megakernel", steps, warmup)
+    hd_q = 1 if cfg.n_heads // cfg.n_kv_heads <= 1 else (2 if cfg.n_heads // cfg.n_kv_heads <= 2 else 4)
+    kname = f"amk_megakernel_w{1 if cfg.wtype == 'int8' else 0}_h{cfg.head_dim}_q{hd_q}"
+    traffic_bytes = profiled_traffic(cfg, kname)
     weight_bytes = info.weight_bytes + 2 * cfg.hidden * cfg.batch  # + embedding rows
     ctxs = [cfg.prefill + i + 1 for i in range(steps)]
     step_bytes = [weight_bytes + kv_bytes_step(cfg, c) for c in ctxs]
@@ -184,8 +213,11 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": (None if traffic_bytes is None
+                        else round(traffic_bytes / (avg_launch_ms * 1e-3) / 1e9, 1)),
         },
+        "traffic_bytes_per_launch": None if traffic_bytes is None else int(traffic_bytes),
+        "kernel": kname,
         "algorithmic_bytes_per_step": int(avg_bytes),
         "launches_per_step": info.launches_per_step,
         "step_ms_p10_p50_p90": [round(sorted(per)[int(q * (steps - 1))], 4) for q in (0.1, 0.5, 0.9)],
