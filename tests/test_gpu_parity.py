@@ -88,3 +88,37 @@ def test_last_position():
     cfg = synth.get_config("tiny")
     rep = teacher_forced(cfg.replace(prefill=40, prompt=0, steps=7), "megakernel", n_calls=7)
     assert_parity(rep)
+
+
+@pytest.mark.parametrize("path", ["megakernel", "unfused"])
+def test_tiny_int8_w8a16(path):
+    """W8A16: int8 layer matrices and LM head with per-row fp32 scales."""
+    cfg = synth.get_config("tiny").replace(wtype="int8")
+    rep = teacher_forced(cfg, path, seed=3, n_calls=20)
+    log(f"tiny int8/{path}: {rep}")
+    assert_parity(rep)
+
+
+@pytest.mark.parametrize("path", ["megakernel", "unfused"])
+def test_tiny_batch3(path):
+    """Three independent sequences sharing the weights and the position."""
+    cfg = synth.get_config("tiny").replace(batch=3)
+    rep = teacher_forced(cfg, path, seed=4, n_calls=12)
+    assert rep.tokens_checked > 0
+    assert_parity(rep)
+
+
+def test_smollm2_135m_batch2_prefill():
+    cfg = synth.get_config("smollm2_135m").replace(batch=2)
+    rep = teacher_forced(cfg, "megakernel", seed=5, n_calls=3)
+    assert_parity(rep)
+
+
+@pytest.mark.parametrize("name", ["llama2_7b", "llama2_7b_w8a16"])
+def test_full_size_first_steps(name):
+    """Full 7B shapes in the launch configuration the bench times (one cooperative launch per
+    step on every CU), checked against the oracle on every logit for the first two steps."""
+    cfg = synth.get_config(name)
+    rep = teacher_forced(cfg, "megakernel", n_calls=2, oracle_dtype=np.float32)
+    log(f"{name}: {rep}")
+    assert_parity(rep)
