@@ -59,7 +59,7 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
 
 template <int WT, int HD, int QMAX>
 __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArgs &s) {
-  extern __shared__ float lds[];
+  extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte reads of xs need it
   const int32_t xa = lds_xs_floats(m.max_batch, m.d, m.qd, m.F);
   const int32_t xb = lds_attn_floats(m.max_batch, m.qpg, m.hd);
   float *xs = lds;

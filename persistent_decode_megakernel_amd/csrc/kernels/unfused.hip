@@ -43,7 +43,7 @@ extern "C" __global__ void __launch_bounds__(1024) amk_uf_rmsnorm(const DevModel
 template <int WT, int MODE>
 __device__ void uf_gemv(const DevModel &m, const StepArgs &s, const void *W, const float *scale,
                         int K, int rows, const float *x, float *y, const float *res, float *out) {
-  extern __shared__ float lds[];
+  extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte reads of xs need it
   float *red = lds;                       // 64 * 8
   float *ys = red + 64 * 8;               // batch * kUfRowsPerBlock
   float *xs = ys + 8 * kUfRowsPerBlock;   // batch * K
@@ -109,7 +109,7 @@ extern "C" __global__ void __launch_bounds__(256) amk_uf_rope_kv(const DevModel 
 
 template <int HD, int QMAX>
 __device__ void uf_attn(const DevModel &m, const StepArgs &s, int l) {
-  extern __shared__ float lds[];
+  extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte reads of xs need it
   float *red = lds;
   float *work = lds + 64 * 8;
   attn_task<HD, QMAX>(m, s, l, blockIdx.x, blockIdx.y, work, red, nullptr, nullptr);

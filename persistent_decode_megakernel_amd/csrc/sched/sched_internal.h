@@ -10,8 +10,9 @@
 
 namespace amk {
 
-// LDS the megakernel declares per workgroup (bytes); the validator checks it against the CU.
-constexpr uint32_t kMaxLdsBytes = 160 * 1024;
+// Dynamic LDS a schedule may ask for per workgroup (bytes): the CU's 160 KiB less what the
+// kernel declares statically (a 16-byte-aligned control word).
+constexpr uint32_t kMaxLdsBytes = 160 * 1024 - 64;
 
 struct Schedule {
   BlobHeader hdr{};
