@@ -179,6 +179,27 @@ __device__ __forceinline__ uint4 gld4(const uint4 *p) {
   const u32x4_t v = *(const AMK_GAS u32x4_t *)p;
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+// 16-byte device-coherent loads go through a raw buffer resource: the buffer intrinsics take a
+// cache-policy operand, plain pointer loads of 16 bytes cannot carry the device-scope bit.
+// Word 3 of the resource selects the 32-bit data format (the only field untyped loads use);
+// offsets at or beyond `bytes` read as zero instead of faulting.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+// 4 bf16 values (8 bytes) at p[i4 * 4 ..] as two packed words
+__device__ __forceinline__ uint2 gld_bf16x4(const uint16_t *p, int i4) {
+  const u32x2_t v = *((const AMK_GAS u32x2_t *)p + i4);
+  return make_uint2(v.x, v.y);
+}
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kCachePolicySc1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ float4 cld4(__amdgpu_buffer_rsrc_t r, uint32_t off_bytes) {
+  const f32x4_t v = __builtin_bit_cast(
+      f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off_bytes, 0, kCachePolicySc1));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
 
 // ------------------------------------------------------------------------------------------
 // dependency flags
@@ -197,17 +218,26 @@ __device__ __forceinline__ void record_error(uint32_t *err, uint32_t code, uint3
   }
 }
 
-// Called by one whole wave. Spins until flags[lo..hi) all reached `epoch`. Returns false (after recording the error and raising the abort flag)
-// when the wait exceeds the timeout or another workgroup has aborted.
+// Called by one whole wave. Spins until flags[lo..hi) all reached `epoch`. Each poll round
+// issues the loads for up to 512 flags (8 per lane, indices clamped into the range) before
+// testing any of them, so a round costs one memory latency whatever the range's size. Returns
+// false (after recording the error and raising the abort flag) when the wait exceeds the timeout
+// or another workgroup has aborted.
 __device__ bool wait_range(const DevModel &m, uint32_t lo, uint32_t hi, uint32_t epoch,
                            uint32_t task) {
-  const int lane = lane_id();
+  constexpr int kPer = 8;
+  const uint32_t lane = (uint32_t)lane_id();
   uint64_t t0 = 0;
-  for (uint32_t base = lo; base < hi; base += 64) {
-    const uint32_t idx = base + (uint32_t)lane;
+  for (uint32_t g = lo; g < hi; g += 64 * kPer) {
+    const uint32_t last = min(hi, g + 64 * kPer) - 1;
     uint32_t spins = 0;
     while (true) {
-      bool ok = idx >= hi || (int32_t)(flag_load(&m.flags[idx]) - epoch) >= 0;
+      uint32_t v[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) v[j] = flag_load(&m.flags[min(g + lane + 64u * j, last)]);
+      bool ok = true;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) ok = ok && (int32_t)(v[j] - epoch) >= 0;
       if (__all(ok)) break;
       if (spins == 0) t0 = wall_clock64();
       ++spins;
@@ -215,7 +245,7 @@ __device__ bool wait_range(const DevModel &m, uint32_t lo, uint32_t hi, uint32_t
         if (flag_load(&m.err[1]) != 0) return false;
         if (wall_clock64() - t0 > m.timeout_ticks) {
           if (lane == 0) {
-            record_error(m.err, ERR_TIMEOUT, task, idx);
+            record_error(m.err, ERR_TIMEOUT, task, g);
             __hip_atomic_store(&m.err[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
           return false;
@@ -225,7 +255,7 @@ __device__ bool wait_range(const DevModel &m, uint32_t lo, uint32_t hi, uint32_t
     }
   }
   // No acquire fence: everything a task reads that was produced in this launch is read with
-  // device-coherent loads (cld), ordered after the flag observation.
+  // device-coherent loads, ordered after the flag observation.
   return true;
 }
 
@@ -425,31 +455,63 @@ __device__ __forceinline__ int32_t token_of(const DevModel &m, const StepArgs &s
   return t;
 }
 
-// xs[b][i] = rmsnorm(src_b)[i] * gain[i]. src = h slot `slot` or, for slot 0, the embedding row.
+// RMSNorm staging, split around the GEMV. The norm's scale 1/rms(src_b) is one number per batch
+// row, so W (src_b * gain) scaled afterwards equals W rmsnorm(src_b) * gain: the input is staged
+// as xs[b][i] = src_b[i] * gain[i] in one round of loads, and the per-wave partial sums of
+// squares go to red[b * nw + wave]; norm_scale_ys applies the scale to the GEMV outputs.
+// src = h slot `slot` or, for slot 0, the embedding row of the token. Needs d % 4 == 0.
+constexpr int kStageVec = 4;  // float4 groups per thread per round (d <= 8192 in one round)
 __device__ void stage_norm(const DevModel &m, const StepArgs &s, int slot, const uint16_t *gain,
                            float *xs, float *red, int nw) {
-  const int d = m.d;
+  const int d = m.d, n4 = d / 4;
+  const int lane = lane_id(), wave = wave_id();
   for (int b = 0; b < s.batch; ++b) {
     float *x = xs + (int64_t)b * d;
+    const uint16_t *e = (slot == 0) ? m.embed + (int64_t)token_of(m, s, b) * d : nullptr;
+    const float *src = m.h + ((int64_t)slot * m.max_batch + b) * d;
+    const __amdgpu_buffer_rsrc_t rs = coh_rsrc(src, (uint32_t)d * 4u);
     float ss = 0.f;
-    if (slot == 0) {
-      const uint16_t *e = m.embed + (int64_t)token_of(m, s, b) * d;
-      for (int i = threadIdx.x; i < d; i += nw * 64) {
-        float v = bf16_to_f32(gld(&e[i]));
-        x[i] = v;
-        ss += v * v;
+    for (int base = 0; base < n4; base += kStageVec * nw * 64) {
+      float4 hv[kStageVec];
+      uint2 gv[kStageVec];
+#pragma unroll
+      for (int j = 0; j < kStageVec; ++j) {
+        const int i4 = min(base + (int)threadIdx.x + j * nw * 64, n4 - 1);
+        if (e) {
+          const uint2 ev = gld_bf16x4(e, i4);
+          hv[j] = make_float4(bf_lo(ev.x), bf_hi(ev.x), bf_lo(ev.y), bf_hi(ev.y));
+        } else {
+          hv[j] = cld4(rs, (uint32_t)i4 * 16u);
+        }
+        gv[j] = gld_bf16x4(gain, i4);
       }
-    } else {
-      const float *src = m.h + ((int64_t)slot * m.max_batch + b) * d;
-      for (int i = threadIdx.x; i < d; i += nw * 64) {
-        float v = cldf(&src[i]);
-        x[i] = v;
-        ss += v * v;
+#pragma unroll
+      for (int j = 0; j < kStageVec; ++j) {
+        const int i4 = base + (int)threadIdx.x + j * nw * 64;
+        if (i4 < n4) {
+          const float4 v = hv[j];
+          ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+          *reinterpret_cast<float4 *>(x + 4 * i4) =
+              make_float4(v.x * bf_lo(gv[j].x), v.y * bf_hi(gv[j].x), v.z * bf_lo(gv[j].y),
+                          v.w * bf_hi(gv[j].y));
+        }
       }
     }
-    const float tot = block_sum(ss, red, nw);
-    const float inv = 1.0f / sqrtf(tot / (float)d + m.eps);
-    for (int i = threadIdx.x; i < d; i += nw * 64) x[i] = x[i] * inv * bf16_to_f32(gld(&gain[i]));
+    ss = wave_sum(ss);
+    if (lane == 0) red[b * nw + wave] = ss;
+  }
+  __syncthreads();
+}
+
+// ys[b][i] *= 1 / sqrt(mean(src_b^2) + eps) with the partial sums stage_norm left in red (read
+// after the workgroup barrier that follows the GEMV). Ends with a barrier.
+__device__ void norm_scale_ys(const DevModel &m, const StepArgs &s, int n, float *ys,
+                              const float *red, int nw) {
+  for (int b = 0; b < s.batch; ++b) {
+    float tot = 0.f;
+    for (int w = 0; w < nw; ++w) tot += red[b * nw + w];
+    const float inv = 1.0f / sqrtf(tot / (float)m.d + m.eps);
+    for (int i = threadIdx.x; i < n; i += nw * 64) ys[b * n + i] *= inv;
   }
   __syncthreads();
 }
@@ -490,9 +552,26 @@ __device__ void stage_combine(const DevModel &m, const StepArgs &s, int l, float
   }
 }
 
+// xs[b][i] = src[b * src_stride + i], i < K (K % 4 == 0, src rows 16-byte aligned): device-
+// coherent 16-byte loads, kStageVec * 2 per thread in flight per round.
 __device__ void stage_plain(const float *src, int64_t src_stride, int K, int B, float *xs, int nw) {
-  for (int b = 0; b < B; ++b)
-    for (int i = threadIdx.x; i < K; i += nw * 64) xs[(int64_t)b * K + i] = cldf(&src[b * src_stride + i]);
+  const int n4 = K / 4;
+  constexpr int V = 2 * kStageVec;
+  for (int b = 0; b < B; ++b) {
+    const __amdgpu_buffer_rsrc_t rs = coh_rsrc(src + b * src_stride, (uint32_t)K * 4u);
+    float *x = xs + (int64_t)b * K;
+    for (int base = 0; base < n4; base += V * nw * 64) {
+      float4 v[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        v[j] = cld4(rs, (uint32_t)min(base + (int)threadIdx.x + j * nw * 64, n4 - 1) * 16u);
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const int i4 = base + (int)threadIdx.x + j * nw * 64;
+        if (i4 < n4) *reinterpret_cast<float4 *>(x + 4 * i4) = v[j];
+      }
+    }
+  }
   __syncthreads();
 }
 

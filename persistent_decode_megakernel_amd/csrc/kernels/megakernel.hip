@@ -15,9 +15,11 @@
 
 namespace amk {
 
-// GEMV tile task: the first weight chunk of every wave is issued before the dependency wait, the
-// input vector is staged (RMSNorm / attention combine / plain copy) after it, then the row stream
-// runs double-buffered and the epilogue writes the tile's outputs.
+// GEMV tile task: the first weight chunk of waves 1.. is issued before the dependency wait (wave
+// 0 polls the flags, and a wave's loads return in order, so its flag reads would queue behind its
+// own prefetch); the input vector is staged (RMSNorm / attention combine / plain copy) after the
+// wait, then the row stream runs double-buffered, the RMSNorm scale is applied to the outputs and
+// the epilogue writes them.
 template <int WT>
 __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, const Task &t,
                                           float *xs, float *ys, float *red, int *abort_slot) {
@@ -32,8 +34,10 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
   GemvStream<WT> st;
   uint4 P[kChunkUnits];
   st.init(W, K, r0, r1, NW);
-  if (b1 && st.S > 0) st.load(P, 0);
+  const bool poller = st.wave == 0;
+  if (b1 && st.S > 0 && !poller) st.load(P, 0);
   if (!wait_task(m, t, s.epoch, abort_slot)) return false;
+  if (b1 && st.S > 0 && poller) st.load(P, 0);
   switch (t.mat) {
     case M_QKV: stage_norm(m, s, 2 * l, m.layers[l].attn_norm, xs, red, NW); break;
     case M_O: stage_combine(m, s, l, xs, red, NW); break;
@@ -47,6 +51,7 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
   else
     gemv_rows<WT>(W, scale, K, r0, r1, xs, ys, s.batch, NW);
   __syncthreads();
+  if (t.mat != M_O && t.mat != M_D) norm_scale_ys(m, s, r1 - r0, ys, red, NW);
   switch (t.mat) {
     case M_QKV: epi_qkv(m, s, l, r0, r1, ys, NW); break;
     case M_O: epi_residual(m, s, 2 * l, 2 * l + 1, r0, r1, ys, NW); break;
