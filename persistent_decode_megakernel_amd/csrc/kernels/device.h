@@ -33,6 +33,8 @@ struct DevModel {
   float *h;            // [2L+1][B][d] residual stream (slot 0 unused: the embedding row)
   float *q;            // [L][B][qd]
   float *part;         // [L][B][nq][nblk][hd+2]
+  float *ao;           // [L][B][qd] attention output, merged over the KV blocks
+  uint32_t *acnt;      // [L][nkv] KV blocks of the group finished in this step (0 between steps)
   float *a;            // [L][B][F]
   float *logits;       // [B][V] used when the caller passes no logits buffer
   float2 *amax;        // [n_lm][B] (value, index bits)
@@ -259,9 +261,11 @@ __device__ bool wait_range(const DevModel &m, uint32_t lo, uint32_t hi, uint32_t
   return true;
 }
 
-// Dependency wait of a task: wave 0 spins on the task's flag ranges, then the workgroup meets at
-// a barrier. Returns false on every thread when the wait timed out or the step was aborted.
-__device__ __forceinline__ bool wait_task(const DevModel &m, const Task &t, uint32_t epoch,
+// Dependency wait of a task in two halves: wait_poll (wave 0 spins on the task's flag ranges;
+// other waves return at once) and wait_join (the workgroup meets at a barrier; false on every
+// thread when the wait timed out or the step was aborted). Work placed between the two runs on
+// waves 1.. before the flags are seen and on wave 0 after.
+__device__ __forceinline__ void wait_poll(const DevModel &m, const Task &t, uint32_t epoch,
                                           int *abort_slot) {
   if (wave_id() == 0) {
     bool ok = true;
@@ -269,9 +273,16 @@ __device__ __forceinline__ bool wait_task(const DevModel &m, const Task &t, uint
     if (ok && t.w1_hi > t.w1_lo) ok = wait_range(m, t.w1_lo, t.w1_hi, epoch, t.id);
     if (lane_id() == 0) *abort_slot = ok ? 0 : 1;
   }
+}
+__device__ __forceinline__ bool wait_join(const DevModel &m, const Task &t, int *abort_slot) {
   __syncthreads();
   if (m.trace && threadIdx.x == 0) m.trace[(uint64_t)t.id * 4 + 1] = wall_clock64();
   return *abort_slot == 0;
+}
+__device__ __forceinline__ bool wait_task(const DevModel &m, const Task &t, uint32_t epoch,
+                                          int *abort_slot) {
+  wait_poll(m, t, epoch, abort_slot);
+  return wait_join(m, t, abort_slot);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -516,42 +527,6 @@ __device__ void norm_scale_ys(const DevModel &m, const StepArgs &s, int n, float
   __syncthreads();
 }
 
-// xs[b][h*hd + j] = attention output of head h, merged over the KV blocks (log-sum-exp):
-// o = sum_k e^{m_k - M} acc_k / sum_k e^{m_k - M} l_k with M = max_k m_k. Two rounds: one thread
-// per head computes the block weights w_k = e^{m_k - M} / sum e^{m - M} l into LDS (wts, >= nq*nblk
-// floats), then every output element sums its nblk weighted accumulators (independent loads).
-__device__ void stage_combine(const DevModel &m, const StepArgs &s, int l, float *xs, float *wts,
-                              int nw) {
-  const int hd = m.hd, nblk = m.nblk, qd = m.qd, nq = m.nq;
-  for (int b = 0; b < s.batch; ++b) {
-    const float *pb = m.part + (((int64_t)l * m.max_batch + b) * nq) * nblk * (hd + 2);
-    for (int h = threadIdx.x; h < nq; h += nw * 64) {
-      const float *ph = pb + (int64_t)h * nblk * (hd + 2);
-      float M = -INFINITY;
-      for (int k = 0; k < nblk; ++k) M = fmaxf(M, cldf(&ph[k * (hd + 2) + hd]));
-      float den = 0.f;
-      for (int k = 0; k < nblk; ++k) {
-        const float w = __expf(cldf(&ph[k * (hd + 2) + hd]) - M);  // empty blocks: m = -inf -> 0
-        wts[h * nblk + k] = w;
-        den = fmaf(w, cldf(&ph[k * (hd + 2) + hd + 1]), den);
-      }
-      const float inv = 1.0f / den;
-      for (int k = 0; k < nblk; ++k) wts[h * nblk + k] *= inv;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < qd; e += nw * 64) {
-      const int h = e / hd, j = e - h * hd;
-      const float *ph = pb + (int64_t)h * nblk * (hd + 2) + j;
-      const float *wh = wts + h * nblk;
-      float acc = 0.f;
-#pragma unroll 8
-      for (int k = 0; k < nblk; ++k) acc = fmaf(wh[k], cldf(&ph[k * (hd + 2)]), acc);
-      xs[(int64_t)b * qd + e] = acc;
-    }
-    __syncthreads();
-  }
-}
-
 // xs[b][i] = src[b * src_stride + i], i < K (K % 4 == 0, src rows 16-byte aligned): device-
 // coherent 16-byte loads, kStageVec * 2 per thread in flight per round.
 __device__ void stage_plain(const float *src, int64_t src_stride, int K, int B, float *xs, int nw) {
@@ -733,7 +708,7 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
     const uint16_t *Kb = s.kv + kv_index(m, s, l, 0, b, g, 0, 0);
     const uint16_t *Vb = s.kv + kv_index(m, s, l, 1, b, g, 0, 0);
     uint4 kr[NIT], vr[NIT];
-    {
+    auto load_history = [&]() {
       const int c1 = min(hi, lo + kAttnRowsPerChunk);
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
@@ -742,10 +717,13 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
         kr[it] = ok ? gld4(reinterpret_cast<const uint4 *>(Kb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
         vr[it] = ok ? gld4(reinterpret_cast<const uint4 *>(Vb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
       }
-    }
-    if (wait_for && b == 0) {
-      if (!wait_task(m, *wait_for, s.epoch, abort_slot)) return false;
-    }
+    };
+    // wave 0 polls the flags and a wave's loads return in order, so it issues its history rows
+    // after polling; the other waves issue theirs before the join
+    const bool waits = wait_for && b == 0;
+    if (waits) wait_poll(m, *wait_for, s.epoch, abort_slot);
+    load_history();
+    if (waits && !wait_join(m, *wait_for, abort_slot)) return false;
     const float *qsrc = m.q + ((int64_t)l * m.max_batch + b) * m.qd + ((int64_t)g * m.qpg + h0) * HD;
     for (int i = threadIdx.x; i < qpg * HD; i += NW * 64) qs[i] = cldf(&qsrc[i]) * m.attn_scale;
     __syncthreads();
@@ -900,6 +878,70 @@ __device__ __forceinline__ bool attn_task(const DevModel &m, const StepArgs &s, 
                               h0 == 0 ? wait_for : nullptr, abort_slot))
       return false;
   return true;
+}
+
+// Merge the nblk partials of KV group g (all batch rows, all of its query heads) into
+// ao[l][b][head * hd + e] = sum_k e^{m_k - M} acc_k[e] / sum_k e^{m_k - M} l_k, M = max_k m_k
+// (log-sum-exp over the blocks; an empty block has m = -inf, l = 0, acc = 0). One element per
+// thread; the blocks are visited eight at a time with all of their loads issued together and
+// the running maximum rescaled between batches.
+__device__ void attn_group_combine(const DevModel &m, const StepArgs &s, int l, int g) {
+  constexpr int KB = 8;
+  const int hd = m.hd, nblk = m.nblk, qpg = m.qpg, nq = m.nq;
+  const int per_b = qpg * hd, total = s.batch * per_b;
+  for (int i = threadIdx.x; i < total; i += kThreads) {
+    const int b = i / per_b, r = i - b * per_b, h = g * qpg + r / hd, e = r % hd;
+    const float *ph = m.part + (((int64_t)l * m.max_batch + b) * nq + h) * nblk * (hd + 2);
+    float M = -INFINITY, den = 0.f, num = 0.f;
+    for (int k0 = 0; k0 < nblk; k0 += KB) {
+      float mk[KB], lk[KB], ak[KB];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        const float *pk = ph + (int64_t)min(k0 + j, nblk - 1) * (hd + 2);
+        mk[j] = cldf(pk + hd);
+        lk[j] = cldf(pk + hd + 1);
+        ak[j] = cldf(pk + e);
+      }
+      float Mb = M;
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+        if (k0 + j < nblk) Mb = fmaxf(Mb, mk[j]);
+      if (Mb == -INFINITY) continue;  // only empty blocks so far
+      const float f = __expf(M - Mb);  // M = -inf: f = 0 and den = num = 0 anyway
+      den *= f;
+      num *= f;
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        if (k0 + j < nblk) {
+          const float w = __expf(mk[j] - Mb);
+          den = fmaf(w, lk[j], den);
+          num = fmaf(w, ak[j], num);
+        }
+      }
+      M = Mb;
+    }
+    cstf(&m.ao[((int64_t)l * m.max_batch + b) * m.qd + (int64_t)h * hd + e], num / den);
+  }
+}
+
+// After a KV block task of group g has stored its partials: count it; the task that completes
+// the group's count for this step merges the group's partials (attn_group_combine). Every wave
+// first waits for its own partial stores, so a block is counted only once its data is visible
+// at device scope; the last counter holds all nblk blocks' data. The last one also sets the
+// counter back to zero for the next step (nothing else touches it before this launch ends).
+__device__ __forceinline__ void attn_count_and_combine(const DevModel &m, const StepArgs &s,
+                                                       int l, int g, int *last_slot) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t *cnt = &m.acnt[(int64_t)l * m.nkv + g];
+    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old + 1u == (uint32_t)m.nblk;
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *last_slot = last;
+  }
+  __syncthreads();
+  if (*last_slot) attn_group_combine(m, s, l, g);
 }
 
 // ------------------------------------------------------------------------------------------

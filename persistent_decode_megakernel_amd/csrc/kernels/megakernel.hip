@@ -15,9 +15,9 @@
 
 namespace amk {
 
-// GEMV tile task: the first weight chunk of waves 1.. is issued before the dependency wait (wave
-// 0 polls the flags, and a wave's loads return in order, so its flag reads would queue behind its
-// own prefetch); the input vector is staged (RMSNorm / attention combine / plain copy) after the
+// GEMV tile task: the first weight chunk of waves 1.. is issued before the dependency wait
+// completes (wave 0 polls the flags and issues its chunk after: a wave's loads return in order,
+// so its flag reads would queue behind its own prefetch); the input vector is staged (RMSNorm / attention combine / plain copy) after the
 // wait, then the row stream runs double-buffered, the RMSNorm scale is applied to the outputs and
 // the epilogue writes them.
 template <int WT>
@@ -34,13 +34,12 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
   GemvStream<WT> st;
   uint4 P[kChunkUnits];
   st.init(W, K, r0, r1, NW);
-  const bool poller = st.wave == 0;
-  if (b1 && st.S > 0 && !poller) st.load(P, 0);
-  if (!wait_task(m, t, s.epoch, abort_slot)) return false;
-  if (b1 && st.S > 0 && poller) st.load(P, 0);
+  wait_poll(m, t, s.epoch, abort_slot);
+  if (b1 && st.S > 0) st.load(P, 0);
+  if (!wait_join(m, t, abort_slot)) return false;
   switch (t.mat) {
     case M_QKV: stage_norm(m, s, 2 * l, m.layers[l].attn_norm, xs, red, NW); break;
-    case M_O: stage_combine(m, s, l, xs, red, NW); break;
+    case M_O: stage_plain(m.ao + (int64_t)l * m.max_batch * m.qd, m.qd, m.qd, s.batch, xs, NW); break;
     case M_GU: stage_norm(m, s, 2 * l + 1, m.layers[l].mlp_norm, xs, red, NW); break;
     case M_D: stage_plain(m.a + (int64_t)l * m.max_batch * m.F, m.F, m.F, s.batch, xs, NW); break;
     default: stage_norm(m, s, 2 * m.L, m.final_norm, xs, red, NW); break;
@@ -70,7 +69,7 @@ __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArg
   float *xs = lds;
   float *red = lds + (xa > xb ? xa : xb);  // kRedFloats floats
   float *ys = red + kRedFloats;            // batch * max_tile_rows floats
-  __shared__ int abort_flag;
+  __shared__ int abort_flag, last_flag;
   const uint32_t t0 = m.offsets[blockIdx.x], t1 = m.offsets[blockIdx.x + 1];
   uint64_t *const trace = m.trace;
   if (trace && threadIdx.x == 0) {
@@ -86,6 +85,7 @@ __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArg
       ok = gemv_task<WT>(m, s, t, xs, ys, red, &abort_flag);
     } else if (t.type == T_ATTN) {
       ok = attn_task<HD, QMAX>(m, s, t.layer, (int)t.a0, (int)t.a1, xs, red, &t, &abort_flag);
+      if (ok) attn_count_and_combine(m, s, t.layer, (int)t.a0, &last_flag);
     } else {
       ok = wait_task(m, t, s.epoch, &abort_flag);
       if (ok) argmax_combine(m, s, (int)t.aux0);

@@ -203,6 +203,7 @@ amk_status map_device_error(uint32_t code, uint32_t task, uint32_t detail) {
 void reset_device_state(amk_model *m, hipStream_t st) {
   (void)hipMemsetAsync(m->dm.err, 0, 4 * sizeof(uint32_t), st);
   (void)hipMemsetAsync(m->dm.flags, 0, sizeof(uint32_t) * std::max<uint32_t>(1, m->sched.hdr.n_tasks), st);
+  (void)hipMemsetAsync(m->dm.acnt, 0, sizeof(uint32_t) * m->cfg.n_layers * m->cfg.n_kv_heads, st);
   (void)hipStreamSynchronize(st);
   m->epoch = 0;
   m->err_pending = false;
@@ -403,6 +404,8 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     dm.h = m->dalloc<float>((size_t)(2 * L + 1) * B * d);
     dm.q = m->dalloc<float>((size_t)L * B * qd);
     dm.part = m->dalloc<float>((size_t)L * B * nq * nblk * (hd + 2));
+    dm.ao = m->dalloc<float>((size_t)L * B * qd);
+    dm.acnt = m->dalloc<uint32_t>((size_t)L * cfg->n_kv_heads);
     dm.a = m->dalloc<float>((size_t)L * B * F);
     dm.logits = m->dalloc<float>((size_t)B * V);
     m->n_lm_uf = (V + kUfRowsPerBlock - 1) / kUfRowsPerBlock;
@@ -415,6 +418,7 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     dm.o = m->dalloc<float>((size_t)B * qd);
     hip_check(hipMemsetAsync(dm.flags, 0, sizeof(uint32_t) * std::max<uint32_t>(1, h.n_tasks), st), "hipMemsetAsync");
     hip_check(hipMemsetAsync(dm.err, 0, 16, st), "hipMemsetAsync");
+    hip_check(hipMemsetAsync(dm.acnt, 0, sizeof(uint32_t) * L * cfg->n_kv_heads, st), "hipMemsetAsync");
     // task tables
     std::vector<uint32_t> offs(h.n_cu + 1);
     std::vector<Task> tasks;

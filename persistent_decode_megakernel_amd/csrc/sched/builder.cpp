@@ -235,13 +235,13 @@ void task_bytes(const BlobHeader &h, const Task &t, int32_t ctx, double *hbm, do
     double w = (t.mat == M_LM && c.tied_lm_head) ? 2.0 : wb;
     *hbm = rows * K * w + (w == 1.0 ? rows * 4.0 : 0.0);
     *act = B * K * 4.0;
-    if (t.mat == M_O)
-      *act += B * c.n_heads * (double)h.attn_blocks * (c.head_dim + 2) * 4.0;
   } else if (t.type == T_ATTN) {
     int32_t lo, hi;
     attn_block_range(ctx, (int32_t)h.attn_blocks, (int32_t)t.a1, &lo, &hi);
     *hbm = B * 2.0 * (double)(hi - lo) * c.head_dim * 2.0;
-    *act = B * (c.n_heads / c.n_kv_heads) * c.head_dim * 4.0;
+    // q, plus (once per group, by the last block) the group's partials for the combine
+    const double qpg = c.n_heads / c.n_kv_heads;
+    *act = B * qpg * c.head_dim * 4.0 + B * qpg * (c.head_dim + 2) * 4.0;
   } else if (t.type == T_ARGMAX) {
     *act = (double)t.aux0 * B * 8.0;
   }

@@ -35,13 +35,18 @@ enum BufId : int32_t {
   BUF_LOGITS = 5,  // [B][V]
   BUF_AMAX = 6,    // argmax partials [slots][B]
   BUF_NEXT = 7,    // [B]
+  BUF_AO = 8,      // attention output merged over the KV blocks, per layer: [B][nq*hd]
 };
 
+// An access with group >= 0 belongs to a combine group (the nblk KV-block tasks of one layer and
+// KV group, group = layer * n_kv_heads + g): it is performed once per step, by whichever member
+// finishes last, after every member's own accesses (a device counter decides and orders it).
 struct Access {
   int32_t buf;    // BufId
-  int32_t index;  // layer (BUF_Q/KVNEW/PART/A) or residual slot (BUF_H); 0 otherwise
+  int32_t index;  // layer (BUF_Q/KVNEW/PART/A/AO) or residual slot (BUF_H); 0 otherwise
   int64_t lo, hi; // element range [lo, hi)
   bool write;
+  int32_t group;  // -1: the task's own access
 };
 
 // Read/write footprint of a task, derived from the task's own fields and the config. Reads of

@@ -31,8 +31,9 @@ std::string fmt(const char *f, long long a = 0, long long b = 0, long long c = 0
   return buf;
 }
 
-void add_range(std::vector<Access> *acc, int buf, int index, int64_t lo, int64_t hi, bool w) {
-  if (hi > lo) acc->push_back(Access{buf, index, lo, hi, w});
+void add_range(std::vector<Access> *acc, int buf, int index, int64_t lo, int64_t hi, bool w,
+               int32_t group = -1) {
+  if (hi > lo) acc->push_back(Access{buf, index, lo, hi, w, group});
 }
 
 // Merge sorted element indices into intervals.
@@ -95,7 +96,7 @@ bool footprint(const BlobHeader &h, const Task &t, std::vector<Access> *acc, std
         break;
       }
       case M_O:
-        add_range(acc, BUF_PART, (int)l, 0, B * nq * nblk * (hd + 2), false);
+        add_range(acc, BUF_AO, (int)l, 0, B * qd, false);
         for (int64_t b = 0; b < B; ++b) {
           if (l > 0) add_range(acc, BUF_H, (int)(2 * l), b * d + a0, b * d + a1, false);
           add_range(acc, BUF_H, (int)(2 * l + 1), b * d + a0, b * d + a1, true);
@@ -137,6 +138,15 @@ bool footprint(const BlobHeader &h, const Task &t, std::vector<Access> *acc, std
         int64_t base = ((b * nq + hh) * nblk + blk) * (hd + 2);
         add_range(acc, BUF_PART, (int)l, base, base + hd + 2, true);
       }
+    }
+    // the group's combine: every block's partials in, the merged heads out
+    const int32_t grp = (int32_t)(l * nkv + g);
+    for (int64_t b = 0; b < B; ++b) {
+      for (int64_t hh = g * qpg; hh < (g + 1) * qpg; ++hh) {
+        int64_t base = (b * nq + hh) * nblk * (hd + 2);
+        add_range(acc, BUF_PART, (int)l, base, base + nblk * (hd + 2), false, grp);
+      }
+      add_range(acc, BUF_AO, (int)l, b * qd + g * qpg * hd, b * qd + (g + 1) * qpg * hd, true, grp);
     }
     return true;
   }
@@ -205,6 +215,7 @@ struct BufKey {
 struct Span {
   int64_t lo, hi;
   uint32_t id;
+  int32_t group;  // >= 0: a combine-group write (ordered after every member of the group)
 };
 
 }  // namespace
@@ -298,13 +309,31 @@ bool validate_schedule(const Schedule &s, std::string *report) {
   if (q.size() != n) return fail(fmt("dependency cycle: %lld of %lld tasks can never start", n - q.size(), n));
   g.stamp.assign(n, 0);
 
-  // footprints grouped by buffer instance
-  std::map<BufKey, std::vector<Span>> writes, reads;
+  // footprints grouped by buffer instance; a combine group's accesses are taken once (from its
+  // first member) and its members collected
+  std::map<BufKey, std::vector<Span>> writes, reads, group_reads;
+  std::map<int32_t, std::vector<uint32_t>> members;
   std::vector<Access> acc;
   for (uint32_t id = 0; id < n; ++id) {
     if (!footprint(h, *g.task[id], &acc, &e)) return fail(e);
+    int32_t grp = -1;
     for (const Access &a : acc)
-      (a.write ? writes : reads)[BufKey{a.buf, a.index}].push_back(Span{a.lo, a.hi, id});
+      if (a.group >= 0) grp = a.group;
+    const bool first = grp >= 0 && members[grp].empty();
+    if (grp >= 0) members[grp].push_back(id);
+    for (const Access &a : acc) {
+      if (a.group < 0)
+        (a.write ? writes : reads)[BufKey{a.buf, a.index}].push_back(Span{a.lo, a.hi, id, -1});
+      else if (first)
+        (a.write ? writes : group_reads)[BufKey{a.buf, a.index}].push_back(Span{a.lo, a.hi, id, a.group});
+    }
+  }
+  std::vector<int32_t> group_of(n, -1);
+  for (auto &kv : members) {
+    if ((uint32_t)kv.second.size() != h.attn_blocks)
+      return fail(fmt("combine group %lld has %lld of %lld KV-block tasks", kv.first,
+                      (long long)kv.second.size(), h.attn_blocks));
+    for (uint32_t id : kv.second) group_of[id] = kv.first;
   }
   size_t checked = 0;
   for (auto &kv : writes) {
@@ -329,11 +358,39 @@ bool validate_schedule(const Schedule &s, std::string *report) {
           return fail(fmt("task %lld reads element %lld that no task writes", rd.id, covered));
         covered = w[i].hi;
         ++checked;
-        if (!g.hb(w[i].id, rd.id))
-          return fail(fmt("race: task %lld reads data of task %lld without waiting for it (buffer %lld)", rd.id, w[i].id, kv.first.buf));
+        if (w[i].group < 0) {
+          if (!g.hb(w[i].id, rd.id))
+            return fail(fmt("race: task %lld reads data of task %lld without waiting for it (buffer %lld)", rd.id, w[i].id, kv.first.buf));
+        } else {
+          // written by the group's last member: the reader must wait for every member
+          for (uint32_t mb : members[w[i].group])
+            if (!g.hb(mb, rd.id))
+              return fail(fmt("race: task %lld reads the combine of group %lld without waiting for task %lld", rd.id, w[i].group, mb));
+        }
       }
       if (covered < rd.hi)
         return fail(fmt("task %lld reads element %lld that no task writes", rd.id, covered));
+    }
+  }
+  // a combine reads only data its own group's members wrote (ordered by the group counter)
+  for (auto &kv : group_reads) {
+    auto it = writes.find(kv.first);
+    for (const Span &rd : kv.second) {
+      if (it == writes.end())
+        return fail(fmt("combine group %lld reads buffer %lld that no task writes", rd.group, kv.first.buf));
+      const auto &w = it->second;
+      size_t i = std::lower_bound(w.begin(), w.end(), rd.lo,
+                                  [](const Span &a, int64_t v) { return a.hi <= v; }) - w.begin();
+      int64_t covered = rd.lo;
+      for (; i < w.size() && w[i].lo < rd.hi; ++i) {
+        if (w[i].lo > covered) break;
+        covered = w[i].hi;
+        ++checked;
+        if (w[i].group >= 0 || group_of[w[i].id] != rd.group)
+          return fail(fmt("combine group %lld reads data of task %lld outside the group", rd.group, w[i].id));
+      }
+      if (covered < rd.hi)
+        return fail(fmt("combine group %lld reads element %lld that no task writes", rd.group, covered));
     }
   }
   // outputs must be complete
@@ -409,18 +466,34 @@ bool sim_run(const Schedule &s, int64_t delayed, std::string *msg) {
     }
     return true;
   };
+  std::map<int32_t, uint32_t> finished;  // combine group -> members finished
   auto exec = [&](const Task &t) -> bool {
     if (!footprint(s.hdr, t, &acc, &e)) { *msg = e; return false; }
-    for (const Access &a : acc)
+    int32_t grp = -1;
+    for (const Access &a : acc) {
+      if (a.group >= 0) { grp = a.group; continue; }
       if (!a.write && !sh.covered(a)) {
         *msg = fmt("stale read: task %lld ran before the data it reads (buffer %lld) was written", t.id, a.buf);
         return false;
       }
+    }
     for (const Access &a : acc)
-      if (a.write) {
+      if (a.write && a.group < 0) {
         if (sh.overlaps(a)) { *msg = fmt("double write by task %lld (buffer %lld)", t.id, a.buf); return false; }
         sh.add(a);
       }
+    if (grp >= 0 && ++finished[grp] == s.hdr.attn_blocks) {  // this task runs the combine
+      for (const Access &a : acc)
+        if (a.group >= 0 && !a.write && !sh.covered(a)) {
+          *msg = fmt("stale read: combine of group %lld before its partials were written (task %lld)", grp, t.id);
+          return false;
+        }
+      for (const Access &a : acc)
+        if (a.group >= 0 && a.write) {
+          if (sh.overlaps(a)) { *msg = fmt("double write by the combine of group %lld", grp); return false; }
+          sh.add(a);
+        }
+    }
     if (t.id < n) done[t.id] = 1;
     --left;
     return true;

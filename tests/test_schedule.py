@@ -65,7 +65,7 @@ def mutate(b: B.Blob, rng: random.Random) -> str:
     cus = [c for c in range(len(b.per_cu)) if len(b.per_cu[c])]
     kind = rng.choice(["drop_wait", "shrink_wait", "shift_wait", "swap_same_cu", "move_cu",
                        "dup_rows", "gap_rows", "self_wait", "wait_later_same_cu", "widen_wait",
-                       "reorder_cu", "bad_field"])
+                       "reorder_cu", "bad_field", "attn_regroup", "attn_reblock"])
     c = rng.choice(cus)
     v = b.per_cu[c]
     i = rng.randrange(len(v))
@@ -108,6 +108,15 @@ def mutate(b: B.Blob, rng: random.Random) -> str:
         t["w1_lo"], t["w1_hi"] = v[j]["id"], v[j]["id"] + 1
     elif kind == "bad_field":
         t["a1"] = 10 ** 6
+    elif kind in ("attn_regroup", "attn_reblock"):
+        # move a KV-block task to another group or block: its group's combine loses a member
+        attn = [(c2, j) for c2 in range(len(b.per_cu)) for j in range(len(b.per_cu[c2]))
+                if b.per_cu[c2][j]["type"] == B.T_ATTN]
+        c2, j = rng.choice(attn)
+        t = b.per_cu[c2][j]
+        field, top = ("a0", b.hdr.cfg.n_kv_heads) if kind == "attn_regroup" else ("a1", b.hdr.attn_blocks)
+        if top > 1:
+            t[field] = (int(t[field]) + rng.randrange(1, top)) % top
     return kind
 
 
@@ -147,3 +156,47 @@ def test_truncated_and_corrupt_blobs_rejected(libamk):
     b = B.Blob(blob)
     b.hdr.lds_bytes = 200 * 1024
     assert _lib.schedule_validate(b.to_bytes())[0] == _lib.AMK_E_SCHEDULE_REJECTED
+
+
+def _o_task_and_attn(b: B.Blob, layer: int):
+    o = [(c, j) for c in range(len(b.per_cu)) for j in range(len(b.per_cu[c]))
+         if b.per_cu[c][j]["type"] == B.T_GEMV and b.per_cu[c][j]["mat"] == B.M_O
+         and b.per_cu[c][j]["layer"] == layer]
+    attn = sorted(int(t["id"]) for v in b.per_cu for t in v
+                  if t["type"] == B.T_ATTN and t["layer"] == layer)
+    return o, attn
+
+
+@pytest.mark.parametrize("drop", ["first", "last"])
+def test_o_task_must_wait_for_every_kv_block_of_the_combine(libamk, drop):
+    """The attention output is merged by whichever KV-block task of a group finishes last (a
+    device counter decides), so an O-projection tile that skips any one block's flag may read an
+    unmerged output: the validator rejects it and the delayed-CU simulation shows the stale read."""
+    cfg = synth.get_config("tiny")
+    b = B.Blob(_lib.schedule_build(_lib.make_config(cfg), 1, 8))
+    o, attn = _o_task_and_attn(b, 1)
+    dropped = attn[0] if drop == "first" else attn[-1]
+    cu_of = {int(t["id"]): c for c in range(len(b.per_cu)) for t in b.per_cu[c]}
+    # an O tile on another CU than the dropped block (program order would still cover it)
+    c, j = next((c, j) for c, j in o if c != cu_of[dropped])
+    t = b.per_cu[c][j]
+    assert (int(t["w0_lo"]), int(t["w0_hi"])) == (attn[0], attn[-1] + 1)
+    if drop == "first":
+        t["w0_lo"] = attn[0] + 1
+    else:
+        t["w0_hi"] = attn[-1]
+    data = b.to_bytes()
+    st, rep = _lib.schedule_validate(data)
+    assert st == _lib.AMK_E_SCHEDULE_REJECTED and "combine" in rep, rep
+    assert _lib.schedule_simulate(data)[0] != _lib.AMK_OK
+
+
+def test_combine_group_needs_all_blocks(libamk):
+    cfg = synth.get_config("tiny")
+    b = B.Blob(_lib.schedule_build(_lib.make_config(cfg), 1, 8))
+    for v in b.per_cu:
+        for t in v:
+            if t["type"] == B.T_ATTN and t["layer"] == 0 and t["a0"] == 0 and t["a1"] == 0:
+                t["a0"] = 1  # block 0 of group 0 now claims group 1: group 0 is one short
+    st, rep = _lib.schedule_validate(b.to_bytes())
+    assert st == _lib.AMK_E_SCHEDULE_REJECTED, rep
