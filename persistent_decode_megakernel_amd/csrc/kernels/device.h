@@ -193,7 +193,13 @@ __device__ __forceinline__ uint2 gld_bf16x4(const uint16_t *p, int i4) {
   return make_uint2(v.x, v.y);
 }
 constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kCachePolicyNt = 2;
 constexpr int kCachePolicySc1 = 16;
+// s_waitcnt immediates (gfx9 layout: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at
+// [15:14]) waiting on vector memory only
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitVm8 = 0x0F78;
+#define AMK_LDS __attribute__((address_space(3)))
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
 }
@@ -396,6 +402,17 @@ struct GemvStream {
 #pragma unroll
     for (int j = 0; j < kChunkUnits; ++j) buf[j] = load_nt(rp + min(base + j * 64, n16 - 1));
   }
+  // chunk s straight into LDS, bypassing registers: 16 bytes per lane per instruction, lane i's
+  // bytes at dst + 16 i (dst: this wave's 8 KB slot)
+  __device__ __forceinline__ void load_lds(int s, uint4 *dst) const {
+    const int row = row_of(s), c = s % nch;
+    const uint4 *rp = reinterpret_cast<const uint4 *>(W + (int64_t)row * K * (WT ? 1 : 2));
+    const int base = c * 64 * kChunkUnits + lane;
+#pragma unroll
+    for (int j = 0; j < kChunkUnits; ++j)
+      __builtin_amdgcn_global_load_lds((const AMK_GAS void *)(rp + min(base + j * 64, n16 - 1)),
+                                       (AMK_LDS void *)(dst + j * 64), 16, 0, kCachePolicyNt);
+  }
   // accumulate chunk s; at the end of a row reduce over the wave and store ys[row - r0]
   __device__ __forceinline__ void consume(const uint4 (&buf)[kChunkUnits], int s, float &acc,
                                           const float *xs, float *ys, const float *scale) const {
@@ -419,6 +436,41 @@ struct GemvStream {
       if constexpr (WT == 1) v *= gld(&scale[row]);
       if (lane == 0) ys[row - r0] = v;
       acc = 0.f;
+    }
+  }
+  // Run the stream with two chunks issued before the dependency wait: chunk 0 in this wave's LDS
+  // slot pf (load_lds), chunk 1 in P. Chunk 2 is issued first, then the LDS chunk is consumed
+  // once the vector-memory count shows its copy done (loads complete in issue order).
+  __device__ __forceinline__ void run_pf(const uint4 *pf, const uint4 (&P)[kChunkUnits],
+                                         const float *xs, float *ys, const float *scale) const {
+    if (S == 0) return;
+    float acc = 0.f;
+    uint4 A[kChunkUnits], Bf[kChunkUnits];
+    if (S > 2) {
+      load(A, 2);
+      __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
+#pragma unroll
+    for (int j = 0; j < kChunkUnits; ++j) Bf[j] = pf[j * 64 + lane];
+    consume(Bf, 0, acc, xs, ys, scale);
+    if (S == 1) return;
+    consume(P, 1, acc, xs, ys, scale);
+    if (S == 2) return;
+    int s = 2;
+    for (; s + 2 < S; s += 2) {
+      load(Bf, s + 1);
+      consume(A, s, acc, xs, ys, scale);
+      load(A, s + 2);
+      consume(Bf, s + 1, acc, xs, ys, scale);
+    }
+    if (s + 1 < S) {
+      load(Bf, s + 1);
+      consume(A, s, acc, xs, ys, scale);
+      consume(Bf, s + 1, acc, xs, ys, scale);
+    } else {
+      consume(A, s, acc, xs, ys, scale);
     }
   }
   // Run the stream. P holds chunk 0, loaded before the task's dependency wait and complete by

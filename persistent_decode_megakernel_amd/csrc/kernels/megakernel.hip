@@ -15,14 +15,16 @@
 
 namespace amk {
 
-// GEMV tile task: the first weight chunk of waves 1.. is issued before the dependency wait
-// completes (wave 0 polls the flags and issues its chunk after: a wave's loads return in order,
-// so its flag reads would queue behind its own prefetch); the input vector is staged (RMSNorm / attention combine / plain copy) after the
+// GEMV tile task: the first two weight chunks of every wave (one into its LDS slot, one into
+// registers) are issued before the dependency wait completes (wave 0 polls the flags and issues
+// its chunks after polling: a wave's loads return in order, so its flag reads would queue behind
+// its own prefetch); the input vector is staged (RMSNorm / attention combine / plain copy) after the
 // wait, then the row stream runs double-buffered, the RMSNorm scale is applied to the outputs and
 // the epilogue writes them.
 template <int WT>
 __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, const Task &t,
-                                          float *xs, float *ys, float *red, int *abort_slot) {
+                                          float *xs, float *ys, float *red, uint4 *pf,
+                                          int *abort_slot) {
   constexpr int NW = kWaves;
   const int l = t.layer;
   const void *W;
@@ -34,8 +36,10 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
   GemvStream<WT> st;
   uint4 P[kChunkUnits];
   st.init(W, K, r0, r1, NW);
+  uint4 *slot = pf + st.wave * (64 * kChunkUnits);
   wait_poll(m, t, s.epoch, abort_slot);
-  if (b1 && st.S > 0) st.load(P, 0);
+  if (b1 && st.S > 0) st.load_lds(0, slot);
+  if (b1 && st.S > 1) st.load(P, 1);
   if (!wait_join(m, t, abort_slot)) return false;
   switch (t.mat) {
     case M_QKV: stage_norm(m, s, 2 * l, m.layers[l].attn_norm, xs, red, NW); break;
@@ -46,7 +50,7 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
   }
   if (m.trace && threadIdx.x == 0) m.trace[(uint64_t)t.id * 4 + 2] = wall_clock64();
   if (b1)
-    st.run(P, xs, ys, scale);
+    st.run_pf(slot, P, xs, ys, scale);
   else
     gemv_rows<WT>(W, scale, K, r0, r1, xs, ys, s.batch, NW);
   __syncthreads();
@@ -68,7 +72,8 @@ __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArg
   const int32_t xb = lds_attn_floats(m.max_batch, m.qpg, m.hd);
   float *xs = lds;
   float *red = lds + (xa > xb ? xa : xb);  // kRedFloats floats
-  float *ys = red + kRedFloats;            // batch * max_tile_rows floats
+  uint4 *pf = reinterpret_cast<uint4 *>(red + kRedFloats);  // lds_prefetch_floats(max_batch)
+  float *ys = red + kRedFloats + lds_prefetch_floats(m.max_batch);  // batch * max_tile_rows
   __shared__ int abort_flag, last_flag;
   const uint32_t t0 = m.offsets[blockIdx.x], t1 = m.offsets[blockIdx.x + 1];
   uint64_t *const trace = m.trace;
@@ -82,7 +87,7 @@ __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArg
     if (trace && threadIdx.x == 0) trace[(uint64_t)t.id * 4 + 0] = wall_clock64();
     bool ok;
     if (t.type == T_GEMV) {
-      ok = gemv_task<WT>(m, s, t, xs, ys, red, &abort_flag);
+      ok = gemv_task<WT>(m, s, t, xs, ys, red, pf, &abort_flag);
     } else if (t.type == T_ATTN) {
       ok = attn_task<HD, QMAX>(m, s, t.layer, (int)t.a0, (int)t.a1, xs, red, &t, &abort_flag);
       if (ok) attn_count_and_combine(m, s, t.layer, (int)t.a0, &last_flag);

@@ -131,11 +131,15 @@ AMK_HD int32_t lds_attn_floats(int32_t batch, int32_t qpg, int32_t hd) {
   // q [B][qpg][hd] + scores [B][qpg][chunk] + partial acc [waves][B*qpg*hd]
   return batch * qpg * hd + batch * qpg * kAttnRowsPerChunk + kWaves * batch * qpg * hd;
 }
+// Batch-1 GEMV tiles stage the first weight chunk of every wave in LDS (8 KB per wave).
+constexpr int32_t kPrefetchFloats = kWaves * 2048;
+AMK_HD int32_t lds_prefetch_floats(int32_t batch) { return batch == 1 ? kPrefetchFloats : 0; }
+// LDS of the megakernel: [xs or attention scratch][red: kRedFloats][prefetch][ys]
 AMK_HD int32_t lds_bytes_for(int32_t batch, int32_t hidden, int32_t qdim, int32_t ffn,
                              int32_t qpg, int32_t hd, int32_t max_tile_rows) {
   int32_t a = lds_xs_floats(batch, hidden, qdim, ffn);
   int32_t b = lds_attn_floats(batch, qpg, hd);
   int32_t region = a > b ? a : b;
-  return 4 * (region + batch * max_tile_rows + kRedFloats);
+  return 4 * (region + kRedFloats + lds_prefetch_floats(batch) + batch * max_tile_rows);
 }
 }  // namespace amk
