@@ -29,9 +29,10 @@ def kv_bytes_step(cfg, ctx):
     return cfg.batch * cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim * 2 * ctx
 
 
-def time_path(cfg, weights, kv_host, path, steps, warmup):
+def time_path(cfg, weights, kv_host, path, steps, warmup, graph=False):
     """Returns (ms per step from events around the whole timed region, per-launch durations ms,
-    model info)."""
+    model info, final token ids). graph=True: each timed step is one hipGraph replay of the step's
+    launches (captured beforehand, one graph per position, since the position is a launch argument)."""
     import torch
     from persistent_decode_megakernel_amd import synth
     from persistent_decode_megakernel_amd.model import Model
@@ -42,11 +43,23 @@ def time_path(cfg, weights, kv_host, path, steps, warmup):
     info = model.info()
     kv = model.kv(cfg.batch, max_seq)
     kv.tensor.copy_(kv_host[..., :max_seq, :].to(kv.tensor.device))
-    log(f"[bench] {path}: model ready in {time.time() - t0:.1f}s "
+    log(f"[bench] {path}{' (hipGraph)' if graph else ''}: model ready in {time.time() - t0:.1f}s "
         f"({info.n_tasks} tasks on {info.n_cu} CUs, {info.launches_per_step} launches/step)")
     first = synth.make_tokens(cfg, 0)[:, 0].to(torch.int32).cuda()
     tok = torch.empty_like(first)
     stream = torch.cuda.current_stream()
+    graphs = []
+    if graph:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            for i in range(steps):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    model.step(kv, tok, cfg.prefill + i, next_out=tok)
+                graphs.append(g)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
     # warmup (positions P .. P+W-1), then the timed region restarts at P
     tok.copy_(first)
     for i in range(warmup):
@@ -58,13 +71,17 @@ def time_path(cfg, weights, kv_host, path, steps, warmup):
     torch.cuda.synchronize()
     ev[0].record(stream)
     for i in range(steps):
-        model.step(kv, tok, cfg.prefill + i, next_out=tok)
+        if graph:
+            graphs[i].replay()
+        else:
+            model.step(kv, tok, cfg.prefill + i, next_out=tok)
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     model.sync()
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     total = ev[0].elapsed_time(ev[steps])
     ids = tok.cpu().tolist()
+    del graphs
     kv.close()
     model.close()
     del kv, model
@@ -86,32 +103,23 @@ def profiled_traffic(cfg, kernel_name):
     return float(rec["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(cfg, weights, kv_host, sample_layers):
-    """The oracle on a bounded sample: one decode step of a model truncated to its first
-    `sample_layers` layers (plus final norm and LM head); per-layer time scaled to all layers."""
+def cpu_baseline(cfg, weights, kv_host, sample_steps):
+    """The oracle (float64 numpy, as it stands) on a bounded sample of the same workload: the first
+    `sample_steps` decode steps of the full model from the same prefilled cache and first token."""
     import numpy as np
     import oracle
     from persistent_decode_megakernel_amd import synth
 
     params, wn = synth.oracle_inputs(weights)
-    k = min(sample_layers, cfg.n_layers)
     pos = cfg.prefill
-    kv = synth.bf16_to_numpy_bits(kv_host[:k, ..., :pos + 1, :]).copy()
+    kv = synth.bf16_to_numpy_bits(kv_host[..., :pos + sample_steps, :]).copy()
     tok = synth.make_tokens(cfg, 0)[:, 0].numpy()
-    # head-only model: 0 layers -> time of embedding + final norm + LM head
-    p0 = dict(params, n_layers=0)
-    w0 = dict(wn, layers=[])
-    dec0 = oracle.Decoder(p0, w0, cache_bytes=0)
+    dec = oracle.Decoder(params, wn, cache_bytes=0)
     t = time.perf_counter()
-    dec0.step(kv[:0], tok, pos)
-    t_head = time.perf_counter() - t
-    pk = dict(params, n_layers=k)
-    wk = dict(wn, layers=wn["layers"][:k])
-    deck = oracle.Decoder(pk, wk, cache_bytes=0)
-    t = time.perf_counter()
-    deck.step(kv, tok, pos)
-    t_k = time.perf_counter() - t
-    t_step = t_head + (t_k - t_head) * cfg.n_layers / k
+    for i in range(sample_steps):
+        logits = dec.step(kv, tok, pos + i)
+        tok = oracle.argmax_lowest(logits)
+    t_step = (time.perf_counter() - t) / sample_steps
     cores = len(os.sched_getaffinity(0))
     threads = cores
     try:
@@ -122,14 +130,14 @@ def cpu_baseline(cfg, weights, kv_host, sample_layers):
     except Exception:
         pass
     return {
-        "value": cfg.batch / t_step,
+        "value": round(cfg.batch / t_step, 4),
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"one decode step at position {pos} of the same model truncated to its first "
-                   f"{k} of {cfg.n_layers} layers plus final norm and LM head "
-                   f"({t_k:.1f}s; head alone {t_head:.2f}s), per-layer time scaled to "
-                   f"{cfg.n_layers} layers; float64 numpy; host has {cores} cores"),
+        "sample": (f"{sample_steps} greedy decode steps of the full {cfg.name} model at positions "
+                   f"{pos}..{pos + sample_steps - 1} ({t_step:.1f} s per step), float64 numpy "
+                   f"matrix-vector products, weights converted per matrix per step; host has "
+                   f"{cores} cores"),
     }
 
 
@@ -141,7 +149,7 @@ def main():
     ap.add_argument("--workload", default="llama2_7b")
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-layers", type=int, default=4)
+    ap.add_argument("--cpu-sample-steps", type=int, default=2)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (a kernel of "
                          "known traffic for scaling hardware byte counters)")
@@ -223,18 +231,20 @@ def main():
         "step_ms_p10_p50_p90": [round(sorted(per)[int(q * (steps - 1))], 4) for q in (0.1, 0.5, 0.9)],
     }
     if not args.no_ablation:
-        ms_u, per_u, info_u, ids_u = time_path(cfg, weights, kv_host, "unfused", steps, warmup)
-        out["ablation_unfused"] = {
-            "ms_per_step": round(ms_u, 4),
-            "tokens_per_s": round(cfg.batch / (ms_u * 1e-3), 2),
-            "launches_per_step": info_u.launches_per_step,
-            "hbm_gbs": round(avg_bytes / (ms_u * 1e-3) / 1e9, 1),
-            "same_final_ids": ids_u == ids,
-            "megakernel_speedup": round(ms_u / ms, 3),
-        }
+        for key, graph in (("ablation_unfused", False), ("ablation_unfused_hipgraph", True)):
+            ms_u, per_u, info_u, ids_u = time_path(cfg, weights, kv_host, "unfused", steps, warmup,
+                                                   graph=graph)
+            out[key] = {
+                "ms_per_step": round(ms_u, 4),
+                "tokens_per_s": round(cfg.batch / (ms_u * 1e-3), 2),
+                "launches_per_step": info_u.launches_per_step,
+                "hbm_gbs": round(avg_bytes / (ms_u * 1e-3) / 1e9, 1),
+                "same_final_ids": ids_u == ids,
+                "megakernel_speedup": round(ms_u / ms, 3),
+            }
     if not args.no_cpu_baseline:
         t = time.time()
-        out["cpu_baseline"] = cpu_baseline(cfg, weights, kv_host, args.cpu_sample_layers)
+        out["cpu_baseline"] = cpu_baseline(cfg, weights, kv_host, args.cpu_sample_steps)
         log(f"[bench] cpu baseline took {time.time() - t:.1f}s")
     print(json.dumps(out), flush=True)
 
