@@ -78,6 +78,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+// A wave-uniform value moved to a scalar register (the builtin takes and returns int).
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
 __device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
 
 // butterfly sum over the 64 lanes; every lane receives the total
@@ -200,7 +205,7 @@ constexpr int kCachePolicySc1 = 16;
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitVm8 = 0x0F78;
 #define AMK_LDS __attribute__((address_space(3)))
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_rsrc(const void *base, uint32_t bytes) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
 }
 __device__ __forceinline__ float4 cld4(__amdgpu_buffer_rsrc_t r, uint32_t off_bytes) {
@@ -532,7 +537,7 @@ __device__ void stage_norm(const DevModel &m, const StepArgs &s, int slot, const
     float *x = xs + (int64_t)b * d;
     const uint16_t *e = (slot == 0) ? m.embed + (int64_t)token_of(m, s, b) * d : nullptr;
     const float *src = m.h + ((int64_t)slot * m.max_batch + b) * d;
-    const __amdgpu_buffer_rsrc_t rs = coh_rsrc(src, (uint32_t)d * 4u);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)d * 4u);
     float ss = 0.f;
     for (int base = 0; base < n4; base += kStageVec * nw * 64) {
       float4 hv[kStageVec];
@@ -585,7 +590,7 @@ __device__ void stage_plain(const float *src, int64_t src_stride, int K, int B, 
   const int n4 = K / 4;
   constexpr int V = 2 * kStageVec;
   for (int b = 0; b < B; ++b) {
-    const __amdgpu_buffer_rsrc_t rs = coh_rsrc(src + b * src_stride, (uint32_t)K * 4u);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + b * src_stride, (uint32_t)K * 4u);
     float *x = xs + (int64_t)b * K;
     for (int base = 0; base < n4; base += V * nw * 64) {
       float4 v[V];
@@ -600,6 +605,162 @@ __device__ void stage_plain(const float *src, int64_t src_stride, int K, int B, 
     }
   }
   __syncthreads();
+}
+
+// ------------------------------------------------------------------------------------------
+// Batch GEMV (B = 2..8 sequences) on the matrix cores:
+//   ys[b * n + (r - r0)] = sum_k X_b[k] W[r][k]  (times scale[r] for int8), r in [r0, r1).
+// v_mfma_f32_16x16x32_bf16 computes a 16 x 16 tile C = A B over 32 k: A = 16 weight rows, B = the
+// sequences' inputs as 16 columns (columns >= B read as zero). Lane l supplies A[l % 16][8 (l/16)
+// + e] and B[8 (l/16) + e][l % 16], e < 8, and receives C[4 (l/16) + i][l % 16], i < 4. K is split
+// over the workgroup's waves (contiguous runs of 32-k steps); the waves' partial tiles are summed
+// in LDS (mred). Inputs are read straight from the device-coherent buffers (no LDS staging) and
+// fed as two bf16 halves x = hi + lo, so the products keep about 16 bits of the fp32 input.
+// Rows are processed kMfmaGroups x 16 at a time. Weights and inputs are addressed through buffer
+// resources, so out-of-range lanes (ragged row group, sequences >= B) read zeros.
+// ------------------------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+constexpr int kMfmaGroups = 4;
+static_assert(kMfmaRedFloats == kWaves * kMfmaGroups * 16 * 8, "LDS for the partial tiles");
+
+struct BatchInput {
+  const float *x;        // fp32 rows, `stride` floats apart (null when emb is set)
+  int32_t stride;
+  const uint16_t *emb;   // bf16 embedding [V][K]: sequence b reads row tokens[b]
+  const uint16_t *gain;  // bf16 [K] multiplied into the input, or null
+  bool sumsq;            // leave sum_k x^2 of sequence b's partial range in red[b * nw + wave]
+};
+
+__device__ __forceinline__ bf16x8_t bf16x8_of_bits(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const u32x4_t v = {a, b, c, d};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+// eight int8 weights (two words) as eight bf16 (exact: |q| <= 127)
+__device__ __forceinline__ bf16x8_t bf16x8_of_i8(uint32_t w0, uint32_t w1) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int32_t v = (int32_t)(i < 2 ? w0 : w1);
+    const int sh = (i & 1) * 16;
+    const float f0 = (float)((v << (24 - sh)) >> 24), f1 = (float)((v << (16 - sh)) >> 24);
+    o[i] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+  }
+  return bf16x8_of_bits(o[0], o[1], o[2], o[3]);
+}
+
+template <int WT>
+__device__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, const float *scale,
+                          int K, int r0, int r1, const BatchInput &in, float *ys, float *red,
+                          float *mred) {
+  constexpr int NW = kWaves;
+  const int B = s.batch, n = r1 - r0, G = (n + 15) / 16;
+  const int lane = lane_id(), wave = (int)uniform_u32((uint32_t)wave_id());
+  const int bq = lane & 15, kq = lane >> 4;
+  const int T = (K + 31) / 32;
+  const int t0 = (int)((int64_t)T * wave / NW), t1 = (int)((int64_t)T * (wave + 1) / NW);
+  const int rb = K * (WT ? 1 : 2);  // weight row bytes
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(static_cast<const uint8_t *>(W) + (int64_t)r0 * rb, (uint32_t)n * (uint32_t)rb);
+  const __amdgpu_buffer_rsrc_t rx =
+      in.emb ? make_rsrc(in.emb, (uint32_t)m.V * (uint32_t)K * 2u)
+             : make_rsrc(in.x, (uint32_t)B * (uint32_t)in.stride * 4u);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(in.gain ? in.gain : m.final_norm, (uint32_t)K * 2u);
+  // this lane's input row: byte offset of X_b[0] (past the range for sequences >= B)
+  uint32_t xrow = 0xffffffffu;
+  if (bq < B) xrow = in.emb ? (uint32_t)token_of(m, s, bq) * (uint32_t)K * 2u : (uint32_t)bq * (uint32_t)in.stride * 4u;
+  float ss = 0.f;
+  for (int g0 = 0; g0 < G; g0 += kMfmaGroups) {
+    const int gn = min(kMfmaGroups, G - g0);
+    f32x4_t acc[kMfmaGroups];
+#pragma unroll
+    for (int g = 0; g < kMfmaGroups; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int t = t0; t < t1; ++t) {
+      const int k = 32 * t + 8 * kq;  // this lane's 8 inputs: k .. k + 7
+      float xv[8];
+      if (in.emb) {
+        const u32x4_t e = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xrow + (uint32_t)k * 2u), 0, 0);
+        const uint32_t ew[4] = {e.x, e.y, e.z, e.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { xv[2 * i] = bf_lo(ew[i]); xv[2 * i + 1] = bf_hi(ew[i]); }
+      } else {
+        const f32x4_t a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          rx, (int)(xrow + (uint32_t)k * 4u), 0, kCachePolicySc1));
+        const f32x4_t b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          rx, (int)(xrow + (uint32_t)k * 4u + 16u), 0, kCachePolicySc1));
+        xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
+        xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
+      }
+      uint32_t gw[4] = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 ones
+      if (in.gain) {
+        const u32x4_t gv = __builtin_amdgcn_raw_buffer_load_b128(rg, k * 2, 0, 0);
+        gw[0] = gv.x; gw[1] = gv.y; gw[2] = gv.z; gw[3] = gv.w;
+      }
+      uint32_t wf[kMfmaGroups][4];
+#pragma unroll
+      for (int g = 0; g < kMfmaGroups; ++g) {
+        if (g < gn) {
+          const uint32_t off = (uint32_t)(16 * (g0 + g) + bq) * (uint32_t)rb + (uint32_t)k * (WT ? 1u : 2u);
+          if constexpr (WT == 0) {
+            const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, kCachePolicyNt);
+            wf[g][0] = w.x; wf[g][1] = w.y; wf[g][2] = w.z; wf[g][3] = w.w;
+          } else {
+            const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rw, (int)off, 0, kCachePolicyNt);
+            wf[g][0] = w.x; wf[g][1] = w.y; wf[g][2] = 0; wf[g][3] = 0;
+          }
+        }
+      }
+      // x * gain as bf16 hi + lo; inputs past K are zero
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v0 = k + 2 * i < K ? xv[2 * i] : 0.f, v1 = k + 2 * i + 1 < K ? xv[2 * i + 1] : 0.f;
+        if (in.sumsq && g0 == 0) ss = fmaf(v0, v0, fmaf(v1, v1, ss));
+        v0 *= bf_lo(gw[i]);
+        v1 *= bf_hi(gw[i]);
+        const uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
+        const uint16_t l0 = f32_to_bf16(v0 - bf16_to_f32(h0)), l1 = f32_to_bf16(v1 - bf16_to_f32(h1));
+        hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lo[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+      const bf16x8_t xh = bf16x8_of_bits(hi[0], hi[1], hi[2], hi[3]);
+      const bf16x8_t xl = bf16x8_of_bits(lo[0], lo[1], lo[2], lo[3]);
+#pragma unroll
+      for (int g = 0; g < kMfmaGroups; ++g) {
+        if (g < gn) {
+          const bf16x8_t a = WT == 0 ? bf16x8_of_bits(wf[g][0], wf[g][1], wf[g][2], wf[g][3])
+                                     : bf16x8_of_i8(wf[g][0], wf[g][1]);
+          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xh, acc[g], 0, 0, 0);
+          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl, acc[g], 0, 0, 0);
+        }
+      }
+    }
+    // partial tiles of all waves -> ys
+    if (bq < 8) {
+#pragma unroll
+      for (int g = 0; g < kMfmaGroups; ++g)
+        if (g < gn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mred[((wave * kMfmaGroups + g) * 16 + 4 * kq + i) * 8 + bq] = acc[g][i];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < gn * 16 * 8; e += NW * 64) {
+      const int g = e >> 7, row = (e >> 3) & 15, b = e & 7;
+      const int r = 16 * (g0 + g) + row;
+      if (b < B && r < n) {
+        float t = 0.f;
+        for (int w = 0; w < NW; ++w) t += mred[((w * kMfmaGroups + g) * 16 + row) * 8 + b];
+        if constexpr (WT == 1) t *= gld(&scale[r0 + r]);
+        ys[b * n + r] = t;
+      }
+    }
+    __syncthreads();
+  }
+  if (in.sumsq) {
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    if (kq == 0 && bq < B) red[bq * NW + wave] = ss;
+  }
 }
 
 // ------------------------------------------------------------------------------------------

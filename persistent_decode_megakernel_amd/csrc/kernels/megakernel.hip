@@ -32,7 +32,9 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
   int K, wtype;
   gemv_matrix(m, t.mat, l, &W, &scale, &K, &wtype);
   const int r0 = (int)t.a0, r1 = (int)t.a1;
-  const bool b1 = s.batch == 1;
+  // the LDS layout (staged input and prefetch slots, or matrix-core partial tiles) follows the
+  // model's batch capacity; a smaller step batch runs the batched GEMV with zero columns
+  const bool b1 = m.max_batch == 1;
   GemvStream<WT> st;
   uint4 P[kChunkUnits];
   st.init(W, K, r0, r1, NW);
@@ -41,18 +43,33 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
   if (b1 && st.S > 0) st.load_lds(0, slot);
   if (b1 && st.S > 1) st.load(P, 1);
   if (!wait_join(m, t, abort_slot)) return false;
-  switch (t.mat) {
-    case M_QKV: stage_norm(m, s, 2 * l, m.layers[l].attn_norm, xs, red, NW); break;
-    case M_O: stage_plain(m.ao + (int64_t)l * m.max_batch * m.qd, m.qd, m.qd, s.batch, xs, NW); break;
-    case M_GU: stage_norm(m, s, 2 * l + 1, m.layers[l].mlp_norm, xs, red, NW); break;
-    case M_D: stage_plain(m.a + (int64_t)l * m.max_batch * m.F, m.F, m.F, s.batch, xs, NW); break;
-    default: stage_norm(m, s, 2 * m.L, m.final_norm, xs, red, NW); break;
-  }
-  if (m.trace && threadIdx.x == 0) m.trace[(uint64_t)t.id * 4 + 2] = wall_clock64();
-  if (b1)
+  if (b1) {
+    switch (t.mat) {
+      case M_QKV: stage_norm(m, s, 2 * l, m.layers[l].attn_norm, xs, red, NW); break;
+      case M_O: stage_plain(m.ao + (int64_t)l * m.max_batch * m.qd, m.qd, m.qd, 1, xs, NW); break;
+      case M_GU: stage_norm(m, s, 2 * l + 1, m.layers[l].mlp_norm, xs, red, NW); break;
+      case M_D: stage_plain(m.a + (int64_t)l * m.max_batch * m.F, m.F, m.F, 1, xs, NW); break;
+      default: stage_norm(m, s, 2 * m.L, m.final_norm, xs, red, NW); break;
+    }
+    if (m.trace && threadIdx.x == 0) m.trace[(uint64_t)t.id * 4 + 2] = wall_clock64();
     st.run_pf(slot, P, xs, ys, scale);
-  else
-    gemv_rows<WT>(W, scale, K, r0, r1, xs, ys, s.batch, NW);
+  } else {
+    // batched: inputs straight from memory into the matrix cores (RMSNorm scale applied after)
+    BatchInput in{nullptr, m.d, nullptr, nullptr, true};
+    const int64_t hb = (int64_t)m.max_batch * m.d;
+    switch (t.mat) {
+      case M_QKV:
+        if (l == 0) in.emb = m.embed; else in.x = m.h + 2 * l * hb;
+        in.gain = m.layers[l].attn_norm;
+        break;
+      case M_O: in = BatchInput{m.ao + (int64_t)l * m.max_batch * m.qd, m.qd, nullptr, nullptr, false}; break;
+      case M_GU: in.x = m.h + (2 * l + 1) * hb; in.gain = m.layers[l].mlp_norm; break;
+      case M_D: in = BatchInput{m.a + (int64_t)l * m.max_batch * m.F, m.F, nullptr, nullptr, false}; break;
+      default: in.x = m.h + 2 * (int64_t)m.L * hb; in.gain = m.final_norm; break;
+    }
+    if (m.trace && threadIdx.x == 0) m.trace[(uint64_t)t.id * 4 + 2] = wall_clock64();
+    gemv_mfma<WT>(m, s, W, scale, K, r0, r1, in, ys, red, xs);
+  }
   __syncthreads();
   if (t.mat != M_O && t.mat != M_D) norm_scale_ys(m, s, r1 - r0, ys, red, NW);
   switch (t.mat) {

@@ -46,10 +46,14 @@ __device__ void uf_gemv(const DevModel &m, const StepArgs &s, const void *W, con
   extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte reads of xs need it
   float *red = lds;                       // 64 * 8
   float *ys = red + 64 * 8;               // batch * kUfRowsPerBlock
-  float *xs = ys + 8 * kUfRowsPerBlock;   // batch * K
+  float *xs = ys + 8 * kUfRowsPerBlock;   // K (batch 1) or the matrix cores' partial tiles
   const int r0 = blockIdx.x * kUfRowsPerBlock, r1 = min(rows, r0 + kUfRowsPerBlock);
-  stage_plain(x, K, K, s.batch, xs, kUfWaves);
-  gemv_rows<WT>(W, scale, K, r0, r1, xs, ys, s.batch, kUfWaves);
+  if (s.batch == 1) {
+    stage_plain(x, K, K, 1, xs, kUfWaves);
+    gemv_rows<WT>(W, scale, K, r0, r1, xs, ys, 1, kUfWaves);
+  } else {
+    gemv_mfma<WT>(m, s, W, scale, K, r0, r1, BatchInput{x, K, nullptr, nullptr, false}, ys, red, xs);
+  }
   __syncthreads();
   const int n = r1 - r0;
   if (MODE == 0) {

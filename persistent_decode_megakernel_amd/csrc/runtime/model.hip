@@ -455,7 +455,9 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
                                                              m->lds_bytes), "occupancy");
       if (per_cu < 1) throw std::runtime_error("megakernel workgroup does not fit on a CU");
     } else {
-      const uint32_t gl = 4u * (64 * 8 + 8 * kUfRowsPerBlock + (uint32_t)(B * kmax));
+      // a step may run any batch up to max_batch: allow the larger of the two GEMV layouts
+      const uint32_t gl = 4u * (64 * 8 + 8 * kUfRowsPerBlock +
+                                (uint32_t)std::max<int>(kmax, B > 1 ? kMfmaRedFloats : 0));
       for (int wt = 0; wt < 2; ++wt)
         for (int mode = 0; mode < 3; ++mode)
           hip_check(hipFuncSetAttribute((const void *)pick_uf_gemv(wt, mode),
@@ -548,7 +550,8 @@ static void launch_unfused(amk_model *m, const StepArgs &s, hipStream_t st) {
   const DevModel *g = m->d_dm;
   const int B = s.batch, L = dm.L, d = dm.d;
   const int wt = dm.wtype;
-  const uint32_t gl = 4u * (64 * 8 + 8 * kUfRowsPerBlock + (uint32_t)(B * std::max(std::max(d, dm.qd), dm.F)));
+  const uint32_t gl = 4u * (64 * 8 + 8 * kUfRowsPerBlock +
+                            (uint32_t)(B == 1 ? std::max(std::max(d, dm.qd), dm.F) : kMfmaRedFloats));
   auto grid = [](int rows) { return dim3((rows + kUfRowsPerBlock - 1) / kUfRowsPerBlock); };
   float *h = dm.h;
   auto hslot = [&](int slot) { return h + (size_t)slot * dm.max_batch * d; };

@@ -122,10 +122,13 @@ constexpr int32_t kThreads = kWaves * 64;
 constexpr int32_t kAttnRowsPerChunk = 256;  // KV rows staged per attention chunk
 constexpr int32_t kRedFloats = 2048;        // reduction scratch; holds n_heads x blocks weights
 
+// Staged GEMV input (batch 1 only: batched GEMVs read their inputs straight from memory and use
+// the region for the partial tiles of the matrix-core reduction instead).
+constexpr int32_t kMfmaRedFloats = kWaves * 4 * 16 * 8;
 AMK_HD int32_t lds_xs_floats(int32_t batch, int32_t hidden, int32_t qdim, int32_t ffn) {
   int32_t k = hidden > qdim ? hidden : qdim;
   k = k > ffn ? k : ffn;
-  return batch * k;
+  return batch == 1 ? k : kMfmaRedFloats;
 }
 AMK_HD int32_t lds_attn_floats(int32_t batch, int32_t qpg, int32_t hd) {
   // q [B][qpg][hd] + scores [B][qpg][chunk] + partial acc [waves][B*qpg*hd]

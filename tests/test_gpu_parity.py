@@ -114,7 +114,7 @@ def test_smollm2_135m_batch2_prefill():
     assert_parity(rep)
 
 
-@pytest.mark.parametrize("name", ["llama2_7b", "llama2_7b_w8a16"])
+@pytest.mark.parametrize("name", ["llama2_7b", "llama2_7b_w8a16", "llama2_7b_b8"])
 def test_full_size_first_steps(name):
     """Full 7B shapes in the launch configuration the bench times (one cooperative launch per
     step on every CU), checked against the oracle on every logit for the first two steps."""
