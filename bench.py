@@ -184,7 +184,8 @@ def main():
 
     ms, per, info, ids = time_path(cfg, weights, kv_host, "megakernel", steps, warmup)
     hd_q = 1 if cfg.n_heads // cfg.n_kv_heads <= 1 else (2 if cfg.n_heads // cfg.n_kv_heads <= 2 else 4)
-    kname = f"amk_megakernel_w{1 if cfg.wtype == 'int8' else 0}_h{cfg.head_dim}_q{hd_q}"
+    kname = (f"amk_megakernel_w{1 if cfg.wtype == 'int8' else 0}_h{cfg.head_dim}_q{hd_q}"
+             + ("_b" if cfg.batch > 1 else ""))
     traffic_bytes = profiled_traffic(cfg, kname)
     weight_bytes = info.weight_bytes + 2 * cfg.hidden * cfg.batch  # + embedding rows
     ctxs = [cfg.prefill + i + 1 for i in range(steps)]

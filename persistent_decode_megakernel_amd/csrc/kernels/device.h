@@ -610,14 +610,16 @@ __device__ void stage_plain(const float *src, int64_t src_stride, int K, int B, 
 // ------------------------------------------------------------------------------------------
 // Batch GEMV (B = 2..8 sequences) on the matrix cores:
 //   ys[b * n + (r - r0)] = sum_k X_b[k] W[r][k]  (times scale[r] for int8), r in [r0, r1).
-// v_mfma_f32_16x16x32_bf16 computes a 16 x 16 tile C = A B over 32 k: A = 16 weight rows, B = the
-// sequences' inputs as 16 columns (columns >= B read as zero). Lane l supplies A[l % 16][8 (l/16)
-// + e] and B[8 (l/16) + e][l % 16], e < 8, and receives C[4 (l/16) + i][l % 16], i < 4. K is split
-// over the workgroup's waves (contiguous runs of 32-k steps); the waves' partial tiles are summed
-// in LDS (mred). Inputs are read straight from the device-coherent buffers (no LDS staging) and
-// fed as two bf16 halves x = hi + lo, so the products keep about 16 bits of the fp32 input.
-// Rows are processed kMfmaGroups x 16 at a time. Weights and inputs are addressed through buffer
-// resources, so out-of-range lanes (ragged row group, sequences >= B) read zeros.
+// v_mfma_f32_16x16x32_bf16 computes a 16 x 16 tile C = A B over 32 k. Lane l supplies
+// A[l % 16][8 (l/16) + e] and B[8 (l/16) + e][l % 16], e < 8, and receives C[4 (l/16) + i][l % 16],
+// i < 4. A holds 16 weight rows. The inputs are split into two bf16 halves, x = hi + lo, and the
+// 16 columns of B carry hi of sequence c (c < 8) and lo of sequence c - 8 (c >= 8), so one
+// instruction multiplies both halves and y_b = C[.][b] + C[.][b + 8] keeps about 16 bits of the
+// fp32 input; columns of sequences >= B are zero. K is split over the workgroup's waves
+// (contiguous runs of 32-k steps); their partial tiles are summed in LDS (mred). Inputs are read
+// straight from the device-coherent buffers (no LDS staging). Each wave issues the loads of U
+// k-steps (GP 16-row groups each) before using any of them.
+// Weights and inputs are addressed through buffer resources: out-of-range lanes read zeros.
 // ------------------------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 constexpr int kMfmaGroups = 4;
@@ -648,6 +650,101 @@ __device__ __forceinline__ bf16x8_t bf16x8_of_i8(uint32_t w0, uint32_t w1) {
   return bf16x8_of_bits(o[0], o[1], o[2], o[3]);
 }
 
+// per-lane view of one batched GEMV tile
+struct MfmaTile {
+  __amdgpu_buffer_rsrc_t rw, rx, rg;
+  int K, rb, n, t0, t1;
+  uint32_t xrow;   // byte offset of this lane's input row (past the range when inactive)
+  int col, kq;     // B/C column (l % 16) and k quarter (l / 16)
+  bool emb, gain, lo_half;
+};
+
+// one pass: groups [g0, g0 + gn) (gn <= GP) over this wave's k steps, the loads of U steps
+// issued before any of them is used; returns the partial tiles
+template <int WT, int GP, int U, bool GAIN>
+__device__ __forceinline__ void mfma_pass(const MfmaTile &T, int g0, int gn, bool sumsq, float &ss,
+                                          f32x4_t (&acc)[kMfmaGroups]) {
+#pragma unroll
+  for (int g = 0; g < kMfmaGroups; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = T.t0; t < T.t1; t += U) {
+    uint32_t xw[U][8];
+    uint32_t gw[GAIN ? U : 1][4];
+    uint32_t wf[U][GP][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (t + u < T.t1) {
+        const int k = 32 * (t + u) + 8 * T.kq;
+        if (T.emb) {
+          const u32x4_t e = __builtin_amdgcn_raw_buffer_load_b128(T.rx, (int)(T.xrow + (uint32_t)k * 2u), 0, 0);
+          xw[u][0] = e.x; xw[u][1] = e.y; xw[u][2] = e.z; xw[u][3] = e.w;
+        } else {
+          const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(T.rx, (int)(T.xrow + (uint32_t)k * 4u), 0, kCachePolicySc1);
+          const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(T.rx, (int)(T.xrow + (uint32_t)k * 4u + 16u), 0, kCachePolicySc1);
+          xw[u][0] = a.x; xw[u][1] = a.y; xw[u][2] = a.z; xw[u][3] = a.w;
+          xw[u][4] = b.x; xw[u][5] = b.y; xw[u][6] = b.z; xw[u][7] = b.w;
+        }
+        if constexpr (GAIN) {
+          const u32x4_t gv = __builtin_amdgcn_raw_buffer_load_b128(T.rg, k * 2, 0, 0);
+          gw[u][0] = gv.x; gw[u][1] = gv.y; gw[u][2] = gv.z; gw[u][3] = gv.w;
+        }
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+          if (g < gn) {
+            const uint32_t off = (uint32_t)(16 * (g0 + g) + T.col) * (uint32_t)T.rb + (uint32_t)k * (WT ? 1u : 2u);
+            if constexpr (WT == 0) {
+              const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(T.rw, (int)off, 0, kCachePolicyNt);
+              wf[u][g][0] = w.x; wf[u][g][1] = w.y; wf[u][g][2] = w.z; wf[u][g][3] = w.w;
+            } else {
+              const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(T.rw, (int)off, 0, kCachePolicyNt);
+              wf[u][g][0] = w.x; wf[u][g][1] = w.y; wf[u][g][2] = 0; wf[u][g][3] = 0;
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (t + u < T.t1) {
+        const int k = 32 * (t + u) + 8 * T.kq;
+        float xv[8];
+        if (T.emb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { xv[2 * i] = bf_lo(xw[u][i]); xv[2 * i + 1] = bf_hi(xw[u][i]); }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xv[i] = __uint_as_float(xw[u][i]);
+        }
+        // x * gain as one bf16 half (hi for columns < 8, lo for the others); inputs past K are 0
+        uint32_t hx[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v0 = k + 2 * i < T.K ? xv[2 * i] : 0.f, v1 = k + 2 * i + 1 < T.K ? xv[2 * i + 1] : 0.f;
+          if (sumsq && !T.lo_half) ss = fmaf(v0, v0, fmaf(v1, v1, ss));
+          if constexpr (GAIN) {
+            v0 *= bf_lo(gw[u][i]);
+            v1 *= bf_hi(gw[u][i]);
+          }
+          uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
+          if (T.lo_half) {
+            h0 = f32_to_bf16(v0 - bf16_to_f32(h0));
+            h1 = f32_to_bf16(v1 - bf16_to_f32(h1));
+          }
+          hx[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        }
+        const bf16x8_t xb = bf16x8_of_bits(hx[0], hx[1], hx[2], hx[3]);
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+          if (g < gn) {
+            const bf16x8_t a = WT == 0 ? bf16x8_of_bits(wf[u][g][0], wf[u][g][1], wf[u][g][2], wf[u][g][3])
+                                       : bf16x8_of_i8(wf[u][g][0], wf[u][g][1]);
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb, acc[g], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+}
+
 template <int WT>
 __device__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, const float *scale,
                           int K, int r0, int r1, const BatchInput &in, float *ys, float *red,
@@ -655,103 +752,66 @@ __device__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, c
   constexpr int NW = kWaves;
   const int B = s.batch, n = r1 - r0, G = (n + 15) / 16;
   const int lane = lane_id(), wave = (int)uniform_u32((uint32_t)wave_id());
-  const int bq = lane & 15, kq = lane >> 4;
-  const int T = (K + 31) / 32;
-  const int t0 = (int)((int64_t)T * wave / NW), t1 = (int)((int64_t)T * (wave + 1) / NW);
-  const int rb = K * (WT ? 1 : 2);  // weight row bytes
-  const __amdgpu_buffer_rsrc_t rw =
-      make_rsrc(static_cast<const uint8_t *>(W) + (int64_t)r0 * rb, (uint32_t)n * (uint32_t)rb);
-  const __amdgpu_buffer_rsrc_t rx =
-      in.emb ? make_rsrc(in.emb, (uint32_t)m.V * (uint32_t)K * 2u)
-             : make_rsrc(in.x, (uint32_t)B * (uint32_t)in.stride * 4u);
-  const __amdgpu_buffer_rsrc_t rg = make_rsrc(in.gain ? in.gain : m.final_norm, (uint32_t)K * 2u);
-  // this lane's input row: byte offset of X_b[0] (past the range for sequences >= B)
-  uint32_t xrow = 0xffffffffu;
-  if (bq < B) xrow = in.emb ? (uint32_t)token_of(m, s, bq) * (uint32_t)K * 2u : (uint32_t)bq * (uint32_t)in.stride * 4u;
+  MfmaTile T;
+  T.K = K;
+  T.n = n;
+  T.rb = K * (WT ? 1 : 2);
+  const int steps = (K + 31) / 32;
+  T.t0 = (int)((int64_t)steps * wave / NW);
+  T.t1 = (int)((int64_t)steps * (wave + 1) / NW);
+  T.col = lane & 15;
+  T.kq = lane >> 4;
+  T.lo_half = T.col >= 8;
+  T.emb = in.emb != nullptr;
+  T.gain = in.gain != nullptr;
+  T.rw = make_rsrc(static_cast<const uint8_t *>(W) + (int64_t)r0 * T.rb, (uint32_t)n * (uint32_t)T.rb);
+  T.rx = in.emb ? make_rsrc(in.emb, (uint32_t)m.V * (uint32_t)K * 2u)
+                : make_rsrc(in.x, (uint32_t)B * (uint32_t)in.stride * 4u);
+  T.rg = make_rsrc(in.gain ? in.gain : m.final_norm, (uint32_t)K * 2u);
+  const int b = T.col & 7;
+  T.xrow = 0xffffffffu;
+  if (b < B) T.xrow = in.emb ? (uint32_t)token_of(m, s, b) * (uint32_t)K * 2u : (uint32_t)b * (uint32_t)in.stride * 4u;
   float ss = 0.f;
   for (int g0 = 0; g0 < G; g0 += kMfmaGroups) {
     const int gn = min(kMfmaGroups, G - g0);
+    const bool sq = in.sumsq && g0 == 0;
     f32x4_t acc[kMfmaGroups];
-#pragma unroll
-    for (int g = 0; g < kMfmaGroups; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-    for (int t = t0; t < t1; ++t) {
-      const int k = 32 * t + 8 * kq;  // this lane's 8 inputs: k .. k + 7
-      float xv[8];
-      if (in.emb) {
-        const u32x4_t e = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xrow + (uint32_t)k * 2u), 0, 0);
-        const uint32_t ew[4] = {e.x, e.y, e.z, e.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { xv[2 * i] = bf_lo(ew[i]); xv[2 * i + 1] = bf_hi(ew[i]); }
-      } else {
-        const f32x4_t a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                          rx, (int)(xrow + (uint32_t)k * 4u), 0, kCachePolicySc1));
-        const f32x4_t b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                          rx, (int)(xrow + (uint32_t)k * 4u + 16u), 0, kCachePolicySc1));
-        xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
-        xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
-      }
-      uint32_t gw[4] = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 ones
-      if (in.gain) {
-        const u32x4_t gv = __builtin_amdgcn_raw_buffer_load_b128(rg, k * 2, 0, 0);
-        gw[0] = gv.x; gw[1] = gv.y; gw[2] = gv.z; gw[3] = gv.w;
-      }
-      uint32_t wf[kMfmaGroups][4];
-#pragma unroll
-      for (int g = 0; g < kMfmaGroups; ++g) {
-        if (g < gn) {
-          const uint32_t off = (uint32_t)(16 * (g0 + g) + bq) * (uint32_t)rb + (uint32_t)k * (WT ? 1u : 2u);
-          if constexpr (WT == 0) {
-            const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, kCachePolicyNt);
-            wf[g][0] = w.x; wf[g][1] = w.y; wf[g][2] = w.z; wf[g][3] = w.w;
-          } else {
-            const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rw, (int)off, 0, kCachePolicyNt);
-            wf[g][0] = w.x; wf[g][1] = w.y; wf[g][2] = 0; wf[g][3] = 0;
-          }
-        }
-      }
-      // x * gain as bf16 hi + lo; inputs past K are zero
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v0 = k + 2 * i < K ? xv[2 * i] : 0.f, v1 = k + 2 * i + 1 < K ? xv[2 * i + 1] : 0.f;
-        if (in.sumsq && g0 == 0) ss = fmaf(v0, v0, fmaf(v1, v1, ss));
-        v0 *= bf_lo(gw[i]);
-        v1 *= bf_hi(gw[i]);
-        const uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
-        const uint16_t l0 = f32_to_bf16(v0 - bf16_to_f32(h0)), l1 = f32_to_bf16(v1 - bf16_to_f32(h1));
-        hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        lo[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-      }
-      const bf16x8_t xh = bf16x8_of_bits(hi[0], hi[1], hi[2], hi[3]);
-      const bf16x8_t xl = bf16x8_of_bits(lo[0], lo[1], lo[2], lo[3]);
-#pragma unroll
-      for (int g = 0; g < kMfmaGroups; ++g) {
-        if (g < gn) {
-          const bf16x8_t a = WT == 0 ? bf16x8_of_bits(wf[g][0], wf[g][1], wf[g][2], wf[g][3])
-                                     : bf16x8_of_i8(wf[g][0], wf[g][1]);
-          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xh, acc[g], 0, 0, 0);
-          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl, acc[g], 0, 0, 0);
-        }
-      }
+    if (T.gain) {
+      if (gn <= 1)
+        mfma_pass<WT, 1, 4, true>(T, g0, gn, sq, ss, acc);
+      else if (gn == 2)
+        mfma_pass<WT, 2, 4, true>(T, g0, gn, sq, ss, acc);
+      else
+        mfma_pass<WT, 4, 2, true>(T, g0, gn, sq, ss, acc);
+    } else {
+      if (gn <= 1)
+        mfma_pass<WT, 1, 4, false>(T, g0, gn, sq, ss, acc);
+      else if (gn == 2)
+        mfma_pass<WT, 2, 4, false>(T, g0, gn, sq, ss, acc);
+      else
+        mfma_pass<WT, 4, 2, false>(T, g0, gn, sq, ss, acc);
     }
-    // partial tiles of all waves -> ys
-    if (bq < 8) {
+    // partial tiles of all waves (16 columns: hi and lo halves) -> ys
 #pragma unroll
-      for (int g = 0; g < kMfmaGroups; ++g)
-        if (g < gn)
+    for (int g = 0; g < kMfmaGroups; ++g)
+      if (g < gn)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mred[((wave * kMfmaGroups + g) * 16 + 4 * kq + i) * 8 + bq] = acc[g][i];
-    }
+        for (int i = 0; i < 4; ++i) {
+          // column c of row 4 kq + i: hi and lo of one sequence land in the same float
+          const int row = 4 * T.kq + i;
+          float v = acc[g][i];
+          v += __shfl_xor(v, 8, 64);  // lanes c and c ^ 8 hold the two halves of sequence c & 7
+          if (T.col < 8) mred[((wave * kMfmaGroups + g) * 16 + row) * 8 + T.col] = v;
+        }
     __syncthreads();
     for (int e = threadIdx.x; e < gn * 16 * 8; e += NW * 64) {
-      const int g = e >> 7, row = (e >> 3) & 15, b = e & 7;
+      const int g = e >> 7, row = (e >> 3) & 15, bb = e & 7;
       const int r = 16 * (g0 + g) + row;
-      if (b < B && r < n) {
+      if (bb < B && r < n) {
         float t = 0.f;
-        for (int w = 0; w < NW; ++w) t += mred[((w * kMfmaGroups + g) * 16 + row) * 8 + b];
+        for (int w = 0; w < NW; ++w) t += mred[((w * kMfmaGroups + g) * 16 + row) * 8 + bb];
         if constexpr (WT == 1) t *= gld(&scale[r0 + r]);
-        ys[b * n + r] = t;
+        ys[bb * n + r] = t;
       }
     }
     __syncthreads();
@@ -759,7 +819,7 @@ __device__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, c
   if (in.sumsq) {
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
-    if (kq == 0 && bq < B) red[bq * NW + wave] = ss;
+    if (T.kq == 0 && T.col < B && T.col < 8) red[T.col * NW + wave] = ss;
   }
 }
 

@@ -21,7 +21,7 @@ namespace amk {
 // its own prefetch); the input vector is staged (RMSNorm / attention combine / plain copy) after the
 // wait, then the row stream runs double-buffered, the RMSNorm scale is applied to the outputs and
 // the epilogue writes them.
-template <int WT>
+template <int WT, bool BATCHED>
 __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, const Task &t,
                                           float *xs, float *ys, float *red, uint4 *pf,
                                           int *abort_slot) {
@@ -32,9 +32,10 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
   int K, wtype;
   gemv_matrix(m, t.mat, l, &W, &scale, &K, &wtype);
   const int r0 = (int)t.a0, r1 = (int)t.a1;
-  // the LDS layout (staged input and prefetch slots, or matrix-core partial tiles) follows the
-  // model's batch capacity; a smaller step batch runs the batched GEMV with zero columns
-  const bool b1 = m.max_batch == 1;
+  // The kernel instance (and its LDS layout: staged input and prefetch slots, or the matrix
+  // cores' partial tiles) follows the model's batch capacity; a smaller step batch runs the
+  // batched GEMV with zero columns.
+  constexpr bool b1 = !BATCHED;
   GemvStream<WT> st;
   uint4 P[kChunkUnits];
   st.init(W, K, r0, r1, NW);
@@ -82,7 +83,7 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
   return true;
 }
 
-template <int WT, int HD, int QMAX>
+template <int WT, int HD, int QMAX, bool BATCHED>
 __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArgs &s) {
   extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte reads of xs need it
   const int32_t xa = lds_xs_floats(m.max_batch, m.d, m.qd, m.F);
@@ -104,7 +105,7 @@ __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArg
     if (trace && threadIdx.x == 0) trace[(uint64_t)t.id * 4 + 0] = wall_clock64();
     bool ok;
     if (t.type == T_GEMV) {
-      ok = gemv_task<WT>(m, s, t, xs, ys, red, pf, &abort_flag);
+      ok = gemv_task<WT, BATCHED>(m, s, t, xs, ys, red, pf, &abort_flag);
     } else if (t.type == T_ATTN) {
       ok = attn_task<HD, QMAX>(m, s, t.layer, (int)t.a0, (int)t.a1, xs, red, &t, &abort_flag);
       if (ok) attn_count_and_combine(m, s, t.layer, (int)t.a0, &last_flag);
@@ -129,12 +130,17 @@ __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArg
 
 using namespace amk;
 
-#define AMK_MK(WT, HD, Q)                                                          \
-  extern "C" __global__ void __launch_bounds__(kThreads, 1)                        \
-      amk_megakernel_w##WT##_h##HD##_q##Q(const DevModel *__restrict__ mp, StepArgs s) { \
-    megakernel_body<WT, HD, Q>(*mp, s);                                            \
+#define AMK_MK(WT, HD, Q)                                                                     \
+  extern "C" __global__ void __launch_bounds__(kThreads, 1)                                   \
+      amk_megakernel_w##WT##_h##HD##_q##Q(const DevModel *__restrict__ mp, StepArgs s) {      \
+    megakernel_body<WT, HD, Q, false>(*mp, s);                                                \
+  }                                                                                           \
+  extern "C" __global__ void __launch_bounds__(kThreads, 1)                                   \
+      amk_megakernel_w##WT##_h##HD##_q##Q##_b(const DevModel *__restrict__ mp, StepArgs s) {  \
+    megakernel_body<WT, HD, Q, true>(*mp, s);                                                 \
   }
 
+// batch-1 instances (weight stream with LDS prefetch) and batched ones (suffix _b: matrix cores)
 AMK_MK(0, 64, 1)
 AMK_MK(0, 64, 2)
 AMK_MK(0, 64, 4)

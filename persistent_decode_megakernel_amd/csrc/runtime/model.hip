@@ -17,8 +17,9 @@
 using namespace amk;
 
 // kernels defined in the other translation units
-#define AMK_DECL_MK(WT, HD, Q) \
-  extern "C" __global__ void amk_megakernel_w##WT##_h##HD##_q##Q(const DevModel *, StepArgs);
+#define AMK_DECL_MK(WT, HD, Q)                                                         \
+  extern "C" __global__ void amk_megakernel_w##WT##_h##HD##_q##Q(const DevModel *, StepArgs); \
+  extern "C" __global__ void amk_megakernel_w##WT##_h##HD##_q##Q##_b(const DevModel *, StepArgs);
 AMK_DECL_MK(0, 64, 1)
 AMK_DECL_MK(0, 64, 2)
 AMK_DECL_MK(0, 64, 4)
@@ -81,9 +82,10 @@ void hip_check(hipError_t e, const char *what) {
 
 using MkFn = void (*)(const DevModel *, StepArgs);
 
-MkFn pick_megakernel(int wt, int hd, int qmax) {
-#define AMK_P(WT, HD, Q) \
-  if (wt == WT && hd == HD && qmax == Q) return amk_megakernel_w##WT##_h##HD##_q##Q;
+MkFn pick_megakernel(int wt, int hd, int qmax, bool batched) {
+#define AMK_P(WT, HD, Q)                                                                    \
+  if (wt == WT && hd == HD && qmax == Q)                                                    \
+    return batched ? amk_megakernel_w##WT##_h##HD##_q##Q##_b : amk_megakernel_w##WT##_h##HD##_q##Q;
   AMK_P(0, 64, 1) AMK_P(0, 64, 2) AMK_P(0, 64, 4) AMK_P(0, 128, 1) AMK_P(0, 128, 2) AMK_P(0, 128, 4)
   AMK_P(1, 64, 1) AMK_P(1, 64, 2) AMK_P(1, 64, 4) AMK_P(1, 128, 1) AMK_P(1, 128, 2) AMK_P(1, 128, 4)
 #undef AMK_P
@@ -443,7 +445,7 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     hip_check(hipMemcpyAsync(m->d_dm, &dm, sizeof dm, hipMemcpyHostToDevice, st), "hipMemcpyAsync");
 
     const int qmax = qmax_for(dm.qpg);
-    m->mk = pick_megakernel(cfg->wtype, hd, qmax);
+    m->mk = pick_megakernel(cfg->wtype, hd, qmax, B > 1);
     m->uf_attn = pick_uf_attn(hd, qmax);
     if (!m->mk || !m->uf_attn) throw std::runtime_error("no kernel instance for this shape");
     m->uf_attn_lds = 4u * (64 * 8 + (uint32_t)lds_attn_floats(1, qmax, hd));
