@@ -997,6 +997,19 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
     if (waits) wait_poll(m, *wait_for, s.epoch, abort_slot);
     load_history();
     if (waits && !wait_join(m, *wait_for, abort_slot)) return false;
+    // The row at pos was appended by this step's QKV tiles: device-coherent loads, issued right
+    // after the wait together with q, for whichever chunk and lane holds it.
+    const int po = pos - lo;
+    const bool own_pos = po >= 0 && pos < hi && (po % ROWS_PER_ITER) == wave * RPW + rs;
+    uint4 kpos = make_uint4(0, 0, 0, 0), vpos = make_uint4(0, 0, 0, 0);
+    if (own_pos) {
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)pos * HD, HD * 2);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + (int64_t)pos * HD, HD * 2);
+      const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(rk, sub * 16, 0, kCachePolicySc1);
+      const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(rv, sub * 16, 0, kCachePolicySc1);
+      kpos = make_uint4(a.x, a.y, a.z, a.w);
+      vpos = make_uint4(c.x, c.y, c.z, c.w);
+    }
     const float *qsrc = m.q + ((int64_t)l * m.max_batch + b) * m.qd + ((int64_t)g * m.qpg + h0) * HD;
     for (int i = threadIdx.x; i < qpg * HD; i += NW * 64) qs[i] = cldf(&qsrc[i]) * m.attn_scale;
     __syncthreads();
@@ -1021,25 +1034,21 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
     }
     for (int c0 = lo; c0 < hi; c0 += kAttnRowsPerChunk) {
       const int c1 = min(hi, c0 + kAttnRowsPerChunk);
-      if (c0 == lo) {
-        // the row appended by this step (visible after the wait)
+      if (c0 != lo) {
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
           const int j = c0 + it * ROWS_PER_ITER + wave * RPW + rs;
-          if (j == pos && j < c1) {  // written by this step: device-coherent loads
-            const uint32_t *kp = reinterpret_cast<const uint32_t *>(Kb + (int64_t)j * HD + sub * 8);
-            const uint32_t *vp = reinterpret_cast<const uint32_t *>(Vb + (int64_t)j * HD + sub * 8);
-            kr[it] = make_uint4(cld(kp), cld(kp + 1), cld(kp + 2), cld(kp + 3));
-            vr[it] = make_uint4(cld(vp), cld(vp + 1), cld(vp + 2), cld(vp + 3));
-          }
-        }
-      } else {
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-          const int j = c0 + it * ROWS_PER_ITER + wave * RPW + rs;
-          const bool ok = j < c1;
+          const bool ok = j < c1 && j != pos;
           kr[it] = ok ? gld4(reinterpret_cast<const uint4 *>(Kb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
           vr[it] = ok ? gld4(reinterpret_cast<const uint4 *>(Vb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
+        }
+      }
+      // the appended row, wherever it falls (its history slot was left zero above)
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        if (c0 + it * ROWS_PER_ITER + wave * RPW + rs == pos) {
+          kr[it] = kpos;
+          vr[it] = vpos;
         }
       }
       // scores of this lane's rows, reduced over the LPR lanes of a row
