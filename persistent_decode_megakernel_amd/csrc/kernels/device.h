@@ -34,6 +34,10 @@ struct DevModel {
   float *q;            // [L][B][qd]
   float *part;         // [L][B][nq][nblk][hd+2]
   float *ao;           // [L][B][qd] attention output, merged over the KV blocks
+  // batch-1 instances: the same activations as (value, epoch) words, the epoch in the high half
+  uint64_t *ht;        // [2L+1][d] residual stream
+  uint64_t *at;        // [L][F] SwiGLU output
+  uint64_t *aot;       // [L][qd] merged attention output
   uint32_t *acnt;      // [L][nkv] KV blocks of the group finished in this step (0 between steps)
   float *a;            // [L][B][F]
   float *logits;       // [B][V] used when the caller passes no logits buffer
@@ -607,6 +611,85 @@ __device__ void stage_plain(const float *src, int64_t src_stride, int K, int B, 
   __syncthreads();
 }
 
+// Tagged activations (batch 1). A value that crosses CUs within a step is stored together with
+// the step's epoch as one 64-bit word (value in the low half): a single aligned store, so a
+// reader sees both halves of one write. The consumer's staging loads are then its dependency
+// wait: it reloads until every tag holds the current epoch, so the producer needs neither to wait
+// for its stores to complete nor to publish a flag, and the consumer saves a separate poll round.
+__device__ __forceinline__ uint64_t tag_pack(float v, uint32_t epoch) {
+  return ((uint64_t)epoch << 32) | __float_as_uint(v);
+}
+
+// xs[i] = v_i * gain[i] (gain may be null) for the n tagged values at src (n even), once every
+// tag holds `epoch`; with a gain the per-wave sums of v^2 go to red[wave]. Eight 16-byte loads
+// (two values each) per thread per round. Returns false after a timeout (recorded as a device
+// error) or when another workgroup aborted.
+__device__ bool stage_tagged(const DevModel &m, const uint64_t *src, int n, const uint16_t *gain,
+                             uint32_t epoch, float *xs, float *red, int *abort_slot,
+                             uint32_t task) {
+  constexpr int V = 8;
+  const int nu = n / 2;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)n * 8u);
+  float ss = 0.f;
+  uint64_t t0 = 0;
+  uint32_t spins = 0;
+  for (int base = 0; base < nu; base += V * kThreads) {
+    while (true) {
+      u32x4_t v[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        v[j] = __builtin_amdgcn_raw_buffer_load_b128(
+            rs, (int)((uint32_t)min(base + (int)threadIdx.x + j * kThreads, nu - 1) * 16u), 0,
+            kCachePolicySc1);
+      int ok = 1;
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        if (base + (int)threadIdx.x + j * kThreads < nu) ok &= (v[j].y == epoch) & (v[j].w == epoch);
+      if (__syncthreads_and(ok)) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          const int u = base + (int)threadIdx.x + j * kThreads;
+          if (u < nu) {
+            float a = __uint_as_float(v[j].x), b = __uint_as_float(v[j].z);
+            if (gain) {
+              ss = fmaf(a, a, fmaf(b, b, ss));
+              const uint32_t g = gld(reinterpret_cast<const uint32_t *>(gain) + u);
+              a *= bf_lo(g);
+              b *= bf_hi(g);
+            }
+            *reinterpret_cast<float2 *>(xs + 2 * u) = make_float2(a, b);
+          }
+        }
+        break;
+      }
+      // not all written yet: bounded wait (thread 0 decides, every retry, whether to give up)
+      if (spins == 0) t0 = wall_clock64();
+      ++spins;
+      if (threadIdx.x == 0) {
+        int ab = 0;
+        if ((spins & 7) == 0) {
+          ab = flag_load(&m.err[1]) != 0;
+          if (!ab && wall_clock64() - t0 > m.timeout_ticks) {
+            record_error(m.err, ERR_TIMEOUT, task, 0xfffffff0u);
+            __hip_atomic_store(&m.err[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ab = 1;
+          }
+        }
+        *abort_slot = ab;
+      }
+      __syncthreads();
+      if (*abort_slot) return false;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  if (gain) {
+    ss = wave_sum(ss);
+    if (lane_id() == 0) red[wave_id()] = ss;
+  }
+  __syncthreads();
+  return true;
+}
+
 // ------------------------------------------------------------------------------------------
 // Batch GEMV (B = 2..8 sequences) on the matrix cores:
 //   ys[b * n + (r - r0)] = sum_k X_b[k] W[r][k]  (times scale[r] for int8), r in [r0, r1).
@@ -886,6 +969,27 @@ __device__ void epi_swiglu(const DevModel &m, const StepArgs &s, int l, int r0, 
     for (int i = threadIdx.x; i < n / 2; i += nw * 64)
       cstf(&a[r0 / 2 + i], silu(ys[b * n + 2 * i]) * ys[b * n + 2 * i + 1]);
   }
+}
+
+// batch-1 (tagged) forms of the residual and SwiGLU epilogues
+__device__ void epi_residual_tagged(const DevModel &m, const StepArgs &s, int res_slot,
+                                    int out_slot, int r0, int r1, const float *ys, int nw) {
+  const int n = r1 - r0, d = m.d;
+  uint64_t *out = m.ht + (int64_t)out_slot * d;
+  const uint64_t *res = m.ht + (int64_t)res_slot * d;
+  const uint16_t *e = (res_slot == 0) ? m.embed + (int64_t)token_of(m, s, 0) * d : nullptr;
+  for (int i = threadIdx.x; i < n; i += nw * 64) {
+    const int r = r0 + i;
+    const float base = e ? bf16_to_f32(gld(&e[r])) : __uint_as_float((uint32_t)cld(&res[r]));
+    cst(&out[r], tag_pack(base + ys[i], s.epoch));
+  }
+}
+__device__ void epi_swiglu_tagged(const DevModel &m, const StepArgs &s, int l, int r0, int r1,
+                                  const float *ys, int nw) {
+  const int n = r1 - r0;
+  uint64_t *a = m.at + (int64_t)l * m.F;
+  for (int i = threadIdx.x; i < n / 2; i += nw * 64)
+    cst(&a[r0 / 2 + i], tag_pack(silu(ys[2 * i]) * ys[2 * i + 1], s.epoch));
 }
 
 // logits rows + (max, lowest index of max) of this tile into amax[slot][b]
@@ -1202,7 +1306,10 @@ __device__ void attn_group_combine(const DevModel &m, const StepArgs &s, int l, 
       }
       M = Mb;
     }
-    cstf(&m.ao[((int64_t)l * m.max_batch + b) * m.qd + (int64_t)h * hd + e], num / den);
+    if (m.max_batch == 1)
+      cst(&m.aot[(int64_t)l * m.qd + (int64_t)h * hd + e], tag_pack(num / den, s.epoch));
+    else
+      cstf(&m.ao[((int64_t)l * m.max_batch + b) * m.qd + (int64_t)h * hd + e], num / den);
   }
 }
 

@@ -15,12 +15,12 @@
 
 namespace amk {
 
-// GEMV tile task: the first two weight chunks of every wave (one into its LDS slot, one into
-// registers) are issued before the dependency wait completes (wave 0 polls the flags and issues
-// its chunks after polling: a wave's loads return in order, so its flag reads would queue behind
-// its own prefetch); the input vector is staged (RMSNorm / attention combine / plain copy) after the
-// wait, then the row stream runs double-buffered, the RMSNorm scale is applied to the outputs and
-// the epilogue writes them.
+// GEMV tile task. Batch 1: the first two weight chunks of every wave (one into its LDS slot, one
+// into registers) are issued at once, then the input is staged from its epoch-tagged producer
+// words (which doubles as the dependency wait; the first layer's QKV tiles read the embedding and
+// have no producer). Batched: a flag wait (wave 0 polls), then the matrix-core GEMV reads its
+// inputs straight from memory. The RMSNorm scale is applied to the outputs and the epilogue writes
+// them (tagged for batch 1).
 template <int WT, bool BATCHED>
 __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, const Task &t,
                                           float *xs, float *ys, float *red, uint4 *pf,
@@ -40,17 +40,42 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
   uint4 P[kChunkUnits];
   st.init(W, K, r0, r1, NW);
   uint4 *slot = pf + st.wave * (64 * kChunkUnits);
-  wait_poll(m, t, s.epoch, abort_slot);
-  if (b1 && st.S > 0) st.load_lds(0, slot);
-  if (b1 && st.S > 1) st.load(P, 1);
-  if (!wait_join(m, t, abort_slot)) return false;
   if (b1) {
+    // Batch 1: inputs produced in this step by other tiles are tagged with the epoch, so their
+    // staging loads are the dependency wait (no flags): the weight prefetch is issued at once.
+    const bool tagged = !(t.mat == M_QKV && l == 0);
+    if (!tagged) wait_poll(m, t, s.epoch, abort_slot);
+    if (st.S > 0) st.load_lds(0, slot);
+    if (st.S > 1) st.load(P, 1);
+    if (!tagged && !wait_join(m, t, abort_slot)) return false;
+    if (m.trace && threadIdx.x == 0) m.trace[(uint64_t)t.id * 4 + 1] = wall_clock64();
+    bool ok = true;
     switch (t.mat) {
-      case M_QKV: stage_norm(m, s, 2 * l, m.layers[l].attn_norm, xs, red, NW); break;
-      case M_O: stage_plain(m.ao + (int64_t)l * m.max_batch * m.qd, m.qd, m.qd, 1, xs, NW); break;
-      case M_GU: stage_norm(m, s, 2 * l + 1, m.layers[l].mlp_norm, xs, red, NW); break;
-      case M_D: stage_plain(m.a + (int64_t)l * m.max_batch * m.F, m.F, m.F, 1, xs, NW); break;
-      default: stage_norm(m, s, 2 * m.L, m.final_norm, xs, red, NW); break;
+      case M_QKV:
+        if (l == 0)
+          stage_norm(m, s, 0, m.layers[0].attn_norm, xs, red, NW);
+        else
+          ok = stage_tagged(m, m.ht + (int64_t)2 * l * m.d, m.d, m.layers[l].attn_norm, s.epoch,
+                            xs, red, abort_slot, t.id);
+        break;
+      case M_O:
+        ok = stage_tagged(m, m.aot + (int64_t)l * m.qd, m.qd, nullptr, s.epoch, xs, red, abort_slot, t.id);
+        break;
+      case M_GU:
+        ok = stage_tagged(m, m.ht + (int64_t)(2 * l + 1) * m.d, m.d, m.layers[l].mlp_norm, s.epoch,
+                          xs, red, abort_slot, t.id);
+        break;
+      case M_D:
+        ok = stage_tagged(m, m.at + (int64_t)l * m.F, m.F, nullptr, s.epoch, xs, red, abort_slot, t.id);
+        break;
+      default:
+        ok = stage_tagged(m, m.ht + (int64_t)2 * m.L * m.d, m.d, m.final_norm, s.epoch, xs, red,
+                          abort_slot, t.id);
+        break;
+    }
+    if (!ok) {
+      __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS may outlive the workgroup
+      return false;
     }
     if (m.trace && threadIdx.x == 0) m.trace[(uint64_t)t.id * 4 + 2] = wall_clock64();
     st.run_pf(slot, P, xs, ys, scale);
@@ -68,6 +93,7 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
       case M_D: in = BatchInput{m.a + (int64_t)l * m.max_batch * m.F, m.F, nullptr, nullptr, false}; break;
       default: in.x = m.h + 2 * (int64_t)m.L * hb; in.gain = m.final_norm; break;
     }
+    if (!wait_task(m, t, s.epoch, abort_slot)) return false;
     if (m.trace && threadIdx.x == 0) m.trace[(uint64_t)t.id * 4 + 2] = wall_clock64();
     gemv_mfma<WT>(m, s, W, scale, K, r0, r1, in, ys, red, xs);
   }
@@ -75,12 +101,28 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
   if (t.mat != M_O && t.mat != M_D) norm_scale_ys(m, s, r1 - r0, ys, red, NW);
   switch (t.mat) {
     case M_QKV: epi_qkv(m, s, l, r0, r1, ys, NW); break;
-    case M_O: epi_residual(m, s, 2 * l, 2 * l + 1, r0, r1, ys, NW); break;
-    case M_GU: epi_swiglu(m, s, l, r0, r1, ys, NW); break;
-    case M_D: epi_residual(m, s, 2 * l + 1, 2 * l + 2, r0, r1, ys, NW); break;
+    case M_O:
+      if (b1) epi_residual_tagged(m, s, 2 * l, 2 * l + 1, r0, r1, ys, NW);
+      else epi_residual(m, s, 2 * l, 2 * l + 1, r0, r1, ys, NW);
+      break;
+    case M_GU:
+      if (b1) epi_swiglu_tagged(m, s, l, r0, r1, ys, NW);
+      else epi_swiglu(m, s, l, r0, r1, ys, NW);
+      break;
+    case M_D:
+      if (b1) epi_residual_tagged(m, s, 2 * l + 1, 2 * l + 2, r0, r1, ys, NW);
+      else epi_residual(m, s, 2 * l + 1, 2 * l + 2, r0, r1, ys, NW);
+      break;
     default: epi_logits(m, s, r0, r1, (int)t.aux0, ys, red, NW); break;
   }
   return true;
+}
+
+// Whether a finished task's consumers learn of it from its flag. Batch-1 O, gate/up and down
+// tiles publish tagged data instead: they neither wait for their stores nor store a flag.
+template <bool BATCHED>
+__device__ __forceinline__ bool publishes_flag(const Task &t) {
+  return BATCHED || t.type != T_GEMV || !(t.mat == M_O || t.mat == M_GU || t.mat == M_D);
 }
 
 template <int WT, int HD, int QMAX, bool BATCHED>
@@ -93,6 +135,8 @@ __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArg
   uint4 *pf = reinterpret_cast<uint4 *>(red + kRedFloats);  // lds_prefetch_floats(max_batch)
   float *ys = red + kRedFloats + lds_prefetch_floats(m.max_batch);  // batch * max_tile_rows
   __shared__ int abort_flag, last_flag;
+  if (threadIdx.x == 0) abort_flag = 0;
+  __syncthreads();
   const uint32_t t0 = m.offsets[blockIdx.x], t1 = m.offsets[blockIdx.x + 1];
   uint64_t *const trace = m.trace;
   if (trace && threadIdx.x == 0) {
@@ -117,11 +161,16 @@ __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArg
     // Publish: every wave waits for its own (device-coherent) stores to complete, the workgroup
     // meets, then one thread stores the flag. Data that crosses CUs is written with device-scope
     // stores, so no L2 writeback is needed before the flag.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      if (trace) trace[(uint64_t)t.id * 4 + 3] = wall_clock64();
-      __hip_atomic_store(&m.flags[t.id], s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (publishes_flag<BATCHED>(t)) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        if (trace) trace[(uint64_t)t.id * 4 + 3] = wall_clock64();
+        __hip_atomic_store(&m.flags[t.id], s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      __syncthreads();
+      if (trace && threadIdx.x == 0) trace[(uint64_t)t.id * 4 + 3] = wall_clock64();
     }
   }
 }

@@ -2,6 +2,7 @@
 // tables), KV caches, and the per-step launch of the megakernel or the unfused ablation.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -65,6 +66,11 @@ amk_gather_rows(uint32_t *dst, const uint32_t *src, const int2 *pairs, int n, in
     uint32_t *d = dst + (int64_t)p.x * row_words;
     for (int k = threadIdx.x; k < row_words; k += 256) d[k] = s[k];
   }
+}
+
+// zero n 32-bit words: used instead of a memset node where the caller may be capturing a graph
+extern "C" __global__ void __launch_bounds__(256) amk_zero_words(uint32_t *p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
 }
 
 namespace {
@@ -201,11 +207,29 @@ amk_status map_device_error(uint32_t code, uint32_t task, uint32_t detail) {
   return set_error(AMK_E_DEVICE_FAULT, "device error code " + std::to_string(code));
 }
 
+void zero_async(void *p, size_t bytes, hipStream_t st) {
+  const size_t n = bytes / 4;
+  const unsigned blocks = (unsigned)std::min<size_t>(1024, (n + 255) / 256);
+  if (n) hipLaunchKernelGGL(amk_zero_words, dim3(blocks), dim3(256), 0, st, static_cast<uint32_t *>(p), n);
+}
+
+// Tagged activations carry an epoch: whenever the epoch restarts they are cleared too, so no
+// word of an earlier run can pass for the new step's. A fill kernel, not a memset, since this runs
+// inside amk_decode_step, which a caller may capture into a graph.
+void clear_tags(amk_model *m, hipStream_t st) {
+  const size_t L = m->cfg.n_layers, d = m->cfg.hidden, F = m->cfg.ffn,
+               qd = (size_t)m->cfg.n_heads * m->cfg.head_dim;
+  zero_async(m->dm.ht, sizeof(uint64_t) * (2 * L + 1) * d, st);
+  zero_async(m->dm.at, sizeof(uint64_t) * L * F, st);
+  zero_async(m->dm.aot, sizeof(uint64_t) * L * qd, st);
+}
+
 // reset device error words, flags and the epoch after a device-side failure
 void reset_device_state(amk_model *m, hipStream_t st) {
   (void)hipMemsetAsync(m->dm.err, 0, 4 * sizeof(uint32_t), st);
   (void)hipMemsetAsync(m->dm.flags, 0, sizeof(uint32_t) * std::max<uint32_t>(1, m->sched.hdr.n_tasks), st);
   (void)hipMemsetAsync(m->dm.acnt, 0, sizeof(uint32_t) * m->cfg.n_layers * m->cfg.n_kv_heads, st);
+  clear_tags(m, st);
   (void)hipStreamSynchronize(st);
   m->epoch = 0;
   m->err_pending = false;
@@ -407,6 +431,10 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     dm.q = m->dalloc<float>((size_t)L * B * qd);
     dm.part = m->dalloc<float>((size_t)L * B * nq * nblk * (hd + 2));
     dm.ao = m->dalloc<float>((size_t)L * B * qd);
+    // batch-1 instances exchange these activations as (value, epoch) words instead
+    dm.ht = m->dalloc<uint64_t>((size_t)(2 * L + 1) * d);
+    dm.at = m->dalloc<uint64_t>((size_t)L * F);
+    dm.aot = m->dalloc<uint64_t>((size_t)L * qd);
     dm.acnt = m->dalloc<uint32_t>((size_t)L * cfg->n_kv_heads);
     dm.a = m->dalloc<float>((size_t)L * B * F);
     dm.logits = m->dalloc<float>((size_t)B * V);
@@ -421,6 +449,7 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     hip_check(hipMemsetAsync(dm.flags, 0, sizeof(uint32_t) * std::max<uint32_t>(1, h.n_tasks), st), "hipMemsetAsync");
     hip_check(hipMemsetAsync(dm.err, 0, 16, st), "hipMemsetAsync");
     hip_check(hipMemsetAsync(dm.acnt, 0, sizeof(uint32_t) * L * cfg->n_kv_heads, st), "hipMemsetAsync");
+    clear_tags(m, st);
     // task tables
     std::vector<uint32_t> offs(h.n_cu + 1);
     std::vector<Task> tasks;
@@ -589,7 +618,8 @@ extern "C" amk_status amk_decode_step(amk_model *m, amk_kv *kv, const int32_t *d
     return set_error(AMK_E_CAPACITY, "amk_decode_step: position beyond max_seq");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (m->epoch >= 0x7ffffff0u) {  // keep the signed flag comparison unambiguous
-    hip_check(hipMemsetAsync(m->dm.flags, 0, sizeof(uint32_t) * std::max<uint32_t>(1, m->sched.hdr.n_tasks), st), "hipMemsetAsync");
+    zero_async(m->dm.flags, sizeof(uint32_t) * std::max<uint32_t>(1, m->sched.hdr.n_tasks), st);
+    clear_tags(m, st);
     m->epoch = 0;
   }
   StepArgs s;

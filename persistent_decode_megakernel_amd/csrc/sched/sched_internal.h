@@ -47,7 +47,15 @@ struct Access {
   int64_t lo, hi; // element range [lo, hi)
   bool write;
   int32_t group;  // -1: the task's own access
+  bool staged;    // the GEMV input vector the tile stages (the dependency of a tagged hand-off)
 };
+
+// Batch-1 megakernel instances (max_batch == 1) hand the activations between GEMV phases over as
+// epoch-tagged words: a tile whose staged input is such an activation waits by reloading it until
+// every tag is current (its flag waits are not consulted), and the O, gate/up and down tiles store
+// no flag. These two predicates mirror the kernel's choice.
+bool tagged_handoff(const BlobHeader &h);
+bool stores_flag(const BlobHeader &h, const Task &t);
 
 // Read/write footprint of a task, derived from the task's own fields and the config. Reads of
 // the embedding row (h[0]), weights and KV history are not listed: nothing in a step writes them.

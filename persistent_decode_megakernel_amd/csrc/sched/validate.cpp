@@ -9,7 +9,10 @@
 //     workgroup co-resident (the runtime launches cooperatively) and flags that only grow, an
 //     acyclic graph means every wait is eventually satisfied;
 //   * race freedom and coverage: every element a task reads from a buffer written during the
-//     step is written by exactly one task, and that writer happens-before the reader.
+//     step is written by exactly one task, and that writer happens-before the reader;
+//   * tagged hand-offs (batch-1 instances): a tile that waits by reloading its tagged input
+//     declares exactly that input's writers as its waits, so the graph checked above is the one
+//     the kernel enforces, and no task waits on the flag of a tile that stores none.
 // The simulator is an independent dynamic check: it executes the tasks under several
 // interleavings (greedy, and one run per delayed CU) with shadow memory, flagging stale reads,
 // double writes and stuck states.
@@ -33,7 +36,12 @@ std::string fmt(const char *f, long long a = 0, long long b = 0, long long c = 0
 
 void add_range(std::vector<Access> *acc, int buf, int index, int64_t lo, int64_t hi, bool w,
                int32_t group = -1) {
-  if (hi > lo) acc->push_back(Access{buf, index, lo, hi, w, group});
+  if (hi > lo) acc->push_back(Access{buf, index, lo, hi, w, group, false});
+}
+
+// the GEMV input vector: read whole, staged into LDS
+void add_staged(std::vector<Access> *acc, int buf, int index, int64_t n) {
+  if (n > 0) acc->push_back(Access{buf, index, 0, n, false, -1, true});
 }
 
 // Merge sorted element indices into intervals.
@@ -49,6 +57,13 @@ void add_elems(std::vector<Access> *acc, int buf, int index, std::vector<int64_t
 }
 
 }  // namespace
+
+bool tagged_handoff(const BlobHeader &h) { return h.cfg.max_batch == 1; }
+
+bool stores_flag(const BlobHeader &h, const Task &t) {
+  return !tagged_handoff(h) || t.type != T_GEMV ||
+         !(t.mat == M_O || t.mat == M_GU || t.mat == M_D);
+}
 
 bool footprint(const BlobHeader &h, const Task &t, std::vector<Access> *acc, std::string *err) {
   const BlobConfig &c = h.cfg;
@@ -80,7 +95,7 @@ bool footprint(const BlobHeader &h, const Task &t, std::vector<Access> *acc, std
     const int64_t a0 = t.a0, a1 = t.a1;
     switch (t.mat) {
       case M_QKV: {
-        if (l > 0) add_range(acc, BUF_H, (int)(2 * l), 0, B * d, false);
+        if (l > 0) add_staged(acc, BUF_H, (int)(2 * l), B * d);
         std::vector<int64_t> qe, ke;
         for (int64_t r = a0; r < a1; ++r) {
           QkvRow q = qkv_decode((int32_t)r, (int32_t)nq, (int32_t)nkv, (int32_t)hd);
@@ -96,18 +111,18 @@ bool footprint(const BlobHeader &h, const Task &t, std::vector<Access> *acc, std
         break;
       }
       case M_O:
-        add_range(acc, BUF_AO, (int)l, 0, B * qd, false);
+        add_staged(acc, BUF_AO, (int)l, B * qd);
         for (int64_t b = 0; b < B; ++b) {
           if (l > 0) add_range(acc, BUF_H, (int)(2 * l), b * d + a0, b * d + a1, false);
           add_range(acc, BUF_H, (int)(2 * l + 1), b * d + a0, b * d + a1, true);
         }
         break;
       case M_GU:
-        add_range(acc, BUF_H, (int)(2 * l + 1), 0, B * d, false);
+        add_staged(acc, BUF_H, (int)(2 * l + 1), B * d);
         for (int64_t b = 0; b < B; ++b) add_range(acc, BUF_A, (int)l, b * F + a0 / 2, b * F + a1 / 2, true);
         break;
       case M_D:
-        add_range(acc, BUF_A, (int)l, 0, B * F, false);
+        add_staged(acc, BUF_A, (int)l, B * F);
         for (int64_t b = 0; b < B; ++b) {
           add_range(acc, BUF_H, (int)(2 * l + 1), b * d + a0, b * d + a1, false);
           add_range(acc, BUF_H, (int)(2 * l + 2), b * d + a0, b * d + a1, true);
@@ -116,7 +131,7 @@ bool footprint(const BlobHeader &h, const Task &t, std::vector<Access> *acc, std
       case M_LM:
         if (t.layer != 0) return bad("LM tile must carry layer 0");
         if (t.aux0 >= h.n_lm_tiles) return bad("argmax slot out of range");
-        add_range(acc, BUF_H, (int)(2 * L), 0, B * d, false);
+        add_staged(acc, BUF_H, (int)(2 * L), B * d);
         for (int64_t b = 0; b < B; ++b) add_range(acc, BUF_LOGITS, 0, b * V + a0, b * V + a1, true);
         add_range(acc, BUF_AMAX, 0, (int64_t)t.aux0 * B, (int64_t)t.aux0 * B + B, true);
         break;
@@ -391,6 +406,42 @@ bool validate_schedule(const Schedule &s, std::string *report) {
       }
       if (covered < rd.hi)
         return fail(fmt("combine group %lld reads element %lld that no task writes", rd.group, covered));
+    }
+  }
+  // tagged hand-offs: the kernel's wait for a tagged tile is its staged input's writers (every
+  // member of a combine group for a merged output); a flag wait must name tiles that store flags
+  if (tagged_handoff(h)) {
+    std::vector<uint32_t> want, have;
+    for (uint32_t id = 0; id < n; ++id) {
+      const Task &t = *g.task[id];
+      if (!footprint(h, t, &acc, &e)) return fail(e);
+      const Access *st = nullptr;
+      for (const Access &a : acc)
+        if (a.staged) st = &a;
+      have.clear();
+      for (int k = 0; k < 2; ++k)
+        for (uint32_t y = k ? t.w1_lo : t.w0_lo; y < (k ? t.w1_hi : t.w0_hi); ++y) have.push_back(y);
+      if (!st) {
+        for (uint32_t y : have)
+          if (!stores_flag(h, *g.task[y]))
+            return fail(fmt("task %lld waits on the flag of task %lld, which stores none", id, y));
+        continue;
+      }
+      want.clear();
+      auto it = writes.find(BufKey{st->buf, st->index});
+      if (it != writes.end())
+        for (const Span &w : it->second) {
+          if (w.hi <= st->lo || w.lo >= st->hi) continue;
+          if (w.group < 0) want.push_back(w.id);
+          else want.insert(want.end(), members[w.group].begin(), members[w.group].end());
+        }
+      std::sort(want.begin(), want.end());
+      want.erase(std::unique(want.begin(), want.end()), want.end());
+      std::sort(have.begin(), have.end());
+      have.erase(std::unique(have.begin(), have.end()), have.end());
+      if (want != have)
+        return fail(fmt("task %lld: declared waits (%lld tasks) differ from the writers of its tagged input (%lld tasks)",
+                        id, (long long)have.size(), (long long)want.size()));
     }
   }
   // outputs must be complete

@@ -200,3 +200,64 @@ def test_combine_group_needs_all_blocks(libamk):
                 t["a0"] = 1  # block 0 of group 0 now claims group 1: group 0 is one short
     st, rep = _lib.schedule_validate(b.to_bytes())
     assert st == _lib.AMK_E_SCHEDULE_REJECTED, rep
+
+
+def _tasks_by(b: B.Blob, typ, mat=None, layer=None):
+    return sorted(int(t["id"]) for v in b.per_cu for t in v
+                  if t["type"] == typ and (mat is None or t["mat"] == mat)
+                  and (layer is None or t["layer"] == layer))
+
+
+def _find(b: B.Blob, tid: int):
+    return next(t for v in b.per_cu for t in v if int(t["id"]) == tid)
+
+
+@pytest.mark.parametrize("max_batch", [1, 2])
+def test_tagged_tile_waits_must_equal_its_input_writers(libamk, max_batch):
+    """Batch-1 instances: a gate/up tile waits by reloading its tagged input, so a declared wait
+    on anything other than that input's writers (here also an attention block, harmless as a flag
+    wait) would be a dependency the kernel never enforces: rejected. The batched instance waits on
+    flags, where the extra wait is merely redundant: accepted."""
+    cfg = synth.get_config("tiny")
+    b = B.Blob(_lib.schedule_build(_lib.make_config(cfg, max_batch=max_batch), 1, 8))
+    gu = _tasks_by(b, B.T_GEMV, B.M_GU, 1)
+    attn = _tasks_by(b, B.T_ATTN, None, 1)
+    t = _find(b, gu[0])
+    assert int(t["w1_lo"]) == int(t["w1_hi"])
+    t["w1_lo"], t["w1_hi"] = attn[0], attn[0] + 1
+    st, rep = _lib.schedule_validate(b.to_bytes())
+    if max_batch == 1:
+        assert st == _lib.AMK_E_SCHEDULE_REJECTED and "tagged" in rep, rep
+    else:
+        assert st == _lib.AMK_OK, rep
+
+
+@pytest.mark.parametrize("max_batch", [1, 2])
+def test_flag_wait_on_a_tile_that_stores_no_flag(libamk, max_batch):
+    """Batch-1 O, gate/up and down tiles publish tagged data and no flag: a task that waits on
+    flags (here the argmax, also on a down tile) would wait forever. Batched tiles store flags."""
+    cfg = synth.get_config("tiny")
+    b = B.Blob(_lib.schedule_build(_lib.make_config(cfg, max_batch=max_batch), 1, 8))
+    dn = _tasks_by(b, B.T_GEMV, B.M_D, cfg.n_layers - 1)
+    t = _find(b, _tasks_by(b, B.T_ARGMAX)[0])
+    assert int(t["w1_lo"]) == int(t["w1_hi"])
+    t["w1_lo"], t["w1_hi"] = dn[0], dn[0] + 1
+    st, rep = _lib.schedule_validate(b.to_bytes())
+    if max_batch == 1:
+        assert st == _lib.AMK_E_SCHEDULE_REJECTED and "stores none" in rep, rep
+    else:
+        assert st == _lib.AMK_OK, rep
+
+
+def test_tagged_waits_of_real_lowerings_are_their_input_writers(libamk):
+    """Dropping one writer from a tagged tile's waits (a shrunk range) is rejected even where the
+    tile's CU order happens to cover it."""
+    cfg = synth.get_config("tiny")
+    b = B.Blob(_lib.schedule_build(_lib.make_config(cfg), 1, 8))
+    d = _tasks_by(b, B.T_GEMV, B.M_D, 0)
+    gu = _tasks_by(b, B.T_GEMV, B.M_GU, 0)
+    t = _find(b, d[0])
+    assert (int(t["w0_lo"]), int(t["w0_hi"])) == (gu[0], gu[-1] + 1)
+    t["w0_hi"] = gu[-1]
+    st, rep = _lib.schedule_validate(b.to_bytes())
+    assert st == _lib.AMK_E_SCHEDULE_REJECTED, rep
