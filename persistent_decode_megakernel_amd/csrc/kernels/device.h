@@ -34,10 +34,10 @@ struct DevModel {
   float *q;            // [L][B][qd]
   float *part;         // [L][B][nq][nblk][hd+2]
   float *ao;           // [L][B][qd] attention output, merged over the KV blocks
-  // batch-1 instances: the same activations as (value, epoch) words, the epoch in the high half
-  uint64_t *ht;        // [2L+1][d] residual stream
-  uint64_t *at;        // [L][F] SwiGLU output
-  uint64_t *aot;       // [L][qd] merged attention output
+  // batch-1 instances: the same activations as tagged fp32 words (tag_word)
+  uint32_t *ht;        // [2L+1][d] residual stream
+  uint32_t *at;        // [L][F] SwiGLU output
+  uint32_t *aot;       // [L][qd] merged attention output
   uint32_t *acnt;      // [L][nkv] KV blocks of the group finished in this step (0 between steps)
   float *a;            // [L][B][F]
   float *logits;       // [B][V] used when the caller passes no logits buffer
@@ -611,74 +611,83 @@ __device__ void stage_plain(const float *src, int64_t src_stride, int K, int B, 
   __syncthreads();
 }
 
-// Tagged activations (batch 1). A value that crosses CUs within a step is stored together with
-// the step's epoch as one 64-bit word (value in the low half): a single aligned store, so a
-// reader sees both halves of one write. The consumer's staging loads are then its dependency
-// wait: it reloads until every tag holds the current epoch, so the producer needs neither to wait
-// for its stores to complete nor to publish a flag, and the consumer saves a separate poll round.
-__device__ __forceinline__ uint64_t tag_pack(float v, uint32_t epoch) {
-  return ((uint64_t)epoch << 32) | __float_as_uint(v);
+// Tagged activations (batch 1). A value that crosses CUs within a step is stored as one fp32
+// word whose two lowest mantissa bits are replaced by the low bits of the step's epoch (the value
+// moves by at most 3 ulp). One aligned 32-bit store carries value and tag together, so the
+// consumer's staging loads are its dependency wait: it reloads until every tag matches, and the
+// producer needs neither to wait for its stores nor to publish a flag.
+//
+// Two tag bits suffice because every slot is written exactly once by every step that completes,
+// so a slot holds either this step's word or the previous step's, whose tag differs. A step that
+// fails leaves the device abort word set until the host resets the model, which also clears every
+// slot; a consumer reads the abort word in its first round, so it never accepts an older word.
+constexpr uint32_t kTagMask = 3u;
+__device__ __forceinline__ uint32_t tag_word(float v, uint32_t epoch) {
+  return (__float_as_uint(v) & ~kTagMask) | (epoch & kTagMask);
 }
 
-// xs[i] = v_i * gain[i] (gain may be null) for the n tagged values at src (n even), once every
-// tag holds `epoch`; with a gain the per-wave sums of v^2 go to red[wave]. Eight 16-byte loads
-// (two values each) per thread per round. Returns false after a timeout (recorded as a device
-// error) or when another workgroup aborted.
-__device__ bool stage_tagged(const DevModel &m, const uint64_t *src, int n, const uint16_t *gain,
-                             uint32_t epoch, float *xs, float *red, int *abort_slot,
-                             uint32_t task) {
+// xs[i] = v_i * gain[i] (gain may be null) for the n tagged words at src (n % 4 == 0), once every
+// tag matches `epoch`; with a gain the per-wave sums of v^2 go to red[wave]. Each thread owns up
+// to eight 16-byte units per round and reloads only those whose tags were stale. Returns false
+// after a timeout (recorded as a device error) or when the abort word is set.
+__device__ bool stage_tagged(const DevModel &m, const uint32_t *src, int n, const uint16_t *gain,
+                             uint32_t epoch, float *xs, float *red, uint32_t task) {
   constexpr int V = 8;
-  const int nu = n / 2;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)n * 8u);
+  const int nu = n >> 2;
+  const uint32_t tag = epoch & kTagMask;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)n * 4u);
   float ss = 0.f;
   uint64_t t0 = 0;
   uint32_t spins = 0;
   for (int base = 0; base < nu; base += V * kThreads) {
+    uint32_t need = 0;
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+      if (base + (int)threadIdx.x + j * kThreads < nu) need |= 1u << j;
     while (true) {
       u32x4_t v[V];
 #pragma unroll
       for (int j = 0; j < V; ++j)
-        v[j] = __builtin_amdgcn_raw_buffer_load_b128(
-            rs, (int)((uint32_t)min(base + (int)threadIdx.x + j * kThreads, nu - 1) * 16u), 0,
-            kCachePolicySc1);
-      int ok = 1;
+        if (need & (1u << j))
+          v[j] = __builtin_amdgcn_raw_buffer_load_b128(
+              rs, (int)((uint32_t)(base + (int)threadIdx.x + j * kThreads) * 16u), 0,
+              kCachePolicySc1);
+      // thread 0: the abort word on the first round and every eighth retry; the timeout
+      int ab = 0;
+      if (threadIdx.x == 0 && (spins == 0 || (spins & 7) == 7)) {
+        ab = flag_load(&m.err[1]) != 0;
+        if (!ab && spins && wall_clock64() - t0 > m.timeout_ticks) {
+          record_error(m.err, ERR_TIMEOUT, task, 0xfffffff0u);
+          __hip_atomic_store(&m.err[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ab = 1;
+        }
+      }
 #pragma unroll
-      for (int j = 0; j < V; ++j)
-        if (base + (int)threadIdx.x + j * kThreads < nu) ok &= (v[j].y == epoch) & (v[j].w == epoch);
-      if (__syncthreads_and(ok)) {
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          const int u = base + (int)threadIdx.x + j * kThreads;
-          if (u < nu) {
-            float a = __uint_as_float(v[j].x), b = __uint_as_float(v[j].z);
+      for (int j = 0; j < V; ++j) {
+        if (need & (1u << j)) {
+          const u32x4_t w = v[j];
+          if ((((w.x ^ tag) | (w.y ^ tag) | (w.z ^ tag) | (w.w ^ tag)) & kTagMask) == 0) {
+            need &= ~(1u << j);
+            const int u = base + (int)threadIdx.x + j * kThreads;
+            float a = __uint_as_float(w.x), b = __uint_as_float(w.y), c = __uint_as_float(w.z),
+                  d = __uint_as_float(w.w);
             if (gain) {
-              ss = fmaf(a, a, fmaf(b, b, ss));
-              const uint32_t g = gld(reinterpret_cast<const uint32_t *>(gain) + u);
-              a *= bf_lo(g);
-              b *= bf_hi(g);
+              ss = fmaf(a, a, fmaf(b, b, fmaf(c, c, fmaf(d, d, ss))));
+              const uint2 g = gld_bf16x4(gain, u);
+              a *= bf_lo(g.x);
+              b *= bf_hi(g.x);
+              c *= bf_lo(g.y);
+              d *= bf_hi(g.y);
             }
-            *reinterpret_cast<float2 *>(xs + 2 * u) = make_float2(a, b);
+            *reinterpret_cast<float4 *>(xs + 4 * u) = make_float4(a, b, c, d);
           }
         }
-        break;
       }
-      // not all written yet: bounded wait (thread 0 decides, every retry, whether to give up)
+      const int pending = __syncthreads_or(need != 0);
+      if (__syncthreads_or(ab)) return false;
+      if (!pending) break;
       if (spins == 0) t0 = wall_clock64();
       ++spins;
-      if (threadIdx.x == 0) {
-        int ab = 0;
-        if ((spins & 7) == 0) {
-          ab = flag_load(&m.err[1]) != 0;
-          if (!ab && wall_clock64() - t0 > m.timeout_ticks) {
-            record_error(m.err, ERR_TIMEOUT, task, 0xfffffff0u);
-            __hip_atomic_store(&m.err[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            ab = 1;
-          }
-        }
-        *abort_slot = ab;
-      }
-      __syncthreads();
-      if (*abort_slot) return false;
       __builtin_amdgcn_s_sleep(1);
     }
   }
@@ -971,25 +980,27 @@ __device__ void epi_swiglu(const DevModel &m, const StepArgs &s, int l, int r0, 
   }
 }
 
-// batch-1 (tagged) forms of the residual and SwiGLU epilogues
+// batch-1 (tagged) forms of the residual and SwiGLU epilogues. The residual word is read untagged:
+// the tile has already staged a complete tagged input whose producers had read that same residual
+// slot, so the slot is current.
 __device__ void epi_residual_tagged(const DevModel &m, const StepArgs &s, int res_slot,
                                     int out_slot, int r0, int r1, const float *ys, int nw) {
   const int n = r1 - r0, d = m.d;
-  uint64_t *out = m.ht + (int64_t)out_slot * d;
-  const uint64_t *res = m.ht + (int64_t)res_slot * d;
+  uint32_t *out = m.ht + (int64_t)out_slot * d;
+  const uint32_t *res = m.ht + (int64_t)res_slot * d;
   const uint16_t *e = (res_slot == 0) ? m.embed + (int64_t)token_of(m, s, 0) * d : nullptr;
   for (int i = threadIdx.x; i < n; i += nw * 64) {
     const int r = r0 + i;
-    const float base = e ? bf16_to_f32(gld(&e[r])) : __uint_as_float((uint32_t)cld(&res[r]));
-    cst(&out[r], tag_pack(base + ys[i], s.epoch));
+    const float base = e ? bf16_to_f32(gld(&e[r])) : __uint_as_float(cld(&res[r]));
+    cst(&out[r], tag_word(base + ys[i], s.epoch));
   }
 }
 __device__ void epi_swiglu_tagged(const DevModel &m, const StepArgs &s, int l, int r0, int r1,
                                   const float *ys, int nw) {
   const int n = r1 - r0;
-  uint64_t *a = m.at + (int64_t)l * m.F;
+  uint32_t *a = m.at + (int64_t)l * m.F;
   for (int i = threadIdx.x; i < n / 2; i += nw * 64)
-    cst(&a[r0 / 2 + i], tag_pack(silu(ys[2 * i]) * ys[2 * i + 1], s.epoch));
+    cst(&a[r0 / 2 + i], tag_word(silu(ys[2 * i]) * ys[2 * i + 1], s.epoch));
 }
 
 // logits rows + (max, lowest index of max) of this tile into amax[slot][b]
@@ -1055,7 +1066,7 @@ __device__ void argmax_combine(const DevModel &m, const StepArgs &s, int n_slots
 
 // ------------------------------------------------------------------------------------------
 // attention partial for (layer l, kv group g, KV block blk) over positions [lo, hi) of ctx.
-// LDS: q [qpg][hd] | scores [qpg][kAttnRowsPerChunk] | acc [nw][qpg*hd] | stats.
+// LDS: q [qpg][hd] | scores [qpg][chunk] | acc [nw][qpg*hd] | stats.
 // Lane layout: LPR = hd/8 lanes per KV row (8 dims each), 64/LPR rows per wave per load.
 // ------------------------------------------------------------------------------------------
 template <int HD, int QMAX>
@@ -1070,8 +1081,9 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
   constexpr int LPR = HD / 8;
   constexpr int RPW = 64 / LPR;  // rows per wave per load
   constexpr int ROWS_PER_ITER = NW * RPW;
-  constexpr int NIT = kAttnRowsPerChunk / ROWS_PER_ITER;
-  static_assert(NIT * ROWS_PER_ITER == kAttnRowsPerChunk, "chunk must be whole iterations");
+  constexpr int CH = attn_chunk_rows(HD, QMAX);
+  constexpr int NIT = CH / ROWS_PER_ITER;
+  static_assert(NIT * ROWS_PER_ITER == CH && CH <= kAttnRowsPerChunk, "chunk must be whole iterations");
   const int qpg = qn, nq = m.nq, nblk = m.nblk;
   const int lane = lane_id(), wave = wave_id();
   const int sub = lane % LPR, rs = lane / LPR;
@@ -1080,13 +1092,13 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
   attn_block_range(pos + 1, nblk, blk, &lo, &hi);
   float *qs = lds;                             // [qpg][HD]
   float *sc = qs + qpg * HD;                   // [qpg][chunk]
-  float *accw = sc + qpg * kAttnRowsPerChunk;  // [NW][qpg*HD]
+  float *accw = sc + qpg * CH;  // [NW][qpg*HD]
   for (int b = 0; b < s.batch; ++b) {
     const uint16_t *Kb = s.kv + kv_index(m, s, l, 0, b, g, 0, 0);
     const uint16_t *Vb = s.kv + kv_index(m, s, l, 1, b, g, 0, 0);
     uint4 kr[NIT], vr[NIT];
     auto load_history = [&]() {
-      const int c1 = min(hi, lo + kAttnRowsPerChunk);
+      const int c1 = min(hi, lo + CH);
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const int j = lo + it * ROWS_PER_ITER + wave * RPW + rs;
@@ -1136,8 +1148,8 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     }
-    for (int c0 = lo; c0 < hi; c0 += kAttnRowsPerChunk) {
-      const int c1 = min(hi, c0 + kAttnRowsPerChunk);
+    for (int c0 = lo; c0 < hi; c0 += CH) {
+      const int c1 = min(hi, c0 + CH);
       if (c0 != lo) {
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
@@ -1165,7 +1177,7 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
             float p = dot8_bf16(kr[it], qs + h * HD + sub * 8);
 #pragma unroll
             for (int o = LPR / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o, 64);
-            if (j < c1 && sub == 0) sc[h * kAttnRowsPerChunk + (j - c0)] = p;
+            if (j < c1 && sub == 0) sc[h * CH + (j - c0)] = p;
           }
         }
       }
@@ -1174,7 +1186,7 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
       const int n = c1 - c0;
       if (wave < qpg) {
         float mx = -INFINITY;
-        for (int i = lane; i < n; i += 64) mx = fmaxf(mx, sc[wave * kAttnRowsPerChunk + i]);
+        for (int i = lane; i < n; i += 64) mx = fmaxf(mx, sc[wave * CH + i]);
         mx = wave_max(mx);
         if (lane == 0) red[wave] = mx;
       }
@@ -1200,7 +1212,7 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
 #pragma unroll
           for (int h = 0; h < QMAX; ++h) {
             if (h < qpg) {
-              const float p = __expf(sc[h * kAttnRowsPerChunk + (j - c0)] - mrun[h]);
+              const float p = __expf(sc[h * CH + (j - c0)] - mrun[h]);
               if (sub == 0) lsum[h] += p;
 #pragma unroll
               for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vv[e], acc[h][e]);
@@ -1307,7 +1319,7 @@ __device__ void attn_group_combine(const DevModel &m, const StepArgs &s, int l, 
       M = Mb;
     }
     if (m.max_batch == 1)
-      cst(&m.aot[(int64_t)l * m.qd + (int64_t)h * hd + e], tag_pack(num / den, s.epoch));
+      cst(&m.aot[(int64_t)l * m.qd + (int64_t)h * hd + e], tag_word(num / den, s.epoch));
     else
       cstf(&m.ao[((int64_t)l * m.max_batch + b) * m.qd + (int64_t)h * hd + e], num / den);
   }

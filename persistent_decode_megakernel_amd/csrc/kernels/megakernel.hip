@@ -56,21 +56,21 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
           stage_norm(m, s, 0, m.layers[0].attn_norm, xs, red, NW);
         else
           ok = stage_tagged(m, m.ht + (int64_t)2 * l * m.d, m.d, m.layers[l].attn_norm, s.epoch,
-                            xs, red, abort_slot, t.id);
+                            xs, red, t.id);
         break;
       case M_O:
-        ok = stage_tagged(m, m.aot + (int64_t)l * m.qd, m.qd, nullptr, s.epoch, xs, red, abort_slot, t.id);
+        ok = stage_tagged(m, m.aot + (int64_t)l * m.qd, m.qd, nullptr, s.epoch, xs, red, t.id);
         break;
       case M_GU:
         ok = stage_tagged(m, m.ht + (int64_t)(2 * l + 1) * m.d, m.d, m.layers[l].mlp_norm, s.epoch,
-                          xs, red, abort_slot, t.id);
+                          xs, red, t.id);
         break;
       case M_D:
-        ok = stage_tagged(m, m.at + (int64_t)l * m.F, m.F, nullptr, s.epoch, xs, red, abort_slot, t.id);
+        ok = stage_tagged(m, m.at + (int64_t)l * m.F, m.F, nullptr, s.epoch, xs, red, t.id);
         break;
       default:
         ok = stage_tagged(m, m.ht + (int64_t)2 * m.L * m.d, m.d, m.final_norm, s.epoch, xs, red,
-                          abort_slot, t.id);
+                          t.id);
         break;
     }
     if (!ok) {
@@ -129,7 +129,7 @@ template <int WT, int HD, int QMAX, bool BATCHED>
 __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArgs &s) {
   extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte reads of xs need it
   const int32_t xa = lds_xs_floats(m.max_batch, m.d, m.qd, m.F);
-  const int32_t xb = lds_attn_floats(m.max_batch, m.qpg, m.hd);
+  const int32_t xb = lds_attn_floats(m.qpg, m.hd);
   float *xs = lds;
   float *red = lds + (xa > xb ? xa : xb);  // kRedFloats floats
   uint4 *pf = reinterpret_cast<uint4 *>(red + kRedFloats);  // lds_prefetch_floats(max_batch)

@@ -115,7 +115,7 @@ UgFn pick_uf_gemv(int wt, int mode) {
   return t[wt][mode];
 }
 
-int qmax_for(int qpg) { return qpg <= 1 ? 1 : (qpg <= 2 ? 2 : 4); }
+int qmax_for(int qpg) { return qpg <= 1 ? 1 : (qpg <= 2 ? 2 : kAttnMaxHeads); }
 
 }  // namespace
 
@@ -219,9 +219,9 @@ void zero_async(void *p, size_t bytes, hipStream_t st) {
 void clear_tags(amk_model *m, hipStream_t st) {
   const size_t L = m->cfg.n_layers, d = m->cfg.hidden, F = m->cfg.ffn,
                qd = (size_t)m->cfg.n_heads * m->cfg.head_dim;
-  zero_async(m->dm.ht, sizeof(uint64_t) * (2 * L + 1) * d, st);
-  zero_async(m->dm.at, sizeof(uint64_t) * L * F, st);
-  zero_async(m->dm.aot, sizeof(uint64_t) * L * qd, st);
+  zero_async(m->dm.ht, sizeof(uint32_t) * (2 * L + 1) * d, st);
+  zero_async(m->dm.at, sizeof(uint32_t) * L * F, st);
+  zero_async(m->dm.aot, sizeof(uint32_t) * L * qd, st);
 }
 
 // reset device error words, flags and the epoch after a device-side failure
@@ -431,10 +431,10 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     dm.q = m->dalloc<float>((size_t)L * B * qd);
     dm.part = m->dalloc<float>((size_t)L * B * nq * nblk * (hd + 2));
     dm.ao = m->dalloc<float>((size_t)L * B * qd);
-    // batch-1 instances exchange these activations as (value, epoch) words instead
-    dm.ht = m->dalloc<uint64_t>((size_t)(2 * L + 1) * d);
-    dm.at = m->dalloc<uint64_t>((size_t)L * F);
-    dm.aot = m->dalloc<uint64_t>((size_t)L * qd);
+    // batch-1 instances exchange these activations as tagged words instead
+    dm.ht = m->dalloc<uint32_t>((size_t)(2 * L + 1) * d);
+    dm.at = m->dalloc<uint32_t>((size_t)L * F);
+    dm.aot = m->dalloc<uint32_t>((size_t)L * qd);
     dm.acnt = m->dalloc<uint32_t>((size_t)L * cfg->n_kv_heads);
     dm.a = m->dalloc<float>((size_t)L * B * F);
     dm.logits = m->dalloc<float>((size_t)B * V);
@@ -477,7 +477,7 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     m->mk = pick_megakernel(cfg->wtype, hd, qmax, B > 1);
     m->uf_attn = pick_uf_attn(hd, qmax);
     if (!m->mk || !m->uf_attn) throw std::runtime_error("no kernel instance for this shape");
-    m->uf_attn_lds = 4u * (64 * 8 + (uint32_t)lds_attn_floats(1, qmax, hd));
+    m->uf_attn_lds = 4u * (64 * 8 + (uint32_t)lds_attn_floats(qmax, hd));
     if (path == AMK_PATH_MEGAKERNEL) {
       hip_check(hipFuncSetAttribute((const void *)m->mk, hipFuncAttributeMaxDynamicSharedMemorySize,
                                     (int)m->lds_bytes), "hipFuncSetAttribute");

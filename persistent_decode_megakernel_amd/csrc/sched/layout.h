@@ -119,7 +119,15 @@ namespace amk {
 // Attention tasks reuse the xs region (q, scores, partial accumulators).
 constexpr int32_t kWaves = 8;
 constexpr int32_t kThreads = kWaves * 64;
-constexpr int32_t kAttnRowsPerChunk = 256;  // KV rows staged per attention chunk
+// KV rows staged per attention chunk (a KV block of up to this many rows is one round of loads):
+// 320 rows (10 row iterations of the eight waves at head_dim 128, 5 at head_dim 64) where the
+// registers allow, 256 for head_dim 128 with several query heads per pass. LDS is sized for the
+// largest.
+constexpr int32_t kAttnRowsPerChunk = 320;
+constexpr int32_t kAttnMaxHeads = 4;  // query heads per attention pass (larger groups take several)
+AMK_HD constexpr int32_t attn_chunk_rows(int32_t hd, int32_t qmax) {
+  return (hd <= 64 || qmax == 1) ? kAttnRowsPerChunk : 256;
+}
 constexpr int32_t kRedFloats = 2048;        // reduction scratch; holds n_heads x blocks weights
 
 // Staged GEMV input (batch 1 only: batched GEMVs read their inputs straight from memory and use
@@ -130,9 +138,11 @@ AMK_HD int32_t lds_xs_floats(int32_t batch, int32_t hidden, int32_t qdim, int32_
   k = k > ffn ? k : ffn;
   return batch == 1 ? k : kMfmaRedFloats;
 }
-AMK_HD int32_t lds_attn_floats(int32_t batch, int32_t qpg, int32_t hd) {
-  // q [B][qpg][hd] + scores [B][qpg][chunk] + partial acc [waves][B*qpg*hd]
-  return batch * qpg * hd + batch * qpg * kAttnRowsPerChunk + kWaves * batch * qpg * hd;
+AMK_HD int32_t lds_attn_floats(int32_t qpg, int32_t hd) {
+  // one sequence and at most kAttnMaxHeads heads per pass:
+  // q [qn][hd] + scores [qn][chunk] + partial acc [waves][qn*hd]
+  const int32_t qn = qpg < kAttnMaxHeads ? qpg : kAttnMaxHeads;
+  return qn * hd + qn * kAttnRowsPerChunk + kWaves * qn * hd;
 }
 // Batch-1 GEMV tiles stage the first weight chunk of every wave in LDS (8 KB per wave).
 constexpr int32_t kPrefetchFloats = kWaves * 2048;
@@ -141,7 +151,7 @@ AMK_HD int32_t lds_prefetch_floats(int32_t batch) { return batch == 1 ? kPrefetc
 AMK_HD int32_t lds_bytes_for(int32_t batch, int32_t hidden, int32_t qdim, int32_t ffn,
                              int32_t qpg, int32_t hd, int32_t max_tile_rows) {
   int32_t a = lds_xs_floats(batch, hidden, qdim, ffn);
-  int32_t b = lds_attn_floats(batch, qpg, hd);
+  int32_t b = lds_attn_floats(qpg, hd);
   int32_t region = a > b ? a : b;
   return 4 * (region + kRedFloats + lds_prefetch_floats(batch) + batch * max_tile_rows);
 }
