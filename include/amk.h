@@ -155,6 +155,28 @@ amk_status amk_trace_enable(amk_model *m, uint64_t *d_trace, size_t bytes);
 /* Copy of the model's frozen schedule blob (host memory, release with amk_blob_free). */
 amk_status amk_model_get_schedule(const amk_model *m, void **blob, size_t *bytes);
 
+/* Replace the frozen schedule of a megakernel model with another one of the same structure: same
+ * config, batch, CU count, task count, KV blocks and LM tiles (e.g. a copy re-tiled by
+ * amk_schedule_rebalance). The blob (host) is validated first (AMK_E_SCHEDULE_REJECTED; a
+ * different structure gives AMK_E_UNSUPPORTED and leaves the model unchanged). Synchronises
+ * `stream`, uploads the task tables and restarts the flag epochs. Not for use while a step of this
+ * model is being captured into a graph. */
+amk_status amk_model_set_schedule(amk_model *m, const void *blob, size_t bytes, void *stream);
+
+/* Profile-guided tuning of the frozen schedule on the device: the offline search that profiles
+ * candidates and solidifies the best path (Ada-MK summary, "Fine-Grained DAG-Based Automatic
+ * Search"), applied to the row boundaries of the GEMV tiles. Times `steps` untraced decode steps
+ * at positions pos .. pos+steps-1 of `kv` with the current schedule, then `rounds` times: runs
+ * those steps with the task trace on, re-tiles the schedule from the traces
+ * (amk_schedule_rebalance with `gain`), installs and times it. The fastest schedule measured is
+ * kept installed; its mean step time (us) goes to best_us (may be NULL). The steps overwrite
+ * those positions' K/V slots of batch row 0..max_batch-1 and use token 0. Allocates a trace buffer
+ * for the duration of the call; any trace set by amk_trace_enable is turned off. Megakernel path
+ * only (AMK_E_UNSUPPORTED otherwise). Read the result with amk_model_get_schedule and pass it to
+ * amk_model_create to reuse it. */
+amk_status amk_model_tune(amk_model *m, amk_kv *kv, int32_t pos, int32_t rounds, int32_t steps,
+                          double gain, void *stream, double *best_us);
+
 amk_status amk_kv_free(amk_kv *kv);
 amk_status amk_destroy(amk_model *m);
 
@@ -179,6 +201,18 @@ amk_status amk_schedule_validate(const void *blob, size_t bytes, char *report, s
 /* Dynamic cross-check: executes the schedule on the host under several interleavings with
  * monotone flags and shadow memory; reports deadlock or a stale read. Same return convention. */
 amk_status amk_schedule_simulate(const void *blob, size_t bytes, char *report, size_t report_cap);
+
+/* Profile-guided re-tiling (host only). traces: n_traces consecutive task traces (each
+ * 4 * n_tasks + n_cu uint64 words, as amk_trace_enable writes them for one step) of steps run with
+ * this schedule. Within every GEMV phase the row boundaries move a fraction `gain` (0 < gain <= 1)
+ * of the way towards those at which the tiles, each starting when it was staged and streaming at
+ * its measured rate, would all finish together (the next phase needs all of them). Task ids,
+ * placement and waits are kept; attention waits follow the new QKV tiling. The input must
+ * validate and so must the result (AMK_E_SCHEDULE_REJECTED). Output in host memory, released with
+ * amk_blob_free. */
+amk_status amk_schedule_rebalance(const void *blob, size_t bytes, const uint64_t *traces,
+                                  int32_t n_traces, double gain, void **out_blob,
+                                  size_t *out_bytes);
 
 /* Cost-model makespan (us) of a schedule at context length ctx. */
 amk_status amk_schedule_predict(const void *blob, size_t bytes, const amk_cost_model *cost,

@@ -82,6 +82,9 @@ SIGNATURES = {
     "amk_trace_enable": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t]),
     "amk_model_get_schedule": (C.c_int, [C.c_void_p, C.POINTER(C.c_void_p),
                                          C.POINTER(C.c_size_t)]),
+    "amk_model_set_schedule": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "amk_model_tune": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
+                                 C.c_double, C.c_void_p, C.POINTER(C.c_double)]),
     "amk_kv_free": (C.c_int, [C.c_void_p]),
     "amk_destroy": (C.c_int, [C.c_void_p]),
     "amk_last_error": (C.c_char_p, []),
@@ -92,6 +95,8 @@ SIGNATURES = {
     "amk_schedule_simulate": (C.c_int, [C.c_void_p, C.c_size_t, C.c_char_p, C.c_size_t]),
     "amk_schedule_predict": (C.c_int, [C.c_void_p, C.c_size_t, C.POINTER(amk_cost_model),
                                        C.c_int32, C.POINTER(C.c_double)]),
+    "amk_schedule_rebalance": (C.c_int, [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int32, C.c_double,
+                                         C.POINTER(C.c_void_p), C.POINTER(C.c_size_t)]),
     "amk_blob_free": (None, [C.c_void_p]),
 }
 
@@ -171,3 +176,20 @@ def schedule_predict(blob: bytes, ctx: int, cost: Optional[amk_cost_model] = Non
     check(load().amk_schedule_predict(blob, len(blob), C.byref(cost) if cost else None, ctx,
                                       C.byref(out)), "amk_schedule_predict")
     return out.value
+
+
+def schedule_rebalance(blob: bytes, traces, gain: float = 0.5) -> bytes:
+    """Re-tile a schedule from task traces (numpy uint64 array, n_traces x (4 n_tasks + n_cu))."""
+    import numpy as np
+    lib = load()
+    tr = np.ascontiguousarray(traces, dtype=np.uint64)
+    n_traces = tr.shape[0] if tr.ndim == 2 else 1
+    out = C.c_void_p()
+    n = C.c_size_t()
+    check(lib.amk_schedule_rebalance(blob, len(blob), tr.ctypes.data_as(C.c_void_p), n_traces,
+                                     float(gain), C.byref(out), C.byref(n)),
+          "amk_schedule_rebalance")
+    try:
+        return C.string_at(out, n.value)
+    finally:
+        lib.amk_blob_free(out)

@@ -17,7 +17,8 @@ OUT = os.path.join(HERE, "libamk.so")
 BUILD = os.path.join(ROOT, "_build")
 
 HIP_SOURCES = ["kernels/megakernel.hip", "kernels/unfused.hip", "runtime/model.hip"]
-CXX_SOURCES = ["runtime/errors.cpp", "sched/builder.cpp", "sched/validate.cpp", "sched/sched_api.cpp"]
+CXX_SOURCES = ["runtime/errors.cpp", "sched/builder.cpp", "sched/validate.cpp", "sched/sched_api.cpp",
+               "sched/rebalance.cpp"]
 ARCH = "gfx950"
 
 

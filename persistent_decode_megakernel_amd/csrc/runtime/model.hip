@@ -706,6 +706,175 @@ extern "C" amk_status amk_model_get_schedule(const amk_model *m, void **blob, si
   return AMK_OK;
 }
 
+namespace {
+
+// Install an already validated schedule of the model's structure: upload its task tables over
+// the current ones, set the kernel's LDS size, restart the flag epochs. Synchronises `st`.
+amk_status install_schedule(amk_model *m, Schedule &&s, std::vector<uint8_t> &&blob,
+                            hipStream_t st) {
+  const BlobHeader &h = s.hdr, &c = m->sched.hdr;
+  if (m->path != AMK_PATH_MEGAKERNEL)
+    return set_error(AMK_E_UNSUPPORTED, "schedule replacement needs the megakernel path");
+  if (std::memcmp(&h.cfg, &c.cfg, sizeof(BlobConfig)) != 0 || h.batch != c.batch ||
+      h.n_cu != c.n_cu || h.n_tasks != c.n_tasks || h.attn_blocks != c.attn_blocks ||
+      h.n_lm_tiles != c.n_lm_tiles)
+    return set_error(AMK_E_UNSUPPORTED,
+                     "schedule differs in structure (config, batch, CUs, tasks, KV blocks or LM "
+                     "tiles): create a new model with it");
+  hip_check(hipStreamSynchronize(st), "hipStreamSynchronize");
+  std::vector<uint32_t> offs(h.n_cu + 1);
+  std::vector<Task> tasks;
+  tasks.reserve(h.n_tasks);
+  for (uint32_t cu = 0; cu < h.n_cu; ++cu) {
+    offs[cu] = (uint32_t)tasks.size();
+    for (const Task &t : s.per_cu[cu]) tasks.push_back(t);
+  }
+  offs[h.n_cu] = (uint32_t)tasks.size();
+  if (h.lds_bytes != m->lds_bytes) {
+    hip_check(hipFuncSetAttribute((const void *)m->mk, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)h.lds_bytes), "hipFuncSetAttribute");
+    int per_cu = 0;
+    hip_check(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)m->mk, kThreads,
+                                                           h.lds_bytes), "occupancy");
+    if (per_cu < 1) return set_error(AMK_E_SCHEDULE_REJECTED, "schedule LDS does not fit on a CU");
+  }
+  hip_check(hipMemcpy(const_cast<Task *>(m->dm.tasks), tasks.data(), tasks.size() * sizeof(Task),
+                      hipMemcpyHostToDevice), "hipMemcpy");
+  hip_check(hipMemcpy(const_cast<uint32_t *>(m->dm.offsets), offs.data(), offs.size() * 4,
+                      hipMemcpyHostToDevice), "hipMemcpy");
+  zero_async(m->dm.flags, sizeof(uint32_t) * std::max<uint32_t>(1, h.n_tasks), st);
+  clear_tags(m, st);
+  hip_check(hipStreamSynchronize(st), "hipStreamSynchronize");
+  m->epoch = 0;
+  m->lds_bytes = h.lds_bytes;
+  m->sched = std::move(s);
+  m->blob = std::move(blob);
+  return AMK_OK;
+}
+
+void set_trace(amk_model *m, uint64_t *d_trace) {
+  m->dm.trace = d_trace;
+  hip_check(hipMemcpy(m->d_dm, &m->dm, sizeof(DevModel), hipMemcpyHostToDevice), "hipMemcpy");
+}
+
+}  // namespace
+
+extern "C" amk_status amk_model_set_schedule(amk_model *m, const void *blob, size_t bytes,
+                                             void *stream) {
+  AMK_API_BEGIN
+  if (!m || !blob) return set_error(AMK_E_INVALID, "amk_model_set_schedule: null argument");
+  Schedule s;
+  std::string e, rep;
+  if (!parse(blob, bytes, &s, &e)) return set_error(AMK_E_SCHEDULE_REJECTED, e);
+  if (!validate_schedule(s, &rep)) return set_error(AMK_E_SCHEDULE_REJECTED, rep);
+  std::vector<uint8_t> copy((const uint8_t *)blob, (const uint8_t *)blob + bytes);
+  amk_status r = install_schedule(m, std::move(s), std::move(copy), static_cast<hipStream_t>(stream));
+  if (r == AMK_OK) clear_error();
+  return r;
+  AMK_API_END
+}
+
+extern "C" amk_status amk_model_tune(amk_model *m, amk_kv *kv, int32_t pos, int32_t rounds,
+                                     int32_t steps, double gain, void *stream, double *best_us) {
+  AMK_API_BEGIN
+  if (!m || !kv) return set_error(AMK_E_INVALID, "amk_model_tune: null argument");
+  if (kv->m != m) return set_error(AMK_E_INVALID, "amk_model_tune: KV cache belongs to another model");
+  if (m->path != AMK_PATH_MEGAKERNEL) return set_error(AMK_E_UNSUPPORTED, "amk_model_tune: megakernel path only");
+  if (rounds < 0 || steps < 1 || !(gain > 0.0 && gain <= 1.0))
+    return set_error(AMK_E_INVALID, "amk_model_tune: rounds >= 0, steps >= 1, 0 < gain <= 1");
+  if (pos < 0 || (int64_t)pos + steps > std::min(kv->max_seq, m->cfg.max_seq))
+    return set_error(AMK_E_CAPACITY, "amk_model_tune: positions beyond max_seq");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int32_t batch = std::min(m->cfg.max_batch, kv->batch);
+  const size_t stride = 4ull * m->sched.hdr.n_tasks + (size_t)m->n_cu;
+  int32_t *d_tok = nullptr;
+  uint64_t *d_trace = nullptr;
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  amk_status status = AMK_OK;
+  try {
+    hip_check(hipMalloc(&d_tok, sizeof(int32_t) * batch), "hipMalloc");
+    hip_check(hipMalloc(&d_trace, 8 * stride), "hipMalloc");
+    hip_check(hipEventCreate(&ev[0]), "hipEventCreate");
+    hip_check(hipEventCreate(&ev[1]), "hipEventCreate");
+    set_trace(m, nullptr);
+    // run the steps (token 0, greedy chaining); traced: collect one trace per step
+    auto run = [&](std::vector<uint64_t> *traces, double *us) -> amk_status {
+      hip_check(hipMemsetAsync(d_tok, 0, sizeof(int32_t) * batch, st), "hipMemsetAsync");
+      if (traces) set_trace(m, d_trace);
+      hip_check(hipEventRecord(ev[0], st), "hipEventRecord");
+      for (int32_t i = 0; i < steps; ++i) {
+        amk_status r = amk_decode_step(m, kv, d_tok, pos + i, batch, nullptr, d_tok, st);
+        if (r != AMK_OK) return r;
+        if (traces) {
+          hip_check(hipStreamSynchronize(st), "hipStreamSynchronize");
+          const size_t off = traces->size();
+          traces->resize(off + stride);
+          hip_check(hipMemcpy(traces->data() + off, d_trace, 8 * stride, hipMemcpyDeviceToHost), "hipMemcpy");
+        }
+      }
+      hip_check(hipEventRecord(ev[1], st), "hipEventRecord");
+      amk_status r = amk_sync(m, stream);
+      if (traces) set_trace(m, nullptr);
+      if (r != AMK_OK) return r;
+      float ms = 0.f;
+      hip_check(hipEventElapsedTime(&ms, ev[0], ev[1]), "hipEventElapsedTime");
+      if (us) *us = 1000.0 * ms / steps;
+      return AMK_OK;
+    };
+    double best = 0.0;
+    if ((status = run(nullptr, nullptr)) == AMK_OK)  // warm-up
+      status = run(nullptr, &best);
+    Schedule best_s = m->sched;
+    std::vector<uint8_t> best_blob = m->blob;
+    for (int32_t r = 0; r < rounds && status == AMK_OK; ++r) {
+      std::vector<uint64_t> traces;
+      if ((status = run(&traces, nullptr)) != AMK_OK) break;
+      Schedule s = m->sched;
+      std::string e, rep;
+      if (!rebalance_schedule(&s, traces.data(), steps, gain, &e)) {
+        status = set_error(AMK_E_INVALID, "amk_model_tune: " + e);
+        break;
+      }
+      if (!validate_schedule(s, &rep)) {
+        status = set_error(AMK_E_SCHEDULE_REJECTED, rep);
+        break;
+      }
+      std::vector<uint8_t> blob = serialize(s);
+      if ((status = install_schedule(m, std::move(s), std::move(blob), st)) != AMK_OK) break;
+      double us = 0.0;
+      if ((status = run(nullptr, &us)) != AMK_OK) break;
+      if (us < best) {
+        best = us;
+        best_s = m->sched;
+        best_blob = m->blob;
+      }
+    }
+    if (status == AMK_OK && best_blob != m->blob)
+      status = install_schedule(m, std::move(best_s), std::move(best_blob), st);
+    if (status == AMK_OK && best_us) *best_us = best;
+  } catch (...) {
+    (void)hipDeviceSynchronize();
+    m->dm.trace = nullptr;
+    (void)hipMemcpy(m->d_dm, &m->dm, sizeof(DevModel), hipMemcpyHostToDevice);
+    if (d_tok) (void)hipFree(d_tok);
+    if (d_trace) (void)hipFree(d_trace);
+    for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
+    throw;
+  }
+  (void)hipDeviceSynchronize();
+  if (m->dm.trace) {
+    m->dm.trace = nullptr;
+    (void)hipMemcpy(m->d_dm, &m->dm, sizeof(DevModel), hipMemcpyHostToDevice);
+  }
+  (void)hipFree(d_tok);
+  (void)hipFree(d_trace);
+  for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  if (status == AMK_OK) clear_error();
+  return status;
+  AMK_API_END
+}
+
 extern "C" amk_status amk_destroy(amk_model *m) {
   if (!m) return set_error(AMK_E_INVALID, "amk_destroy: null model");
   (void)hipDeviceSynchronize();

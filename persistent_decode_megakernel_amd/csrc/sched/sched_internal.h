@@ -10,9 +10,10 @@
 
 namespace amk {
 
-// Dynamic LDS a schedule may ask for per workgroup (bytes): the CU's 160 KiB less what the
-// kernel declares statically (a 16-byte-aligned control word).
-constexpr uint32_t kMaxLdsBytes = 160 * 1024 - 64;
+// Dynamic LDS a schedule may ask for per workgroup (bytes): the CU's 160 KiB less a reserve for
+// what the kernels declare statically (272 bytes today: control words and the block-wide vote of
+// __syncthreads_or); model creation checks that the workgroup still fits.
+constexpr uint32_t kMaxLdsBytes = 160 * 1024 - 1024;
 
 struct Schedule {
   BlobHeader hdr{};
@@ -77,5 +78,10 @@ bool validate_schedule(const Schedule &s, std::string *report);
 bool simulate_schedule(const Schedule &s, std::string *report, int32_t max_delay_runs);
 
 bool config_ok(const amk_config &c, std::string *err);
+
+// Move the GEMV tile boundaries of *s towards equal finish times measured in task traces (see
+// amk_schedule_rebalance). Keeps ids, placement and waits; attention waits follow the QKV tiles.
+bool rebalance_schedule(Schedule *s, const uint64_t *traces, int n_traces, double gain,
+                        std::string *err);
 
 }  // namespace amk

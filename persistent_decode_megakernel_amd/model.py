@@ -120,6 +120,19 @@ class Model:
         finally:
             self.lib.amk_blob_free(b)
 
+    def set_schedule(self, blob: bytes) -> None:
+        _lib.check(self.lib.amk_model_set_schedule(self.handle, blob, len(blob), _stream_ptr()),
+                   "amk_model_set_schedule")
+
+    def tune(self, kv: "KVCache", pos: int, rounds: int = 6, steps: int = 4,
+             gain: float = 0.6) -> float:
+        """Profile-guided re-tiling on the device (amk_model_tune); returns the mean step time
+        (us) of the schedule it keeps installed."""
+        best = C.c_double()
+        _lib.check(self.lib.amk_model_tune(self.handle, kv.handle, pos, rounds, steps, float(gain),
+                                           _stream_ptr(), C.byref(best)), "amk_model_tune")
+        return best.value
+
     def enable_trace(self) -> torch.Tensor:
         """Turn on the megakernel's task trace; returns the device buffer it fills each step."""
         inf = self.info()
