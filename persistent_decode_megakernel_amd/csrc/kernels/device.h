@@ -38,7 +38,8 @@ struct DevModel {
   uint32_t *ht;        // [2L+1][d] residual stream
   uint32_t *at;        // [L][F] SwiGLU output
   uint32_t *aot;       // [L][qd] merged attention output
-  uint32_t *acnt;      // [L][nkv] KV blocks of the group finished in this step (0 between steps)
+  uint32_t *qt;        // [L][qd] q after RoPE
+  uint32_t *kvt;       // [L][2][nkv][hd] the K/V row appended at pos: bf16 bits << 16 | tag
   float *a;            // [L][B][F]
   float *logits;       // [B][V] used when the caller passes no logits buffer
   float2 *amax;        // [n_lm][B] (value, index bits)
@@ -218,20 +219,36 @@ __device__ __forceinline__ float4 cld4(__amdgpu_buffer_rsrc_t r, uint32_t off_by
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
+// The per-CU task tables do not change during a launch: read them through the constant address
+// space, so the (uniform) loads are scalar. A vector load here would have to wait until the
+// previous task's outstanding stores complete (loads and stores share the vector memory count),
+// delaying every task start by the store latency.
+#define AMK_CAS __attribute__((address_space(4)))
+typedef uint32_t u32x4c_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ Task load_task(const Task *p) {
+  static_assert(sizeof(Task) == 48, "task record size");
+  const AMK_CAS u32x4c_t *q = (const AMK_CAS u32x4c_t *)p;
+  const u32x4c_t w[3] = {q[0], q[1], q[2]};
+  Task t;
+  __builtin_memcpy(&t, w, sizeof t);
+  return t;
+}
+__device__ __forceinline__ uint32_t load_const(const uint32_t *p) { return *(const AMK_CAS uint32_t *)p; }
+
 // ------------------------------------------------------------------------------------------
 // dependency flags
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t flag_load(const uint32_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(gptr(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void record_error(uint32_t *err, uint32_t code, uint32_t task,
                                              uint32_t detail) {
   uint32_t expected = 0;
-  if (__hip_atomic_compare_exchange_strong(&err[0], &expected, code, __ATOMIC_RELAXED,
+  if (__hip_atomic_compare_exchange_strong(gptr(&err[0]), &expected, code, __ATOMIC_RELAXED,
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-    __hip_atomic_store(&err[2], task, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&err[3], detail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gptr(&err[2]), task, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gptr(&err[3]), detail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -263,7 +280,7 @@ __device__ bool wait_range(const DevModel &m, uint32_t lo, uint32_t hi, uint32_t
         if (wall_clock64() - t0 > m.timeout_ticks) {
           if (lane == 0) {
             record_error(m.err, ERR_TIMEOUT, task, g);
-            __hip_atomic_store(&m.err[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(gptr(&m.err[1]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
           return false;
         }
@@ -291,7 +308,7 @@ __device__ __forceinline__ void wait_poll(const DevModel &m, const Task &t, uint
 }
 __device__ __forceinline__ bool wait_join(const DevModel &m, const Task &t, int *abort_slot) {
   __syncthreads();
-  if (m.trace && threadIdx.x == 0) m.trace[(uint64_t)t.id * 4 + 1] = wall_clock64();
+  if (m.trace && threadIdx.x == 0) gst(&m.trace[(uint64_t)t.id * 4 + 1], (uint64_t)wall_clock64());
   return *abort_slot == 0;
 }
 __device__ __forceinline__ bool wait_task(const DevModel &m, const Task &t, uint32_t epoch,
@@ -636,6 +653,8 @@ __device__ bool stage_tagged(const DevModel &m, const uint32_t *src, int n, cons
   const int nu = n >> 2;
   const uint32_t tag = epoch & kTagMask;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)n * 4u);
+  uint32_t *const err = m.err;  // read here, in uniform code, so they come from scalar loads
+  const uint64_t tmo = m.timeout_ticks;
   float ss = 0.f;
   uint64_t t0 = 0;
   uint32_t spins = 0;
@@ -655,10 +674,10 @@ __device__ bool stage_tagged(const DevModel &m, const uint32_t *src, int n, cons
       // thread 0: the abort word on the first round and every eighth retry; the timeout
       int ab = 0;
       if (threadIdx.x == 0 && (spins == 0 || (spins & 7) == 7)) {
-        ab = flag_load(&m.err[1]) != 0;
-        if (!ab && spins && wall_clock64() - t0 > m.timeout_ticks) {
-          record_error(m.err, ERR_TIMEOUT, task, 0xfffffff0u);
-          __hip_atomic_store(&m.err[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ab = flag_load(&err[1]) != 0;
+        if (!ab && spins && wall_clock64() - t0 > tmo) {
+          record_error(err, ERR_TIMEOUT, task, 0xfffffff0u);
+          __hip_atomic_store(gptr(&err[1]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           ab = 1;
         }
       }
@@ -693,7 +712,7 @@ __device__ bool stage_tagged(const DevModel &m, const uint32_t *src, int n, cons
   }
   if (gain) {
     ss = wave_sum(ss);
-    if (lane_id() == 0) red[wave_id()] = ss;
+    if (lane_id() == 0) *(AMK_LDS float *)(red + wave_id()) = ss;
   }
   __syncthreads();
   return true;
@@ -936,19 +955,42 @@ __device__ void epi_qkv(const DevModel &m, const StepArgs &s, int l, int r0, int
       const QkvRow q1 = qkv_decode(r + 1, m.nq, m.nkv, hd);
       float v0 = ys[b * n + 2 * pi], v1 = ys[b * n + 2 * pi + 1];
       if (q0.kind != KIND_V) {  // rotary pair (dim j, dim j + hd/2)
-        const float2 c = cs[q0.dim];
+        const u32x2_t cw = *(const AMK_GAS u32x2_t *)&cs[q0.dim];
+        const float2 c = make_float2(__uint_as_float(cw.x), __uint_as_float(cw.y));
         const float a = v0, bb = v1;
         v0 = a * c.x - bb * c.y;
         v1 = bb * c.x + a * c.y;
       }
       if (q0.kind == KIND_Q) {
-        float *qb = m.q + ((int64_t)l * m.max_batch + b) * m.qd;
-        cstf(&qb[q0.head * hd + q0.dim], v0);
-        cstf(&qb[q1.head * hd + q1.dim], v1);
+        if (m.max_batch == 1) {  // batch 1: q only as tagged words, for the attention blocks
+          uint32_t *qb = m.qt + (int64_t)l * m.qd;
+          cst(&qb[q0.head * hd + q0.dim], tag_word(v0, s.epoch));
+          cst(&qb[q1.head * hd + q1.dim], tag_word(v1, s.epoch));
+        } else {
+          float *qb = m.q + ((int64_t)l * m.max_batch + b) * m.qd;
+          cstf(&qb[q0.head * hd + q0.dim], v0);
+          cstf(&qb[q1.head * hd + q1.dim], v1);
+        }
       } else {
         const int kvi = (q0.kind == KIND_K) ? 0 : 1;
-        cst(&s.kv[kv_index(m, s, l, kvi, b, q0.head, s.pos, q0.dim)], f32_to_bf16(v0));
-        cst(&s.kv[kv_index(m, s, l, kvi, b, q1.head, s.pos, q1.dim)], f32_to_bf16(v1));
+        const uint16_t k0 = f32_to_bf16(v0), k1 = f32_to_bf16(v1);
+        uint16_t *c0 = &s.kv[kv_index(m, s, l, kvi, b, q0.head, s.pos, q0.dim)];
+        uint16_t *c1 = &s.kv[kv_index(m, s, l, kvi, b, q1.head, s.pos, q1.dim)];
+        if (m.max_batch == 1) {
+          // This step's attention blocks take the row from tagged words; the cache row is read
+          // only by later launches (the kernel boundary makes it visible), so plain stores do.
+          // Device-coherent 2-byte stores are slow to complete, and any later load in this
+          // workgroup would wait for them (loads and stores share one counter).
+          gst(c0, k0);
+          gst(c1, k1);
+          uint32_t *kb = m.kvt + (((int64_t)l * 2 + kvi) * m.nkv + q0.head) * hd;
+          const uint32_t tg = s.epoch & kTagMask;
+          cst(&kb[q0.dim], ((uint32_t)k0 << 16) | tg);
+          cst(&kb[q1.dim], ((uint32_t)k1 << 16) | tg);
+        } else {
+          cst(c0, k0);
+          cst(c1, k1);
+        }
       }
     }
   }
@@ -1066,17 +1108,81 @@ __device__ void argmax_combine(const DevModel &m, const StepArgs &s, int n_slots
 
 // ------------------------------------------------------------------------------------------
 // attention partial for (layer l, kv group g, KV block blk) over positions [lo, hi) of ctx.
-// LDS: q [qpg][hd] | scores [qpg][chunk] | acc [nw][qpg*hd] | stats.
+// LDS: q [qpg][hd] | scores [qpg][chunk] | acc [nw][qpg*hd] | appended K/V row [2][hd] bf16.
 // Lane layout: LPR = hd/8 lanes per KV row (8 dims each), 64/LPR rows per wave per load.
 // ------------------------------------------------------------------------------------------
-template <int HD, int QMAX>
+// An empty KV block's partial: (m, l, acc) = (kEmptyBlockM, 0, 0). The value is finite (tagged
+// words replace its low mantissa bits) and so far below any score that its merge weight
+// e^{m - M} is exactly 0.
+constexpr float kEmptyBlockM = -3.0e38f;
+
+// Batch 1: q of this pass's heads and the K/V row appended at pos, read from the QKV tiles'
+// tagged words and reloaded until every tag matches (this is the wait for those tiles): q, scaled
+// by 1/sqrt(hd), into qs [qn][hd]; the row's bf16 values into kvrow [2][hd]. Returns false after
+// a timeout (recorded) or when the abort word is set.
+__device__ bool attn_stage_tagged(const DevModel &m, const StepArgs &s, int l, int g, int h0,
+                                  int qn, float *qs, uint16_t *kvrow, uint32_t task) {
+  constexpr int V = 4;  // words per thread per round: qn * hd + 2 * hd <= 6 * 256 < V * kThreads
+  const int hd = m.hd, nqw = qn * hd, n = nqw + 2 * hd;
+  const uint32_t tag = s.epoch & kTagMask;
+  const uint32_t *qsrc = m.qt + (int64_t)l * m.qd + (int64_t)(g * m.qpg + h0) * hd;
+  const uint32_t *ksrc = m.kvt + ((int64_t)l * 2 * m.nkv + g) * hd;
+  const uint32_t *vsrc = m.kvt + ((int64_t)(l * 2 + 1) * m.nkv + g) * hd;
+  uint32_t *const err = m.err;
+  const uint64_t tmo = m.timeout_ticks;
+  uint32_t need = 0;
+#pragma unroll
+  for (int j = 0; j < V; ++j)
+    if ((int)threadIdx.x + j * kThreads < n) need |= 1u << j;
+  uint64_t t0 = 0;
+  uint32_t spins = 0;
+  while (true) {
+    uint32_t w[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int i = (int)threadIdx.x + j * kThreads;
+      if (need & (1u << j))
+        w[j] = cld(i < nqw ? &qsrc[i] : (i < nqw + hd ? &ksrc[i - nqw] : &vsrc[i - nqw - hd]));
+    }
+    int ab = 0;
+    if (threadIdx.x == 0 && (spins == 0 || (spins & 7) == 7)) {
+      ab = flag_load(&err[1]) != 0;
+      if (!ab && spins && wall_clock64() - t0 > tmo) {
+        record_error(err, ERR_TIMEOUT, task, 0xfffffff1u);
+        __hip_atomic_store(gptr(&err[1]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ab = 1;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int i = (int)threadIdx.x + j * kThreads;
+      if ((need & (1u << j)) && (w[j] & kTagMask) == tag) {
+        need &= ~(1u << j);
+        if (i < nqw)
+          qs[i] = __uint_as_float(w[j]) * m.attn_scale;
+        else
+          kvrow[i - nqw] = (uint16_t)(w[j] >> 16);
+      }
+    }
+    const int pending = __syncthreads_or(need != 0);
+    if (__syncthreads_or(ab)) return false;
+    if (!pending) return true;
+    if (spins == 0) t0 = wall_clock64();
+    ++spins;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// TAGGED (batch-1 megakernel): q and the appended row come from attn_stage_tagged, the partial is
+// stored as tagged words. Otherwise the QKV tiles' flags are waited on when wait_for is set
+// (batched megakernel) and q and the appended row are read from q and the KV cache.
+template <int HD, int QMAX, bool TAGGED>
 __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, int blk,
                            int h0, int qn, float *lds, float *red, const Task *wait_for,
                            int *abort_slot) {
   // heads [h0, h0 + qn) of the group (qn <= QMAX), i.e. query heads g*qpg + h0 + i.
-  // When wait_for is set, the first chunk of KV history (rows written by earlier steps) is
-  // loaded before the dependency wait; only the row at `pos`, appended by this step's QKV tiles,
-  // is read after it.
+  // The first chunk of KV history (rows written by earlier steps) is loaded before the
+  // dependency wait; only the row at `pos`, appended by this step's QKV tiles, is read after it.
   constexpr int NW = kWaves;
   constexpr int LPR = HD / 8;
   constexpr int RPW = 64 / LPR;  // rows per wave per load
@@ -1092,7 +1198,8 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
   attn_block_range(pos + 1, nblk, blk, &lo, &hi);
   float *qs = lds;                             // [qpg][HD]
   float *sc = qs + qpg * HD;                   // [qpg][chunk]
-  float *accw = sc + qpg * CH;  // [NW][qpg*HD]
+  float *accw = sc + qpg * CH;                 // [NW][qpg*HD]
+  uint16_t *kvrow = reinterpret_cast<uint16_t *>(accw + NW * qpg * HD);  // [2][HD]
   for (int b = 0; b < s.batch; ++b) {
     const uint16_t *Kb = s.kv + kv_index(m, s, l, 0, b, g, 0, 0);
     const uint16_t *Vb = s.kv + kv_index(m, s, l, 1, b, g, 0, 0);
@@ -1103,37 +1210,61 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
       for (int it = 0; it < NIT; ++it) {
         const int j = lo + it * ROWS_PER_ITER + wave * RPW + rs;
         const bool ok = j < c1 && j != pos;
-        kr[it] = ok ? gld4(reinterpret_cast<const uint4 *>(Kb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
-        vr[it] = ok ? gld4(reinterpret_cast<const uint4 *>(Vb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
+        kr[it] = ok ? load_nt(reinterpret_cast<const uint4 *>(Kb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
+        vr[it] = ok ? load_nt(reinterpret_cast<const uint4 *>(Vb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
       }
     };
-    // wave 0 polls the flags and a wave's loads return in order, so it issues its history rows
-    // after polling; the other waves issue theirs before the join
-    const bool waits = wait_for && b == 0;
-    if (waits) wait_poll(m, *wait_for, s.epoch, abort_slot);
-    load_history();
-    if (waits && !wait_join(m, *wait_for, abort_slot)) return false;
-    // The row at pos was appended by this step's QKV tiles: device-coherent loads, issued right
-    // after the wait together with q, for whichever chunk and lane holds it.
     const int po = pos - lo;
     const bool own_pos = po >= 0 && pos < hi && (po % ROWS_PER_ITER) == wave * RPW + rs;
     uint4 kpos = make_uint4(0, 0, 0, 0), vpos = make_uint4(0, 0, 0, 0);
-    if (own_pos) {
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)pos * HD, HD * 2);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + (int64_t)pos * HD, HD * 2);
-      const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(rk, sub * 16, 0, kCachePolicySc1);
-      const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(rv, sub * 16, 0, kCachePolicySc1);
-      kpos = make_uint4(a.x, a.y, a.z, a.w);
-      vpos = make_uint4(c.x, c.y, c.z, c.w);
+    if constexpr (TAGGED) {
+      load_history();
+      // keep the history loads issued here, ahead of the staging loads (the compiler would
+      // otherwise sink them to their first use, after the wait)
+      asm volatile("" ::: "memory");
+      if (!attn_stage_tagged(m, s, l, g, h0, qn, qs, kvrow, wait_for ? wait_for->id : 0u)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        return false;
+      }
+      if (m.trace && wait_for && h0 == 0 && threadIdx.x == 0)
+        gst(&m.trace[(uint64_t)wait_for->id * 4 + 1], (uint64_t)wall_clock64());
+      if (own_pos) {
+        kpos = *reinterpret_cast<const uint4 *>(kvrow + sub * 8);
+        vpos = *reinterpret_cast<const uint4 *>(kvrow + HD + sub * 8);
+      }
+    } else {
+      // wave 0 polls the flags and a wave's loads return in order, so it issues its history rows
+      // after polling; the other waves issue theirs before the join
+      const bool waits = wait_for && b == 0;
+      if (waits) wait_poll(m, *wait_for, s.epoch, abort_slot);
+      load_history();
+      asm volatile("" ::: "memory");  // issue them before the join, not at their first use
+      if (waits && !wait_join(m, *wait_for, abort_slot)) return false;
+      // The row at pos was appended by this step's QKV tiles: device-coherent loads, issued right
+      // after the wait together with q, for whichever chunk and lane holds it.
+      if (own_pos) {
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)pos * HD, HD * 2);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + (int64_t)pos * HD, HD * 2);
+        const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(rk, sub * 16, 0, kCachePolicySc1);
+        const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(rv, sub * 16, 0, kCachePolicySc1);
+        kpos = make_uint4(a.x, a.y, a.z, a.w);
+        vpos = make_uint4(c.x, c.y, c.z, c.w);
+      }
+      const float *qsrc = m.q + ((int64_t)l * m.max_batch + b) * m.qd + ((int64_t)g * m.qpg + h0) * HD;
+      for (int i = threadIdx.x; i < qpg * HD; i += NW * 64) qs[i] = cldf(&qsrc[i]) * m.attn_scale;
     }
-    const float *qsrc = m.q + ((int64_t)l * m.max_batch + b) * m.qd + ((int64_t)g * m.qpg + h0) * HD;
-    for (int i = threadIdx.x; i < qpg * HD; i += NW * 64) qs[i] = cldf(&qsrc[i]) * m.attn_scale;
     __syncthreads();
     float *pout = m.part + ((((int64_t)l * m.max_batch + b) * nq + (int64_t)g * m.qpg + h0) * nblk + blk) * (HD + 2);
+    auto put = [&](float *p, float v) {
+      if constexpr (TAGGED)
+        cst(reinterpret_cast<uint32_t *>(p), tag_word(v, s.epoch));
+      else
+        cstf(p, v);
+    };
     if (hi <= lo) {
       for (int i = threadIdx.x; i < qpg * (HD + 2); i += NW * 64) {
         const int h = i / (HD + 2), e = i - h * (HD + 2);
-        cstf(&pout[(int64_t)h * nblk * (HD + 2) + e], (e == HD) ? -INFINITY : 0.f);
+        put(&pout[(int64_t)h * nblk * (HD + 2) + e], (e == HD) ? kEmptyBlockM : 0.f);
       }
       __syncthreads();
       continue;
@@ -1155,8 +1286,8 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
         for (int it = 0; it < NIT; ++it) {
           const int j = c0 + it * ROWS_PER_ITER + wave * RPW + rs;
           const bool ok = j < c1 && j != pos;
-          kr[it] = ok ? gld4(reinterpret_cast<const uint4 *>(Kb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
-          vr[it] = ok ? gld4(reinterpret_cast<const uint4 *>(Vb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
+          kr[it] = ok ? load_nt(reinterpret_cast<const uint4 *>(Kb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
+          vr[it] = ok ? load_nt(reinterpret_cast<const uint4 *>(Vb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
         }
       }
       // the appended row, wherever it falls (its history slot was left zero above)
@@ -1246,18 +1377,18 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
       float t = 0.f;
       for (int w = 0; w < NW; ++w) t += accw[(int64_t)w * qpg * HD + i];
       const int h = i / HD, e = i - h * HD;
-      cstf(&pout[(int64_t)h * nblk * (HD + 2) + e], t);
+      put(&pout[(int64_t)h * nblk * (HD + 2) + e], t);
     }
     if (threadIdx.x < qpg) {
       const int h = threadIdx.x;
       float t = 0.f;
       for (int w = 0; w < NW; ++w) t += red[16 + w * 8 + h];
-      float mh = -INFINITY;
+      float mh = kEmptyBlockM;
 #pragma unroll
       for (int k = 0; k < QMAX; ++k)
         if (k == h) mh = mrun[k];
-      cstf(&pout[(int64_t)h * nblk * (HD + 2) + HD], mh);
-      cstf(&pout[(int64_t)h * nblk * (HD + 2) + HD + 1], t);
+      put(&pout[(int64_t)h * nblk * (HD + 2) + HD], mh);
+      put(&pout[(int64_t)h * nblk * (HD + 2) + HD + 1], t);
     }
     __syncthreads();
   }
@@ -1267,82 +1398,117 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
 // Attention tasks always run with kWaves waves (kThreads threads). A group of more query heads than
 // QMAX is processed QMAX heads at a time (the KV block is re-read from cache for each pass).
 // wait_for (megakernel) is waited on inside the first pass, after the KV-history prefetch.
-template <int HD, int QMAX>
+template <int HD, int QMAX, bool TAGGED>
 __device__ __forceinline__ bool attn_task(const DevModel &m, const StepArgs &s, int l, int g,
                                           int blk, float *lds, float *red, const Task *wait_for,
                                           int *abort_slot) {
+  // the partial waits for the QKV tiles only; a merger's wait for its group's other blocks (the
+  // second range) comes in attn_merge
+  Task first{};
+  if (wait_for) {
+    first = *wait_for;
+    first.w1_lo = first.w1_hi = 0;
+  }
   for (int h0 = 0; h0 < m.qpg; h0 += QMAX)
-    if (!attn_block<HD, QMAX>(m, s, l, g, blk, h0, min(QMAX, m.qpg - h0), lds, red,
-                              h0 == 0 ? wait_for : nullptr, abort_slot))
+    if (!attn_block<HD, QMAX, TAGGED>(m, s, l, g, blk, h0, min(QMAX, m.qpg - h0), lds, red,
+                                      (wait_for && (TAGGED || h0 == 0)) ? &first : nullptr,
+                                      abort_slot))
       return false;
   return true;
 }
 
-// Merge the nblk partials of KV group g (all batch rows, all of its query heads) into
-// ao[l][b][head * hd + e] = sum_k e^{m_k - M} acc_k[e] / sum_k e^{m_k - M} l_k, M = max_k m_k
-// (log-sum-exp over the blocks; an empty block has m = -inf, l = 0, acc = 0). One element per
-// thread; the blocks are visited eight at a time with all of their loads issued together and
-// the running maximum rescaled between batches.
-__device__ void attn_group_combine(const DevModel &m, const StepArgs &s, int l, int g) {
+// Merge of KV group g's nblk partials into the attention output, run by the group's last block
+// (the designated merger) after its own partial:
+//   o[h][e] = sum_k e^{m_k - M} acc_k[e] / sum_k e^{m_k - M} l_k,  M = max_k m_k
+// (log-sum-exp over the blocks; an empty block's weight is exactly 0). TAGGED (batch 1): the other
+// blocks store no flag, their partials are tagged words reloaded until every tag matches, and
+// the output is written tagged. Otherwise the other blocks' flags (the task's second wait range)
+// are waited on first. The merger's own partial is read back like the others once its stores
+// are complete. Each thread merges whole output elements, eight blocks' loads at a time.
+template <bool TAGGED>
+__device__ bool attn_merge(const DevModel &m, const StepArgs &s, const Task &t, int *abort_slot) {
+  const int l = t.layer, g = (int)t.a0;
+  if constexpr (!TAGGED) {
+    Task others = t;  // the group's other blocks (the QKV tiles were waited on for the partial)
+    others.w0_lo = others.w0_hi = 0;
+    if (!wait_task(m, others, s.epoch, abort_slot)) return false;
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this block's own partial stores are complete
+  __syncthreads();
   constexpr int KB = 8;
   const int hd = m.hd, nblk = m.nblk, qpg = m.qpg, nq = m.nq;
   const int per_b = qpg * hd, total = s.batch * per_b;
-  for (int i = threadIdx.x; i < total; i += kThreads) {
-    const int b = i / per_b, r = i - b * per_b, h = g * qpg + r / hd, e = r % hd;
-    const float *ph = m.part + (((int64_t)l * m.max_batch + b) * nq + h) * nblk * (hd + 2);
-    float M = -INFINITY, den = 0.f, num = 0.f;
-    for (int k0 = 0; k0 < nblk; k0 += KB) {
-      float mk[KB], lk[KB], ak[KB];
+  const uint32_t tag = s.epoch & kTagMask;
+  uint32_t *const err = m.err;
+  const uint64_t tmo = m.timeout_ticks;
+  uint32_t done = 0;  // elements (one bit per loop iteration of this thread) already written
+  uint64_t t0 = 0;
+  uint32_t spins = 0;
+  while (true) {
+    int stale = 0;
+    int it = 0;
+    for (int i = threadIdx.x; i < total; i += kThreads, ++it) {
+      if (TAGGED && (done & (1u << it))) continue;  // TAGGED: at most 8 elements per thread
+      const int b = i / per_b, r = i - b * per_b, h = g * qpg + r / hd, e = r % hd;
+      const uint32_t *ph = reinterpret_cast<const uint32_t *>(m.part) +
+                           (((int64_t)l * m.max_batch + b) * nq + h) * nblk * (hd + 2);
+      float M = kEmptyBlockM, den = 0.f, num = 0.f;
+      uint32_t bad = 0;
+      for (int k0 = 0; k0 < nblk; k0 += KB) {
+        uint32_t wm[KB], wl[KB], wa[KB];
 #pragma unroll
-      for (int j = 0; j < KB; ++j) {
-        const float *pk = ph + (int64_t)min(k0 + j, nblk - 1) * (hd + 2);
-        mk[j] = cldf(pk + hd);
-        lk[j] = cldf(pk + hd + 1);
-        ak[j] = cldf(pk + e);
-      }
-      float Mb = M;
-#pragma unroll
-      for (int j = 0; j < KB; ++j)
-        if (k0 + j < nblk) Mb = fmaxf(Mb, mk[j]);
-      if (Mb == -INFINITY) continue;  // only empty blocks so far
-      const float f = __expf(M - Mb);  // M = -inf: f = 0 and den = num = 0 anyway
-      den *= f;
-      num *= f;
-#pragma unroll
-      for (int j = 0; j < KB; ++j) {
-        if (k0 + j < nblk) {
-          const float w = __expf(mk[j] - Mb);
-          den = fmaf(w, lk[j], den);
-          num = fmaf(w, ak[j], num);
+        for (int j = 0; j < KB; ++j) {
+          const uint32_t *pk = ph + (int64_t)min(k0 + j, nblk - 1) * (hd + 2);
+          wm[j] = cld(pk + hd);
+          wl[j] = cld(pk + hd + 1);
+          wa[j] = cld(pk + e);
         }
+        float Mb = M;
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+          if (TAGGED) bad |= ((wm[j] ^ tag) | (wl[j] ^ tag) | (wa[j] ^ tag)) & kTagMask;
+          if (k0 + j < nblk) Mb = fmaxf(Mb, __uint_as_float(wm[j]));
+        }
+        const float f = __expf(M - Mb);
+        den *= f;
+        num *= f;
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+          if (k0 + j < nblk) {
+            const float w = __expf(__uint_as_float(wm[j]) - Mb);
+            den = fmaf(w, __uint_as_float(wl[j]), den);
+            num = fmaf(w, __uint_as_float(wa[j]), num);
+          }
+        }
+        M = Mb;
       }
-      M = Mb;
+      if (bad) {
+        stale = 1;
+        continue;
+      }
+      if constexpr (TAGGED) done |= 1u << it;
+      if constexpr (TAGGED)
+        cst(&m.aot[(int64_t)l * m.qd + (int64_t)h * hd + e], tag_word(num / den, s.epoch));
+      else
+        cstf(&m.ao[((int64_t)l * m.max_batch + b) * m.qd + (int64_t)h * hd + e], num / den);
     }
-    if (m.max_batch == 1)
-      cst(&m.aot[(int64_t)l * m.qd + (int64_t)h * hd + e], tag_word(num / den, s.epoch));
-    else
-      cstf(&m.ao[((int64_t)l * m.max_batch + b) * m.qd + (int64_t)h * hd + e], num / den);
+    if constexpr (!TAGGED) return true;
+    int ab = 0;
+    if (threadIdx.x == 0 && (spins & 7) == 7) {
+      ab = flag_load(&err[1]) != 0;
+      if (!ab && wall_clock64() - t0 > tmo) {
+        record_error(err, ERR_TIMEOUT, t.id, 0xfffffff2u);
+        __hip_atomic_store(gptr(&err[1]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ab = 1;
+      }
+    }
+    const int pending = __syncthreads_or(stale);
+    if (__syncthreads_or(ab)) return false;
+    if (!pending) return true;
+    if (spins == 0) t0 = wall_clock64();
+    ++spins;
+    __builtin_amdgcn_s_sleep(1);
   }
-}
-
-// After a KV block task of group g has stored its partials: count it; the task that completes
-// the group's count for this step merges the group's partials (attn_group_combine). Every wave
-// first waits for its own partial stores, so a block is counted only once its data is visible
-// at device scope; the last counter holds all nblk blocks' data. The last one also sets the
-// counter back to zero for the next step (nothing else touches it before this launch ends).
-__device__ __forceinline__ void attn_count_and_combine(const DevModel &m, const StepArgs &s,
-                                                       int l, int g, int *last_slot) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t *cnt = &m.acnt[(int64_t)l * m.nkv + g];
-    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = old + 1u == (uint32_t)m.nblk;
-    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *last_slot = last;
-  }
-  __syncthreads();
-  if (*last_slot) attn_group_combine(m, s, l, g);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1352,10 +1518,10 @@ __device__ __forceinline__ void gemv_matrix(const DevModel &m, int mat, int l, c
                                             const float **scale, int *K, int *wtype) {
   *wtype = m.wtype;
   switch (mat) {
-    case M_QKV: *W = m.layers[l].qkv; *scale = m.layers[l].s_qkv; *K = m.d; break;
-    case M_O: *W = m.layers[l].o; *scale = m.layers[l].s_o; *K = m.qd; break;
-    case M_GU: *W = m.layers[l].gu; *scale = m.layers[l].s_gu; *K = m.d; break;
-    case M_D: *W = m.layers[l].dn; *scale = m.layers[l].s_dn; *K = m.F; break;
+    case M_QKV: *W = gld(&m.layers[l].qkv); *scale = gld(&m.layers[l].s_qkv); *K = m.d; break;
+    case M_O: *W = gld(&m.layers[l].o); *scale = gld(&m.layers[l].s_o); *K = m.qd; break;
+    case M_GU: *W = gld(&m.layers[l].gu); *scale = gld(&m.layers[l].s_gu); *K = m.d; break;
+    case M_D: *W = gld(&m.layers[l].dn); *scale = gld(&m.layers[l].s_dn); *K = m.F; break;
     default:
       *W = m.lm;
       *scale = m.lm_scale;

@@ -47,22 +47,24 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
     if (!tagged) wait_poll(m, t, s.epoch, abort_slot);
     if (st.S > 0) st.load_lds(0, slot);
     if (st.S > 1) st.load(P, 1);
+    // keep the register prefetch issued here, ahead of the staging loads, not at its first use
+    asm volatile("" ::: "memory");
     if (!tagged && !wait_join(m, t, abort_slot)) return false;
-    if (m.trace && threadIdx.x == 0) m.trace[(uint64_t)t.id * 4 + 1] = wall_clock64();
+    if (m.trace && threadIdx.x == 0) gst(&m.trace[(uint64_t)t.id * 4 + 1], (uint64_t)wall_clock64());
     bool ok = true;
     switch (t.mat) {
       case M_QKV:
         if (l == 0)
-          stage_norm(m, s, 0, m.layers[0].attn_norm, xs, red, NW);
+          stage_norm(m, s, 0, gld(&m.layers[0].attn_norm), xs, red, NW);
         else
-          ok = stage_tagged(m, m.ht + (int64_t)2 * l * m.d, m.d, m.layers[l].attn_norm, s.epoch,
+          ok = stage_tagged(m, m.ht + (int64_t)2 * l * m.d, m.d, gld(&m.layers[l].attn_norm), s.epoch,
                             xs, red, t.id);
         break;
       case M_O:
         ok = stage_tagged(m, m.aot + (int64_t)l * m.qd, m.qd, nullptr, s.epoch, xs, red, t.id);
         break;
       case M_GU:
-        ok = stage_tagged(m, m.ht + (int64_t)(2 * l + 1) * m.d, m.d, m.layers[l].mlp_norm, s.epoch,
+        ok = stage_tagged(m, m.ht + (int64_t)(2 * l + 1) * m.d, m.d, gld(&m.layers[l].mlp_norm), s.epoch,
                           xs, red, t.id);
         break;
       case M_D:
@@ -77,7 +79,7 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
       __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS may outlive the workgroup
       return false;
     }
-    if (m.trace && threadIdx.x == 0) m.trace[(uint64_t)t.id * 4 + 2] = wall_clock64();
+    if (m.trace && threadIdx.x == 0) gst(&m.trace[(uint64_t)t.id * 4 + 2], (uint64_t)wall_clock64());
     st.run_pf(slot, P, xs, ys, scale);
   } else {
     // batched: inputs straight from memory into the matrix cores (RMSNorm scale applied after)
@@ -86,15 +88,15 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
     switch (t.mat) {
       case M_QKV:
         if (l == 0) in.emb = m.embed; else in.x = m.h + 2 * l * hb;
-        in.gain = m.layers[l].attn_norm;
+        in.gain = gld(&m.layers[l].attn_norm);
         break;
       case M_O: in = BatchInput{m.ao + (int64_t)l * m.max_batch * m.qd, m.qd, nullptr, nullptr, false}; break;
-      case M_GU: in.x = m.h + (2 * l + 1) * hb; in.gain = m.layers[l].mlp_norm; break;
+      case M_GU: in.x = m.h + (2 * l + 1) * hb; in.gain = gld(&m.layers[l].mlp_norm); break;
       case M_D: in = BatchInput{m.a + (int64_t)l * m.max_batch * m.F, m.F, nullptr, nullptr, false}; break;
       default: in.x = m.h + 2 * (int64_t)m.L * hb; in.gain = m.final_norm; break;
     }
     if (!wait_task(m, t, s.epoch, abort_slot)) return false;
-    if (m.trace && threadIdx.x == 0) m.trace[(uint64_t)t.id * 4 + 2] = wall_clock64();
+    if (m.trace && threadIdx.x == 0) gst(&m.trace[(uint64_t)t.id * 4 + 2], (uint64_t)wall_clock64());
     gemv_mfma<WT>(m, s, W, scale, K, r0, r1, in, ys, red, xs);
   }
   __syncthreads();
@@ -118,11 +120,14 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
   return true;
 }
 
-// Whether a finished task's consumers learn of it from its flag. Batch-1 O, gate/up and down
-// tiles publish tagged data instead: they neither wait for their stores nor store a flag.
+// Whether a finished task's consumers learn of it from its flag. In batch-1 instances only the LM
+// tiles (for the argmax) and the argmax do: every other task publishes tagged data (QKV: q and the
+// appended K/V row; attention blocks: partials and the merged output; O, gate/up, down: their
+// outputs) and neither waits for its stores nor stores a flag. The schedule validator's
+// stores_flag is the same rule.
 template <bool BATCHED>
 __device__ __forceinline__ bool publishes_flag(const Task &t) {
-  return BATCHED || t.type != T_GEMV || !(t.mat == M_O || t.mat == M_GU || t.mat == M_D);
+  return BATCHED || t.type == T_ARGMAX || (t.type == T_GEMV && t.mat == M_LM);
 }
 
 template <int WT, int HD, int QMAX, bool BATCHED>
@@ -134,25 +139,26 @@ __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArg
   float *red = lds + (xa > xb ? xa : xb);  // kRedFloats floats
   uint4 *pf = reinterpret_cast<uint4 *>(red + kRedFloats);  // lds_prefetch_floats(max_batch)
   float *ys = red + kRedFloats + lds_prefetch_floats(m.max_batch);  // batch * max_tile_rows
-  __shared__ int abort_flag, last_flag;
+  __shared__ int abort_flag;
   if (threadIdx.x == 0) abort_flag = 0;
   __syncthreads();
-  const uint32_t t0 = m.offsets[blockIdx.x], t1 = m.offsets[blockIdx.x + 1];
+  const uint32_t t0 = load_const(&m.offsets[blockIdx.x]), t1 = load_const(&m.offsets[blockIdx.x + 1]);
   uint64_t *const trace = m.trace;
   if (trace && threadIdx.x == 0) {
     // XCC (XCD) that runs this workgroup: HW_REG_XCC_ID, bits [3:0]
     const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20);
-    trace[(uint64_t)m.n_tasks * 4 + blockIdx.x] = xcc;
+    gst(&trace[(uint64_t)m.n_tasks * 4 + blockIdx.x], (uint64_t)xcc);
   }
   for (uint32_t ti = t0; ti < t1; ++ti) {
-    const Task t = m.tasks[ti];
-    if (trace && threadIdx.x == 0) trace[(uint64_t)t.id * 4 + 0] = wall_clock64();
+    const Task t = load_task(&m.tasks[ti]);
+    if (trace && threadIdx.x == 0) gst(&trace[(uint64_t)t.id * 4 + 0], (uint64_t)wall_clock64());
     bool ok;
     if (t.type == T_GEMV) {
       ok = gemv_task<WT, BATCHED>(m, s, t, xs, ys, red, pf, &abort_flag);
     } else if (t.type == T_ATTN) {
-      ok = attn_task<HD, QMAX>(m, s, t.layer, (int)t.a0, (int)t.a1, xs, red, &t, &abort_flag);
-      if (ok) attn_count_and_combine(m, s, t.layer, (int)t.a0, &last_flag);
+      ok = attn_task<HD, QMAX, !BATCHED>(m, s, t.layer, (int)t.a0, (int)t.a1, xs, red, &t, &abort_flag);
+      if (trace && threadIdx.x == 0) gst(&trace[(uint64_t)t.id * 4 + 2], (uint64_t)wall_clock64());
+      if (ok && t.aux1) ok = attn_merge<!BATCHED>(m, s, t, &abort_flag);
     } else {
       ok = wait_task(m, t, s.epoch, &abort_flag);
       if (ok) argmax_combine(m, s, (int)t.aux0);
@@ -165,12 +171,12 @@ __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArg
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (threadIdx.x == 0) {
-        if (trace) trace[(uint64_t)t.id * 4 + 3] = wall_clock64();
-        __hip_atomic_store(&m.flags[t.id], s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (trace) gst(&trace[(uint64_t)t.id * 4 + 3], (uint64_t)wall_clock64());
+        __hip_atomic_store(gptr(&m.flags[t.id]), s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     } else {
       __syncthreads();
-      if (trace && threadIdx.x == 0) trace[(uint64_t)t.id * 4 + 3] = wall_clock64();
+      if (trace && threadIdx.x == 0) gst(&trace[(uint64_t)t.id * 4 + 3], (uint64_t)wall_clock64());
     }
   }
 }

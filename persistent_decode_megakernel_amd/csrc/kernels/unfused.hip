@@ -116,7 +116,7 @@ __device__ void uf_attn(const DevModel &m, const StepArgs &s, int l) {
   extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte reads of xs need it
   float *red = lds;
   float *work = lds + 64 * 8;
-  attn_task<HD, QMAX>(m, s, l, blockIdx.x, blockIdx.y, work, red, nullptr, nullptr);
+  attn_task<HD, QMAX, false>(m, s, l, blockIdx.x, blockIdx.y, work, red, nullptr, nullptr);
 }
 
 #define AMK_UF_ATTN(HD, Q)                                                                   \

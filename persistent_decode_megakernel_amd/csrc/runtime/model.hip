@@ -217,18 +217,20 @@ void zero_async(void *p, size_t bytes, hipStream_t st) {
 // word of an earlier run can pass for the new step's. A fill kernel, not a memset, since this runs
 // inside amk_decode_step, which a caller may capture into a graph.
 void clear_tags(amk_model *m, hipStream_t st) {
-  const size_t L = m->cfg.n_layers, d = m->cfg.hidden, F = m->cfg.ffn,
-               qd = (size_t)m->cfg.n_heads * m->cfg.head_dim;
+  const size_t L = m->cfg.n_layers, d = m->cfg.hidden, F = m->cfg.ffn, hd = m->cfg.head_dim,
+               qd = (size_t)m->cfg.n_heads * hd, B = m->cfg.max_batch;
   zero_async(m->dm.ht, sizeof(uint32_t) * (2 * L + 1) * d, st);
   zero_async(m->dm.at, sizeof(uint32_t) * L * F, st);
   zero_async(m->dm.aot, sizeof(uint32_t) * L * qd, st);
+  zero_async(m->dm.qt, sizeof(uint32_t) * L * qd, st);
+  zero_async(m->dm.kvt, sizeof(uint32_t) * L * 2 * m->cfg.n_kv_heads * hd, st);
+  zero_async(m->dm.part, sizeof(float) * L * B * m->cfg.n_heads * m->dm.nblk * (hd + 2), st);
 }
 
 // reset device error words, flags and the epoch after a device-side failure
 void reset_device_state(amk_model *m, hipStream_t st) {
   (void)hipMemsetAsync(m->dm.err, 0, 4 * sizeof(uint32_t), st);
   (void)hipMemsetAsync(m->dm.flags, 0, sizeof(uint32_t) * std::max<uint32_t>(1, m->sched.hdr.n_tasks), st);
-  (void)hipMemsetAsync(m->dm.acnt, 0, sizeof(uint32_t) * m->cfg.n_layers * m->cfg.n_kv_heads, st);
   clear_tags(m, st);
   (void)hipStreamSynchronize(st);
   m->epoch = 0;
@@ -435,7 +437,8 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     dm.ht = m->dalloc<uint32_t>((size_t)(2 * L + 1) * d);
     dm.at = m->dalloc<uint32_t>((size_t)L * F);
     dm.aot = m->dalloc<uint32_t>((size_t)L * qd);
-    dm.acnt = m->dalloc<uint32_t>((size_t)L * cfg->n_kv_heads);
+    dm.qt = m->dalloc<uint32_t>((size_t)L * qd);
+    dm.kvt = m->dalloc<uint32_t>((size_t)L * 2 * cfg->n_kv_heads * hd);
     dm.a = m->dalloc<float>((size_t)L * B * F);
     dm.logits = m->dalloc<float>((size_t)B * V);
     m->n_lm_uf = (V + kUfRowsPerBlock - 1) / kUfRowsPerBlock;
@@ -448,7 +451,6 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     dm.o = m->dalloc<float>((size_t)B * qd);
     hip_check(hipMemsetAsync(dm.flags, 0, sizeof(uint32_t) * std::max<uint32_t>(1, h.n_tasks), st), "hipMemsetAsync");
     hip_check(hipMemsetAsync(dm.err, 0, 16, st), "hipMemsetAsync");
-    hip_check(hipMemsetAsync(dm.acnt, 0, sizeof(uint32_t) * L * cfg->n_kv_heads, st), "hipMemsetAsync");
     clear_tags(m, st);
     // task tables
     std::vector<uint32_t> offs(h.n_cu + 1);

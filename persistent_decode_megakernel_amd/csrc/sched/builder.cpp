@@ -151,9 +151,13 @@ struct Builder {
     for (uint32_t l = 0; l < L; ++l) {
       Tiling qt;
       auto qkv = gemv(M_QKV, (uint16_t)l, qkvr, 2, d, wb, d_lo, d_hi, &qt);
-      // attention: one task per (kv group, KV block); waits on the QKV tiles of its group
-      uint32_t a_first = next_id;
+      // attention: one task per (kv group, KV block); waits on the QKV tiles of its group. The
+      // group's last block also merges the group's partials and so waits on the other blocks too.
+      // Mergers are numbered after all other blocks of the layer, so the O tiles wait on the id
+      // range of the mergers and each merger on the id range of its group's other blocks.
+      const uint32_t a_first = next_id;
       const uint32_t n_attn = nkv * nblk;
+      const uint32_t m_first = a_first + nkv * (nblk - 1);
       for (uint32_t g = 0; g < nkv; ++g) {
         uint32_t r0 = g * grows, r1 = (g + 1) * grows;
         uint32_t lo = qkv.second, hi = qkv.first;
@@ -164,21 +168,27 @@ struct Builder {
           }
         }
         for (uint32_t b = 0; b < nblk; ++b) {
+          const bool merger = b + 1 == nblk;
           Task k{};
           k.type = T_ATTN;
           k.layer = (uint16_t)l;
-          k.id = next_id++;
+          k.id = merger ? m_first + g : a_first + g * (nblk - 1) + b;
           k.a0 = g;
           k.a1 = b;
           k.w0_lo = lo;
           k.w0_hi = hi;
+          if (merger) {
+            k.w1_lo = a_first + g * (nblk - 1);
+            k.w1_hi = k.w1_lo + (nblk - 1);
+          }
           k.aux0 = nblk;
+          k.aux1 = merger ? 1u : 0u;
           s.per_cu[place(g * nblk + b, n_attn)].push_back(k);
         }
       }
+      next_id = a_first + n_attn;
       ++phase;
-      uint32_t a_last = next_id;
-      auto o = gemv(M_O, (uint16_t)l, d, 1, nq * hd, wb, a_first, a_last, nullptr);
+      auto o = gemv(M_O, (uint16_t)l, d, 1, nq * hd, wb, m_first, next_id, nullptr);
       auto gu = gemv(M_GU, (uint16_t)l, 2 * F, 2, d, wb, o.first, o.second, nullptr);
       auto dn = gemv(M_D, (uint16_t)l, d, 1, F, wb, gu.first, gu.second, nullptr);
       d_lo = dn.first;
@@ -239,7 +249,7 @@ void task_bytes(const BlobHeader &h, const Task &t, int32_t ctx, double *hbm, do
     int32_t lo, hi;
     attn_block_range(ctx, (int32_t)h.attn_blocks, (int32_t)t.a1, &lo, &hi);
     *hbm = B * 2.0 * (double)(hi - lo) * c.head_dim * 2.0;
-    // q, plus (once per group, by the last block) the group's partials for the combine
+    // q, plus (once per group, by the merger) the group's partials
     const double qpg = c.n_heads / c.n_kv_heads;
     *act = B * qpg * c.head_dim * 4.0 + B * qpg * (c.head_dim + 2) * 4.0;
   } else if (t.type == T_ARGMAX) {
@@ -261,7 +271,8 @@ double predict_makespan(const Schedule &s, const amk_cost_model &cm, int32_t ctx
     for (size_t c = 0; c < s.per_cu.size(); ++c) {
       while (head[c] < s.per_cu[c].size()) {
         const Task &t = s.per_cu[c][head[c]];
-        double ready = cu_free[c];
+        // ready[r]: when the producers of wait range r have finished and been seen
+        double ready[2] = {cu_free[c], 0.0};
         bool ok = true;
         for (int r = 0; r < 2 && ok; ++r) {
           uint32_t lo = r ? t.w1_lo : t.w0_lo, hi = r ? t.w1_hi : t.w0_hi;
@@ -270,15 +281,23 @@ double predict_makespan(const Schedule &s, const amk_cost_model &cm, int32_t ctx
               ok = false;
               break;
             }
-            ready = std::max(ready, finish[i] + cm.hop_us);
+            ready[r] = std::max(ready[r], finish[i] + cm.hop_us);
           }
         }
         if (!ok) break;
         double hbm, act;
         task_bytes(s.hdr, t, ctx, &hbm, &act);
         double dur = cm.task_us + hbm / (cm.cu_stream_gbs * 1e3) + act / (cm.l2_gbs * 1e3);
-        finish[t.id] = ready + dur;
-        cu_free[c] = ready + dur;
+        double end;
+        if (t.type == T_ATTN && t.aux1) {
+          // a merger computes its own partial after the QKV wait, then merges once its group's
+          // other blocks are done as well
+          end = std::max(ready[0] + dur, ready[1]) + cm.task_us;
+        } else {
+          end = std::max(ready[0], ready[1]) + dur;
+        }
+        finish[t.id] = end;
+        cu_free[c] = end;
         ++head[c];
         ++done;
         progress = true;

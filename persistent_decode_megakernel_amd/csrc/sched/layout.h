@@ -140,9 +140,9 @@ AMK_HD int32_t lds_xs_floats(int32_t batch, int32_t hidden, int32_t qdim, int32_
 }
 AMK_HD int32_t lds_attn_floats(int32_t qpg, int32_t hd) {
   // one sequence and at most kAttnMaxHeads heads per pass:
-  // q [qn][hd] + scores [qn][chunk] + partial acc [waves][qn*hd]
+  // q [qn][hd] + scores [qn][chunk] + partial acc [waves][qn*hd] + appended K/V row [2][hd] bf16
   const int32_t qn = qpg < kAttnMaxHeads ? qpg : kAttnMaxHeads;
-  return qn * hd + qn * kAttnRowsPerChunk + kWaves * qn * hd;
+  return qn * hd + qn * kAttnRowsPerChunk + kWaves * qn * hd + hd;
 }
 // Batch-1 GEMV tiles stage the first weight chunk of every wave in LDS (8 KB per wave).
 constexpr int32_t kPrefetchFloats = kWaves * 2048;

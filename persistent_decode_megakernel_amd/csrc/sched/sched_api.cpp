@@ -58,7 +58,6 @@ Schedule search_schedule(const amk_config &cfg, int32_t batch, int32_t n_cu,
           p.min_tile_kb = tk;
           Schedule s = build_schedule(cfg, batch, n_cu, p);
           if (s.hdr.lds_bytes > kMaxLdsBytes) continue;
-          if ((int64_t)cfg.n_heads * s.hdr.attn_blocks > kRedFloats) continue;
           double t = predict_makespan(s, cost, ctx);
           if (!have || t < best_t) {
             best_t = t;

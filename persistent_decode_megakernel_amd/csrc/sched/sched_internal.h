@@ -39,22 +39,19 @@ enum BufId : int32_t {
   BUF_AO = 8,      // attention output merged over the KV blocks, per layer: [B][nq*hd]
 };
 
-// An access with group >= 0 belongs to a combine group (the nblk KV-block tasks of one layer and
-// KV group, group = layer * n_kv_heads + g): it is performed once per step, by whichever member
-// finishes last, after every member's own accesses (a device counter decides and orders it).
 struct Access {
   int32_t buf;    // BufId
   int32_t index;  // layer (BUF_Q/KVNEW/PART/A/AO) or residual slot (BUF_H); 0 otherwise
   int64_t lo, hi; // element range [lo, hi)
   bool write;
-  int32_t group;  // -1: the task's own access
-  bool staged;    // the GEMV input vector the tile stages (the dependency of a tagged hand-off)
+  bool staged;    // read as the task's staged input: the dependency of a tagged hand-off
 };
 
-// Batch-1 megakernel instances (max_batch == 1) hand the activations between GEMV phases over as
-// epoch-tagged words: a tile whose staged input is such an activation waits by reloading it until
-// every tag is current (its flag waits are not consulted), and the O, gate/up and down tiles store
-// no flag. These two predicates mirror the kernel's choice.
+// Batch-1 megakernel instances (max_batch == 1) hand every step-local value over as epoch-tagged
+// words: a task with staged inputs (GEMV input vectors; the attention blocks' q and appended K/V
+// row; the merger's other partials) waits by reloading them until every tag is current (its flag
+// waits are not consulted), and only the LM tiles and the argmax store flags. These two
+// predicates mirror the kernel's choice.
 bool tagged_handoff(const BlobHeader &h);
 bool stores_flag(const BlobHeader &h, const Task &t);
 

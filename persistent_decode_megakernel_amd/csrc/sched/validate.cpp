@@ -35,13 +35,13 @@ std::string fmt(const char *f, long long a = 0, long long b = 0, long long c = 0
 }
 
 void add_range(std::vector<Access> *acc, int buf, int index, int64_t lo, int64_t hi, bool w,
-               int32_t group = -1) {
-  if (hi > lo) acc->push_back(Access{buf, index, lo, hi, w, group, false});
+               bool staged = false) {
+  if (hi > lo) acc->push_back(Access{buf, index, lo, hi, w, staged});
 }
 
 // the GEMV input vector: read whole, staged into LDS
 void add_staged(std::vector<Access> *acc, int buf, int index, int64_t n) {
-  if (n > 0) acc->push_back(Access{buf, index, 0, n, false, -1, true});
+  add_range(acc, buf, index, 0, n, false, true);
 }
 
 // Merge sorted element indices into intervals.
@@ -61,8 +61,7 @@ void add_elems(std::vector<Access> *acc, int buf, int index, std::vector<int64_t
 bool tagged_handoff(const BlobHeader &h) { return h.cfg.max_batch == 1; }
 
 bool stores_flag(const BlobHeader &h, const Task &t) {
-  return !tagged_handoff(h) || t.type != T_GEMV ||
-         !(t.mat == M_O || t.mat == M_GU || t.mat == M_D);
+  return !tagged_handoff(h) || t.type == T_ARGMAX || (t.type == T_GEMV && t.mat == M_LM);
 }
 
 bool footprint(const BlobHeader &h, const Task &t, std::vector<Access> *acc, std::string *err) {
@@ -143,25 +142,29 @@ bool footprint(const BlobHeader &h, const Task &t, std::vector<Access> *acc, std
     if (l >= L) return bad("layer out of range");
     if (g >= nkv) return bad("kv group out of range");
     if (blk >= nblk || t.aux0 != h.attn_blocks) return bad("KV block out of range");
+    // the group's last block merges the group's partials (and only it)
+    const bool merger = blk == nblk - 1;
+    if (t.aux1 != (merger ? 1u : 0u)) return bad("the merger must be the group's last KV block");
     for (int64_t b = 0; b < B; ++b) {
-      add_range(acc, BUF_Q, (int)l, b * qd + g * qpg * hd, b * qd + (g + 1) * qpg * hd, false);
+      add_range(acc, BUF_Q, (int)l, b * qd + g * qpg * hd, b * qd + (g + 1) * qpg * hd, false, true);
       for (int64_t kvi = 0; kvi < 2; ++kvi) {
         int64_t base = ((kvi * B + b) * nkv + g) * hd;
-        add_range(acc, BUF_KVNEW, (int)l, base, base + hd, false);
+        add_range(acc, BUF_KVNEW, (int)l, base, base + hd, false, true);
       }
       for (int64_t hh = g * qpg; hh < (g + 1) * qpg; ++hh) {
         int64_t base = ((b * nq + hh) * nblk + blk) * (hd + 2);
         add_range(acc, BUF_PART, (int)l, base, base + hd + 2, true);
       }
     }
-    // the group's combine: every block's partials in, the merged heads out
-    const int32_t grp = (int32_t)(l * nkv + g);
-    for (int64_t b = 0; b < B; ++b) {
-      for (int64_t hh = g * qpg; hh < (g + 1) * qpg; ++hh) {
-        int64_t base = (b * nq + hh) * nblk * (hd + 2);
-        add_range(acc, BUF_PART, (int)l, base, base + nblk * (hd + 2), false, grp);
+    if (merger) {
+      // every other block's partials in (its own it reads back after its stores), merged heads out
+      for (int64_t b = 0; b < B; ++b) {
+        for (int64_t hh = g * qpg; hh < (g + 1) * qpg; ++hh) {
+          int64_t base = (b * nq + hh) * nblk * (hd + 2);
+          add_range(acc, BUF_PART, (int)l, base, base + blk * (hd + 2), false, true);
+        }
+        add_range(acc, BUF_AO, (int)l, b * qd + g * qpg * hd, b * qd + (g + 1) * qpg * hd, true);
       }
-      add_range(acc, BUF_AO, (int)l, b * qd + g * qpg * hd, b * qd + (g + 1) * qpg * hd, true, grp);
     }
     return true;
   }
@@ -230,7 +233,6 @@ struct BufKey {
 struct Span {
   int64_t lo, hi;
   uint32_t id;
-  int32_t group;  // >= 0: a combine-group write (ordered after every member of the group)
 };
 
 }  // namespace
@@ -249,8 +251,6 @@ bool validate_schedule(const Schedule &s, std::string *report) {
   if (h.batch < 1 || (int32_t)h.batch > cfg.max_batch) return fail("batch outside [1, max_batch]");
   if (h.attn_blocks < 1) return fail("attn_blocks must be >= 1");
   if (h.n_lm_tiles < 1) return fail("no LM tiles");
-  if ((int64_t)cfg.n_heads * h.attn_blocks > kRedFloats)
-    return fail("n_heads x attn_blocks exceeds the combine scratch");
   if (s.per_cu.size() != h.n_cu) return fail("CU table size mismatch");
   if (h.lds_bytes > kMaxLdsBytes) return fail(fmt("LDS %lld bytes exceeds %lld", h.lds_bytes, kMaxLdsBytes));
   const uint32_t n = s.n_tasks();
@@ -324,31 +324,13 @@ bool validate_schedule(const Schedule &s, std::string *report) {
   if (q.size() != n) return fail(fmt("dependency cycle: %lld of %lld tasks can never start", n - q.size(), n));
   g.stamp.assign(n, 0);
 
-  // footprints grouped by buffer instance; a combine group's accesses are taken once (from its
-  // first member) and its members collected
-  std::map<BufKey, std::vector<Span>> writes, reads, group_reads;
-  std::map<int32_t, std::vector<uint32_t>> members;
+  // footprints grouped by buffer instance
+  std::map<BufKey, std::vector<Span>> writes, reads;
   std::vector<Access> acc;
   for (uint32_t id = 0; id < n; ++id) {
     if (!footprint(h, *g.task[id], &acc, &e)) return fail(e);
-    int32_t grp = -1;
     for (const Access &a : acc)
-      if (a.group >= 0) grp = a.group;
-    const bool first = grp >= 0 && members[grp].empty();
-    if (grp >= 0) members[grp].push_back(id);
-    for (const Access &a : acc) {
-      if (a.group < 0)
-        (a.write ? writes : reads)[BufKey{a.buf, a.index}].push_back(Span{a.lo, a.hi, id, -1});
-      else if (first)
-        (a.write ? writes : group_reads)[BufKey{a.buf, a.index}].push_back(Span{a.lo, a.hi, id, a.group});
-    }
-  }
-  std::vector<int32_t> group_of(n, -1);
-  for (auto &kv : members) {
-    if ((uint32_t)kv.second.size() != h.attn_blocks)
-      return fail(fmt("combine group %lld has %lld of %lld KV-block tasks", kv.first,
-                      (long long)kv.second.size(), h.attn_blocks));
-    for (uint32_t id : kv.second) group_of[id] = kv.first;
+      (a.write ? writes : reads)[BufKey{a.buf, a.index}].push_back(Span{a.lo, a.hi, id});
   }
   size_t checked = 0;
   for (auto &kv : writes) {
@@ -373,74 +355,45 @@ bool validate_schedule(const Schedule &s, std::string *report) {
           return fail(fmt("task %lld reads element %lld that no task writes", rd.id, covered));
         covered = w[i].hi;
         ++checked;
-        if (w[i].group < 0) {
-          if (!g.hb(w[i].id, rd.id))
-            return fail(fmt("race: task %lld reads data of task %lld without waiting for it (buffer %lld)", rd.id, w[i].id, kv.first.buf));
-        } else {
-          // written by the group's last member: the reader must wait for every member
-          for (uint32_t mb : members[w[i].group])
-            if (!g.hb(mb, rd.id))
-              return fail(fmt("race: task %lld reads the combine of group %lld without waiting for task %lld", rd.id, w[i].group, mb));
-        }
+        if (!g.hb(w[i].id, rd.id))
+          return fail(fmt("race: task %lld reads data of task %lld without waiting for it (buffer %lld)", rd.id, w[i].id, kv.first.buf));
       }
       if (covered < rd.hi)
         return fail(fmt("task %lld reads element %lld that no task writes", rd.id, covered));
     }
   }
-  // a combine reads only data its own group's members wrote (ordered by the group counter)
-  for (auto &kv : group_reads) {
-    auto it = writes.find(kv.first);
-    for (const Span &rd : kv.second) {
-      if (it == writes.end())
-        return fail(fmt("combine group %lld reads buffer %lld that no task writes", rd.group, kv.first.buf));
-      const auto &w = it->second;
-      size_t i = std::lower_bound(w.begin(), w.end(), rd.lo,
-                                  [](const Span &a, int64_t v) { return a.hi <= v; }) - w.begin();
-      int64_t covered = rd.lo;
-      for (; i < w.size() && w[i].lo < rd.hi; ++i) {
-        if (w[i].lo > covered) break;
-        covered = w[i].hi;
-        ++checked;
-        if (w[i].group >= 0 || group_of[w[i].id] != rd.group)
-          return fail(fmt("combine group %lld reads data of task %lld outside the group", rd.group, w[i].id));
-      }
-      if (covered < rd.hi)
-        return fail(fmt("combine group %lld reads element %lld that no task writes", rd.group, covered));
-    }
-  }
-  // tagged hand-offs: the kernel's wait for a tagged tile is its staged input's writers (every
-  // member of a combine group for a merged output); a flag wait must name tiles that store flags
+  // tagged hand-offs: the kernel's wait for a task with staged inputs is those inputs' writers;
+  // a flag wait must name tasks that store flags
   if (tagged_handoff(h)) {
     std::vector<uint32_t> want, have;
     for (uint32_t id = 0; id < n; ++id) {
       const Task &t = *g.task[id];
       if (!footprint(h, t, &acc, &e)) return fail(e);
-      const Access *st = nullptr;
-      for (const Access &a : acc)
-        if (a.staged) st = &a;
       have.clear();
       for (int k = 0; k < 2; ++k)
         for (uint32_t y = k ? t.w1_lo : t.w0_lo; y < (k ? t.w1_hi : t.w0_hi); ++y) have.push_back(y);
-      if (!st) {
+      want.clear();
+      bool staged = false;
+      for (const Access &a : acc) {
+        if (!a.staged) continue;
+        staged = true;
+        auto it = writes.find(BufKey{a.buf, a.index});
+        if (it == writes.end()) continue;
+        for (const Span &w : it->second)
+          if (w.hi > a.lo && w.lo < a.hi) want.push_back(w.id);
+      }
+      if (!staged) {
         for (uint32_t y : have)
           if (!stores_flag(h, *g.task[y]))
             return fail(fmt("task %lld waits on the flag of task %lld, which stores none", id, y));
         continue;
       }
-      want.clear();
-      auto it = writes.find(BufKey{st->buf, st->index});
-      if (it != writes.end())
-        for (const Span &w : it->second) {
-          if (w.hi <= st->lo || w.lo >= st->hi) continue;
-          if (w.group < 0) want.push_back(w.id);
-          else want.insert(want.end(), members[w.group].begin(), members[w.group].end());
-        }
       std::sort(want.begin(), want.end());
       want.erase(std::unique(want.begin(), want.end()), want.end());
       std::sort(have.begin(), have.end());
       have.erase(std::unique(have.begin(), have.end()), have.end());
       if (want != have)
-        return fail(fmt("task %lld: declared waits (%lld tasks) differ from the writers of its tagged input (%lld tasks)",
+        return fail(fmt("task %lld: declared waits (%lld tasks) differ from the writers of its tagged inputs (%lld tasks)",
                         id, (long long)have.size(), (long long)want.size()));
     }
   }
@@ -517,34 +470,18 @@ bool sim_run(const Schedule &s, int64_t delayed, std::string *msg) {
     }
     return true;
   };
-  std::map<int32_t, uint32_t> finished;  // combine group -> members finished
   auto exec = [&](const Task &t) -> bool {
     if (!footprint(s.hdr, t, &acc, &e)) { *msg = e; return false; }
-    int32_t grp = -1;
-    for (const Access &a : acc) {
-      if (a.group >= 0) { grp = a.group; continue; }
+    for (const Access &a : acc)
       if (!a.write && !sh.covered(a)) {
         *msg = fmt("stale read: task %lld ran before the data it reads (buffer %lld) was written", t.id, a.buf);
         return false;
       }
-    }
     for (const Access &a : acc)
-      if (a.write && a.group < 0) {
+      if (a.write) {
         if (sh.overlaps(a)) { *msg = fmt("double write by task %lld (buffer %lld)", t.id, a.buf); return false; }
         sh.add(a);
       }
-    if (grp >= 0 && ++finished[grp] == s.hdr.attn_blocks) {  // this task runs the combine
-      for (const Access &a : acc)
-        if (a.group >= 0 && !a.write && !sh.covered(a)) {
-          *msg = fmt("stale read: combine of group %lld before its partials were written (task %lld)", grp, t.id);
-          return false;
-        }
-      for (const Access &a : acc)
-        if (a.group >= 0 && a.write) {
-          if (sh.overlaps(a)) { *msg = fmt("double write by the combine of group %lld", grp); return false; }
-          sh.add(a);
-        }
-    }
     if (t.id < n) done[t.id] = 1;
     --left;
     return true;

@@ -65,7 +65,8 @@ def mutate(b: B.Blob, rng: random.Random) -> str:
     cus = [c for c in range(len(b.per_cu)) if len(b.per_cu[c])]
     kind = rng.choice(["drop_wait", "shrink_wait", "shift_wait", "swap_same_cu", "move_cu",
                        "dup_rows", "gap_rows", "self_wait", "wait_later_same_cu", "widen_wait",
-                       "reorder_cu", "bad_field", "attn_regroup", "attn_reblock"])
+                       "reorder_cu", "bad_field", "attn_regroup", "attn_reblock",
+                       "shrink_w1"])
     c = rng.choice(cus)
     v = b.per_cu[c]
     i = rng.randrange(len(v))
@@ -108,8 +109,18 @@ def mutate(b: B.Blob, rng: random.Random) -> str:
         t["w1_lo"], t["w1_hi"] = v[j]["id"], v[j]["id"] + 1
     elif kind == "bad_field":
         t["a1"] = 10 ** 6
+    elif kind == "shrink_w1":
+        # a merger that skips one block of its group
+        ms = [t2 for v2 in b.per_cu for t2 in v2 if t2["w1_hi"] > t2["w1_lo"] + 0 and t2["type"] == B.T_ATTN]
+        if ms:
+            t2 = rng.choice(ms)
+            if rng.random() < 0.5:
+                t2["w1_lo"] = int(t2["w1_lo"]) + 1
+            else:
+                t2["w1_hi"] = int(t2["w1_hi"]) - 1
     elif kind in ("attn_regroup", "attn_reblock"):
-        # move a KV-block task to another group or block: its group's combine loses a member
+        # move a KV-block task to another group or block: two tasks write the same partials
+        # and the group it left misses one (or its merger role no longer matches its block)
         attn = [(c2, j) for c2 in range(len(b.per_cu)) for j in range(len(b.per_cu[c2]))
                 if b.per_cu[c2][j]["type"] == B.T_ATTN]
         c2, j = rng.choice(attn)
@@ -158,48 +169,67 @@ def test_truncated_and_corrupt_blobs_rejected(libamk):
     assert _lib.schedule_validate(b.to_bytes())[0] == _lib.AMK_E_SCHEDULE_REJECTED
 
 
-def _o_task_and_attn(b: B.Blob, layer: int):
+def FOUR_BLOCKS():
+    return _lib.amk_sched_params(attn_blocks=4, search=0)
+
+
+def _attn(b: B.Blob, layer: int):
+    """[(cu, index)] of the layer's O tiles; sorted ids of its mergers and of its other blocks."""
     o = [(c, j) for c in range(len(b.per_cu)) for j in range(len(b.per_cu[c]))
          if b.per_cu[c][j]["type"] == B.T_GEMV and b.per_cu[c][j]["mat"] == B.M_O
          and b.per_cu[c][j]["layer"] == layer]
-    attn = sorted(int(t["id"]) for v in b.per_cu for t in v
-                  if t["type"] == B.T_ATTN and t["layer"] == layer)
-    return o, attn
+    attn = [t for v in b.per_cu for t in v if t["type"] == B.T_ATTN and t["layer"] == layer]
+    mergers = sorted(int(t["id"]) for t in attn if t["aux1"])
+    others = sorted(int(t["id"]) for t in attn if not t["aux1"])
+    return o, mergers, others
 
 
 @pytest.mark.parametrize("drop", ["first", "last"])
-def test_o_task_must_wait_for_every_kv_block_of_the_combine(libamk, drop):
-    """The attention output is merged by whichever KV-block task of a group finishes last (a
-    device counter decides), so an O-projection tile that skips any one block's flag may read an
-    unmerged output: the validator rejects it and the delayed-CU simulation shows the stale read."""
+def test_o_tile_must_wait_for_every_merger(libamk, drop):
+    """Each KV group's last block merges the group's partials into the attention output, so an
+    O-projection tile that skips any one merger may read an unmerged output: the validator
+    rejects it and the delayed-CU simulation shows the stale read."""
     cfg = synth.get_config("tiny")
-    b = B.Blob(_lib.schedule_build(_lib.make_config(cfg), 1, 8))
-    o, attn = _o_task_and_attn(b, 1)
-    dropped = attn[0] if drop == "first" else attn[-1]
+    b = B.Blob(_lib.schedule_build(_lib.make_config(cfg), 1, 8, FOUR_BLOCKS()))
+    o, mergers, others = _attn(b, 1)
+    assert len(mergers) == cfg.n_kv_heads and mergers[0] > max(others)
+    dropped = mergers[0] if drop == "first" else mergers[-1]
     cu_of = {int(t["id"]): c for c in range(len(b.per_cu)) for t in b.per_cu[c]}
-    # an O tile on another CU than the dropped block (program order would still cover it)
     c, j = next((c, j) for c, j in o if c != cu_of[dropped])
     t = b.per_cu[c][j]
-    assert (int(t["w0_lo"]), int(t["w0_hi"])) == (attn[0], attn[-1] + 1)
+    assert (int(t["w0_lo"]), int(t["w0_hi"])) == (mergers[0], mergers[-1] + 1)
     if drop == "first":
-        t["w0_lo"] = attn[0] + 1
+        t["w0_lo"] = mergers[0] + 1
     else:
-        t["w0_hi"] = attn[-1]
+        t["w0_hi"] = mergers[-1]
     data = b.to_bytes()
     st, rep = _lib.schedule_validate(data)
-    assert st == _lib.AMK_E_SCHEDULE_REJECTED and "combine" in rep, rep
+    assert st == _lib.AMK_E_SCHEDULE_REJECTED and "race" in rep, rep
     assert _lib.schedule_simulate(data)[0] != _lib.AMK_OK
 
 
-def test_combine_group_needs_all_blocks(libamk):
+def test_merger_must_wait_for_every_block_of_its_group(libamk):
     cfg = synth.get_config("tiny")
-    b = B.Blob(_lib.schedule_build(_lib.make_config(cfg), 1, 8))
+    b = B.Blob(_lib.schedule_build(_lib.make_config(cfg), 1, 8, FOUR_BLOCKS()))
+    o, mergers, others = _attn(b, 0)
+    t = next(t for v in b.per_cu for t in v if int(t["id"]) == mergers[0])
+    assert int(t["w1_hi"]) - int(t["w1_lo"]) == b.hdr.attn_blocks - 1 > 0
+    t["w1_hi"] = int(t["w1_hi"]) - 1
+    data = b.to_bytes()
+    st, rep = _lib.schedule_validate(data)
+    assert st == _lib.AMK_E_SCHEDULE_REJECTED and "race" in rep, rep
+    assert _lib.schedule_simulate(data)[0] != _lib.AMK_OK
+
+
+def test_merger_must_be_the_groups_last_block(libamk):
+    cfg = synth.get_config("tiny")
+    b = B.Blob(_lib.schedule_build(_lib.make_config(cfg), 1, 8, FOUR_BLOCKS()))
     for v in b.per_cu:
         for t in v:
             if t["type"] == B.T_ATTN and t["layer"] == 0 and t["a0"] == 0 and t["a1"] == 0:
-                t["a0"] = 1  # block 0 of group 0 now claims group 1: group 0 is one short
+                t["aux1"] = 1
     st, rep = _lib.schedule_validate(b.to_bytes())
-    assert st == _lib.AMK_E_SCHEDULE_REJECTED, rep
+    assert st == _lib.AMK_E_SCHEDULE_REJECTED and "merger" in rep, rep
 
 
 def _tasks_by(b: B.Blob, typ, mat=None, layer=None):
