@@ -89,6 +89,40 @@ def time_path(cfg, weights, kv_host, path, steps, warmup, graph=False):
     return total / steps, per, info, ids
 
 
+def time_multistep(cfg, weights, kv_host, steps, warmup):
+    """The same positions as time_path's megakernel run, decoded as ONE launch of `steps` greedy
+    steps (amk_decode_steps: each step's first tiles wait on the previous step's argmax inside the
+    kernel). Returns (ms per step, final token ids)."""
+    import torch
+    from persistent_decode_megakernel_amd import synth
+    from persistent_decode_megakernel_amd.model import Model
+
+    max_seq = cfg.prefill + max(steps, warmup) + 1
+    model = Model(cfg, weights, path="megakernel", max_seq=max_seq)
+    kv = model.kv(cfg.batch, max_seq)
+    kv.tensor.copy_(kv_host[..., :max_seq, :].to(kv.tensor.device))
+    first = synth.make_tokens(cfg, 0)[:, 0].to(torch.int32).cuda()
+    out = torch.empty((max(steps, warmup), cfg.batch), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    if warmup:
+        model.steps(kv, first, cfg.prefill, warmup, out=out[:warmup])
+    model.sync()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    model.steps(kv, first, cfg.prefill, steps, out=out[:steps])
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    model.sync()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    ids = out[steps - 1].cpu().tolist()
+    kv.close()
+    model.close()
+    del kv, model
+    torch.cuda.empty_cache()
+    return ms, ids
+
+
 def profiled_traffic(cfg, kernel_name):
     """Per-launch HBM bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from the committed
     rocprofv3 summary of this workload, or None when the kernel sources changed since."""
@@ -149,6 +183,7 @@ def main():
     ap.add_argument("--workload", default="llama2_7b")
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-multistep", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=2)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (a kernel of "
@@ -231,6 +266,16 @@ def main():
         "launches_per_step": info.launches_per_step,
         "step_ms_p10_p50_p90": [round(sorted(per)[int(q * (steps - 1))], 4) for q in (0.1, 0.5, 0.9)],
     }
+    if not args.no_multistep:
+        ms_m, ids_m = time_multistep(cfg, weights, kv_host, steps, warmup)
+        out["multistep_one_launch"] = {
+            "steps_per_launch": steps,
+            "ms_per_step": round(ms_m, 4),
+            "tokens_per_s": round(cfg.batch / (ms_m * 1e-3), 2),
+            "hbm_gbs": round(avg_bytes / (ms_m * 1e-3) / 1e9, 1),
+            "same_final_ids": ids_m == ids,
+        }
+        log(f"[bench] multistep: {ms_m:.4f} ms/step in one launch of {steps}")
     if not args.no_ablation:
         for key, graph in (("ablation_unfused", False), ("ablation_unfused_hipgraph", True)):
             ms_u, per_u, info_u, ids_u = time_path(cfg, weights, kv_host, "unfused", steps, warmup,

@@ -141,6 +141,19 @@ amk_status amk_kv_data(const amk_kv *kv, void **d_ptr);
 amk_status amk_decode_step(amk_model *m, amk_kv *kv, const int32_t *d_tokens, int32_t pos,
                            int32_t batch, float *d_logits, int32_t *d_next, void *stream);
 
+/* n_steps consecutive greedy decode steps in ONE launch (megakernel path): step i runs at position
+ * pos + i on the tokens step i-1 produced (step 0 on d_tokens) and writes them to d_out[i][b]
+ * (device int32 [n_steps][batch]); d_logits, when not NULL, receives each step's logits
+ * (device float32 [n_steps][batch][vocab]). Removes the per-token launch and host round trip:
+ * inside the launch a step's first-layer QKV tiles wait for the previous step's argmax, which
+ * every task of that step precedes (checked by the schedule validator). The unfused path runs
+ * the same steps as consecutive launch sequences. pos + n_steps must not exceed max_seq. Same
+ * ordering and error rules as amk_decode_step, which is this call with n_steps = 1. Source: the
+ * pages' launch-overhead motivation (Ada-MK summary, "Methodology"). */
+amk_status amk_decode_steps(amk_model *m, amk_kv *kv, const int32_t *d_tokens, int32_t pos,
+                            int32_t n_steps, int32_t batch, float *d_logits, int32_t *d_out,
+                            void *stream);
+
 /* Synchronise `stream` and report a device-side error recorded by earlier steps (and clear it). */
 amk_status amk_sync(amk_model *m, void *stream);
 

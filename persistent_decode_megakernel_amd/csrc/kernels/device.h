@@ -24,6 +24,7 @@ struct DevModel {
   int32_t wtype, tied, max_batch, max_seq;
   int32_t nblk, n_lm;
   uint32_t n_tasks;
+  uint32_t argmax_id;  // the step's last task: every other task of the step precedes it
   float eps, attn_scale;
   const DevLayer *layers;
   const uint16_t *embed, *final_norm;
@@ -55,6 +56,9 @@ struct DevModel {
   uint64_t *trace;         // optional: [n_tasks][4] timestamps, then [n_cu] XCC ids; null = off
 };
 
+// One decode step: tokens at position pos in, next tokens (and optionally logits) out. A launch
+// may run n_steps consecutive steps (step = 0 .. n_steps-1): step i takes the tokens step i-1
+// wrote, at position pos + i, with flag epoch epoch + i.
 struct StepArgs {
   const int32_t *tokens;
   float *logits;
@@ -63,6 +67,7 @@ struct StepArgs {
   int32_t kv_batch, kv_max_seq;
   int32_t pos, batch;
   uint32_t epoch;
+  int32_t step, n_steps;
 };
 
 constexpr uint32_t ERR_TIMEOUT = 7;
@@ -536,7 +541,7 @@ struct GemvStream {
 // ------------------------------------------------------------------------------------------
 // token of sequence b, validated (an out-of-range id is recorded as a device error and read as 0)
 __device__ __forceinline__ int32_t token_of(const DevModel &m, const StepArgs &s, int b) {
-  int32_t t = gld(&s.tokens[b]);
+  int32_t t = cld(&s.tokens[b]);  // device-coherent: a previous step of the launch may have written it
   if (t < 0 || t >= m.V) {
     if (threadIdx.x == 0) record_error(m.err, ERR_TOKEN, 0xffffffffu, (uint32_t)t);
     t = 0;
@@ -977,12 +982,18 @@ __device__ void epi_qkv(const DevModel &m, const StepArgs &s, int l, int r0, int
         uint16_t *c0 = &s.kv[kv_index(m, s, l, kvi, b, q0.head, s.pos, q0.dim)];
         uint16_t *c1 = &s.kv[kv_index(m, s, l, kvi, b, q1.head, s.pos, q1.dim)];
         if (m.max_batch == 1) {
-          // This step's attention blocks take the row from tagged words; the cache row is read
-          // only by later launches (the kernel boundary makes it visible), so plain stores do.
-          // Device-coherent 2-byte stores are slow to complete, and any later load in this
-          // workgroup would wait for them (loads and stores share one counter).
-          gst(c0, k0);
-          gst(c1, k1);
+          // This step's attention blocks take the row from tagged words. A single-step launch's
+          // cache row is read only by later launches (the kernel boundary makes it visible), so
+          // plain stores do: device-coherent 2-byte stores are slow to complete, and any later
+          // load in this workgroup would wait for them (loads and stores share one counter). In
+          // a multi-step launch the next step reads it as history, from any XCD.
+          if (s.n_steps > 1) {
+            cst(c0, k0);
+            cst(c1, k1);
+          } else {
+            gst(c0, k0);
+            gst(c1, k1);
+          }
           uint32_t *kb = m.kvt + (((int64_t)l * 2 + kvi) * m.nkv + q0.head) * hd;
           const uint32_t tg = s.epoch & kTagMask;
           cst(&kb[q0.dim], ((uint32_t)k0 << 16) | tg);
@@ -1102,7 +1113,7 @@ __device__ void argmax_combine(const DevModel &m, const StepArgs &s, int n_slots
       const int oi = __shfl_xor(bi, o, 64);
       if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
     }
-    if (lane_id() == 0) gst(&s.next[b], (bi == 0x7fffffff) ? 0 : bi);
+    if (lane_id() == 0) cst(&s.next[b], (bi == 0x7fffffff) ? 0 : bi);
   }
 }
 

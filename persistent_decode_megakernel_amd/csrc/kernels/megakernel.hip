@@ -15,6 +15,15 @@
 
 namespace amk {
 
+// Task t waiting instead on the previous step's argmax (multi-step launches).
+__device__ __forceinline__ Task prev_step(const DevModel &m, const Task &t) {
+  Task w = t;
+  w.w0_lo = m.argmax_id;
+  w.w0_hi = m.argmax_id + 1;
+  w.w1_lo = w.w1_hi = 0;
+  return w;
+}
+
 // GEMV tile task. Batch 1: the first two weight chunks of every wave (one into its LDS slot, one
 // into registers) are issued at once, then the input is staged from its epoch-tagged producer
 // words (which doubles as the dependency wait; the first layer's QKV tiles read the embedding and
@@ -44,7 +53,9 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
     // Batch 1: inputs produced in this step by other tiles are tagged with the epoch, so their
     // staging loads are the dependency wait (no flags): the weight prefetch is issued at once.
     const bool tagged = !(t.mat == M_QKV && l == 0);
-    if (!tagged) wait_poll(m, t, s.epoch, abort_slot);
+    // the first layer's QKV tiles read the token: in a later step of a multi-step launch they
+    // wait for the previous step's argmax (which every task of that step precedes)
+    if (!tagged) wait_poll(m, s.step > 0 ? prev_step(m, t) : t, s.epoch - (s.step > 0), abort_slot);
     if (st.S > 0) st.load_lds(0, slot);
     if (st.S > 1) st.load(P, 1);
     // keep the register prefetch issued here, ahead of the staging loads, not at its first use
@@ -95,6 +106,8 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
       case M_D: in = BatchInput{m.a + (int64_t)l * m.max_batch * m.F, m.F, nullptr, nullptr, false}; break;
       default: in.x = m.h + 2 * (int64_t)m.L * hb; in.gain = m.final_norm; break;
     }
+    if (s.step > 0 && t.mat == M_QKV && l == 0 && !wait_task(m, prev_step(m, t), s.epoch - 1, abort_slot))
+      return false;
     if (!wait_task(m, t, s.epoch, abort_slot)) return false;
     if (m.trace && threadIdx.x == 0) gst(&m.trace[(uint64_t)t.id * 4 + 2], (uint64_t)wall_clock64());
     gemv_mfma<WT>(m, s, W, scale, K, r0, r1, in, ys, red, xs);
@@ -131,7 +144,7 @@ __device__ __forceinline__ bool publishes_flag(const Task &t) {
 }
 
 template <int WT, int HD, int QMAX, bool BATCHED>
-__device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArgs &s) {
+__device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArgs &s0) {
   extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte reads of xs need it
   const int32_t xa = lds_xs_floats(m.max_batch, m.d, m.qd, m.F);
   const int32_t xb = lds_attn_floats(m.qpg, m.hd);
@@ -149,34 +162,43 @@ __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArg
     const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20);
     gst(&trace[(uint64_t)m.n_tasks * 4 + blockIdx.x], (uint64_t)xcc);
   }
-  for (uint32_t ti = t0; ti < t1; ++ti) {
-    const Task t = load_task(&m.tasks[ti]);
-    if (trace && threadIdx.x == 0) gst(&trace[(uint64_t)t.id * 4 + 0], (uint64_t)wall_clock64());
-    bool ok;
-    if (t.type == T_GEMV) {
-      ok = gemv_task<WT, BATCHED>(m, s, t, xs, ys, red, pf, &abort_flag);
-    } else if (t.type == T_ATTN) {
-      ok = attn_task<HD, QMAX, !BATCHED>(m, s, t.layer, (int)t.a0, (int)t.a1, xs, red, &t, &abort_flag);
-      if (trace && threadIdx.x == 0) gst(&trace[(uint64_t)t.id * 4 + 2], (uint64_t)wall_clock64());
-      if (ok && t.aux1) ok = attn_merge<!BATCHED>(m, s, t, &abort_flag);
-    } else {
-      ok = wait_task(m, t, s.epoch, &abort_flag);
-      if (ok) argmax_combine(m, s, (int)t.aux0);
-    }
-    if (!ok) return;
-    // Publish: every wave waits for its own (device-coherent) stores to complete, the workgroup
-    // meets, then one thread stores the flag. Data that crosses CUs is written with device-scope
-    // stores, so no L2 writeback is needed before the flag.
-    if (publishes_flag<BATCHED>(t)) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        if (trace) gst(&trace[(uint64_t)t.id * 4 + 3], (uint64_t)wall_clock64());
-        __hip_atomic_store(gptr(&m.flags[t.id]), s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int step = 0; step < s0.n_steps; ++step) {
+    StepArgs s = s0;
+    s.step = step;
+    s.epoch = s0.epoch + (uint32_t)step;
+    s.pos = s0.pos + step;
+    if (step > 0) s.tokens = s0.next + (int64_t)(step - 1) * s0.batch;
+    s.next = s0.next + (int64_t)step * s0.batch;
+    if (s0.logits) s.logits = s0.logits + (int64_t)step * s0.batch * m.V;
+    for (uint32_t ti = t0; ti < t1; ++ti) {
+      const Task t = load_task(&m.tasks[ti]);
+      if (trace && threadIdx.x == 0) gst(&trace[(uint64_t)t.id * 4 + 0], (uint64_t)wall_clock64());
+      bool ok;
+      if (t.type == T_GEMV) {
+        ok = gemv_task<WT, BATCHED>(m, s, t, xs, ys, red, pf, &abort_flag);
+      } else if (t.type == T_ATTN) {
+        ok = attn_task<HD, QMAX, !BATCHED>(m, s, t.layer, (int)t.a0, (int)t.a1, xs, red, &t, &abort_flag);
+        if (trace && threadIdx.x == 0) gst(&trace[(uint64_t)t.id * 4 + 2], (uint64_t)wall_clock64());
+        if (ok && t.aux1) ok = attn_merge<!BATCHED>(m, s, t, &abort_flag);
+      } else {
+        ok = wait_task(m, t, s.epoch, &abort_flag);
+        if (ok) argmax_combine(m, s, (int)t.aux0);
       }
-    } else {
-      __syncthreads();
-      if (trace && threadIdx.x == 0) gst(&trace[(uint64_t)t.id * 4 + 3], (uint64_t)wall_clock64());
+      if (!ok) return;
+      // Publish: every wave waits for its own (device-coherent) stores to complete, the workgroup
+      // meets, then one thread stores the flag. Data that crosses CUs is written with device-scope
+      // stores, so no L2 writeback is needed before the flag.
+      if (publishes_flag<BATCHED>(t)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          if (trace) gst(&trace[(uint64_t)t.id * 4 + 3], (uint64_t)wall_clock64());
+          __hip_atomic_store(gptr(&m.flags[t.id]), s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      } else {
+        __syncthreads();
+        if (trace && threadIdx.x == 0) gst(&trace[(uint64_t)t.id * 4 + 3], (uint64_t)wall_clock64());
+      }
     }
   }
 }

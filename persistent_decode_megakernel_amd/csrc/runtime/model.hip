@@ -213,6 +213,14 @@ void zero_async(void *p, size_t bytes, hipStream_t st) {
   if (n) hipLaunchKernelGGL(amk_zero_words, dim3(blocks), dim3(256), 0, st, static_cast<uint32_t *>(p), n);
 }
 
+// id of the schedule's argmax task (validated: exactly one, and every task precedes it)
+uint32_t argmax_of(const Schedule &s) {
+  for (const auto &v : s.per_cu)
+    for (const Task &t : v)
+      if (t.type == T_ARGMAX) return t.id;
+  return 0;
+}
+
 // Tagged activations carry an epoch: whenever the epoch restarts they are cleared too, so no
 // word of an earlier run can pass for the new step's. A fill kernel, not a memset, since this runs
 // inside amk_decode_step, which a caller may capture into a graph.
@@ -469,6 +477,7 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
               "hipMemcpyAsync");
     dm.tasks = d_tasks;
     dm.offsets = d_offs;
+    dm.argmax_id = argmax_of(m->sched);
     double wd_ms = 2000.0;
     if (const char *env = std::getenv("AMK_WATCHDOG_MS")) wd_ms = std::atof(env);
     dm.timeout_ticks = (uint64_t)(wd_ms * clock_khz);
@@ -608,18 +617,20 @@ static void launch_unfused(amk_model *m, const StepArgs &s, hipStream_t st) {
   hipLaunchKernelGGL(amk_uf_argmax, dim3(1), dim3(64), 0, st, g, s, m->n_lm_uf);
 }
 
-extern "C" amk_status amk_decode_step(amk_model *m, amk_kv *kv, const int32_t *d_tokens,
-                                      int32_t pos, int32_t batch, float *d_logits,
-                                      int32_t *d_next, void *stream) {
+extern "C" amk_status amk_decode_steps(amk_model *m, amk_kv *kv, const int32_t *d_tokens,
+                                       int32_t pos, int32_t n_steps, int32_t batch,
+                                       float *d_logits, int32_t *d_out, void *stream) {
   AMK_API_BEGIN
-  if (!m || !kv || !d_tokens || !d_next) return set_error(AMK_E_INVALID, "amk_decode_step: null argument");
-  if (kv->m != m) return set_error(AMK_E_INVALID, "amk_decode_step: KV cache belongs to another model");
+  if (!m || !kv || !d_tokens || !d_out) return set_error(AMK_E_INVALID, "amk_decode_steps: null argument");
+  if (kv->m != m) return set_error(AMK_E_INVALID, "amk_decode_steps: KV cache belongs to another model");
+  if (n_steps < 1) return set_error(AMK_E_INVALID, "amk_decode_steps: n_steps must be >= 1");
   if (batch < 1 || batch > m->cfg.max_batch || batch > kv->batch)
-    return set_error(AMK_E_CAPACITY, "amk_decode_step: batch exceeds max_batch or the KV cache");
-  if (pos < 0 || pos >= kv->max_seq || pos >= m->cfg.max_seq)
-    return set_error(AMK_E_CAPACITY, "amk_decode_step: position beyond max_seq");
+    return set_error(AMK_E_CAPACITY, "amk_decode_steps: batch exceeds max_batch or the KV cache");
+  if (pos < 0 || (int64_t)pos + n_steps > std::min(kv->max_seq, m->cfg.max_seq))
+    return set_error(AMK_E_CAPACITY, "amk_decode_steps: positions beyond max_seq");
+  if (n_steps > 0x100000) return set_error(AMK_E_INVALID, "amk_decode_steps: n_steps too large");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (m->epoch >= 0x7ffffff0u) {  // keep the signed flag comparison unambiguous
+  if (m->epoch >= 0x7ffffff0u - (uint32_t)n_steps) {  // keep the signed flag comparison unambiguous
     zero_async(m->dm.flags, sizeof(uint32_t) * std::max<uint32_t>(1, m->sched.hdr.n_tasks), st);
     clear_tags(m, st);
     m->epoch = 0;
@@ -627,13 +638,16 @@ extern "C" amk_status amk_decode_step(amk_model *m, amk_kv *kv, const int32_t *d
   StepArgs s;
   s.tokens = d_tokens;
   s.logits = d_logits;
-  s.next = d_next;
+  s.next = d_out;
   s.kv = static_cast<uint16_t *>(kv->data);
   s.kv_batch = kv->batch;
   s.kv_max_seq = kv->max_seq;
   s.pos = pos;
   s.batch = batch;
-  s.epoch = ++m->epoch;
+  s.epoch = m->epoch + 1;
+  s.step = 0;
+  s.n_steps = n_steps;
+  m->epoch += (uint32_t)n_steps;
   if (m->path == AMK_PATH_MEGAKERNEL) {
     const DevModel *g = m->d_dm;
     void *args[] = {(void *)&g, (void *)&s};
@@ -641,13 +655,29 @@ extern "C" amk_status amk_decode_step(amk_model *m, amk_kv *kv, const int32_t *d
                                               args, m->lds_bytes, st);
     if (e != hipSuccess) return set_error(AMK_E_HIP, std::string("megakernel launch: ") + hipGetErrorString(e));
   } else {
-    launch_unfused(m, s, st);
+    // the ablation runs each step as its own sequence of launches, chaining tokens on the device
+    for (int32_t i = 0; i < n_steps; ++i) {
+      StepArgs si = s;
+      si.n_steps = 1;
+      si.pos = pos + i;
+      si.epoch = s.epoch + (uint32_t)i;
+      si.tokens = i ? d_out + (int64_t)(i - 1) * batch : d_tokens;
+      si.next = d_out + (int64_t)i * batch;
+      si.logits = d_logits ? d_logits + (int64_t)i * batch * m->cfg.vocab : nullptr;
+      launch_unfused(m, si, st);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return set_error(AMK_E_HIP, std::string("unfused launch: ") + hipGetErrorString(e));
   }
   clear_error();
   return AMK_OK;
   AMK_API_END
+}
+
+extern "C" amk_status amk_decode_step(amk_model *m, amk_kv *kv, const int32_t *d_tokens,
+                                      int32_t pos, int32_t batch, float *d_logits,
+                                      int32_t *d_next, void *stream) {
+  return amk_decode_steps(m, kv, d_tokens, pos, 1, batch, d_logits, d_next, stream);
 }
 
 extern "C" amk_status amk_sync(amk_model *m, void *stream) {
@@ -751,6 +781,8 @@ amk_status install_schedule(amk_model *m, Schedule &&s, std::vector<uint8_t> &&b
   m->lds_bytes = h.lds_bytes;
   m->sched = std::move(s);
   m->blob = std::move(blob);
+  m->dm.argmax_id = argmax_of(m->sched);
+  hip_check(hipMemcpy(m->d_dm, &m->dm, sizeof(DevModel), hipMemcpyHostToDevice), "hipMemcpy");
   return AMK_OK;
 }
 

@@ -41,6 +41,8 @@ bool config_ok(const amk_config &c, std::string *err) {
   if (c.wtype != AMK_WT_BF16 && c.wtype != AMK_WT_INT8) return fail("config: unknown wtype");
   if (c.wtype == AMK_WT_INT8 && c.tied_lm_head)
     return fail("config: int8 weights with a tied LM head are unsupported");
+  if (c.wtype == AMK_WT_INT8 && (c.hidden % 16 || c.ffn % 16))
+    return fail("config: int8 weights need hidden and ffn multiples of 16");
   if (!(c.rms_eps > 0.f) || !(c.rope_theta > 0.f)) return fail("config: eps/theta must be > 0");
   return true;
 }

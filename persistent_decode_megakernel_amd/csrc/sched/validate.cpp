@@ -12,7 +12,10 @@
 //     step is written by exactly one task, and that writer happens-before the reader;
 //   * tagged hand-offs (batch-1 instances): a tile that waits by reloading its tagged input
 //     declares exactly that input's writers as its waits, so the graph checked above is the one
-//     the kernel enforces, and no task waits on the flag of a tile that stores none.
+//     the kernel enforces, and no task waits on the flag of a tile that stores none;
+//   * step ordering: exactly one argmax task, and every task precedes it (through waits and
+//     program order). A multi-step launch starts a step's first-layer QKV tiles after the
+//     previous step's argmax, so no task of a step can overlap the next step's writes.
 // The simulator is an independent dynamic check: it executes the tasks under several
 // interleavings (greedy, and one run per delayed CU) with shadow memory, flagging stale reads,
 // double writes and stuck states.
@@ -396,6 +399,38 @@ bool validate_schedule(const Schedule &s, std::string *report) {
         return fail(fmt("task %lld: declared waits (%lld tasks) differ from the writers of its tagged inputs (%lld tasks)",
                         id, (long long)have.size(), (long long)want.size()));
     }
+  }
+  // step ordering: one argmax, and every task an ancestor of it
+  {
+    int64_t am = -1;
+    for (uint32_t id = 0; id < n; ++id)
+      if (g.task[id]->type == T_ARGMAX) {
+        if (am >= 0) return fail("more than one argmax task");
+        am = id;
+      }
+    if (am < 0) return fail("no argmax task");
+    std::vector<uint8_t> seen(n, 0);
+    std::vector<uint32_t> st{(uint32_t)am};
+    seen[am] = 1;
+    size_t reached = 1;
+    while (!st.empty()) {
+      const uint32_t x = st.back();
+      st.pop_back();
+      auto visit = [&](uint32_t y) {
+        if (y < n && !seen[y]) {
+          seen[y] = 1;
+          ++reached;
+          st.push_back(y);
+        }
+      };
+      if (g.prev_same_cu[x] >= 0) visit((uint32_t)g.prev_same_cu[x]);
+      const Task &t = *g.task[x];
+      for (int k = 0; k < 2; ++k)
+        for (uint32_t y = k ? t.w1_lo : t.w0_lo; y < (k ? t.w1_hi : t.w0_hi); ++y) visit(y);
+    }
+    if (reached != n)
+      return fail(fmt("%lld tasks do not precede the argmax (steps of one launch could overlap)",
+                      (long long)(n - reached)));
   }
   // outputs must be complete
   {

@@ -157,6 +157,20 @@ class Model:
         _lib.check(st, "amk_decode_step")
         return next_out
 
+    def steps(self, kv: KVCache, tokens: torch.Tensor, pos: int, n_steps: int,
+              logits: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """n_steps greedy decode steps in one launch (amk_decode_steps). tokens: device int32 [B].
+        Returns the device int32 [n_steps, B] tokens; logits (if given): [n_steps, B, V] float32."""
+        B = tokens.numel()
+        if out is None:
+            out = torch.empty((n_steps, B), dtype=torch.int32, device=self.device)
+        st = self.lib.amk_decode_steps(self.handle, kv.handle, C.c_void_p(tokens.data_ptr()), pos,
+                                       n_steps, B,
+                                       C.c_void_p(_ptr(logits)) if logits is not None else None,
+                                       C.c_void_p(out.data_ptr()), _stream_ptr())
+        _lib.check(st, "amk_decode_steps")
+        return out
+
     def sync(self):
         _lib.check(self.lib.amk_sync(self.handle, _stream_ptr()), "amk_sync")
 

@@ -291,3 +291,17 @@ def test_tagged_waits_of_real_lowerings_are_their_input_writers(libamk):
     t["w0_hi"] = gu[-1]
     st, rep = _lib.schedule_validate(b.to_bytes())
     assert st == _lib.AMK_E_SCHEDULE_REJECTED, rep
+
+
+def test_schedule_without_an_argmax_is_rejected(libamk):
+    """Several steps run in one launch: a step's first tiles wait on the previous step's argmax,
+    which must therefore exist and follow every task of the step. Without one the validator
+    rejects the schedule before looking at output coverage."""
+    cfg = synth.get_config("tiny")
+    b = B.Blob(_lib.schedule_build(_lib.make_config(cfg), 1, 8))
+    am = _tasks_by(b, B.T_ARGMAX)
+    assert am == [b.n_tasks - 1]
+    for c, v in enumerate(b.per_cu):
+        b.per_cu[c] = v[v["type"] != B.T_ARGMAX]
+    st, rep = _lib.schedule_validate(b.to_bytes())
+    assert st == _lib.AMK_E_SCHEDULE_REJECTED and "argmax" in rep, rep
