@@ -2,9 +2,11 @@
 // gfx950 only: wave64, kWaves (8) waves per workgroup in the megakernel.
 //
 // Numerics: weights are bf16 (or int8 with per-row fp32 scales) and are converted exactly to
-// fp32; activations, accumulations, norms, softmax and residuals are fp32. Appended K/V rows are
-// rounded to bf16 (round to nearest even). Every reduction runs in a fixed order, so results do
-// not depend on which CU ran a tile or when.
+// fp32; activations, accumulations, norms, softmax and residuals are fp32. The exception is the
+// batch-1 int8 GEMV, which takes its input as a 23-bit fixed-point integer (one power-of-two
+// scale per vector, see stage_digits) and sums the products exactly in int32. Appended K/V rows
+// are rounded to bf16 (round to nearest even). Every reduction runs in a fixed order, so results
+// do not depend on which CU ran a tile or when.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -105,6 +107,19 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
+}
+
+// max over the 64 lanes of non-negative values, every lane receives it: DPP within rows of 16
+// lanes (float bits of non-negative values order as integers), then the four row maxima
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  int x = __float_as_int(v);
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));   // quad_perm(1,0,3,2)
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));   // quad_perm(2,3,0,1)
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false));  // row_mirror
+  const int a = max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16));
+  const int b = max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48));
+  return __int_as_float(max(a, b));
 }
 
 // sum over the threads of a workgroup of nw waves; red = LDS scratch of >= nw floats.
@@ -537,6 +552,216 @@ struct GemvStream {
 };
 
 // ------------------------------------------------------------------------------------------
+// Batch-1 int8 GEMV over integer digits of the input
+// ------------------------------------------------------------------------------------------
+// The staged input x (K fp32 values in LDS) is rounded once per task to fixed-point integers
+// X_k = rint(x_k 2^(22-e)), with 2^e > max|x| so that |X_k| <= 2^22, and each X_k is split into
+// balanced base-256 digits X = 65536 d2 + 256 d1 + d0, every digit in [-128, 127]. A row's dot
+// product with its int8 weights q is then three exact int32 sums A_p = sum_k q_k d_p,k (v_dot4:
+// four int8 products per instruction, no conversion of the weights) and
+//   sum_k q_k x_k  ~=  2^(e-22) (65536 A2 + 256 A1 + A0),
+// where |x_k - X_k 2^(e-22)| <= 2^(e-23) <= 2^-22 max|x|: the input is rounded 14 bits finer
+// than bf16. |A_p| <= 128 * 127 * K stays within int32 for K <= 2^17.
+// LDS layout, unit-interleaved: unit u (elements 16u .. 16u+15) holds d2[16], d1[16], d0[16] at
+// byte 48u, so a lane's three 16-byte reads share one address and lanes 48 bytes apart fall on
+// distinct banks; unit K/16 is all zero, and lanes past a row's end read it. The digits overwrite
+// the fp32 input (3K + 48 <= 4K bytes); every thread holds its share in registers across a barrier
+// before any digit is written, which bounds K by kDigitMaxK.
+constexpr int kDigitRedSlot = kRedFloats - kWaves;  // red[] floats that hold the per-wave maxima
+
+// The digit scale from the per-wave maxima of |x| in red (published before a barrier): returns
+// 2^(22-e), the factor that takes x to its digit integer.
+__device__ __forceinline__ float digit_up(const float *red, int *e_out) {
+  const AMK_LDS float *rm = (const AMK_LDS float *)red + kDigitRedSlot;
+  float top = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) top = fmaxf(top, rm[w]);
+  int e;
+  frexpf(top, &e);  // top < 2^e (top = 0: e = 0)
+  *e_out = e;
+  return ldexpf(1.0f, 22 - e);
+}
+// The digits of four consecutive elements 4i .. 4i+3 into the digit layout.
+__device__ __forceinline__ void put_digits(float *xs, int i, float a, float b, float c, float d,
+                                           float up) {
+  const float f[4] = {a, b, c, d};
+  uint32_t w2 = 0, w1 = 0, w0 = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int X = (int)rintf(f[k] * up);
+    const int d0 = (int)(int8_t)(X & 0xff);
+    const int X1 = (X - d0) >> 8;  // exact: X - d0 is a multiple of 256
+    const int d1 = (int)(int8_t)(X1 & 0xff);
+    const int d2 = (X1 - d1) >> 8;  // |d2| <= 65
+    w0 |= (uint32_t)(d0 & 0xff) << (8 * k);
+    w1 |= (uint32_t)(d1 & 0xff) << (8 * k);
+    w2 |= (uint32_t)(d2 & 0xff) << (8 * k);
+  }
+  AMK_LDS uint32_t *p = (AMK_LDS uint32_t *)((AMK_LDS uint8_t *)xs + 48 * (i >> 2) + 4 * (i & 3));
+  p[0] = w2;
+  p[4] = w1;
+  p[8] = w0;
+}
+__device__ __forceinline__ void put_zero_unit(float *xs, int K) {
+  if (threadIdx.x < 12) ((AMK_LDS uint32_t *)((AMK_LDS uint8_t *)xs + 48 * (K >> 4)))[threadIdx.x] = 0u;
+}
+
+// In place, for an input already staged as fp32 in xs: returns 2^(e-22), the weight of one unit
+// of the digit integers.
+__device__ __forceinline__ float stage_digits(float *xs, int K, float *red) {
+  constexpr int R = kDigitMaxK / 4 / kThreads;
+  const int n4 = K >> 2;
+  const AMK_LDS u32x4_t *x4 = (const AMK_LDS u32x4_t *)xs;
+  float4 v[R];
+  float mx = 0.f;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int i = (int)threadIdx.x + j * kThreads;
+    v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < n4) {
+      const u32x4_t r = x4[i];
+      v[j] = make_float4(__uint_as_float(r.x), __uint_as_float(r.y), __uint_as_float(r.z),
+                         __uint_as_float(r.w));
+    }
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+  }
+  mx = wave_max_nonneg(mx);
+  if (lane_id() == 0) ((AMK_LDS float *)red)[kDigitRedSlot + wave_id()] = mx;
+  __syncthreads();
+  int e;
+  const float up = digit_up(red, &e);
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int i = (int)threadIdx.x + j * kThreads;
+    if (i < n4) put_digits(xs, i, v[j].x, v[j].y, v[j].z, v[j].w, up);
+  }
+  put_zero_unit(xs, K);
+  __syncthreads();
+  return ldexpf(1.0f, e - 22);
+}
+
+// The int8 stream itself: the same per-wave chunks, register double buffering and LDS prefetch as
+// GemvStream, with RPC rows per chunk. RPC = 1: a row is nch chunks and lanes past its end read
+// the zero digit unit. RPC > 1 (rows of exactly 64 * kChunkUnits / RPC units, e.g. K = 4096 with
+// RPC = 2): unit slot j of a lane belongs to row slot j / UPL, so no chunk is half empty.
+template <int RPC>
+struct GemvStreamI8 {
+  static constexpr int UPL = kChunkUnits / RPC;  // units per lane per row in one chunk
+  const uint8_t *W;
+  int K, r0, nw, n16, nch, S, rows_w;
+  int wave, lane;
+
+  __device__ __forceinline__ void init(const void *w, int k, int a, int b, int nwaves) {
+    W = static_cast<const uint8_t *>(w);
+    K = k;
+    r0 = a;
+    nw = nwaves;
+    wave = __builtin_amdgcn_readfirstlane(wave_id());
+    lane = lane_id();
+    n16 = K / 16;
+    nch = RPC == 1 ? (n16 + 64 * kChunkUnits - 1) / (64 * kChunkUnits) : 1;
+    const int n = b - a;
+    rows_w = (n > wave) ? (n - wave + nw - 1) / nw : 0;
+    S = RPC == 1 ? rows_w * nch : (rows_w + RPC - 1) / RPC;
+  }
+  // index, in this wave's row list, of row slot q of chunk s, and the row an index names (an
+  // index past the wave's last row re-reads that row; its result is dropped)
+  __device__ __forceinline__ int slot_idx(int s, int q) const { return RPC == 1 ? s / nch : s * RPC + q; }
+  __device__ __forceinline__ int row_at(int i) const { return r0 + wave + min(i, rows_w - 1) * nw; }
+  __device__ __forceinline__ int unit_of(int s, int j) const {
+    return RPC == 1 ? (s % nch) * 64 * kChunkUnits + lane + 64 * j : lane + 64 * (j % UPL);
+  }
+  __device__ __forceinline__ const uint4 *unit_ptr(int s, int j) const {
+    const int row = row_at(slot_idx(s, j / UPL));
+    return reinterpret_cast<const uint4 *>(W + (int64_t)row * K) + min(unit_of(s, j), n16 - 1);
+  }
+  __device__ __forceinline__ void load(uint4 (&buf)[kChunkUnits], int s) const {
+#pragma unroll
+    for (int j = 0; j < kChunkUnits; ++j) buf[j] = load_nt(unit_ptr(s, j));
+  }
+  __device__ __forceinline__ void load_lds(int s, uint4 *dst) const {
+#pragma unroll
+    for (int j = 0; j < kChunkUnits; ++j)
+      __builtin_amdgcn_global_load_lds((const AMK_GAS void *)unit_ptr(s, j),
+                                       (AMK_LDS void *)(dst + j * 64), 16, 0, kCachePolicyNt);
+  }
+  __device__ __forceinline__ void consume(const uint4 (&buf)[kChunkUnits], int s, int (&acc)[RPC][3],
+                                          const uint8_t *xd, float sx, float *ys,
+                                          const float *scale) const {
+#pragma unroll
+    for (int j = 0; j < kChunkUnits; ++j) {
+      const int q = j / UPL;
+      const int u = unit_of(s, j);
+      const AMK_LDS u32x4_t *dp =
+          (const AMK_LDS u32x4_t *)((const AMK_LDS uint8_t *)xd + 48 * (RPC == 1 ? min(u, n16) : u));
+      const u32x4_t d2 = dp[0], d1 = dp[1], d0 = dp[2];
+      const uint4 w = buf[j];
+      acc[q][0] = __builtin_amdgcn_sdot4((int)w.x, (int)d2.x, acc[q][0], false);
+      acc[q][1] = __builtin_amdgcn_sdot4((int)w.x, (int)d1.x, acc[q][1], false);
+      acc[q][2] = __builtin_amdgcn_sdot4((int)w.x, (int)d0.x, acc[q][2], false);
+      acc[q][0] = __builtin_amdgcn_sdot4((int)w.y, (int)d2.y, acc[q][0], false);
+      acc[q][1] = __builtin_amdgcn_sdot4((int)w.y, (int)d1.y, acc[q][1], false);
+      acc[q][2] = __builtin_amdgcn_sdot4((int)w.y, (int)d0.y, acc[q][2], false);
+      acc[q][0] = __builtin_amdgcn_sdot4((int)w.z, (int)d2.z, acc[q][0], false);
+      acc[q][1] = __builtin_amdgcn_sdot4((int)w.z, (int)d1.z, acc[q][1], false);
+      acc[q][2] = __builtin_amdgcn_sdot4((int)w.z, (int)d0.z, acc[q][2], false);
+      acc[q][0] = __builtin_amdgcn_sdot4((int)w.w, (int)d2.w, acc[q][0], false);
+      acc[q][1] = __builtin_amdgcn_sdot4((int)w.w, (int)d1.w, acc[q][1], false);
+      acc[q][2] = __builtin_amdgcn_sdot4((int)w.w, (int)d0.w, acc[q][2], false);
+    }
+    if (RPC > 1 || s % nch == nch - 1) {
+#pragma unroll
+      for (int q = 0; q < RPC; ++q) {
+        const int i = slot_idx(s, q);
+        float v = fmaf((float)acc[q][0], 65536.0f, fmaf((float)acc[q][1], 256.0f, (float)acc[q][2]));
+        v = wave_sum(v);
+        if (lane == 0 && i < rows_w) {
+          const int row = row_at(i);
+          ys[row - r0] = v * sx * gld(&scale[row]);
+        }
+        acc[q][0] = acc[q][1] = acc[q][2] = 0;
+      }
+    }
+  }
+  // as GemvStream::run_pf: chunk 0 in this wave's LDS slot pf, chunk 1 in P
+  __device__ __forceinline__ void run_pf(const uint4 *pf, const uint4 (&P)[kChunkUnits],
+                                         const uint8_t *xd, float sx, float *ys,
+                                         const float *scale) const {
+    if (S == 0) return;
+    int acc[RPC][3];
+#pragma unroll
+    for (int q = 0; q < RPC; ++q) acc[q][0] = acc[q][1] = acc[q][2] = 0;
+    uint4 A[kChunkUnits], Bf[kChunkUnits];
+    if (S > 2) {
+      load(A, 2);
+      __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
+#pragma unroll
+    for (int j = 0; j < kChunkUnits; ++j) Bf[j] = pf[j * 64 + lane];
+    consume(Bf, 0, acc, xd, sx, ys, scale);
+    if (S == 1) return;
+    consume(P, 1, acc, xd, sx, ys, scale);
+    if (S == 2) return;
+    int s = 2;
+    for (; s + 2 < S; s += 2) {
+      load(Bf, s + 1);
+      consume(A, s, acc, xd, sx, ys, scale);
+      load(A, s + 2);
+      consume(Bf, s + 1, acc, xd, sx, ys, scale);
+    }
+    if (s + 1 < S) {
+      load(Bf, s + 1);
+      consume(A, s, acc, xd, sx, ys, scale);
+      consume(Bf, s + 1, acc, xd, sx, ys, scale);
+    } else {
+      consume(A, s, acc, xd, sx, ys, scale);
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------------------
 // input staging (LDS)
 // ------------------------------------------------------------------------------------------
 // token of sequence b, validated (an out-of-range id is recorded as a device error and read as 0)
@@ -652,17 +877,24 @@ __device__ __forceinline__ uint32_t tag_word(float v, uint32_t epoch) {
 // tag matches `epoch`; with a gain the per-wave sums of v^2 go to red[wave]. Each thread owns up
 // to eight 16-byte units per round and reloads only those whose tags were stale. Returns false
 // after a timeout (recorded as a device error) or when the abort word is set.
+// DIGITS: the input of a batch-1 int8 GEMV. The values stay in registers until all have arrived
+// (one round: n <= kDigitMaxK), then go to LDS as integer digits (see stage_digits) instead of
+// fp32; *sx receives the weight of one digit unit.
+template <bool DIGITS>
 __device__ bool stage_tagged(const DevModel &m, const uint32_t *src, int n, const uint16_t *gain,
-                             uint32_t epoch, float *xs, float *red, uint32_t task) {
+                             uint32_t epoch, float *xs, float *red, uint32_t task,
+                             float *sx = nullptr) {
   constexpr int V = 8;
+  static_assert(!DIGITS || kDigitMaxK <= 4 * V * kThreads, "digit staging takes one round");
   const int nu = n >> 2;
   const uint32_t tag = epoch & kTagMask;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)n * 4u);
   uint32_t *const err = m.err;  // read here, in uniform code, so they come from scalar loads
   const uint64_t tmo = m.timeout_ticks;
-  float ss = 0.f;
+  float ss = 0.f, mx = 0.f;
   uint64_t t0 = 0;
   uint32_t spins = 0;
+  u32x4_t keep[DIGITS ? V : 1];  // DIGITS: the staged values, until all have arrived
   for (int base = 0; base < nu; base += V * kThreads) {
     uint32_t need = 0;
 #pragma unroll
@@ -703,7 +935,13 @@ __device__ bool stage_tagged(const DevModel &m, const uint32_t *src, int n, cons
               c *= bf_lo(g.y);
               d *= bf_hi(g.y);
             }
-            *reinterpret_cast<float4 *>(xs + 4 * u) = make_float4(a, b, c, d);
+            if constexpr (DIGITS) {
+              mx = fmaxf(mx, fmaxf(fmaxf(fabsf(a), fabsf(b)), fmaxf(fabsf(c), fabsf(d))));
+              keep[j] = u32x4_t{__float_as_uint(a), __float_as_uint(b), __float_as_uint(c),
+                                __float_as_uint(d)};
+            } else {
+              *reinterpret_cast<float4 *>(xs + 4 * u) = make_float4(a, b, c, d);
+            }
           }
         }
       }
@@ -719,7 +957,25 @@ __device__ bool stage_tagged(const DevModel &m, const uint32_t *src, int n, cons
     ss = wave_sum(ss);
     if (lane_id() == 0) *(AMK_LDS float *)(red + wave_id()) = ss;
   }
+  if constexpr (DIGITS) {
+    mx = wave_max_nonneg(mx);
+    if (lane_id() == 0) ((AMK_LDS float *)red)[kDigitRedSlot + wave_id()] = mx;
+  }
   __syncthreads();
+  if constexpr (DIGITS) {
+    int e;
+    const float up = digit_up(red, &e);
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int u = (int)threadIdx.x + j * kThreads;
+      if (u < nu)
+        put_digits(xs, u, __uint_as_float(keep[j].x), __uint_as_float(keep[j].y),
+                   __uint_as_float(keep[j].z), __uint_as_float(keep[j].w), up);
+    }
+    put_zero_unit(xs, n);
+    __syncthreads();
+    *sx = ldexpf(1.0f, e - 22);
+  }
   return true;
 }
 
@@ -1096,7 +1352,7 @@ __device__ void epi_logits(const DevModel &m, const StepArgs &s, int r0, int r1,
 }
 
 // next[b] = argmax over the LM tiles' partials (value desc, index asc); one wave.
-__device__ void argmax_combine(const DevModel &m, const StepArgs &s, int n_slots) {
+__device__ __forceinline__ void argmax_combine(const DevModel &m, const StepArgs &s, int n_slots) {
   if (wave_id() != 0) return;
   for (int b = 0; b < s.batch; ++b) {
     float best = -INFINITY;
@@ -1437,7 +1693,7 @@ __device__ __forceinline__ bool attn_task(const DevModel &m, const StepArgs &s, 
 // are waited on first. The merger's own partial is read back like the others once its stores
 // are complete. Each thread merges whole output elements, eight blocks' loads at a time.
 template <bool TAGGED>
-__device__ bool attn_merge(const DevModel &m, const StepArgs &s, const Task &t, int *abort_slot) {
+__device__ __forceinline__ bool attn_merge(const DevModel &m, const StepArgs &s, const Task &t, int *abort_slot) {
   const int l = t.layer, g = (int)t.a0;
   if constexpr (!TAGGED) {
     Task others = t;  // the group's other blocks (the QKV tiles were waited on for the partial)

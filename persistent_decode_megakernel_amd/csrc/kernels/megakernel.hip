@@ -24,12 +24,85 @@ __device__ __forceinline__ Task prev_step(const DevModel &m, const Task &t) {
   return w;
 }
 
+// Batch-1 staging of an int8 GEMV's input from its epoch-tagged producer words (which doubles as
+// the dependency wait; the first layer's QKV tiles read the embedding and have no producer): the
+// input goes to LDS as integer digits and *sx receives their unit weight.
+__device__ __forceinline__ bool stage_b1_digits(const DevModel &m, const StepArgs &s, const Task &t,
+                                                int K, float *xs, float *red, float *sx) {
+  const int l = t.layer;
+  switch (t.mat) {
+    case M_QKV:
+      if (l == 0) {
+        stage_norm(m, s, 0, gld(&m.layers[0].attn_norm), xs, red, kWaves);
+        *sx = stage_digits(xs, K, red);
+        return true;
+      }
+      return stage_tagged<true>(m, m.ht + (int64_t)2 * l * m.d, m.d, gld(&m.layers[l].attn_norm),
+                                  s.epoch, xs, red, t.id, sx);
+    case M_O:
+      return stage_tagged<true>(m, m.aot + (int64_t)l * m.qd, m.qd, nullptr, s.epoch, xs, red,
+                                  t.id, sx);
+    case M_GU:
+      return stage_tagged<true>(m, m.ht + (int64_t)(2 * l + 1) * m.d, m.d,
+                                  gld(&m.layers[l].mlp_norm), s.epoch, xs, red, t.id, sx);
+    case M_D:
+      return stage_tagged<true>(m, m.at + (int64_t)l * m.F, m.F, nullptr, s.epoch, xs, red, t.id,
+                                  sx);
+    default:
+      return stage_tagged<true>(m, m.ht + (int64_t)2 * m.L * m.d, m.d, m.final_norm, s.epoch, xs,
+                                  red, t.id, sx);
+  }
+}
+
+// Batch-1 int8 GEMV body: as the bf16 body in gemv_task, with one of two stream shapes (SA rows
+// longer than half a chunk, SB two rows per chunk) and the input staged as digits.
+template <class SA, class SB>
+__device__ __forceinline__ bool gemv_b1_i8(const DevModel &m, const StepArgs &s, const Task &t,
+                                           const void *W, const float *scale, int K, bool use_b,
+                                           float *xs, float *ys, float *red, uint4 *pf,
+                                           int *abort_slot) {
+  SA sa;
+  SB sb;
+  uint4 P[kChunkUnits];
+  uint4 *slot;
+  if (use_b) {
+    sb.init(W, K, (int)t.a0, (int)t.a1, kWaves);
+    slot = pf + sb.wave * (64 * kChunkUnits);
+  } else {
+    sa.init(W, K, (int)t.a0, (int)t.a1, kWaves);
+    slot = pf + sa.wave * (64 * kChunkUnits);
+  }
+  const bool tagged = !(t.mat == M_QKV && t.layer == 0);
+  if (!tagged) wait_poll(m, s.step > 0 ? prev_step(m, t) : t, s.epoch - (s.step > 0), abort_slot);
+  if (use_b) {
+    if (sb.S > 0) sb.load_lds(0, slot);
+    if (sb.S > 1) sb.load(P, 1);
+  } else {
+    if (sa.S > 0) sa.load_lds(0, slot);
+    if (sa.S > 1) sa.load(P, 1);
+  }
+  asm volatile("" ::: "memory");
+  if (!tagged && !wait_join(m, t, abort_slot)) return false;
+  if (m.trace && threadIdx.x == 0) gst(&m.trace[(uint64_t)t.id * 4 + 1], (uint64_t)wall_clock64());
+  float sx = 0.f;
+  if (!stage_b1_digits(m, s, t, K, xs, red, &sx)) {
+    __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS may outlive the workgroup
+    return false;
+  }
+  if (m.trace && threadIdx.x == 0) gst(&m.trace[(uint64_t)t.id * 4 + 2], (uint64_t)wall_clock64());
+  const uint8_t *xd = reinterpret_cast<const uint8_t *>(xs);
+  if (use_b)
+    sb.run_pf(slot, P, xd, sx, ys, scale);
+  else
+    sa.run_pf(slot, P, xd, sx, ys, scale);
+  return true;
+}
+
 // GEMV tile task. Batch 1: the first two weight chunks of every wave (one into its LDS slot, one
 // into registers) are issued at once, then the input is staged from its epoch-tagged producer
-// words (which doubles as the dependency wait; the first layer's QKV tiles read the embedding and
-// have no producer). Batched: a flag wait (wave 0 polls), then the matrix-core GEMV reads its
-// inputs straight from memory. The RMSNorm scale is applied to the outputs and the epilogue writes
-// them (tagged for batch 1).
+// words, which is also the dependency wait (int8: gemv_b1_i8). Batched: a flag wait (wave 0 polls), then the matrix-core GEMV reads its inputs
+// straight from memory. The RMSNorm scale is applied to the outputs and the epilogue writes them
+// (tagged for batch 1).
 template <int WT, bool BATCHED>
 __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, const Task &t,
                                           float *xs, float *ys, float *red, uint4 *pf,
@@ -45,53 +118,62 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
   // cores' partial tiles) follows the model's batch capacity; a smaller step batch runs the
   // batched GEMV with zero columns.
   constexpr bool b1 = !BATCHED;
-  GemvStream<WT> st;
-  uint4 P[kChunkUnits];
-  st.init(W, K, r0, r1, NW);
-  uint4 *slot = pf + st.wave * (64 * kChunkUnits);
   if (b1) {
-    // Batch 1: inputs produced in this step by other tiles are tagged with the epoch, so their
-    // staging loads are the dependency wait (no flags): the weight prefetch is issued at once.
-    const bool tagged = !(t.mat == M_QKV && l == 0);
-    // the first layer's QKV tiles read the token: in a later step of a multi-step launch they
-    // wait for the previous step's argmax (which every task of that step precedes)
-    if (!tagged) wait_poll(m, s.step > 0 ? prev_step(m, t) : t, s.epoch - (s.step > 0), abort_slot);
-    if (st.S > 0) st.load_lds(0, slot);
-    if (st.S > 1) st.load(P, 1);
-    // keep the register prefetch issued here, ahead of the staging loads, not at its first use
-    asm volatile("" ::: "memory");
-    if (!tagged && !wait_join(m, t, abort_slot)) return false;
-    if (m.trace && threadIdx.x == 0) gst(&m.trace[(uint64_t)t.id * 4 + 1], (uint64_t)wall_clock64());
-    bool ok = true;
-    switch (t.mat) {
-      case M_QKV:
-        if (l == 0)
-          stage_norm(m, s, 0, gld(&m.layers[0].attn_norm), xs, red, NW);
-        else
-          ok = stage_tagged(m, m.ht + (int64_t)2 * l * m.d, m.d, gld(&m.layers[l].attn_norm), s.epoch,
-                            xs, red, t.id);
-        break;
-      case M_O:
-        ok = stage_tagged(m, m.aot + (int64_t)l * m.qd, m.qd, nullptr, s.epoch, xs, red, t.id);
-        break;
-      case M_GU:
-        ok = stage_tagged(m, m.ht + (int64_t)(2 * l + 1) * m.d, m.d, gld(&m.layers[l].mlp_norm), s.epoch,
-                          xs, red, t.id);
-        break;
-      case M_D:
-        ok = stage_tagged(m, m.at + (int64_t)l * m.F, m.F, nullptr, s.epoch, xs, red, t.id);
-        break;
-      default:
-        ok = stage_tagged(m, m.ht + (int64_t)2 * m.L * m.d, m.d, m.final_norm, s.epoch, xs, red,
-                          t.id);
-        break;
+    if constexpr (WT == 0) {
+      GemvStream<0> st;
+      uint4 P[kChunkUnits];
+      st.init(W, K, r0, r1, NW);
+      uint4 *slot = pf + st.wave * (64 * kChunkUnits);
+      // inputs produced in this step by other tiles are tagged with the epoch, so their staging
+      // loads are the dependency wait (no flags): the weight prefetch is issued at once
+      const bool tagged = !(t.mat == M_QKV && l == 0);
+      // the first layer's QKV tiles read the token: in a later step of a multi-step launch they
+      // wait for the previous step's argmax (which every task of that step precedes)
+      if (!tagged) wait_poll(m, s.step > 0 ? prev_step(m, t) : t, s.epoch - (s.step > 0), abort_slot);
+      if (st.S > 0) st.load_lds(0, slot);
+      if (st.S > 1) st.load(P, 1);
+      // keep the register prefetch issued here, ahead of the staging loads, not at its first use
+      asm volatile("" ::: "memory");
+      if (!tagged && !wait_join(m, t, abort_slot)) return false;
+      if (m.trace && threadIdx.x == 0) gst(&m.trace[(uint64_t)t.id * 4 + 1], (uint64_t)wall_clock64());
+      bool ok = true;
+      switch (t.mat) {
+        case M_QKV:
+          if (l == 0)
+            stage_norm(m, s, 0, gld(&m.layers[0].attn_norm), xs, red, NW);
+          else
+            ok = stage_tagged<false>(m, m.ht + (int64_t)2 * l * m.d, m.d,
+                                     gld(&m.layers[l].attn_norm), s.epoch, xs, red, t.id);
+          break;
+        case M_O:
+          ok = stage_tagged<false>(m, m.aot + (int64_t)l * m.qd, m.qd, nullptr, s.epoch, xs, red,
+                                   t.id);
+          break;
+        case M_GU:
+          ok = stage_tagged<false>(m, m.ht + (int64_t)(2 * l + 1) * m.d, m.d,
+                                   gld(&m.layers[l].mlp_norm), s.epoch, xs, red, t.id);
+          break;
+        case M_D:
+          ok = stage_tagged<false>(m, m.at + (int64_t)l * m.F, m.F, nullptr, s.epoch, xs, red, t.id);
+          break;
+        default:
+          ok = stage_tagged<false>(m, m.ht + (int64_t)2 * m.L * m.d, m.d, m.final_norm, s.epoch, xs,
+                                   red, t.id);
+          break;
+      }
+      if (!ok) {
+        __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS may outlive the workgroup
+        return false;
+      }
+      if (m.trace && threadIdx.x == 0) gst(&m.trace[(uint64_t)t.id * 4 + 2], (uint64_t)wall_clock64());
+      st.run_pf(slot, P, xs, ys, scale);
+    } else {
+      // int8 rows of 256 units (K = 4096) fill half a chunk: two rows per chunk
+      if (!gemv_b1_i8<GemvStreamI8<1>, GemvStreamI8<2>>(m, s, t, W, scale, K,
+                                                        K == 16 * 32 * kChunkUnits, xs, ys, red,
+                                                        pf, abort_slot))
+        return false;
     }
-    if (!ok) {
-      __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS may outlive the workgroup
-      return false;
-    }
-    if (m.trace && threadIdx.x == 0) gst(&m.trace[(uint64_t)t.id * 4 + 2], (uint64_t)wall_clock64());
-    st.run_pf(slot, P, xs, ys, scale);
   } else {
     // batched: inputs straight from memory into the matrix cores (RMSNorm scale applied after)
     BatchInput in{nullptr, m.d, nullptr, nullptr, true};

@@ -43,6 +43,9 @@ bool config_ok(const amk_config &c, std::string *err) {
     return fail("config: int8 weights with a tied LM head are unsupported");
   if (c.wtype == AMK_WT_INT8 && (c.hidden % 16 || c.ffn % 16))
     return fail("config: int8 weights need hidden and ffn multiples of 16");
+  if (c.wtype == AMK_WT_INT8 &&
+      std::max(std::max(c.hidden, c.n_heads * c.head_dim), c.ffn) > kDigitMaxK)
+    return fail("config: int8 weights need hidden, n_heads * head_dim and ffn <= 16384");
   if (!(c.rms_eps > 0.f) || !(c.rope_theta > 0.f)) return fail("config: eps/theta must be > 0");
   return true;
 }

@@ -129,6 +129,9 @@ AMK_HD constexpr int32_t attn_chunk_rows(int32_t hd, int32_t qmax) {
   return (hd <= 64 || qmax == 1) ? kAttnRowsPerChunk : 256;
 }
 constexpr int32_t kRedFloats = 2048;        // reduction scratch; holds n_heads x blocks weights
+// Batch-1 int8 GEMV: the staged input is converted in place to integer digits, holding every
+// thread's share in registers; that bounds the input length of an int8 matrix.
+constexpr int32_t kDigitMaxK = 16384;
 
 // Staged GEMV input (batch 1 only: batched GEMVs read their inputs straight from memory and use
 // the region for the partial tiles of the matrix-core reduction instead).

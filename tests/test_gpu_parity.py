@@ -99,6 +99,18 @@ def test_tiny_int8_w8a16(path):
     assert_parity(rep)
 
 
+def test_int8_hidden_4096_two_rows_per_chunk():
+    """W8A16 with hidden 4096 (32 heads of 128, 8 KV heads): batch-1 int8 rows of K = 4096 (QKV, O,
+    gate/up, LM head) run two rows per weight chunk, the down rows (K = 688) one ragged row per
+    chunk; the input goes to the integer dot products as digits. Random norm gains widen the
+    input's range."""
+    cfg = synth.get_config("tiny").replace(wtype="int8", hidden=4096, n_heads=32, n_kv_heads=8,
+                                           head_dim=128)
+    rep = teacher_forced(cfg, "megakernel", seed=6, n_calls=12, random_gains=True)
+    log(f"int8 hidden 4096: {rep}")
+    assert_parity(rep)
+
+
 @pytest.mark.parametrize("path", ["megakernel", "unfused"])
 def test_tiny_batch3(path):
     """Three independent sequences sharing the weights and the position."""
