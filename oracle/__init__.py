@@ -9,8 +9,10 @@ bf16_to_float, Decoder.step (brute-force full recompute, closed forms, GQA/int8/
 an independent torch forward). The full-size end-to-end logits are "parity unpinned" by any
 closed form: the pinned pieces plus brute force on small shapes are what pin them.
 """
-from .decoder import (Decoder, apply_rope, argmax_lowest, attend, bf16_to_float, float_to_bf16,
+from .decoder import (Decoder, apply_rope, argmax_lowest, attend, bf16_to_float, dequant_int4,
+                      float_to_bf16, unpack_int4,
                       rmsnorm, rope_cos_sin, silu, softmax, top2_margin)
 
-__all__ = ["Decoder", "apply_rope", "argmax_lowest", "attend", "bf16_to_float", "float_to_bf16",
+__all__ = ["Decoder", "apply_rope", "argmax_lowest", "attend", "bf16_to_float", "dequant_int4",
+           "float_to_bf16", "unpack_int4",
            "rmsnorm", "rope_cos_sin", "silu", "softmax", "top2_margin"]

@@ -14,7 +14,13 @@ What is computed, and where it comes from:
     greedy argmax with ties broken towards the lowest index.
 
 Precision: computed in float64 by default (float32 on request). Weights are read exactly from
-their bfloat16 / int8 bit patterns. The only rounding the method itself fixes is the bf16 KV
+their bfloat16 / int8 / packed int4 bit patterns.
+
+W4A16 (the Ada-MK technical summary, "Key Contributions" item 4 and "Experimental Results", names
+GPTQ-W4A16 and nothing of its format): read here as symmetric 4-bit integers q in [-8, 7] with
+one float32 scale per output row and group of G consecutive inputs, W[o, i] = s[o, i // G] *
+q[o, i]; activations stay floating point. Storage: uint8 [out, in / 2], element 2j in the low
+nibble of byte j and 2j + 1 in the high nibble, each nibble two's complement. The only rounding the method itself fixes is the bf16 KV
 cache: newly appended K/V rows are rounded to bf16 (round-to-nearest-even) before they are
 stored, exactly as a bf16 cache holds them. RoPE angles are always formed in float64.
 
@@ -53,6 +59,29 @@ def float_to_bf16(x: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------------------------
 # operators
 # --------------------------------------------------------------------------------------------
+def unpack_int4(packed: np.ndarray) -> np.ndarray:
+    """uint8 [out, in / 2] -> int8 [out, in]: byte j holds elements 2j (low nibble) and 2j + 1
+    (high nibble), each a 4-bit two's complement integer."""
+    p = np.asarray(packed, dtype=np.uint8)
+    lo = (p & 0xF).astype(np.int8)
+    hi = (p >> 4).astype(np.int8)
+    lo = np.where(lo >= 8, lo - 16, lo).astype(np.int8)
+    hi = np.where(hi >= 8, hi - 16, hi).astype(np.int8)
+    out = np.empty((p.shape[0], 2 * p.shape[1]), dtype=np.int8)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    return out
+
+
+def dequant_int4(packed: np.ndarray, scales: np.ndarray, group: int, dtype=np.float64) -> np.ndarray:
+    """W[o, i] = scales[o, i // group] * q[o, i] (exact in float64: a 4-bit integer times a
+    float32)."""
+    q = unpack_int4(packed).astype(dtype)
+    sc = np.asarray(scales, dtype=np.float32).astype(dtype)
+    assert sc.shape == (q.shape[0], q.shape[1] // group)
+    return q * np.repeat(sc, group, axis=1)
+
+
 def rmsnorm(r: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
     """y_i = g_i * r_i / sqrt(mean_j(r_j^2) + eps); the mean runs over the last axis."""
     ms = np.mean(r * r, axis=-1, keepdims=True)
@@ -114,13 +143,14 @@ class Decoder:
     """A Llama-style decoder given as raw weight bytes.
 
     params: dict with n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab, rms_eps,
-            rope_theta, int8 (bool).
+            rope_theta, int8 (bool), int4 (bool), group (int4 inputs per scale group).
     weights: dict with
         embed [V, d] bf16 bits; final_norm [d] bf16 bits;
-        lm_head [V, d] (bf16 bits, or int8 when int8) or None when tied to the embedding;
-        lm_head_scale [V] float32 (int8 only);
-        layers: list of dicts wq wk wv wo wg wu wd ([out, in]; bf16 bits or int8),
-                sq sk sv so sg su sd (float32 [out], int8 only), attn_norm, mlp_norm (bf16 bits).
+        lm_head [V, d] (bf16 bits, int8, or packed int4 [V, d / 2]) or None when tied to the
+        embedding; lm_head_scale [V] float32 (int8) or [V, d / group] (int4);
+        layers: list of dicts wq wk wv wo wg wu wd ([out, in]; bf16 bits or int8; int4: packed
+                uint8 [out, in / 2]), sq sk sv so sg su sd (float32 [out] for int8,
+                [out, in / group] for int4), attn_norm, mlp_norm (bf16 bits).
     """
 
     def __init__(self, params: Dict, weights: Dict, dtype=np.float64,
@@ -133,10 +163,14 @@ class Decoder:
 
     # weights in the compute dtype -----------------------------------------------------------
     def _mat(self, key, bits: np.ndarray, scale: Optional[np.ndarray]):
-        """Return (matrix, scale) in the compute dtype; int8 values convert exactly."""
+        """Return (matrix, scale) in the compute dtype; int8 values convert exactly; int4 matrices
+        are dequantised with their group scales (the returned scale is then None)."""
         if key in self._cache:
             return self._cache[key]
-        if bits.dtype == np.int8:
+        if bits.dtype == np.uint8:
+            m = dequant_int4(bits, scale, int(self.p["group"]), self.dtype)
+            sc = None
+        elif bits.dtype == np.int8:
             m = bits.astype(self.dtype)
             sc = np.asarray(scale, dtype=np.float32).astype(self.dtype)
         else:

@@ -89,6 +89,12 @@ MUTATIONS = {
     "final norm skipped": ("x = rmsnorm(r, self._vec(w[\"final_norm\"]), eps)", "x = r"),
     "square weight transposed": ("y = x @ m.T", "y = x @ (m if m.shape[0] == m.shape[1] else m.T)"),
     "int8 scale dropped": ("y = y * sc", "y = y"),
+    "int4 nibbles swapped": ("out[:, 0::2] = lo\n    out[:, 1::2] = hi", "out[:, 0::2] = hi\n    out[:, 1::2] = lo"),
+    "int4 not sign extended": ("lo = np.where(lo >= 8, lo - 16, lo).astype(np.int8)", "lo = lo"),
+    "int4 groups interleaved": ("return q * np.repeat(sc, group, axis=1)",
+                                "return q * np.tile(sc, (1, group))"),
+    "int4 group too wide": ("return q * np.repeat(sc, group, axis=1)",
+                            "return q * np.repeat(np.repeat(sc[:, ::2], 2, axis=1), group, axis=1)"),
     "argmax highest tie": ("return np.argmax(logits, axis=-1).astype(np.int32)",
                            "return (logits.shape[-1] - 1 - np.argmax(logits[..., ::-1], axis=-1)).astype(np.int32)"),
     "bf16 truncation": ("rounded = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)",
@@ -108,6 +114,15 @@ def test_mutation_is_caught(name):
         a = pins._incremental(params, wn, [1, 2, 3], kv, 0, mod=m)
         b = pins.brute_force_logits(params, wn, [1, 2, 3])
         assert np.max(np.abs(a - b)) > 1e-6
+        return
+    if name.startswith("int4"):
+        m = mutant(old, new)
+        ok = True
+        try:
+            ok = pins.pin_int4(m) and pins.pin_int4_brute_force(m) < 1e-12
+        except Exception:
+            ok = False
+        assert not ok
         return
     if name == "bf16 truncation":
         m = mutant(old, new)

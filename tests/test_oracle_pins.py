@@ -179,6 +179,27 @@ def _bf16_round(x):
     return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).double().numpy()
 
 
+def _nibbles(packed):
+    """Signed 4-bit values of a packed [out, in / 2] byte array, element by element: byte j of a
+    row holds element 2j in its low and 2j + 1 in its high nibble."""
+    rows, half = packed.shape
+    out = np.zeros((rows, 2 * half), dtype=np.int64)
+    for o in range(rows):
+        for j in range(half):
+            b = int(packed[o, j])
+            for k, nib in enumerate((b & 15, b >> 4)):
+                out[o, 2 * j + k] = nib - 16 if nib >= 8 else nib
+    return out
+
+
+def _int4_dense(packed, scales, group):
+    """Dense float64 matrix of an int4 weight, one scale group (a column block) at a time."""
+    q = _nibbles(packed).astype(np.float64)
+    for g in range(q.shape[1] // group):
+        q[:, g * group:(g + 1) * group] *= np.asarray(scales, np.float64)[:, g:g + 1]
+    return q
+
+
 def brute_force_logits(params, w, tokens, prefill_k=None, prefill_v=None):
     """Logits at every fed position, recomputing the whole prefix (no cache).
     prefill_k/v: [L][n_kv][P][hd] values taken as already-rotated keys and plain values."""
@@ -195,6 +216,8 @@ def brute_force_logits(params, w, tokens, prefill_k=None, prefill_v=None):
 
     def mat(lw, m):
         W = lw[m]
+        if W.dtype == np.uint8:
+            return _int4_dense(W, lw["s" + m[1]], params["group"])
         if W.dtype == np.int8:
             return W.astype(np.float64) * lw["s" + m[1]].astype(np.float64)[:, None]
         return f(W)
@@ -236,6 +259,8 @@ def brute_force_logits(params, w, tokens, prefill_k=None, prefill_v=None):
     X = norm(R, w["final_norm"])
     if w.get("lm_head") is None:
         lm = f(w["embed"])
+    elif w["lm_head"].dtype == np.uint8:
+        lm = _int4_dense(w["lm_head"], w["lm_head_scale"], params["group"])
     elif w["lm_head"].dtype == np.int8:
         lm = w["lm_head"].astype(np.float64) * w["lm_head_scale"].astype(np.float64)[:, None]
     else:
@@ -343,6 +368,76 @@ def test_p8_int8_equals_dequantised():
     kv = np.zeros((2, 2, 1, 1, 3, 32), np.uint16)
     a = _incremental(params, wn, toks, kv, 0)
     b = brute_force_logits(params, wn, toks)  # dequantises as s_o * Q_oi up front
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
+# ---------------------------------------------------------------------------------------------
+# P12 W4A16: unpacking and group scales by a hand-computed example, the decoder against the brute
+# force (its own per-group dequantisation), and W4A16 with one scale per row == W8A16
+# ---------------------------------------------------------------------------------------------
+def pin_int4(mod=od):
+    # row 0: q = [1, -1, 2, 3] -> bytes 0xF1 (1, -1), 0x32 (2, 3); row 1: q = [-8, 7, 0, -2] ->
+    # bytes 0x78 (-8, 7), 0xE0 (0, -2); groups of 2 inputs: scales [[0.5, 2], [4, 0.25]]
+    packed = np.array([[0xF1, 0x32], [0x78, 0xE0]], dtype=np.uint8)
+    if list(mod.unpack_int4(packed).ravel()) != [1, -1, 2, 3, -8, 7, 0, -2]:
+        return False
+    W = mod.dequant_int4(packed, np.array([[0.5, 2.0], [4.0, 0.25]], np.float32), 2)
+    return np.array_equal(W, np.array([[0.5, -0.5, 4.0, 6.0], [-32.0, 28.0, 0.0, -0.5]]))
+
+
+def test_p12_int4_known_answer():
+    assert pin_int4()
+    # every byte value: the low nibble is element 2j, the high nibble element 2j + 1
+    allb = np.arange(256, dtype=np.uint8)[None, :]
+    q = od.unpack_int4(allb)
+    assert np.array_equal(q, _nibbles(allb))
+    assert q.min() == -8 and q.max() == 7
+
+
+def pin_int4_brute_force(mod=od, seed=8):
+    cfg = synth.micro_config(L=2, d=64, nq=4, nkv=2, hd=16, F=96, V=100, wtype="int4", group=32)
+    w = synth.make_weights(cfg, seed)
+    params, wn = synth.oracle_inputs(w)
+    toks = [5, 17, 99, 0]
+    kv = np.zeros((2, 2, 1, 2, len(toks), 16), np.uint16)
+    a = _incremental(params, wn, toks, kv, 0, mod=mod)
+    b = brute_force_logits(params, wn, toks)
+    return float(np.max(np.abs(a - b)))
+
+
+def test_p12_int4_decoder_equals_brute_force():
+    assert pin_int4_brute_force() < 1e-12
+
+
+def test_p12_int4_with_row_scales_equals_int8():
+    """Every group of a row given the same scale: W4A16 reduces to W8A16 with the same integers
+    and that per-row scale (the int8 path is pinned against the brute force by P8)."""
+    cfg4 = synth.micro_config(L=2, d=64, nq=2, nkv=1, hd=32, F=96, V=128, wtype="int4", group=16)
+    w = synth.make_weights(cfg4, 9)
+    params4, wn4 = synth.oracle_inputs(w)
+    params8 = dict(params4, int4=False, int8=True, group=0)
+
+    def to_row_scales(packed, sc):
+        row = np.asarray(sc, np.float32)[:, :1]
+        return np.repeat(row, sc.shape[1], axis=1), _nibbles(packed).astype(np.int8), row[:, 0].copy()
+
+    layers4, layers8 = [], []
+    for lw in wn4["layers"]:
+        l4, l8 = dict(lw), dict(lw)
+        for m in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+            s4, q8, s8 = to_row_scales(lw[m], lw["s" + m[1]])
+            l4["s" + m[1]] = s4
+            l8[m], l8["s" + m[1]] = q8, s8
+        layers4.append(l4)
+        layers8.append(l8)
+    s4, q8, s8 = to_row_scales(wn4["lm_head"], wn4["lm_head_scale"])
+    wa = dict(wn4, layers=layers4, lm_head_scale=s4)
+    wb = dict(wn4, layers=layers8, lm_head=q8, lm_head_scale=s8)
+    toks = [3, 70, 12]
+    kv1 = np.zeros((2, 2, 1, 1, 3, 32), np.uint16)
+    kv2 = kv1.copy()
+    a = _incremental(params4, wa, toks, kv1, 0)
+    b = _incremental(params8, wb, toks, kv2, 0)
     assert np.max(np.abs(a - b)) < 1e-12
 
 
