@@ -219,7 +219,8 @@ def main():
 
     ms, per, info, ids = time_path(cfg, weights, kv_host, "megakernel", steps, warmup)
     hd_q = 1 if cfg.n_heads // cfg.n_kv_heads <= 1 else (2 if cfg.n_heads // cfg.n_kv_heads <= 2 else 4)
-    kname = (f"amk_megakernel_w{1 if cfg.wtype == 'int8' else 0}_h{cfg.head_dim}_q{hd_q}"
+    wt = {"bf16": 0, "int8": 1, "int4": 2}[cfg.wtype]
+    kname = (f"amk_megakernel_w{wt}_h{cfg.head_dim}_q{hd_q}"
              + ("_b" if cfg.batch > 1 else ""))
     traffic_bytes = profiled_traffic(cfg, kname)
     weight_bytes = info.weight_bytes + 2 * cfg.hidden * cfg.batch  # + embedding rows
@@ -240,7 +241,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.wtype == "bf16" else "int8",
+        "dtype": cfg.wtype,
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: {cfg.n_layers} layers, hidden {cfg.hidden}, "

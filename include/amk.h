@@ -42,7 +42,9 @@ typedef enum {
   AMK_E_DEVICE_FAULT = 8        /* the device flagged bad data (e.g. token id out of range) */
 } amk_status;
 
-typedef enum { AMK_WT_BF16 = 0, AMK_WT_INT8 = 1 } amk_wtype;
+/* Weight formats (the Ada-MK technical summary, "Key Contributions" item 4, quantises to GPTQ
+ * W4A16; W8A16 and bf16 are the other two). Activations are floating point in every format. */
+typedef enum { AMK_WT_BF16 = 0, AMK_WT_INT8 = 1, AMK_WT_INT4 = 2 } amk_wtype;
 
 typedef enum {
   AMK_PATH_MEGAKERNEL = 0,  /* one persistent launch per step, frozen per-CU task tables */
@@ -58,19 +60,26 @@ typedef struct {
   int32_t wtype;        /* amk_wtype of the 7 layer matrices and the (untied) LM head */
   int32_t max_batch;    /* largest batch a decode step will be called with */
   int32_t max_seq;      /* largest position + 1 the model will be asked to decode */
+  int32_t group_size;   /* AMK_WT_INT4: inputs per scale group (a multiple of 32 dividing hidden
+                         * and ffn); must be 0 for the other formats */
 } amk_config;
 
 /* Per-layer weights: device pointers, [out, in] row-major. bf16 matrices hold bfloat16 bit
  * patterns; int8 matrices hold int8 values with one float32 scale per output row (s* arrays,
- * NULL for bf16). Norm gains are bfloat16 [hidden]. */
+ * NULL for bf16); int4 matrices are uint8 [out, in / 2], byte j of a row holding input 2j in its
+ * low and 2j + 1 in its high nibble (4-bit two's complement, -8..7), with float32 scales
+ * [out, in / group_size]: W[o][i] = s[o][i / group_size] * q[o][i]. Norm gains are bfloat16
+ * [hidden]. */
 typedef struct {
   const void *wq, *wk, *wv, *wo, *wg, *wu, *wd;
   const float *sq, *sk, *sv, *so, *sg, *su, *sd;
   const void *attn_norm, *mlp_norm;
 } amk_layer_weights;
 
-/* embed: bf16 [vocab, hidden]; final_norm: bf16 [hidden]; lm_head: [vocab, hidden] (bf16, or int8
- * with lm_head_scale [vocab]) or NULL when tied. `layers` is a HOST array of n_layers entries. */
+/* embed: bf16 [vocab, hidden]; final_norm: bf16 [hidden]; lm_head: [vocab, hidden] (bf16, int8
+ * with lm_head_scale [vocab], or int4 packed as above with lm_head_scale
+ * [vocab, hidden / group_size]) or NULL when tied (bf16 only). `layers` is a HOST array of n_layers
+ * entries. */
 typedef struct {
   const void *embed, *final_norm, *lm_head;
   const float *lm_head_scale;

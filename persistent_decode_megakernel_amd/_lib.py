@@ -23,6 +23,7 @@ AMK_E_DEVICE_FAULT = 8
 
 AMK_WT_BF16 = 0
 AMK_WT_INT8 = 1
+AMK_WT_INT4 = 2
 AMK_PATH_MEGAKERNEL = 0
 AMK_PATH_UNFUSED = 1
 
@@ -36,7 +37,7 @@ class amk_config(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
                 ("vocab", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_float),
                 ("tied_lm_head", C.c_int32), ("wtype", C.c_int32), ("max_batch", C.c_int32),
-                ("max_seq", C.c_int32)]
+                ("max_seq", C.c_int32), ("group_size", C.c_int32)]
 
 
 class amk_layer_weights(C.Structure):
@@ -140,8 +141,9 @@ def make_config(cfg, max_batch: Optional[int] = None, max_seq: Optional[int] = N
     """amk_config from a synth.Config."""
     return amk_config(cfg.n_layers, cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim,
                       cfg.ffn, cfg.vocab, cfg.rms_eps, cfg.rope_theta, int(cfg.tied),
-                      AMK_WT_INT8 if cfg.wtype == "int8" else AMK_WT_BF16,
-                      max_batch or cfg.batch, max_seq or cfg.max_seq)
+                      {"bf16": AMK_WT_BF16, "int8": AMK_WT_INT8, "int4": AMK_WT_INT4}[cfg.wtype],
+                      max_batch or cfg.batch, max_seq or cfg.max_seq,
+                      cfg.group if cfg.wtype == "int4" else 0)
 
 
 def schedule_build(cfg: amk_config, batch: int, n_cu: int,

@@ -22,7 +22,8 @@ class BlobConfig(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("n_layers", "hidden", "n_heads", "n_kv_heads",
                                          "head_dim", "ffn", "vocab")] + \
                [("rms_eps", C.c_float), ("rope_theta", C.c_float)] + \
-               [(n, C.c_int32) for n in ("tied_lm_head", "wtype", "max_batch", "max_seq")]
+               [(n, C.c_int32) for n in ("tied_lm_head", "wtype", "max_batch", "max_seq",
+                                         "group_size")]
 
 
 class BlobHeader(C.Structure):

@@ -17,13 +17,14 @@ namespace amk {
 
 struct DevLayer {
   const void *qkv, *o, *gu, *dn;           // packed weights (bf16 bits or int8)
-  const float *s_qkv, *s_o, *s_gu, *s_dn;  // per-row scales (int8) or null
+  const float *s_qkv, *s_o, *s_gu, *s_dn;  // scales: per row (int8), per row and group (int4)
   const uint16_t *attn_norm, *mlp_norm;
 };
 
 struct DevModel {
   int32_t L, d, nq, nkv, hd, F, V, qkvr, qd, qpg;
   int32_t wtype, tied, max_batch, max_seq;
+  int32_t gs;  // int4: inputs per scale group
   int32_t nblk, n_lm;
   uint32_t n_tasks;
   uint32_t argmax_id;  // the step's last task: every other task of the step precedes it
@@ -166,6 +167,29 @@ __device__ __forceinline__ float dot16_i8(const uint4 w, const float *x) {
   return a + b;
 }
 
+// 32 int4 weights (one 16-byte unit) dotted with 32 floats. Nibble order within each 32-bit word
+// (the library's repacked layout): byte j holds input j in its low and input j + 4 in its high
+// nibble, so word i covers inputs 8i .. 8i + 7.
+__device__ __forceinline__ float dot32_i4(const uint4 w, const float *x) {
+  float a = 0.f, b = 0.f;
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int32_t v = (int32_t)ws[i];
+    const float4 xl = *reinterpret_cast<const float4 *>(x + 8 * i);
+    const float4 xh = *reinterpret_cast<const float4 *>(x + 8 * i + 4);
+    a = fmaf((float)((v << 28) >> 28), xl.x, a);
+    b = fmaf((float)((v << 24) >> 28), xh.x, b);
+    a = fmaf((float)((v << 20) >> 28), xl.y, a);
+    b = fmaf((float)((v << 16) >> 28), xh.y, b);
+    a = fmaf((float)((v << 12) >> 28), xl.z, a);
+    b = fmaf((float)((v << 8) >> 28), xh.z, b);
+    a = fmaf((float)((v << 4) >> 28), xl.w, a);
+    b = fmaf((float)(v >> 28), xh.w, b);
+  }
+  return a + b;
+}
+
 // Global-memory accesses. Pointers held in DevModel are generic (flat) to the compiler; flat
 // accesses count against both vmcnt and lgkmcnt, so every LDS access would also wait for all
 // outstanding global loads. Casting to the global address space keeps the two counters apart.
@@ -229,6 +253,7 @@ constexpr int kCachePolicySc1 = 16;
 // [15:14]) waiting on vector memory only
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitVm8 = 0x0F78;
+constexpr int kWaitVm16 = 0x4F70;  // vmcnt 16: its bits 5:4 sit in bits 15:14
 #define AMK_LDS __attribute__((address_space(3)))
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
@@ -388,17 +413,32 @@ __device__ __forceinline__ float row_dot_i8(const int8_t *__restrict__ W, int64_
   return wave_sum(acc);
 }
 
+// int4 row: each 16-byte unit (32 inputs) times its group's scale
+__device__ __forceinline__ float row_dot_i4(const uint8_t *__restrict__ W, const float *scale,
+                                            int gs, int64_t row, int K, const float *xs) {
+  const uint4 *wr = reinterpret_cast<const uint4 *>(W + row * (int64_t)(K / 2));
+  const float *sr = scale + row * (int64_t)(K / gs);
+  const int n32 = K >> 5, upg = gs >> 5;
+  const int lane = lane_id();
+  float acc = 0.f;
+  for (int u = lane; u < n32; u += 64) acc = fmaf(gld(&sr[u / upg]), dot32_i4(load_nt(wr + u), xs + 32 * u), acc);
+  return wave_sum(acc);
+}
+
 // rows [r0, r1) of a matrix for B staged vectors (xs + b*K); ys[b*(r1-r0) + r - r0].
-// WT = 0: bf16 weights; WT = 1: int8 weights times scale[r].
+// WT = 0: bf16 weights; WT = 1: int8 weights times scale[r]; WT = 2: int4 weights, scale[r][g]
+// per group of gs inputs.
 template <int WT>
 __device__ void gemv_rows(const void *W, const float *scale, int K, int r0, int r1,
-                          const float *xs, float *ys, int B, int nw) {
+                          const float *xs, float *ys, int B, int nw, int gs = 0) {
   const int n = r1 - r0;
   for (int i = wave_id(); i < n; i += nw) {
     const int64_t r = r0 + i;
     for (int b = 0; b < B; ++b) {
       float v;
-      if constexpr (WT == 1)
+      if constexpr (WT == 2)
+        v = row_dot_i4(static_cast<const uint8_t *>(W), scale, gs, r, K, xs + (int64_t)b * K);
+      else if constexpr (WT == 1)
         v = row_dot_i8<4>(static_cast<const int8_t *>(W), r, K, xs + (int64_t)b * K) * gld(&scale[r]);
       else
         v = row_dot_bf16<8>(static_cast<const uint16_t *>(W), r, K, xs + (int64_t)b * K);
@@ -564,9 +604,9 @@ struct GemvStream {
 // than bf16. |A_p| <= 128 * 127 * K stays within int32 for K <= 2^17.
 // LDS layout, unit-interleaved: unit u (elements 16u .. 16u+15) holds d2[16], d1[16], d0[16] at
 // byte 48u, so a lane's three 16-byte reads share one address and lanes 48 bytes apart fall on
-// distinct banks; unit K/16 is all zero, and lanes past a row's end read it. The digits overwrite
-// the fp32 input (3K + 48 <= 4K bytes); every thread holds its share in registers across a barrier
-// before any digit is written, which bounds K by kDigitMaxK.
+// distinct banks; the 96 bytes after the last unit are zero, and lanes past a row's end read them.
+// The digits overwrite the fp32 input (3K + 96 <= 4K bytes); every thread holds its share in
+// registers across a barrier before any digit is written, which bounds K by kDigitMaxK.
 constexpr int kDigitRedSlot = kRedFloats - kWaves;  // red[] floats that hold the per-wave maxima
 
 // The digit scale from the per-wave maxima of |x| in red (published before a barrier): returns
@@ -602,8 +642,9 @@ __device__ __forceinline__ void put_digits(float *xs, int i, float a, float b, f
   p[4] = w1;
   p[8] = w0;
 }
+// 96 zero bytes after the last unit: one int8 digit unit of 16 inputs, or the int4 one of 32
 __device__ __forceinline__ void put_zero_unit(float *xs, int K) {
-  if (threadIdx.x < 12) ((AMK_LDS uint32_t *)((AMK_LDS uint8_t *)xs + 48 * (K >> 4)))[threadIdx.x] = 0u;
+  if (threadIdx.x < 24) ((AMK_LDS uint32_t *)((AMK_LDS uint8_t *)xs + 48 * (K >> 4)))[threadIdx.x] = 0u;
 }
 
 // In place, for an input already staged as fp32 in xs: returns 2^(e-22), the weight of one unit
@@ -651,7 +692,8 @@ struct GemvStreamI8 {
   int K, r0, nw, n16, nch, S, rows_w;
   int wave, lane;
 
-  __device__ __forceinline__ void init(const void *w, int k, int a, int b, int nwaves) {
+  __device__ __forceinline__ void init(const void *w, const float *, int, int k, int a, int b,
+                                       int nwaves) {
     W = static_cast<const uint8_t *>(w);
     K = k;
     r0 = a;
@@ -757,6 +799,152 @@ struct GemvStreamI8 {
       consume(Bf, s + 1, acc, xd, sx, ys, scale);
     } else {
       consume(A, s, acc, xd, sx, ys, scale);
+    }
+  }
+};
+
+// The int4 stream: as GemvStreamI8, with 16-byte units of 32 inputs (rows of K / 2 bytes) and
+// one fp32 scale per row and group of gs inputs (a multiple of 32, so a unit lies in one group).
+// A unit's nibbles go to the integer dot products as int8 lanes holding 16 q: for word i (inputs
+// 8i .. 8i + 7), (w << 4) & 0xF0F0F0F0 holds inputs 8i .. 8i + 3 and w & 0xF0F0F0F0 inputs
+// 8i + 4 .. 8i + 7. Each unit's exact int32 sums are scaled by its group's scale into an fp32
+// accumulator; the row's sum carries a factor 16 that the end of the row removes. A unit's digits
+// are two consecutive int8 digit units (96 bytes). RPC > 1: rows of exactly 64 * kChunkUnits / RPC
+// units (K = 4096 with RPC = 4).
+template <int RPC>
+struct GemvStreamI4 {
+  static constexpr int UPL = kChunkUnits / RPC;
+  const uint8_t *W;
+  const float *scale;
+  int K, r0, nw, n32, nch, S, rows_w, ng, upg;
+  int wave, lane;
+  float sc0[kChunkUnits], scP[kChunkUnits];  // scales of the chunks issued before the wait
+
+  __device__ __forceinline__ void init(const void *w, const float *sc, int gs, int k, int a, int b,
+                                       int nwaves) {
+    W = static_cast<const uint8_t *>(w);
+    scale = sc;
+    K = k;
+    r0 = a;
+    nw = nwaves;
+    wave = __builtin_amdgcn_readfirstlane(wave_id());
+    lane = lane_id();
+    n32 = K / 32;
+    ng = K / gs;
+    upg = gs / 32;
+    nch = RPC == 1 ? (n32 + 64 * kChunkUnits - 1) / (64 * kChunkUnits) : 1;
+    const int n = b - a;
+    rows_w = (n > wave) ? (n - wave + nw - 1) / nw : 0;
+    S = RPC == 1 ? rows_w * nch : (rows_w + RPC - 1) / RPC;
+  }
+  __device__ __forceinline__ int slot_idx(int s, int q) const { return RPC == 1 ? s / nch : s * RPC + q; }
+  __device__ __forceinline__ int row_at(int i) const { return r0 + wave + min(i, rows_w - 1) * nw; }
+  __device__ __forceinline__ int unit_of(int s, int j) const {
+    return RPC == 1 ? (s % nch) * 64 * kChunkUnits + lane + 64 * j : lane + 64 * (j % UPL);
+  }
+  __device__ __forceinline__ void addr(int s, int j, const uint4 **wp, const float **sp) const {
+    const int row = row_at(slot_idx(s, j / UPL));
+    const int u = min(unit_of(s, j), n32 - 1);
+    *wp = reinterpret_cast<const uint4 *>(W + (int64_t)row * (K / 2)) + u;
+    *sp = scale + (int64_t)row * ng + u / upg;
+  }
+  __device__ __forceinline__ void load2(uint4 (&buf)[kChunkUnits], float (&sb)[kChunkUnits], int s) const {
+#pragma unroll
+    for (int j = 0; j < kChunkUnits; ++j) {
+      const uint4 *wp;
+      const float *sp;
+      addr(s, j, &wp, &sp);
+      buf[j] = load_nt(wp);
+      sb[j] = gld(sp);
+    }
+  }
+  // the register chunk issued before the wait (its scales kept in scP)
+  __device__ __forceinline__ void load(uint4 (&buf)[kChunkUnits], int s) { load2(buf, scP, s); }
+  // chunk s straight into LDS (its scales into sc0)
+  __device__ __forceinline__ void load_lds(int s, uint4 *dst) {
+#pragma unroll
+    for (int j = 0; j < kChunkUnits; ++j) {
+      const uint4 *wp;
+      const float *sp;
+      addr(s, j, &wp, &sp);
+      __builtin_amdgcn_global_load_lds((const AMK_GAS void *)wp, (AMK_LDS void *)(dst + j * 64), 16,
+                                       0, kCachePolicyNt);
+      sc0[j] = gld(sp);
+    }
+  }
+  __device__ __forceinline__ void consume(const uint4 (&buf)[kChunkUnits], const float (&sb)[kChunkUnits],
+                                          int s, float (&acc)[RPC], const uint8_t *xd, float sx,
+                                          float *ys) const {
+#pragma unroll
+    for (int j = 0; j < kChunkUnits; ++j) {
+      const int q = j / UPL;
+      const int u = unit_of(s, j);
+      const AMK_LDS u32x4_t *dp =
+          (const AMK_LDS u32x4_t *)((const AMK_LDS uint8_t *)xd + 96 * (RPC == 1 ? min(u, n32) : u));
+      const u32x4_t d2a = dp[0], d1a = dp[1], d0a = dp[2], d2b = dp[3], d1b = dp[4], d0b = dp[5];
+      const uint4 w = buf[j];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      int a2 = 0, a1 = 0, a0 = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int lo = (int)((ws[i] << 4) & 0xF0F0F0F0u), hi = (int)(ws[i] & 0xF0F0F0F0u);
+        const u32x4_t &D2 = i < 2 ? d2a : d2b, &D1 = i < 2 ? d1a : d1b, &D0 = i < 2 ? d0a : d0b;
+        const int wl = 2 * (i & 1);
+        a2 = __builtin_amdgcn_sdot4(lo, (int)D2[wl], a2, false);
+        a1 = __builtin_amdgcn_sdot4(lo, (int)D1[wl], a1, false);
+        a0 = __builtin_amdgcn_sdot4(lo, (int)D0[wl], a0, false);
+        a2 = __builtin_amdgcn_sdot4(hi, (int)D2[wl + 1], a2, false);
+        a1 = __builtin_amdgcn_sdot4(hi, (int)D1[wl + 1], a1, false);
+        a0 = __builtin_amdgcn_sdot4(hi, (int)D0[wl + 1], a0, false);
+      }
+      // |a_p| <= 32 * 128 * 128: exact in fp32
+      const float v = fmaf((float)a2, 65536.0f, fmaf((float)a1, 256.0f, (float)a0));
+      acc[q] = fmaf(v, sb[j], acc[q]);
+    }
+    if (RPC > 1 || s % nch == nch - 1) {
+#pragma unroll
+      for (int q = 0; q < RPC; ++q) {
+        const int i = slot_idx(s, q);
+        const float v = wave_sum(acc[q]);
+        if (lane == 0 && i < rows_w) ys[row_at(i) - r0] = v * (sx * 0.0625f);
+        acc[q] = 0.f;
+      }
+    }
+  }
+  __device__ __forceinline__ void run_pf(const uint4 *pf, const uint4 (&P)[kChunkUnits],
+                                         const uint8_t *xd, float sx, float *ys,
+                                         const float *) const {
+    if (S == 0) return;
+    float acc[RPC];
+#pragma unroll
+    for (int q = 0; q < RPC; ++q) acc[q] = 0.f;
+    uint4 A[kChunkUnits], Bf[kChunkUnits];
+    float sA[kChunkUnits], sB[kChunkUnits];
+    if (S > 2) {
+      load2(A, sA, 2);
+      __builtin_amdgcn_s_waitcnt(kWaitVm16);
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
+#pragma unroll
+    for (int j = 0; j < kChunkUnits; ++j) Bf[j] = pf[j * 64 + lane];
+    consume(Bf, sc0, 0, acc, xd, sx, ys);
+    if (S == 1) return;
+    consume(P, scP, 1, acc, xd, sx, ys);
+    if (S == 2) return;
+    int s = 2;
+    for (; s + 2 < S; s += 2) {
+      load2(Bf, sB, s + 1);
+      consume(A, sA, s, acc, xd, sx, ys);
+      load2(A, sA, s + 2);
+      consume(Bf, sB, s + 1, acc, xd, sx, ys);
+    }
+    if (s + 1 < S) {
+      load2(Bf, sB, s + 1);
+      consume(A, sA, s, acc, xd, sx, ys);
+      consume(Bf, sB, s + 1, acc, xd, sx, ys);
+    } else {
+      consume(A, sA, s, acc, xd, sx, ys);
     }
   }
 };
@@ -1022,10 +1210,24 @@ __device__ __forceinline__ bf16x8_t bf16x8_of_i8(uint32_t w0, uint32_t w1) {
   return bf16x8_of_bits(o[0], o[1], o[2], o[3]);
 }
 
+// eight int4 weights (one word, inputs k .. k + 7 in the library's nibble order) as the eight bf16
+// values q + 136 (exact: 128 + (q + 8) with q + 8 in [0, 15] is the bf16 0x4300 | (q + 8)); the
+// caller subtracts 136 times the column sums of the input
+__device__ __forceinline__ bf16x8_t bf16x8_of_i4_offset(uint32_t w) {
+  const uint32_t lo = (w & 0x0F0F0F0Fu) ^ 0x08080808u, hi = ((w >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
+  // byte selectors 0-3 take the second operand's bytes, 4 the first's (0x43)
+  return bf16x8_of_bits(__builtin_amdgcn_perm(0x43434343u, lo, 0x04010400u),
+                        __builtin_amdgcn_perm(0x43434343u, lo, 0x04030402u),
+                        __builtin_amdgcn_perm(0x43434343u, hi, 0x04010400u),
+                        __builtin_amdgcn_perm(0x43434343u, hi, 0x04030402u));
+}
+
 // per-lane view of one batched GEMV tile
 struct MfmaTile {
   __amdgpu_buffer_rsrc_t rw, rx, rg;
   int K, rb, n, t0, t1;
+  const float *sc;  // int4: the tile's scale rows [n][ng]
+  int ng, gs;
   uint32_t xrow;   // byte offset of this lane's input row (past the range when inactive)
   int col, kq;     // B/C column (l % 16) and k quarter (l / 16)
   bool emb, gain, lo_half;
@@ -1062,8 +1264,12 @@ __device__ __forceinline__ void mfma_pass(const MfmaTile &T, int g0, int gn, boo
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
           if (g < gn) {
-            const uint32_t off = (uint32_t)(16 * (g0 + g) + T.col) * (uint32_t)T.rb + (uint32_t)k * (WT ? 1u : 2u);
-            if constexpr (WT == 0) {
+            const uint32_t off = (uint32_t)(16 * (g0 + g) + T.col) * (uint32_t)T.rb +
+                                 (WT == 2 ? (uint32_t)k / 2u : (uint32_t)k * (WT ? 1u : 2u));
+            if constexpr (WT == 2) {
+              wf[u][g][0] = __builtin_amdgcn_raw_buffer_load_b32(T.rw, (int)off, 0, kCachePolicyNt);
+              wf[u][g][1] = wf[u][g][2] = wf[u][g][3] = 0;
+            } else if constexpr (WT == 0) {
               const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(T.rw, (int)off, 0, kCachePolicyNt);
               wf[u][g][0] = w.x; wf[u][g][1] = w.y; wf[u][g][2] = w.z; wf[u][g][3] = w.w;
             } else {
@@ -1104,12 +1310,34 @@ __device__ __forceinline__ void mfma_pass(const MfmaTile &T, int g0, int gn, boo
           hx[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
         }
         const bf16x8_t xb = bf16x8_of_bits(hx[0], hx[1], hx[2], hx[3]);
+        if constexpr (WT == 2) {
+          // int4: each k step's products, less 136 times the input column sums, times the
+          // step's group scale of each row (a k step of 32 inputs lies in one group)
+          const uint32_t c136 = 0x43084308u;  // bf16 136.0, twice
+          const f32x4_t corr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              bf16x8_of_bits(c136, c136, c136, c136), xb, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          const f32x4_t ncorr = -corr;
+          const int grp = (32 * (t + u)) / T.gs;
 #pragma unroll
-        for (int g = 0; g < GP; ++g) {
-          if (g < gn) {
-            const bf16x8_t a = WT == 0 ? bf16x8_of_bits(wf[u][g][0], wf[u][g][1], wf[u][g][2], wf[u][g][3])
-                                       : bf16x8_of_i8(wf[u][g][0], wf[u][g][1]);
-            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb, acc[g], 0, 0, 0);
+          for (int g = 0; g < GP; ++g) {
+            if (g < gn) {
+              const f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  bf16x8_of_i4_offset(wf[u][g][0]), xb, ncorr, 0, 0, 0);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int r = min(16 * (g0 + g) + 4 * T.kq + i, T.n - 1);
+                acc[g][i] = fmaf(p[i], gld(&T.sc[(int64_t)r * T.ng + grp]), acc[g][i]);
+              }
+            }
+          }
+        } else {
+#pragma unroll
+          for (int g = 0; g < GP; ++g) {
+            if (g < gn) {
+              const bf16x8_t a = WT == 0 ? bf16x8_of_bits(wf[u][g][0], wf[u][g][1], wf[u][g][2], wf[u][g][3])
+                                         : bf16x8_of_i8(wf[u][g][0], wf[u][g][1]);
+              acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb, acc[g], 0, 0, 0);
+            }
           }
         }
       }
@@ -1127,7 +1355,10 @@ __device__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, c
   MfmaTile T;
   T.K = K;
   T.n = n;
-  T.rb = K * (WT ? 1 : 2);
+  T.rb = WT == 2 ? K / 2 : K * (WT ? 1 : 2);
+  T.gs = WT == 2 ? m.gs : 32;
+  T.ng = K / T.gs;
+  T.sc = WT == 2 ? scale + (int64_t)r0 * T.ng : nullptr;
   const int steps = (K + 31) / 32;
   T.t0 = (int)((int64_t)steps * wave / NW);
   T.t1 = (int)((int64_t)steps * (wave + 1) / NW);

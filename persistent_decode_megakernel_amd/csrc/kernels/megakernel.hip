@@ -54,10 +54,10 @@ __device__ __forceinline__ bool stage_b1_digits(const DevModel &m, const StepArg
   }
 }
 
-// Batch-1 int8 GEMV body: as the bf16 body in gemv_task, with one of two stream shapes (SA rows
-// longer than half a chunk, SB two rows per chunk) and the input staged as digits.
+// Batch-1 int8 / int4 GEMV body: as the bf16 body in gemv_task, with one of two stream shapes
+// (SA one row per chunk, SB several) and the input staged as digits.
 template <class SA, class SB>
-__device__ __forceinline__ bool gemv_b1_i8(const DevModel &m, const StepArgs &s, const Task &t,
+__device__ __forceinline__ bool gemv_b1_q(const DevModel &m, const StepArgs &s, const Task &t,
                                            const void *W, const float *scale, int K, bool use_b,
                                            float *xs, float *ys, float *red, uint4 *pf,
                                            int *abort_slot) {
@@ -66,10 +66,10 @@ __device__ __forceinline__ bool gemv_b1_i8(const DevModel &m, const StepArgs &s,
   uint4 P[kChunkUnits];
   uint4 *slot;
   if (use_b) {
-    sb.init(W, K, (int)t.a0, (int)t.a1, kWaves);
+    sb.init(W, scale, m.gs, K, (int)t.a0, (int)t.a1, kWaves);
     slot = pf + sb.wave * (64 * kChunkUnits);
   } else {
-    sa.init(W, K, (int)t.a0, (int)t.a1, kWaves);
+    sa.init(W, scale, m.gs, K, (int)t.a0, (int)t.a1, kWaves);
     slot = pf + sa.wave * (64 * kChunkUnits);
   }
   const bool tagged = !(t.mat == M_QKV && t.layer == 0);
@@ -100,7 +100,7 @@ __device__ __forceinline__ bool gemv_b1_i8(const DevModel &m, const StepArgs &s,
 
 // GEMV tile task. Batch 1: the first two weight chunks of every wave (one into its LDS slot, one
 // into registers) are issued at once, then the input is staged from its epoch-tagged producer
-// words, which is also the dependency wait (int8: gemv_b1_i8). Batched: a flag wait (wave 0 polls), then the matrix-core GEMV reads its inputs
+// words, which is also the dependency wait (int8, int4: gemv_b1_q). Batched: a flag wait (wave 0 polls), then the matrix-core GEMV reads its inputs
 // straight from memory. The RMSNorm scale is applied to the outputs and the epilogue writes them
 // (tagged for batch 1).
 template <int WT, bool BATCHED>
@@ -167,11 +167,17 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
       }
       if (m.trace && threadIdx.x == 0) gst(&m.trace[(uint64_t)t.id * 4 + 2], (uint64_t)wall_clock64());
       st.run_pf(slot, P, xs, ys, scale);
-    } else {
+    } else if constexpr (WT == 1) {
       // int8 rows of 256 units (K = 4096) fill half a chunk: two rows per chunk
-      if (!gemv_b1_i8<GemvStreamI8<1>, GemvStreamI8<2>>(m, s, t, W, scale, K,
-                                                        K == 16 * 32 * kChunkUnits, xs, ys, red,
-                                                        pf, abort_slot))
+      if (!gemv_b1_q<GemvStreamI8<1>, GemvStreamI8<2>>(m, s, t, W, scale, K,
+                                                       K == 16 * 32 * kChunkUnits, xs, ys, red,
+                                                       pf, abort_slot))
+        return false;
+    } else {
+      // int4 rows of 128 units (K = 4096): four rows per chunk
+      if (!gemv_b1_q<GemvStreamI4<1>, GemvStreamI4<4>>(m, s, t, W, scale, K,
+                                                       K == 32 * 16 * kChunkUnits, xs, ys, red,
+                                                       pf, abort_slot))
         return false;
     }
   } else {
@@ -312,3 +318,9 @@ AMK_MK(1, 64, 4)
 AMK_MK(1, 128, 1)
 AMK_MK(1, 128, 2)
 AMK_MK(1, 128, 4)
+AMK_MK(2, 64, 1)
+AMK_MK(2, 64, 2)
+AMK_MK(2, 64, 4)
+AMK_MK(2, 128, 1)
+AMK_MK(2, 128, 2)
+AMK_MK(2, 128, 4)

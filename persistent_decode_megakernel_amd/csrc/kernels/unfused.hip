@@ -50,7 +50,7 @@ __device__ void uf_gemv(const DevModel &m, const StepArgs &s, const void *W, con
   const int r0 = blockIdx.x * kUfRowsPerBlock, r1 = min(rows, r0 + kUfRowsPerBlock);
   if (s.batch == 1) {
     stage_plain(x, K, K, 1, xs, kUfWaves);
-    gemv_rows<WT>(W, scale, K, r0, r1, xs, ys, 1, kUfWaves);
+    gemv_rows<WT>(W, scale, K, r0, r1, xs, ys, 1, kUfWaves, m.gs);
   } else {
     gemv_mfma<WT>(m, s, W, scale, K, r0, r1, BatchInput{x, K, nullptr, nullptr, false}, ys, red, xs);
   }
@@ -81,6 +81,9 @@ AMK_UF_GEMV(0, 2)
 AMK_UF_GEMV(1, 0)
 AMK_UF_GEMV(1, 1)
 AMK_UF_GEMV(1, 2)
+AMK_UF_GEMV(2, 0)
+AMK_UF_GEMV(2, 1)
+AMK_UF_GEMV(2, 2)
 
 // RoPE + KV append from the raw packed QKV outputs y[b][qkvr]; one thread per row pair
 extern "C" __global__ void __launch_bounds__(256) amk_uf_rope_kv(const DevModel *__restrict__ mp,

@@ -33,6 +33,12 @@ AMK_DECL_MK(1, 64, 4)
 AMK_DECL_MK(1, 128, 1)
 AMK_DECL_MK(1, 128, 2)
 AMK_DECL_MK(1, 128, 4)
+AMK_DECL_MK(2, 64, 1)
+AMK_DECL_MK(2, 64, 2)
+AMK_DECL_MK(2, 64, 4)
+AMK_DECL_MK(2, 128, 1)
+AMK_DECL_MK(2, 128, 2)
+AMK_DECL_MK(2, 128, 4)
 extern "C" __global__ void amk_uf_embed(const DevModel *, StepArgs);
 extern "C" __global__ void amk_uf_rmsnorm(const DevModel *, const float *, const uint16_t *, float *);
 #define AMK_DECL_UG(WT, MODE)                                                                  \
@@ -45,6 +51,9 @@ AMK_DECL_UG(0, 2)
 AMK_DECL_UG(1, 0)
 AMK_DECL_UG(1, 1)
 AMK_DECL_UG(1, 2)
+AMK_DECL_UG(2, 0)
+AMK_DECL_UG(2, 1)
+AMK_DECL_UG(2, 2)
 extern "C" __global__ void amk_uf_rope_kv(const DevModel *, StepArgs, int);
 #define AMK_DECL_UA(HD, Q) extern "C" __global__ void amk_uf_attn_h##HD##_q##Q(const DevModel *, StepArgs, int);
 AMK_DECL_UA(64, 1)
@@ -65,6 +74,20 @@ amk_gather_rows(uint32_t *dst, const uint32_t *src, const int2 *pairs, int n, in
     const uint32_t *s = src + (int64_t)p.y * row_words;
     uint32_t *d = dst + (int64_t)p.x * row_words;
     for (int k = threadIdx.x; k < row_words; k += 256) d[k] = s[k];
+  }
+}
+
+// int4 matrices: nibble order within each 32-bit word, from the interface's (byte j: inputs 2j in
+// the low and 2j + 1 in the high nibble, so input e at bits 4e) to the kernels' (byte j: input j in
+// the low and j + 4 in the high nibble), where one mask or a shift and a mask yield four inputs as
+// the high nibbles of four bytes
+extern "C" __global__ void __launch_bounds__(256) amk_int4_reorder(uint32_t *w, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const uint32_t v = w[i];
+    uint32_t o = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o |= ((v >> (4 * e)) & 0xFu) << (8 * (e & 3) + 4 * (e >> 2));
+    w[i] = o;
   }
 }
 
@@ -94,6 +117,7 @@ MkFn pick_megakernel(int wt, int hd, int qmax, bool batched) {
     return batched ? amk_megakernel_w##WT##_h##HD##_q##Q##_b : amk_megakernel_w##WT##_h##HD##_q##Q;
   AMK_P(0, 64, 1) AMK_P(0, 64, 2) AMK_P(0, 64, 4) AMK_P(0, 128, 1) AMK_P(0, 128, 2) AMK_P(0, 128, 4)
   AMK_P(1, 64, 1) AMK_P(1, 64, 2) AMK_P(1, 64, 4) AMK_P(1, 128, 1) AMK_P(1, 128, 2) AMK_P(1, 128, 4)
+  AMK_P(2, 64, 1) AMK_P(2, 64, 2) AMK_P(2, 64, 4) AMK_P(2, 128, 1) AMK_P(2, 128, 2) AMK_P(2, 128, 4)
 #undef AMK_P
   return nullptr;
 }
@@ -110,8 +134,9 @@ UaFn pick_uf_attn(int hd, int qmax) {
 using UgFn = void (*)(const DevModel *, StepArgs, const void *, const float *, int, int,
                       const float *, float *, const float *, float *);
 UgFn pick_uf_gemv(int wt, int mode) {
-  static const UgFn t[2][3] = {{amk_uf_gemv_w0_m0, amk_uf_gemv_w0_m1, amk_uf_gemv_w0_m2},
-                               {amk_uf_gemv_w1_m0, amk_uf_gemv_w1_m1, amk_uf_gemv_w1_m2}};
+  static const UgFn t[3][3] = {{amk_uf_gemv_w0_m0, amk_uf_gemv_w0_m1, amk_uf_gemv_w0_m2},
+                               {amk_uf_gemv_w1_m0, amk_uf_gemv_w1_m1, amk_uf_gemv_w1_m2},
+                               {amk_uf_gemv_w2_m0, amk_uf_gemv_w2_m1, amk_uf_gemv_w2_m2}};
   return t[wt][mode];
 }
 
@@ -264,17 +289,17 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
       return set_error(AMK_E_UNSUPPORTED, "int8 weights need hidden and ffn multiples of 16");
     if (!w->embed || !w->final_norm || !w->layers || (!cfg->tied_lm_head && !w->lm_head))
       return set_error(AMK_E_INVALID, "amk_model_create: missing weight pointer");
-    const bool i8 = cfg->wtype == AMK_WT_INT8;
+    const bool i8 = cfg->wtype == AMK_WT_INT8, i4 = cfg->wtype == AMK_WT_INT4;
     for (int l = 0; l < cfg->n_layers; ++l) {
       const amk_layer_weights &lw = w->layers[l];
       if (!lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.wg || !lw.wu || !lw.wd || !lw.attn_norm ||
           !lw.mlp_norm)
         return set_error(AMK_E_INVALID, "amk_model_create: missing layer weight pointer");
-      if (i8 && (!lw.sq || !lw.sk || !lw.sv || !lw.so || !lw.sg || !lw.su || !lw.sd))
-        return set_error(AMK_E_INVALID, "amk_model_create: int8 weights need scales");
+      if ((i8 || i4) && (!lw.sq || !lw.sk || !lw.sv || !lw.so || !lw.sg || !lw.su || !lw.sd))
+        return set_error(AMK_E_INVALID, "amk_model_create: int8/int4 weights need scales");
     }
-    if (i8 && !cfg->tied_lm_head && !w->lm_head_scale)
-      return set_error(AMK_E_INVALID, "amk_model_create: int8 LM head needs scales");
+    if ((i8 || i4) && !cfg->tied_lm_head && !w->lm_head_scale)
+      return set_error(AMK_E_INVALID, "amk_model_create: int8/int4 LM head needs scales");
 
     m = new amk_model();
     m->cfg = *cfg;
@@ -338,11 +363,21 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     const int L = cfg->n_layers, d = cfg->hidden, nq = cfg->n_heads, nkv = cfg->n_kv_heads,
               hd = cfg->head_dim, F = cfg->ffn, V = cfg->vocab, B = cfg->max_batch;
     const int qd = nq * hd, qkvr = qkv_rows(nq, nkv, hd);
-    const size_t wb = i8 ? 1 : 2;
+    // bytes of a weight row of K inputs, and of its scales (one per row, or one per group)
+    auto row_b = [&](int K) -> size_t { return i4 ? (size_t)K / 2 : (size_t)K * (i8 ? 1 : 2); };
+    auto scale_b = [&](int K) -> size_t { return i4 ? (size_t)(K / cfg->group_size) * 4 : 4; };
+    auto reorder = [&](void *w, size_t bytes) {
+      if (!i4) return;
+      const size_t n = bytes / 4;
+      hipLaunchKernelGGL(amk_int4_reorder, dim3((unsigned)std::min<size_t>((n + 255) / 256, 65535)),
+                         dim3(256), 0, st, (uint32_t *)w, n);
+      hip_check(hipGetLastError(), "amk_int4_reorder");
+    };
     DevModel &dm = m->dm;
     dm.L = L; dm.d = d; dm.nq = nq; dm.nkv = nkv; dm.hd = hd; dm.F = F; dm.V = V;
     dm.qkvr = qkvr; dm.qd = qd; dm.qpg = nq / nkv;
     dm.wtype = cfg->wtype; dm.tied = cfg->tied_lm_head; dm.max_batch = B; dm.max_seq = cfg->max_seq;
+    dm.gs = cfg->group_size;
     dm.nblk = (int32_t)h.attn_blocks;
     dm.n_lm = (int32_t)h.n_lm_tiles;
     dm.n_tasks = h.n_tasks;
@@ -354,10 +389,10 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     for (int l = 0; l < L; ++l) {
       const amk_layer_weights &lw = w->layers[l];
       DevLayer &dl = m->layers[l];
-      void *qkv = m->dalloc<uint8_t>((size_t)qkvr * d * wb);
-      void *gu = m->dalloc<uint8_t>((size_t)2 * F * d * wb);
-      void *o = m->dalloc<uint8_t>((size_t)d * qd * wb);
-      void *dn = m->dalloc<uint8_t>((size_t)d * F * wb);
+      void *qkv = m->dalloc<uint8_t>((size_t)qkvr * row_b(d));
+      void *gu = m->dalloc<uint8_t>((size_t)2 * F * row_b(d));
+      void *o = m->dalloc<uint8_t>((size_t)d * row_b(qd));
+      void *dn = m->dalloc<uint8_t>((size_t)d * row_b(F));
       std::vector<int2> pq, pk, pv, pg, pu;
       for (int r = 0; r < qkvr; ++r) {
         QkvRow q = qkv_decode(r, nq, nkv, hd);
@@ -368,34 +403,40 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
         pg.push_back(make_int2(2 * i, i));
         pu.push_back(make_int2(2 * i + 1, i));
       }
-      gather(m, qkv, lw.wq, pq, d * wb, st);
-      gather(m, qkv, lw.wk, pk, d * wb, st);
-      gather(m, qkv, lw.wv, pv, d * wb, st);
-      gather(m, gu, lw.wg, pg, d * wb, st);
-      gather(m, gu, lw.wu, pu, d * wb, st);
-      copy_d2d(o, lw.wo, (size_t)d * qd * wb, st);
-      copy_d2d(dn, lw.wd, (size_t)d * F * wb, st);
+      gather(m, qkv, lw.wq, pq, row_b(d), st);
+      gather(m, qkv, lw.wk, pk, row_b(d), st);
+      gather(m, qkv, lw.wv, pv, row_b(d), st);
+      gather(m, gu, lw.wg, pg, row_b(d), st);
+      gather(m, gu, lw.wu, pu, row_b(d), st);
+      copy_d2d(o, lw.wo, (size_t)d * row_b(qd), st);
+      copy_d2d(dn, lw.wd, (size_t)d * row_b(F), st);
+      reorder(qkv, (size_t)qkvr * row_b(d));
+      reorder(gu, (size_t)2 * F * row_b(d));
+      reorder(o, (size_t)d * row_b(qd));
+      reorder(dn, (size_t)d * row_b(F));
       dl.qkv = qkv; dl.gu = gu; dl.o = o; dl.dn = dn;
       dl.s_qkv = dl.s_gu = dl.s_o = dl.s_dn = nullptr;
-      if (i8) {
-        float *sqkv = m->dalloc<float>(qkvr), *sgu = m->dalloc<float>(2 * F);
-        float *so = m->dalloc<float>(d), *sdn = m->dalloc<float>(d);
-        gather(m, sqkv, lw.sq, pq, 4, st);
-        gather(m, sqkv, lw.sk, pk, 4, st);
-        gather(m, sqkv, lw.sv, pv, 4, st);
-        gather(m, sgu, lw.sg, pg, 4, st);
-        gather(m, sgu, lw.su, pu, 4, st);
-        copy_d2d(so, lw.so, (size_t)d * 4, st);
-        copy_d2d(sdn, lw.sd, (size_t)d * 4, st);
+      if (i8 || i4) {
+        float *sqkv = (float *)m->dalloc<uint8_t>(qkvr * scale_b(d));
+        float *sgu = (float *)m->dalloc<uint8_t>(2 * F * scale_b(d));
+        float *so = (float *)m->dalloc<uint8_t>(d * scale_b(qd));
+        float *sdn = (float *)m->dalloc<uint8_t>(d * scale_b(F));
+        gather(m, sqkv, lw.sq, pq, scale_b(d), st);
+        gather(m, sqkv, lw.sk, pk, scale_b(d), st);
+        gather(m, sqkv, lw.sv, pv, scale_b(d), st);
+        gather(m, sgu, lw.sg, pg, scale_b(d), st);
+        gather(m, sgu, lw.su, pu, scale_b(d), st);
+        copy_d2d(so, lw.so, (size_t)d * scale_b(qd), st);
+        copy_d2d(sdn, lw.sd, (size_t)d * scale_b(F), st);
         dl.s_qkv = sqkv; dl.s_gu = sgu; dl.s_o = so; dl.s_dn = sdn;
-        m->weight_bytes += 4ull * (qkvr + 2 * F + 2 * d);
+        m->weight_bytes += (uint64_t)(qkvr + 2 * F) * scale_b(d) + (uint64_t)d * (scale_b(qd) + scale_b(F));
       }
       uint16_t *an = m->dalloc<uint16_t>(d), *mn = m->dalloc<uint16_t>(d);
       copy_d2d(an, lw.attn_norm, (size_t)d * 2, st);
       copy_d2d(mn, lw.mlp_norm, (size_t)d * 2, st);
       dl.attn_norm = an;
       dl.mlp_norm = mn;
-      m->weight_bytes += wb * ((uint64_t)qkvr * d + 2ull * F * d + (uint64_t)d * qd + (uint64_t)d * F) + 4ull * d;
+      m->weight_bytes += (uint64_t)(qkvr + 2 * F) * row_b(d) + (uint64_t)d * (row_b(qd) + row_b(F)) + 4ull * d;
     }
     uint16_t *emb = m->dalloc<uint16_t>((size_t)V * d);
     copy_d2d(emb, w->embed, (size_t)V * d * 2, st);
@@ -409,15 +450,16 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
       dm.lm_scale = nullptr;
       m->weight_bytes += 2ull * V * d;
     } else {
-      void *lm = m->dalloc<uint8_t>((size_t)V * d * wb);
-      copy_d2d(lm, w->lm_head, (size_t)V * d * wb, st);
+      void *lm = m->dalloc<uint8_t>((size_t)V * row_b(d));
+      copy_d2d(lm, w->lm_head, (size_t)V * row_b(d), st);
+      reorder(lm, (size_t)V * row_b(d));
       dm.lm = lm;
-      m->weight_bytes += wb * (uint64_t)V * d;
-      if (i8) {
-        float *ls = m->dalloc<float>(V);
-        copy_d2d(ls, w->lm_head_scale, (size_t)V * 4, st);
+      m->weight_bytes += (uint64_t)V * row_b(d);
+      if (i8 || i4) {
+        float *ls = (float *)m->dalloc<uint8_t>((size_t)V * scale_b(d));
+        copy_d2d(ls, w->lm_head_scale, (size_t)V * scale_b(d), st);
         dm.lm_scale = ls;
-        m->weight_bytes += 4ull * V;
+        m->weight_bytes += (uint64_t)V * scale_b(d);
       }
     }
     DevLayer *d_layers = m->dalloc<DevLayer>(L);

@@ -21,6 +21,10 @@ uint32_t Schedule::n_tasks() const {
   return n;
 }
 
+uint32_t weight_bits(int wtype) {
+  return wtype == AMK_WT_INT4 ? 4u : (wtype == AMK_WT_INT8 ? 8u : 16u);
+}
+
 bool config_ok(const amk_config &c, std::string *err) {
   auto fail = [&](const char *m) {
     if (err) *err = m;
@@ -38,9 +42,23 @@ bool config_ok(const amk_config &c, std::string *err) {
   if (c.n_heads / c.n_kv_heads > 16) return fail("config: more than 16 query heads per KV head");
   if (c.max_batch < 1 || c.max_batch > 8) return fail("config: max_batch must be in [1, 8]");
   if (c.max_seq < 1) return fail("config: max_seq must be >= 1");
-  if (c.wtype != AMK_WT_BF16 && c.wtype != AMK_WT_INT8) return fail("config: unknown wtype");
-  if (c.wtype == AMK_WT_INT8 && c.tied_lm_head)
-    return fail("config: int8 weights with a tied LM head are unsupported");
+  if (c.wtype != AMK_WT_BF16 && c.wtype != AMK_WT_INT8 && c.wtype != AMK_WT_INT4)
+    return fail("config: unknown wtype");
+  if (c.wtype != AMK_WT_BF16 && c.tied_lm_head)
+    return fail("config: int8/int4 weights with a tied LM head are unsupported");
+  // batch-1 int8/int4 tiles write their input's digits and a 96-byte zero unit over its fp32
+  // staging area: 3K + 96 <= 4 max(hidden, ffn) bytes
+  if (c.wtype != AMK_WT_BF16 && c.hidden < 128)
+    return fail("config: int8/int4 weights need hidden >= 128");
+  if ((c.wtype == AMK_WT_INT4) != (c.group_size != 0))
+    return fail("config: group_size is set for int4 weights and only for them");
+  if (c.wtype == AMK_WT_INT4) {
+    const int g = c.group_size;
+    if (g < 32 || g % 32 || c.hidden % g || c.ffn % g || (c.n_heads * c.head_dim) % g)
+      return fail("config: int4 group_size must be a multiple of 32 dividing hidden and ffn");
+    if (std::max(c.hidden, c.ffn) > kDigitMaxK)
+      return fail("config: int4 weights need hidden and ffn <= 16384");
+  }
   if (c.wtype == AMK_WT_INT8 && (c.hidden % 16 || c.ffn % 16))
     return fail("config: int8 weights need hidden and ffn multiples of 16");
   if (c.wtype == AMK_WT_INT8 &&
@@ -99,10 +117,10 @@ struct Builder {
 
   // Emit a GEMV phase; returns [first id, last id + 1) and the tiling.
   std::pair<uint32_t, uint32_t> gemv(uint8_t mat, uint16_t layer, uint32_t rows, uint32_t align,
-                                     uint32_t K, uint32_t wbytes, uint32_t w_lo, uint32_t w_hi,
+                                     uint32_t K, uint32_t wbits, uint32_t w_lo, uint32_t w_hi,
                                      Tiling *out_tiling) {
     const uint32_t min_bytes = (uint32_t)std::max(1, p.min_tile_kb) * 1024u;
-    uint32_t row_bytes = K * wbytes;
+    uint32_t row_bytes = std::max<uint32_t>(1, K * wbits / 8);
     uint32_t min_rows = (min_bytes + row_bytes - 1) / row_bytes;
     min_rows = (min_rows + align - 1) / align * align;
     // keep ys (batch x tile rows floats) bounded
@@ -140,7 +158,7 @@ struct Builder {
   void run() {
     const uint32_t L = c.n_layers, d = c.hidden, nq = c.n_heads, nkv = c.n_kv_heads,
                    hd = c.head_dim, F = c.ffn, V = c.vocab;
-    const uint32_t wb = (c.wtype == AMK_WT_INT8) ? 1 : 2;
+    const uint32_t wb = weight_bits(c.wtype);
     const uint32_t qkvr = qkv_rows(nq, nkv, hd);
     const uint32_t grows = qkv_group_rows(nq, nkv, hd);
     const uint32_t ctx_hint = p.ctx_hint > 0 ? (uint32_t)p.ctx_hint : (uint32_t)c.max_seq;
@@ -199,7 +217,7 @@ struct Builder {
       d_lo = dn.first;
       d_hi = dn.second;
     }
-    const uint32_t lmwb = c.tied_lm_head ? 2 : wb;
+    const uint32_t lmwb = c.tied_lm_head ? 16 : wb;
     Tiling lt;
     auto lm = gemv(M_LM, 0, V, 1, d, lmwb, d_lo, d_hi, &lt);
     Task k{};
@@ -241,14 +259,16 @@ amk_cost_model default_cost_model() {
 void task_bytes(const BlobHeader &h, const Task &t, int32_t ctx, double *hbm, double *act) {
   const BlobConfig &c = h.cfg;
   const double B = h.batch;
-  const double wb = (c.wtype == AMK_WT_INT8) ? 1.0 : 2.0;
   *hbm = 0;
   *act = 0;
   if (t.type == T_GEMV) {
     const double rows = (double)t.a1 - t.a0;
     const double K = (double)t.aux2 - t.aux1;
-    double w = (t.mat == M_LM && c.tied_lm_head) ? 2.0 : wb;
-    *hbm = rows * K * w + (w == 1.0 ? rows * 4.0 : 0.0);
+    const int wt = (t.mat == M_LM && c.tied_lm_head) ? (int)AMK_WT_BF16 : c.wtype;
+    // weights plus their fp32 scales: one per row (int8) or per row and group (int4)
+    *hbm = rows * K * weight_bits(wt) / 8.0;
+    if (wt == AMK_WT_INT8) *hbm += rows * 4.0;
+    if (wt == AMK_WT_INT4) *hbm += rows * (K / c.group_size) * 4.0;
     *act = B * K * 4.0;
   } else if (t.type == T_ATTN) {
     int32_t lo, hi;

@@ -61,7 +61,7 @@ AMK_HD int32_t qkv_source_row(int32_t r, int32_t nq, int32_t nkv, int32_t hd) {
 // Frozen schedule format
 // ------------------------------------------------------------------------------------------
 constexpr uint32_t kBlobMagic = 0x534b4d41u;  // "AMKS"
-constexpr uint32_t kBlobVersion = 1;
+constexpr uint32_t kBlobVersion = 2;
 
 enum TaskType : uint8_t { T_GEMV = 1, T_ATTN = 2, T_ARGMAX = 3 };
 enum MatId : uint8_t { M_QKV = 0, M_O = 1, M_GU = 2, M_D = 3, M_LM = 4 };
@@ -88,6 +88,7 @@ struct BlobConfig {  // plain copy of amk_config (kept layout-stable inside the 
   int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab;
   float rms_eps, rope_theta;
   int32_t tied_lm_head, wtype, max_batch, max_seq;
+  int32_t group_size;
 };
 
 struct BlobHeader {

@@ -84,7 +84,7 @@ class Model:
             lw = layers[l]
             for m in MATS:
                 setattr(lw, m, _ptr(up(weights.layers[l][m])))
-            if cfg.wtype == "int8":
+            if cfg.wtype in ("int8", "int4"):
                 for m in MATS:
                     setattr(lw, "s" + m[1], _ptr(up(weights.scales[l][m])))
             lw.attn_norm = _ptr(up(weights.attn_norm[l]))

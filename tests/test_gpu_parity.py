@@ -111,6 +111,39 @@ def test_int8_hidden_4096_two_rows_per_chunk():
     assert_parity(rep)
 
 
+# int4 groups must divide the FFN: the tiny shape with FFN 768 and groups of 128
+TINY_INT4 = dict(wtype="int4", ffn=768, group=128)
+
+
+@pytest.mark.parametrize("path", ["megakernel", "unfused"])
+def test_tiny_int4_w4a16(path):
+    """W4A16: packed int4 layer matrices and LM head with one fp32 scale per row and group."""
+    cfg = synth.get_config("tiny").replace(**TINY_INT4)
+    rep = teacher_forced(cfg, path, seed=3, n_calls=20)
+    log(f"tiny int4/{path}: {rep}")
+    assert_parity(rep)
+
+
+@pytest.mark.parametrize("path", ["megakernel", "unfused"])
+def test_tiny_int4_batch3(path):
+    """Batched W4A16 on the matrix cores: nibbles as exact bf16 (q + 136), a correction product
+    for the offset, each k step scaled by its group's scale."""
+    cfg = synth.get_config("tiny").replace(batch=3, **TINY_INT4)
+    rep = teacher_forced(cfg, path, seed=4, n_calls=12)
+    assert rep.tokens_checked > 0
+    assert_parity(rep)
+
+
+def test_int4_hidden_4096_four_rows_per_chunk():
+    """W4A16 with hidden 4096 and groups of 64: batch-1 int4 rows of K = 4096 run four rows per
+    weight chunk, the down rows (K = 768) one ragged row per chunk."""
+    cfg = synth.get_config("tiny").replace(wtype="int4", hidden=4096, n_heads=32, n_kv_heads=8,
+                                           head_dim=128, ffn=768, group=64)
+    rep = teacher_forced(cfg, "megakernel", seed=7, n_calls=12, random_gains=True)
+    log(f"int4 hidden 4096: {rep}")
+    assert_parity(rep)
+
+
 @pytest.mark.parametrize("path", ["megakernel", "unfused"])
 def test_tiny_batch3(path):
     """Three independent sequences sharing the weights and the position."""
@@ -126,7 +159,7 @@ def test_smollm2_135m_batch2_prefill():
     assert_parity(rep)
 
 
-@pytest.mark.parametrize("name", ["llama2_7b", "llama2_7b_w8a16", "llama2_7b_b8"])
+@pytest.mark.parametrize("name", ["llama2_7b", "llama2_7b_w8a16", "llama2_7b_w4a16", "llama2_7b_b8"])
 def test_full_size_first_steps(name):
     """Full 7B shapes in the launch configuration the bench times (one cooperative launch per
     step on every CU), checked against the oracle on every logit for the first two steps."""

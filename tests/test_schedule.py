@@ -8,7 +8,7 @@ import pytest
 from persistent_decode_megakernel_amd import _lib, synth
 from persistent_decode_megakernel_amd import blob as B
 
-CONFIGS = ["tiny", "smollm2_135m", "tinyllama_1b", "llama2_7b", "llama2_7b_w8a16"]
+CONFIGS = ["tiny", "smollm2_135m", "tinyllama_1b", "llama2_7b", "llama2_7b_w8a16", "llama2_7b_w4a16"]
 
 
 @pytest.mark.parametrize("name", CONFIGS)
@@ -305,3 +305,24 @@ def test_schedule_without_an_argmax_is_rejected(libamk):
         b.per_cu[c] = v[v["type"] != B.T_ARGMAX]
     st, rep = _lib.schedule_validate(b.to_bytes())
     assert st == _lib.AMK_E_SCHEDULE_REJECTED and "argmax" in rep, rep
+
+
+def test_int4_weight_bytes_and_config_checks(libamk):
+    """W4A16: the schedule's byte model counts half a byte per weight plus one fp32 scale per row
+    and group; configurations the int4 kernels cannot take are refused by the builder."""
+    cfg = synth.get_config("llama2_7b_w4a16")
+    c4 = _lib.make_config(cfg)
+    c8 = _lib.make_config(synth.get_config("llama2_7b_w8a16"))
+    p4 = _lib.schedule_predict(_lib.schedule_build(c4, 1, 256), 4096)
+    p8 = _lib.schedule_predict(_lib.schedule_build(c8, 1, 256), 4096)
+    assert p4 < p8
+    for bad in (dict(group=48), dict(group=16), dict(ffn=11008 + 32), dict(hidden=64, n_heads=1,
+                                                                            head_dim=64)):
+        with pytest.raises(_lib.AmkError) as e:
+            _lib.schedule_build(_lib.make_config(cfg.replace(**bad)), 1, 256)
+        assert e.value.status == _lib.AMK_E_INVALID
+    # a group size on a non-int4 model is refused too
+    c = _lib.make_config(synth.get_config("llama2_7b"))
+    c.group_size = 128
+    with pytest.raises(_lib.AmkError):
+        _lib.schedule_build(c, 1, 256)
