@@ -184,6 +184,8 @@ def main():
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-multistep", action="store_true")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="override the workload's batch (sequences per step, 1..16)")
     ap.add_argument("--cpu-sample-steps", type=int, default=2)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (a kernel of "
@@ -201,6 +203,8 @@ def main():
     _lib.load()
     torch.cuda.set_device(0)
     cfg = synth.get_config(args.workload)
+    if args.batch:
+        cfg = cfg.replace(batch=args.batch)
     steps, warmup = args.steps, args.warmup
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20

@@ -52,7 +52,7 @@ typedef enum {
 } amk_path;
 
 /* Model shape. hidden = n_heads * head_dim; n_heads % n_kv_heads == 0; head_dim even and a
- * multiple of 8; hidden and ffn multiples of 8; 1 <= max_batch <= 8. */
+ * multiple of 8; hidden and ffn multiples of 8; 1 <= max_batch <= 16. */
 typedef struct {
   int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab;
   float rms_eps, rope_theta;
@@ -162,6 +162,15 @@ amk_status amk_decode_step(amk_model *m, amk_kv *kv, const int32_t *d_tokens, in
 amk_status amk_decode_steps(amk_model *m, amk_kv *kv, const int32_t *d_tokens, int32_t pos,
                             int32_t n_steps, int32_t batch, float *d_logits, int32_t *d_out,
                             void *stream);
+
+/* As amk_decode_steps with a position per sequence: h_pos is a HOST array of `batch` positions
+ * (read before the call returns), sequence b decodes at h_pos[b] + i in step i, attends over
+ * [0, h_pos[b] + i] of its own cache and appends there. Sequences of different lengths share the
+ * batched steps, as in the pages' batch sweeps (Ada-MK summary, "Experimental Results", batch
+ * sizes 1 to 16). Every h_pos[b] >= 0 and h_pos[b] + n_steps <= max_seq, else AMK_E_CAPACITY. */
+amk_status amk_decode_steps_ragged(amk_model *m, amk_kv *kv, const int32_t *d_tokens,
+                                   const int32_t *h_pos, int32_t n_steps, int32_t batch,
+                                   float *d_logits, int32_t *d_out, void *stream);
 
 /* Synchronise `stream` and report a device-side error recorded by earlier steps (and clear it). */
 amk_status amk_sync(amk_model *m, void *stream);

@@ -59,9 +59,12 @@ struct DevModel {
   uint64_t *trace;         // optional: [n_tasks][4] timestamps, then [n_cu] XCC ids; null = off
 };
 
-// One decode step: tokens at position pos in, next tokens (and optionally logits) out. A launch
-// may run n_steps consecutive steps (step = 0 .. n_steps-1): step i takes the tokens step i-1
-// wrote, at position pos + i, with flag epoch epoch + i.
+// One decode step: tokens at their positions in, next tokens (and optionally logits) out.
+// Sequence b is at position pos_in[b] + step (pos = pos_in[0]; positions may differ between
+// sequences). A launch may run n_steps consecutive steps (step = 0 .. n_steps-1): step i takes the
+// tokens step i-1 wrote, at positions pos_in[b] + i, with flag epoch epoch + i. The device reads
+// the positions through posp, which each kernel entry points at its own kernel-argument copy of
+// pos_in (a run-time index into a private copy would put the whole struct in scratch memory).
 struct StepArgs {
   const int32_t *tokens;
   float *logits;
@@ -71,6 +74,8 @@ struct StepArgs {
   int32_t pos, batch;
   uint32_t epoch;
   int32_t step, n_steps;
+  int32_t pos_in[kMaxBatch];
+  const int32_t *posp;
 };
 
 constexpr uint32_t ERR_TIMEOUT = 7;
@@ -279,6 +284,17 @@ __device__ __forceinline__ Task load_task(const Task *p) {
   return t;
 }
 __device__ __forceinline__ uint32_t load_const(const uint32_t *p) { return *(const AMK_CAS uint32_t *)p; }
+
+// position of sequence b in this step
+__device__ __forceinline__ int pos_of(const StepArgs &s, int b) {
+  return (int)load_const(reinterpret_cast<const uint32_t *>(s.posp + b)) + s.step;
+}
+// a kernel's arguments with posp pointing at their own positions
+__device__ __forceinline__ StepArgs with_positions(const StepArgs &s) {
+  StepArgs t = s;
+  t.posp = &s.pos_in[0];
+  return t;
+}
 
 // ------------------------------------------------------------------------------------------
 // dependency flags
@@ -1168,14 +1184,15 @@ __device__ bool stage_tagged(const DevModel &m, const uint32_t *src, int n, cons
 }
 
 // ------------------------------------------------------------------------------------------
-// Batch GEMV (B = 2..8 sequences) on the matrix cores:
+// Batch GEMV (B = 2..16 sequences) on the matrix cores:
 //   ys[b * n + (r - r0)] = sum_k X_b[k] W[r][k]  (times scale[r] for int8), r in [r0, r1).
 // v_mfma_f32_16x16x32_bf16 computes a 16 x 16 tile C = A B over 32 k. Lane l supplies
 // A[l % 16][8 (l/16) + e] and B[8 (l/16) + e][l % 16], e < 8, and receives C[4 (l/16) + i][l % 16],
 // i < 4. A holds 16 weight rows. The inputs are split into two bf16 halves, x = hi + lo, and the
 // 16 columns of B carry hi of sequence c (c < 8) and lo of sequence c - 8 (c >= 8), so one
 // instruction multiplies both halves and y_b = C[.][b] + C[.][b + 8] keeps about 16 bits of the
-// fp32 input; columns of sequences >= B are zero. K is split over the workgroup's waves
+// fp32 input; columns of sequences >= B are zero. Wide (B > 8): column c carries sequence c, and
+// two instructions, one per half, accumulate into the same tile. K is split over the workgroup's waves
 // (contiguous runs of 32-k steps); their partial tiles are summed in LDS (mred). Inputs are read
 // straight from the device-coherent buffers (no LDS staging). Each wave issues the loads of U
 // k-steps (GP 16-row groups each) before using any of them.
@@ -1183,7 +1200,7 @@ __device__ bool stage_tagged(const DevModel &m, const uint32_t *src, int n, cons
 // ------------------------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 constexpr int kMfmaGroups = 4;
-static_assert(kMfmaRedFloats == kWaves * kMfmaGroups * 16 * 8, "LDS for the partial tiles");
+static_assert(kMfmaRedFloats == kWaves * kMfmaGroups * 16 * 16, "LDS for the partial tiles");
 
 struct BatchInput {
   const float *x;        // fp32 rows, `stride` floats apart (null when emb is set)
@@ -1235,7 +1252,7 @@ struct MfmaTile {
 
 // one pass: groups [g0, g0 + gn) (gn <= GP) over this wave's k steps, the loads of U steps
 // issued before any of them is used; returns the partial tiles
-template <int WT, int GP, int U, bool GAIN>
+template <int WT, int GP, int U, bool GAIN, bool WIDE>
 __device__ __forceinline__ void mfma_pass(const MfmaTile &T, int g0, int gn, bool sumsq, float &ss,
                                           f32x4_t (&acc)[kMfmaGroups]) {
 #pragma unroll
@@ -1292,37 +1309,42 @@ __device__ __forceinline__ void mfma_pass(const MfmaTile &T, int g0, int gn, boo
 #pragma unroll
           for (int i = 0; i < 8; ++i) xv[i] = __uint_as_float(xw[u][i]);
         }
-        // x * gain as one bf16 half (hi for columns < 8, lo for the others); inputs past K are 0
-        uint32_t hx[4];
+        // x * gain as bf16 halves: packed, the hi half for columns < 8 and the lo half for the
+        // others; wide, both halves of the column's sequence. Inputs past K are 0.
+        uint32_t hx[4], lx[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v0 = k + 2 * i < T.K ? xv[2 * i] : 0.f, v1 = k + 2 * i + 1 < T.K ? xv[2 * i + 1] : 0.f;
-          if (sumsq && !T.lo_half) ss = fmaf(v0, v0, fmaf(v1, v1, ss));
+          if (sumsq && (WIDE || !T.lo_half)) ss = fmaf(v0, v0, fmaf(v1, v1, ss));
           if constexpr (GAIN) {
             v0 *= bf_lo(gw[u][i]);
             v1 *= bf_hi(gw[u][i]);
           }
-          uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
-          if (T.lo_half) {
-            h0 = f32_to_bf16(v0 - bf16_to_f32(h0));
-            h1 = f32_to_bf16(v1 - bf16_to_f32(h1));
-          }
-          hx[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          const uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
+          const uint16_t l0 = f32_to_bf16(v0 - bf16_to_f32(h0)), l1 = f32_to_bf16(v1 - bf16_to_f32(h1));
+          if (!WIDE && T.lo_half)
+            hx[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+          else
+            hx[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          lx[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
         }
         const bf16x8_t xb = bf16x8_of_bits(hx[0], hx[1], hx[2], hx[3]);
+        const bf16x8_t xl = bf16x8_of_bits(lx[0], lx[1], lx[2], lx[3]);  // wide only
         if constexpr (WT == 2) {
           // int4: each k step's products, less 136 times the input column sums, times the
           // step's group scale of each row (a k step of 32 inputs lies in one group)
           const uint32_t c136 = 0x43084308u;  // bf16 136.0, twice
-          const f32x4_t corr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              bf16x8_of_bits(c136, c136, c136, c136), xb, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          const bf16x8_t a136 = bf16x8_of_bits(c136, c136, c136, c136);
+          f32x4_t corr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a136, xb, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          if constexpr (WIDE) corr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a136, xl, corr, 0, 0, 0);
           const f32x4_t ncorr = -corr;
           const int grp = (32 * (t + u)) / T.gs;
 #pragma unroll
           for (int g = 0; g < GP; ++g) {
             if (g < gn) {
-              const f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  bf16x8_of_i4_offset(wf[u][g][0]), xb, ncorr, 0, 0, 0);
+              const bf16x8_t a = bf16x8_of_i4_offset(wf[u][g][0]);
+              f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb, ncorr, 0, 0, 0);
+              if constexpr (WIDE) p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl, p, 0, 0, 0);
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int r = min(16 * (g0 + g) + 4 * T.kq + i, T.n - 1);
@@ -1337,11 +1359,32 @@ __device__ __forceinline__ void mfma_pass(const MfmaTile &T, int g0, int gn, boo
               const bf16x8_t a = WT == 0 ? bf16x8_of_bits(wf[u][g][0], wf[u][g][1], wf[u][g][2], wf[u][g][3])
                                          : bf16x8_of_i8(wf[u][g][0], wf[u][g][1]);
               acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb, acc[g], 0, 0, 0);
+              if constexpr (WIDE) acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl, acc[g], 0, 0, 0);
             }
           }
         }
       }
     }
+  }
+}
+
+template <int WT, bool WIDE>
+__device__ __forceinline__ void mfma_dispatch(const MfmaTile &T, int g0, int gn, bool sq, float &ss,
+                                              f32x4_t (&acc)[kMfmaGroups]) {
+  if (T.gain) {
+    if (gn <= 1)
+      mfma_pass<WT, 1, 4, true, WIDE>(T, g0, gn, sq, ss, acc);
+    else if (gn == 2)
+      mfma_pass<WT, 2, 4, true, WIDE>(T, g0, gn, sq, ss, acc);
+    else
+      mfma_pass<WT, 4, 2, true, WIDE>(T, g0, gn, sq, ss, acc);
+  } else {
+    if (gn <= 1)
+      mfma_pass<WT, 1, 4, false, WIDE>(T, g0, gn, sq, ss, acc);
+    else if (gn == 2)
+      mfma_pass<WT, 2, 4, false, WIDE>(T, g0, gn, sq, ss, acc);
+    else
+      mfma_pass<WT, 4, 2, false, WIDE>(T, g0, gn, sq, ss, acc);
   }
 }
 
@@ -1364,14 +1407,16 @@ __device__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, c
   T.t1 = (int)((int64_t)steps * (wave + 1) / NW);
   T.col = lane & 15;
   T.kq = lane >> 4;
-  T.lo_half = T.col >= 8;
+  const bool wide = B > 8;  // one column per sequence, both halves by two instructions
+  const int NC = wide ? 16 : 8;  // columns of the partial tiles in LDS
+  T.lo_half = !wide && T.col >= 8;
   T.emb = in.emb != nullptr;
   T.gain = in.gain != nullptr;
   T.rw = make_rsrc(static_cast<const uint8_t *>(W) + (int64_t)r0 * T.rb, (uint32_t)n * (uint32_t)T.rb);
   T.rx = in.emb ? make_rsrc(in.emb, (uint32_t)m.V * (uint32_t)K * 2u)
                 : make_rsrc(in.x, (uint32_t)B * (uint32_t)in.stride * 4u);
   T.rg = make_rsrc(in.gain ? in.gain : m.final_norm, (uint32_t)K * 2u);
-  const int b = T.col & 7;
+  const int b = wide ? T.col : (T.col & 7);
   T.xrow = 0xffffffffu;
   if (b < B) T.xrow = in.emb ? (uint32_t)token_of(m, s, b) * (uint32_t)K * 2u : (uint32_t)b * (uint32_t)in.stride * 4u;
   float ss = 0.f;
@@ -1379,21 +1424,10 @@ __device__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, c
     const int gn = min(kMfmaGroups, G - g0);
     const bool sq = in.sumsq && g0 == 0;
     f32x4_t acc[kMfmaGroups];
-    if (T.gain) {
-      if (gn <= 1)
-        mfma_pass<WT, 1, 4, true>(T, g0, gn, sq, ss, acc);
-      else if (gn == 2)
-        mfma_pass<WT, 2, 4, true>(T, g0, gn, sq, ss, acc);
-      else
-        mfma_pass<WT, 4, 2, true>(T, g0, gn, sq, ss, acc);
-    } else {
-      if (gn <= 1)
-        mfma_pass<WT, 1, 4, false>(T, g0, gn, sq, ss, acc);
-      else if (gn == 2)
-        mfma_pass<WT, 2, 4, false>(T, g0, gn, sq, ss, acc);
-      else
-        mfma_pass<WT, 4, 2, false>(T, g0, gn, sq, ss, acc);
-    }
+    if (wide)
+      mfma_dispatch<WT, true>(T, g0, gn, sq, ss, acc);
+    else
+      mfma_dispatch<WT, false>(T, g0, gn, sq, ss, acc);
     // partial tiles of all waves (16 columns: hi and lo halves) -> ys
 #pragma unroll
     for (int g = 0; g < kMfmaGroups; ++g)
@@ -1403,16 +1437,16 @@ __device__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, c
           // column c of row 4 kq + i: hi and lo of one sequence land in the same float
           const int row = 4 * T.kq + i;
           float v = acc[g][i];
-          v += __shfl_xor(v, 8, 64);  // lanes c and c ^ 8 hold the two halves of sequence c & 7
-          if (T.col < 8) mred[((wave * kMfmaGroups + g) * 16 + row) * 8 + T.col] = v;
+          if (!wide) v += __shfl_xor(v, 8, 64);  // lanes c and c ^ 8: the halves of sequence c & 7
+          if (T.col < NC) mred[((wave * kMfmaGroups + g) * 16 + row) * NC + T.col] = v;
         }
     __syncthreads();
-    for (int e = threadIdx.x; e < gn * 16 * 8; e += NW * 64) {
-      const int g = e >> 7, row = (e >> 3) & 15, bb = e & 7;
+    for (int e = threadIdx.x; e < gn * 16 * NC; e += NW * 64) {
+      const int g = e / (16 * NC), row = (e / NC) & 15, bb = e % NC;
       const int r = 16 * (g0 + g) + row;
       if (bb < B && r < n) {
         float t = 0.f;
-        for (int w = 0; w < NW; ++w) t += mred[((w * kMfmaGroups + g) * 16 + row) * 8 + bb];
+        for (int w = 0; w < NW; ++w) t += mred[((w * kMfmaGroups + g) * 16 + row) * NC + bb];
         if constexpr (WT == 1) t *= gld(&scale[r0 + r]);
         ys[bb * n + r] = t;
       }
@@ -1422,7 +1456,7 @@ __device__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, c
   if (in.sumsq) {
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
-    if (T.kq == 0 && T.col < B && T.col < 8) red[T.col * NW + wave] = ss;
+    if (T.kq == 0 && T.col < B && (wide || T.col < 8)) red[T.col * NW + wave] = ss;
   }
 }
 
@@ -1439,8 +1473,9 @@ __device__ __forceinline__ int64_t kv_index(const DevModel &m, const StepArgs &s
 __device__ void epi_qkv(const DevModel &m, const StepArgs &s, int l, int r0, int r1,
                         const float *ys, int nw) {
   const int n = r1 - r0, hd = m.hd, half = hd / 2;
-  const float2 *cs = m.rope + (int64_t)s.pos * half;
   for (int b = 0; b < s.batch; ++b) {
+    const int pb = pos_of(s, b);
+    const float2 *cs = m.rope + (int64_t)pb * half;
     for (int pi = threadIdx.x; pi < n / 2; pi += nw * 64) {
       const int r = r0 + 2 * pi;
       const QkvRow q0 = qkv_decode(r, m.nq, m.nkv, hd);
@@ -1466,8 +1501,8 @@ __device__ void epi_qkv(const DevModel &m, const StepArgs &s, int l, int r0, int
       } else {
         const int kvi = (q0.kind == KIND_K) ? 0 : 1;
         const uint16_t k0 = f32_to_bf16(v0), k1 = f32_to_bf16(v1);
-        uint16_t *c0 = &s.kv[kv_index(m, s, l, kvi, b, q0.head, s.pos, q0.dim)];
-        uint16_t *c1 = &s.kv[kv_index(m, s, l, kvi, b, q1.head, s.pos, q1.dim)];
+        uint16_t *c0 = &s.kv[kv_index(m, s, l, kvi, b, q0.head, pb, q0.dim)];
+        uint16_t *c1 = &s.kv[kv_index(m, s, l, kvi, b, q1.head, pb, q1.dim)];
         if (m.max_batch == 1) {
           // This step's attention blocks take the row from tagged words. A single-step launch's
           // cache row is read only by later launches (the kernel boundary makes it visible), so
@@ -1691,14 +1726,15 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
   const int qpg = qn, nq = m.nq, nblk = m.nblk;
   const int lane = lane_id(), wave = wave_id();
   const int sub = lane % LPR, rs = lane / LPR;
-  const int pos = s.pos;
-  int lo, hi;
-  attn_block_range(pos + 1, nblk, blk, &lo, &hi);
   float *qs = lds;                             // [qpg][HD]
   float *sc = qs + qpg * HD;                   // [qpg][chunk]
   float *accw = sc + qpg * CH;                 // [NW][qpg*HD]
   uint16_t *kvrow = reinterpret_cast<uint16_t *>(accw + NW * qpg * HD);  // [2][HD]
   for (int b = 0; b < s.batch; ++b) {
+    // this sequence's position and its part of the KV block's range
+    const int pos = pos_of(s, b);
+    int lo, hi;
+    attn_block_range(pos + 1, nblk, blk, &lo, &hi);
     const uint16_t *Kb = s.kv + kv_index(m, s, l, 0, b, g, 0, 0);
     const uint16_t *Vb = s.kv + kv_index(m, s, l, 1, b, g, 0, 0);
     uint4 kr[NIT], vr[NIT];

@@ -255,6 +255,7 @@ __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArg
     s.step = step;
     s.epoch = s0.epoch + (uint32_t)step;
     s.pos = s0.pos + step;
+    s.posp = &s0.pos_in[0];
     if (step > 0) s.tokens = s0.next + (int64_t)(step - 1) * s0.batch;
     s.next = s0.next + (int64_t)step * s0.batch;
     if (s0.logits) s.logits = s0.logits + (int64_t)step * s0.batch * m.V;

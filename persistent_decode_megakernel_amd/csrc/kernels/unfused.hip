@@ -46,7 +46,7 @@ __device__ void uf_gemv(const DevModel &m, const StepArgs &s, const void *W, con
   extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte reads of xs need it
   float *red = lds;                       // 64 * 8
   float *ys = red + 64 * 8;               // batch * kUfRowsPerBlock
-  float *xs = ys + 8 * kUfRowsPerBlock;   // K (batch 1) or the matrix cores' partial tiles
+  float *xs = ys + kMaxBatch * kUfRowsPerBlock;  // K (batch 1) or the matrix cores' partial tiles
   const int r0 = blockIdx.x * kUfRowsPerBlock, r1 = min(rows, r0 + kUfRowsPerBlock);
   if (s.batch == 1) {
     stage_plain(x, K, K, 1, xs, kUfWaves);
@@ -89,6 +89,7 @@ AMK_UF_GEMV(2, 2)
 extern "C" __global__ void __launch_bounds__(256) amk_uf_rope_kv(const DevModel *__restrict__ mp,
                                                                  StepArgs s, int l) {
   const DevModel &m = *mp;
+  const StepArgs sp = with_positions(s);
   const int b = blockIdx.y;
   const int pi = blockIdx.x * 256 + threadIdx.x;
   if (pi >= m.qkvr / 2) return;
@@ -98,7 +99,7 @@ extern "C" __global__ void __launch_bounds__(256) amk_uf_rope_kv(const DevModel 
   const QkvRow q1 = qkv_decode(r + 1, m.nq, m.nkv, hd);
   float v0 = y[r], v1 = y[r + 1];
   if (q0.kind != KIND_V) {
-    const float2 c = m.rope[(int64_t)s.pos * (hd / 2) + q0.dim];
+    const float2 c = m.rope[(int64_t)pos_of(sp, b) * (hd / 2) + q0.dim];
     const float a = v0, bb = v1;
     v0 = a * c.x - bb * c.y;
     v1 = bb * c.x + a * c.y;
@@ -109,8 +110,8 @@ extern "C" __global__ void __launch_bounds__(256) amk_uf_rope_kv(const DevModel 
     qb[q1.head * hd + q1.dim] = v1;
   } else {
     const int kvi = (q0.kind == KIND_K) ? 0 : 1;
-    s.kv[kv_index(m, s, l, kvi, b, q0.head, s.pos, q0.dim)] = f32_to_bf16(v0);
-    s.kv[kv_index(m, s, l, kvi, b, q1.head, s.pos, q1.dim)] = f32_to_bf16(v1);
+    s.kv[kv_index(m, s, l, kvi, b, q0.head, pos_of(sp, b), q0.dim)] = f32_to_bf16(v0);
+    s.kv[kv_index(m, s, l, kvi, b, q1.head, pos_of(sp, b), q1.dim)] = f32_to_bf16(v1);
   }
 }
 
@@ -119,7 +120,8 @@ __device__ void uf_attn(const DevModel &m, const StepArgs &s, int l) {
   extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte reads of xs need it
   float *red = lds;
   float *work = lds + 64 * 8;
-  attn_task<HD, QMAX, false>(m, s, l, blockIdx.x, blockIdx.y, work, red, nullptr, nullptr);
+  attn_task<HD, QMAX, false>(m, with_positions(s), l, blockIdx.x, blockIdx.y, work, red, nullptr,
+                             nullptr);
 }
 
 #define AMK_UF_ATTN(HD, Q)                                                                   \

@@ -540,9 +540,9 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
       if (per_cu < 1) throw std::runtime_error("megakernel workgroup does not fit on a CU");
     } else {
       // a step may run any batch up to max_batch: allow the larger of the two GEMV layouts
-      const uint32_t gl = 4u * (64 * 8 + 8 * kUfRowsPerBlock +
+      const uint32_t gl = 4u * (64 * 8 + kMaxBatch * kUfRowsPerBlock +
                                 (uint32_t)std::max<int>(kmax, B > 1 ? kMfmaRedFloats : 0));
-      for (int wt = 0; wt < 2; ++wt)
+      for (int wt = 0; wt < 3; ++wt)
         for (int mode = 0; mode < 3; ++mode)
           hip_check(hipFuncSetAttribute((const void *)pick_uf_gemv(wt, mode),
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)gl),
@@ -634,7 +634,7 @@ static void launch_unfused(amk_model *m, const StepArgs &s, hipStream_t st) {
   const DevModel *g = m->d_dm;
   const int B = s.batch, L = dm.L, d = dm.d;
   const int wt = dm.wtype;
-  const uint32_t gl = 4u * (64 * 8 + 8 * kUfRowsPerBlock +
+  const uint32_t gl = 4u * (64 * 8 + kMaxBatch * kUfRowsPerBlock +
                             (uint32_t)(B == 1 ? std::max(std::max(d, dm.qd), dm.F) : kMfmaRedFloats));
   auto grid = [](int rows) { return dim3((rows + kUfRowsPerBlock - 1) / kUfRowsPerBlock); };
   float *h = dm.h;
@@ -659,18 +659,22 @@ static void launch_unfused(amk_model *m, const StepArgs &s, hipStream_t st) {
   hipLaunchKernelGGL(amk_uf_argmax, dim3(1), dim3(64), 0, st, g, s, m->n_lm_uf);
 }
 
-extern "C" amk_status amk_decode_steps(amk_model *m, amk_kv *kv, const int32_t *d_tokens,
-                                       int32_t pos, int32_t n_steps, int32_t batch,
-                                       float *d_logits, int32_t *d_out, void *stream) {
-  AMK_API_BEGIN
-  if (!m || !kv || !d_tokens || !d_out) return set_error(AMK_E_INVALID, "amk_decode_steps: null argument");
-  if (kv->m != m) return set_error(AMK_E_INVALID, "amk_decode_steps: KV cache belongs to another model");
-  if (n_steps < 1) return set_error(AMK_E_INVALID, "amk_decode_steps: n_steps must be >= 1");
+namespace {
+
+// n_steps greedy steps of `batch` sequences, sequence b at position pos[b] in the first step
+amk_status decode(amk_model *m, amk_kv *kv, const int32_t *d_tokens, const int32_t *pos,
+                  int32_t n_steps, int32_t batch, float *d_logits, int32_t *d_out, void *stream,
+                  const char *fn) {
+  const std::string f(fn);
+  if (!m || !kv || !d_tokens || !d_out || !pos) return set_error(AMK_E_INVALID, f + ": null argument");
+  if (kv->m != m) return set_error(AMK_E_INVALID, f + ": KV cache belongs to another model");
+  if (n_steps < 1) return set_error(AMK_E_INVALID, f + ": n_steps must be >= 1");
+  if (n_steps > 0x100000) return set_error(AMK_E_INVALID, f + ": n_steps too large");
   if (batch < 1 || batch > m->cfg.max_batch || batch > kv->batch)
-    return set_error(AMK_E_CAPACITY, "amk_decode_steps: batch exceeds max_batch or the KV cache");
-  if (pos < 0 || (int64_t)pos + n_steps > std::min(kv->max_seq, m->cfg.max_seq))
-    return set_error(AMK_E_CAPACITY, "amk_decode_steps: positions beyond max_seq");
-  if (n_steps > 0x100000) return set_error(AMK_E_INVALID, "amk_decode_steps: n_steps too large");
+    return set_error(AMK_E_CAPACITY, f + ": batch exceeds max_batch or the KV cache");
+  for (int32_t b = 0; b < batch; ++b)
+    if (pos[b] < 0 || (int64_t)pos[b] + n_steps > std::min(kv->max_seq, m->cfg.max_seq))
+      return set_error(AMK_E_CAPACITY, f + ": positions beyond max_seq");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (m->epoch >= 0x7ffffff0u - (uint32_t)n_steps) {  // keep the signed flag comparison unambiguous
     zero_async(m->dm.flags, sizeof(uint32_t) * std::max<uint32_t>(1, m->sched.hdr.n_tasks), st);
@@ -684,7 +688,9 @@ extern "C" amk_status amk_decode_steps(amk_model *m, amk_kv *kv, const int32_t *
   s.kv = static_cast<uint16_t *>(kv->data);
   s.kv_batch = kv->batch;
   s.kv_max_seq = kv->max_seq;
-  s.pos = pos;
+  s.pos = pos[0];
+  for (int32_t b = 0; b < kMaxBatch; ++b) s.pos_in[b] = b < batch ? pos[b] : 0;
+  s.posp = nullptr;  // set on the device
   s.batch = batch;
   s.epoch = m->epoch + 1;
   s.step = 0;
@@ -701,7 +707,8 @@ extern "C" amk_status amk_decode_steps(amk_model *m, amk_kv *kv, const int32_t *
     for (int32_t i = 0; i < n_steps; ++i) {
       StepArgs si = s;
       si.n_steps = 1;
-      si.pos = pos + i;
+      si.pos = pos[0] + i;
+      for (int32_t b = 0; b < batch; ++b) si.pos_in[b] = pos[b] + i;
       si.epoch = s.epoch + (uint32_t)i;
       si.tokens = i ? d_out + (int64_t)(i - 1) * batch : d_tokens;
       si.next = d_out + (int64_t)i * batch;
@@ -713,6 +720,27 @@ extern "C" amk_status amk_decode_steps(amk_model *m, amk_kv *kv, const int32_t *
   }
   clear_error();
   return AMK_OK;
+}
+
+}  // namespace
+
+extern "C" amk_status amk_decode_steps(amk_model *m, amk_kv *kv, const int32_t *d_tokens,
+                                       int32_t pos, int32_t n_steps, int32_t batch,
+                                       float *d_logits, int32_t *d_out, void *stream) {
+  AMK_API_BEGIN
+  int32_t pv[kMaxBatch];
+  for (int32_t b = 0; b < kMaxBatch; ++b) pv[b] = pos;
+  if (batch > kMaxBatch) return set_error(AMK_E_CAPACITY, "amk_decode_steps: batch exceeds max_batch");
+  return decode(m, kv, d_tokens, pv, n_steps, batch, d_logits, d_out, stream, "amk_decode_steps");
+  AMK_API_END
+}
+
+extern "C" amk_status amk_decode_steps_ragged(amk_model *m, amk_kv *kv, const int32_t *d_tokens,
+                                              const int32_t *h_pos, int32_t n_steps, int32_t batch,
+                                              float *d_logits, int32_t *d_out, void *stream) {
+  AMK_API_BEGIN
+  return decode(m, kv, d_tokens, h_pos, n_steps, batch, d_logits, d_out, stream,
+                "amk_decode_steps_ragged");
   AMK_API_END
 }
 

@@ -40,7 +40,7 @@ bool config_ok(const amk_config &c, std::string *err) {
     return fail("config: hidden must equal n_heads * head_dim");
   if (c.head_dim > 256) return fail("config: head_dim > 256 unsupported");
   if (c.n_heads / c.n_kv_heads > 16) return fail("config: more than 16 query heads per KV head");
-  if (c.max_batch < 1 || c.max_batch > 8) return fail("config: max_batch must be in [1, 8]");
+  if (c.max_batch < 1 || c.max_batch > kMaxBatch) return fail("config: max_batch must be in [1, 16]");
   if (c.max_seq < 1) return fail("config: max_seq must be >= 1");
   if (c.wtype != AMK_WT_BF16 && c.wtype != AMK_WT_INT8 && c.wtype != AMK_WT_INT4)
     return fail("config: unknown wtype");

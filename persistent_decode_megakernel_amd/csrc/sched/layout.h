@@ -136,7 +136,9 @@ constexpr int32_t kDigitMaxK = 16384;
 
 // Staged GEMV input (batch 1 only: batched GEMVs read their inputs straight from memory and use
 // the region for the partial tiles of the matrix-core reduction instead).
-constexpr int32_t kMfmaRedFloats = kWaves * 4 * 16 * 8;
+constexpr int32_t kMaxBatch = 16;  // sequences per step
+// partial 16-row tiles of the batched GEMV: waves x row groups x 16 rows x 16 columns
+constexpr int32_t kMfmaRedFloats = kWaves * 4 * 16 * 16;
 AMK_HD int32_t lds_xs_floats(int32_t batch, int32_t hidden, int32_t qdim, int32_t ffn) {
   int32_t k = hidden > qdim ? hidden : qdim;
   k = k > ffn ? k : ffn;

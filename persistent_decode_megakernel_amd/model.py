@@ -157,13 +157,24 @@ class Model:
         _lib.check(st, "amk_decode_step")
         return next_out
 
-    def steps(self, kv: KVCache, tokens: torch.Tensor, pos: int, n_steps: int,
+    def steps(self, kv: KVCache, tokens: torch.Tensor, pos, n_steps: int,
               logits: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-        """n_steps greedy decode steps in one launch (amk_decode_steps). tokens: device int32 [B].
+        """n_steps greedy decode steps in one launch (amk_decode_steps). tokens: device int32 [B];
+        pos: one position for all sequences, or a sequence of B positions (amk_decode_steps_ragged).
         Returns the device int32 [n_steps, B] tokens; logits (if given): [n_steps, B, V] float32."""
         B = tokens.numel()
         if out is None:
             out = torch.empty((n_steps, B), dtype=torch.int32, device=self.device)
+        if not isinstance(pos, int):
+            pv = (C.c_int32 * B)(*[int(p) for p in pos])
+            if len(pos) != B:
+                raise ValueError("one position per sequence")
+            st = self.lib.amk_decode_steps_ragged(
+                self.handle, kv.handle, C.c_void_p(tokens.data_ptr()), pv, n_steps, B,
+                C.c_void_p(_ptr(logits)) if logits is not None else None,
+                C.c_void_p(out.data_ptr()), _stream_ptr())
+            _lib.check(st, "amk_decode_steps_ragged")
+            return out
         st = self.lib.amk_decode_steps(self.handle, kv.handle, C.c_void_p(tokens.data_ptr()), pos,
                                        n_steps, B,
                                        C.c_void_p(_ptr(logits)) if logits is not None else None,

@@ -153,13 +153,24 @@ def test_tiny_batch3(path):
     assert_parity(rep)
 
 
+@pytest.mark.parametrize("path", ["megakernel", "unfused"])
+def test_tiny_batch16(path):
+    """Sixteen sequences: the matrix cores take one column per sequence and multiply the two bf16
+    halves of the input by two instructions."""
+    cfg = synth.get_config("tiny").replace(batch=16)
+    rep = teacher_forced(cfg, path, seed=8, n_calls=6)
+    assert rep.tokens_checked > 0
+    assert_parity(rep)
+
+
 def test_smollm2_135m_batch2_prefill():
     cfg = synth.get_config("smollm2_135m").replace(batch=2)
     rep = teacher_forced(cfg, "megakernel", seed=5, n_calls=3)
     assert_parity(rep)
 
 
-@pytest.mark.parametrize("name", ["llama2_7b", "llama2_7b_w8a16", "llama2_7b_w4a16", "llama2_7b_b8"])
+@pytest.mark.parametrize("name", ["llama2_7b", "llama2_7b_w8a16", "llama2_7b_w4a16", "llama2_7b_b8",
+                                  "llama2_7b_b16"])
 def test_full_size_first_steps(name):
     """Full 7B shapes in the launch configuration the bench times (one cooperative launch per
     step on every CU), checked against the oracle on every logit for the first two steps."""
