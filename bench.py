@@ -123,6 +123,51 @@ def time_multistep(cfg, weights, kv_host, steps, warmup):
     return ms, ids
 
 
+def time_prompt_scenario(cfg, weights, n_in=64, n_out=12, reps=3):
+    """The pages' fixed short-sequence scenario (input 64 tokens, output 12; Ada-MK summary,
+    "Experimental Results"), from an empty cache. Hybrid: the prompt through amk_prefill (up to 16
+    tokens per matrix-core pass), then the 12 greedy steps as one megakernel launch. Decode only:
+    the 64 prompt tokens fed as 64 single megakernel steps, then the same 12 steps. Returns ms of
+    each (best of `reps`) and whether both produced the same 12 tokens."""
+    import numpy as np
+    import torch
+    from persistent_decode_megakernel_amd.model import Model
+
+    cfg1 = cfg.replace(batch=1)
+    max_seq = n_in + n_out + 1
+    model = Model(cfg1, weights, path="megakernel", max_seq=max_seq)
+    prompt = torch.from_numpy(
+        np.random.default_rng(64).integers(0, cfg.vocab, n_in).astype(np.int32)).cuda()
+    stream = torch.cuda.current_stream()
+    best = {"hybrid": 1e30, "decode_only": 1e30}
+    outs = {}
+    for _ in range(reps):
+        for mode in ("hybrid", "decode_only"):
+            kv = model.kv(1, max_seq)
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            if mode == "hybrid":
+                nxt = model.prefill(kv, prompt, 0)
+            else:
+                nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+                for i in range(n_in):
+                    model.step(kv, prompt[i:i + 1], i, next_out=nxt)
+            out = model.steps(kv, nxt, n_in, n_out)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            model.sync()
+            best[mode] = min(best[mode], ev[0].elapsed_time(ev[1]))
+            outs[mode] = out.cpu().numpy().ravel().tolist()
+            kv.close()
+    model.close()
+    torch.cuda.empty_cache()
+    return {"input_tokens": n_in, "output_tokens": n_out,
+            "hybrid_ms": round(best["hybrid"], 3), "decode_only_ms": round(best["decode_only"], 3),
+            "hybrid_speedup": round(best["decode_only"] / best["hybrid"], 3),
+            "same_output_tokens": outs["hybrid"] == outs["decode_only"]}
+
+
 def profiled_traffic(cfg, kernel_name):
     """Per-launch HBM bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from the committed
     rocprofv3 summary of this workload, or None when the kernel sources changed since."""
@@ -184,6 +229,7 @@ def main():
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-multistep", action="store_true")
+    ap.add_argument("--no-scenario", action="store_true")
     ap.add_argument("--batch", type=int, default=0,
                     help="override the workload's batch (sequences per step, 1..16)")
     ap.add_argument("--cpu-sample-steps", type=int, default=2)
@@ -281,6 +327,9 @@ def main():
             "same_final_ids": ids_m == ids,
         }
         log(f"[bench] multistep: {ms_m:.4f} ms/step in one launch of {steps}")
+    if not args.no_scenario and cfg.batch == 1:
+        out["scenario_in64_out12"] = time_prompt_scenario(cfg, weights)
+        log(f"[bench] in64/out12: {out['scenario_in64_out12']}")
     if not args.no_ablation:
         for key, graph in (("ablation_unfused", False), ("ablation_unfused_hipgraph", True)):
             ms_u, per_u, info_u, ids_u = time_path(cfg, weights, kv_host, "unfused", steps, warmup,

@@ -172,6 +172,21 @@ amk_status amk_decode_steps_ragged(amk_model *m, amk_kv *kv, const int32_t *d_to
                                    const int32_t *h_pos, int32_t n_steps, int32_t batch,
                                    float *d_logits, int32_t *d_out, void *stream);
 
+/* Prompt processing: the n_tokens prompt ids d_tokens (device int32 [n_tokens]) of KV sequence
+ * `seq` at positions pos0 .. pos0 + n_tokens - 1, run as operator launches whose GEMVs take up to 16
+ * tokens at once on the matrix cores (each token a column at its own position, all columns
+ * reading and appending the one sequence's KV rows). It writes those KV rows, the greedy next token
+ * after the prompt to d_next (device int32 [1]) and, when d_logits is not NULL, the last prompt
+ * token's logits (device float32 [vocab]). Decoding then continues at pos0 + n_tokens with
+ * amk_decode_step(s). This is the pages' hybrid engine: prompt processing on ordinary fused
+ * operators, decoding on the megakernel (Ada-MK summary, "Methodology", Phase II). The first call
+ * allocates the scratch of the prompt engine (freed with the model); it is stream-ordered with the
+ * model's other calls. Errors: AMK_E_CAPACITY if seq is outside the KV cache or the positions
+ * exceed max_seq, AMK_E_INVALID for null pointers or n_tokens < 1. */
+amk_status amk_prefill(amk_model *m, amk_kv *kv, int32_t seq, const int32_t *d_tokens,
+                       int32_t pos0, int32_t n_tokens, float *d_logits, int32_t *d_next,
+                       void *stream);
+
 /* Synchronise `stream` and report a device-side error recorded by earlier steps (and clear it). */
 amk_status amk_sync(amk_model *m, void *stream);
 

@@ -82,6 +82,8 @@ SIGNATURES = {
                                    C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
     "amk_decode_steps_ragged": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(C.c_int32),
                                           C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "amk_prefill": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_int32,
+                              C.c_void_p, C.c_void_p, C.c_void_p]),
     "amk_sync": (C.c_int, [C.c_void_p, C.c_void_p]),
     "amk_model_get_info": (C.c_int, [C.c_void_p, C.POINTER(amk_model_info)]),
     "amk_trace_enable": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t]),

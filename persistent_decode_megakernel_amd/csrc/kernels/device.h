@@ -76,6 +76,9 @@ struct StepArgs {
   int32_t step, n_steps;
   int32_t pos_in[kMaxBatch];
   const int32_t *posp;
+  // -1: column b is KV sequence b. Otherwise every column is a position of KV sequence kv_seq
+  // (prompt processing: the columns are consecutive tokens of one sequence).
+  int32_t kv_seq;
 };
 
 constexpr uint32_t ERR_TIMEOUT = 7;
@@ -1465,7 +1468,8 @@ __device__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, c
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ int64_t kv_index(const DevModel &m, const StepArgs &s, int l, int kvi,
                                             int b, int g, int p, int dim) {
-  return (((((int64_t)l * 2 + kvi) * s.kv_batch + b) * m.nkv + g) * s.kv_max_seq + p) *
+  const int64_t kb = s.kv_seq >= 0 ? s.kv_seq : b;  // the KV sequence of column b
+  return (((((int64_t)l * 2 + kvi) * s.kv_batch + kb) * m.nkv + g) * s.kv_max_seq + p) *
              (int64_t)m.hd + dim;
 }
 

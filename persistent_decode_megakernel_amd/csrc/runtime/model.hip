@@ -154,6 +154,11 @@ struct amk_model {
   std::vector<void *> allocs;
   DevModel dm{};
   DevModel *d_dm = nullptr;
+  // prompt processing (amk_prefill): the model's weights with scratch for kMaxBatch columns,
+  // created by the first call
+  DevModel dm_pf{};
+  DevModel *d_dm_pf = nullptr;
+  int32_t *pf_next = nullptr;  // device int32 [kMaxBatch]
   std::vector<DevLayer> layers;
   uint32_t epoch = 0;
   uint32_t lds_bytes = 0;
@@ -629,9 +634,10 @@ extern "C" amk_status amk_kv_free(amk_kv *kv) {
   return AMK_OK;
 }
 
-static void launch_unfused(amk_model *m, const StepArgs &s, hipStream_t st) {
-  const DevModel &dm = m->dm;
-  const DevModel *g = m->d_dm;
+// One step as a sequence of operator launches, on the model's scratch (dm, g = its device copy):
+// the unfused ablation, and prompt processing.
+static void launch_unfused(amk_model *m, const DevModel &dm, const DevModel *g, const StepArgs &s,
+                           hipStream_t st) {
   const int B = s.batch, L = dm.L, d = dm.d;
   const int wt = dm.wtype;
   const uint32_t gl = 4u * (64 * 8 + kMaxBatch * kUfRowsPerBlock +
@@ -690,6 +696,7 @@ amk_status decode(amk_model *m, amk_kv *kv, const int32_t *d_tokens, const int32
   s.kv_max_seq = kv->max_seq;
   s.pos = pos[0];
   for (int32_t b = 0; b < kMaxBatch; ++b) s.pos_in[b] = b < batch ? pos[b] : 0;
+  s.kv_seq = -1;
   s.posp = nullptr;  // set on the device
   s.batch = batch;
   s.epoch = m->epoch + 1;
@@ -713,7 +720,7 @@ amk_status decode(amk_model *m, amk_kv *kv, const int32_t *d_tokens, const int32
       si.tokens = i ? d_out + (int64_t)(i - 1) * batch : d_tokens;
       si.next = d_out + (int64_t)i * batch;
       si.logits = d_logits ? d_logits + (int64_t)i * batch * m->cfg.vocab : nullptr;
-      launch_unfused(m, si, st);
+      launch_unfused(m, m->dm, m->d_dm, si, st);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return set_error(AMK_E_HIP, std::string("unfused launch: ") + hipGetErrorString(e));
@@ -748,6 +755,93 @@ extern "C" amk_status amk_decode_step(amk_model *m, amk_kv *kv, const int32_t *d
                                       int32_t pos, int32_t batch, float *d_logits,
                                       int32_t *d_next, void *stream) {
   return amk_decode_steps(m, kv, d_tokens, pos, 1, batch, d_logits, d_next, stream);
+}
+
+namespace {
+
+// The prompt-processing copy of the model: weights shared, scratch for kMaxBatch columns.
+void prefill_init(amk_model *m, hipStream_t st) {
+  if (m->d_dm_pf) return;
+  DevModel dp = m->dm;
+  const int L = dp.L, d = dp.d, qd = dp.qd, F = dp.F, V = dp.V, C = kMaxBatch;
+  const int kmax = std::max(std::max(d, qd), F);
+  dp.max_batch = C;
+  dp.h = m->dalloc<float>((size_t)(2 * L + 1) * C * d);
+  dp.q = m->dalloc<float>((size_t)L * C * qd);
+  dp.part = m->dalloc<float>((size_t)L * C * dp.nq * dp.nblk * (dp.hd + 2));
+  dp.ao = m->dalloc<float>((size_t)L * C * qd);
+  dp.a = m->dalloc<float>((size_t)L * C * F);
+  dp.logits = m->dalloc<float>((size_t)C * V);
+  dp.amax = m->dalloc<float2>((size_t)std::max<int>(m->n_lm_uf, dp.n_lm) * C);
+  dp.xn = m->dalloc<float>((size_t)C * kmax);
+  dp.y = m->dalloc<float>((size_t)C * std::max(std::max(dp.qkvr, 2 * F), std::max(V, d)));
+  dp.o = m->dalloc<float>((size_t)C * qd);
+  m->pf_next = m->dalloc<int32_t>(C);
+  DevModel *g = m->dalloc<DevModel>(1);
+  hip_check(hipMemcpyAsync(g, &dp, sizeof dp, hipMemcpyHostToDevice, st), "hipMemcpyAsync");
+  // the operator kernels at the widest layout (a megakernel model has not set them)
+  const uint32_t gl = 4u * (64 * 8 + kMaxBatch * kUfRowsPerBlock + (uint32_t)std::max<int>(kmax, kMfmaRedFloats));
+  for (int wt = 0; wt < 3; ++wt)
+    for (int mode = 0; mode < 3; ++mode)
+      hip_check(hipFuncSetAttribute((const void *)pick_uf_gemv(wt, mode),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)gl),
+                "hipFuncSetAttribute");
+  hip_check(hipFuncSetAttribute((const void *)m->uf_attn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)m->uf_attn_lds), "hipFuncSetAttribute");
+  m->dm_pf = dp;
+  m->d_dm_pf = g;
+}
+
+}  // namespace
+
+extern "C" amk_status amk_prefill(amk_model *m, amk_kv *kv, int32_t seq, const int32_t *d_tokens,
+                                  int32_t pos0, int32_t n_tokens, float *d_logits,
+                                  int32_t *d_next, void *stream) {
+  AMK_API_BEGIN
+  if (!m || !kv || !d_tokens || !d_next) return set_error(AMK_E_INVALID, "amk_prefill: null argument");
+  if (kv->m != m) return set_error(AMK_E_INVALID, "amk_prefill: KV cache belongs to another model");
+  if (n_tokens < 1) return set_error(AMK_E_INVALID, "amk_prefill: n_tokens must be >= 1");
+  if (seq < 0 || seq >= kv->batch) return set_error(AMK_E_CAPACITY, "amk_prefill: seq outside the KV cache");
+  if (pos0 < 0 || (int64_t)pos0 + n_tokens > std::min(kv->max_seq, m->cfg.max_seq))
+    return set_error(AMK_E_CAPACITY, "amk_prefill: positions beyond max_seq");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  try {
+    prefill_init(m, st);
+  } catch (const std::bad_alloc &) {
+    return set_error(AMK_E_OOM, "amk_prefill: allocation failed");
+  }
+  const DevModel &dp = m->dm_pf;
+  int32_t last = 0;
+  for (int32_t c0 = 0; c0 < n_tokens; c0 += kMaxBatch) {
+    const int32_t C = std::min<int32_t>(kMaxBatch, n_tokens - c0);
+    StepArgs s;
+    s.tokens = d_tokens + c0;
+    s.logits = nullptr;  // the scratch logits of the prefill model
+    s.next = m->pf_next;
+    s.kv = static_cast<uint16_t *>(kv->data);
+    s.kv_batch = kv->batch;
+    s.kv_max_seq = kv->max_seq;
+    s.pos = pos0 + c0;
+    for (int32_t b = 0; b < kMaxBatch; ++b) s.pos_in[b] = pos0 + c0 + std::min(b, C - 1);
+    s.posp = nullptr;
+    s.kv_seq = seq;
+    s.batch = C;
+    s.epoch = 0;
+    s.step = 0;
+    s.n_steps = 1;
+    launch_unfused(m, dp, m->d_dm_pf, s, st);
+    last = C - 1;
+  }
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(d_next, m->pf_next + last, sizeof(int32_t), hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess && d_logits)
+    e = hipMemcpyAsync(d_logits, dp.logits + (size_t)last * dp.V, sizeof(float) * dp.V,
+                       hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) return set_error(AMK_E_HIP, std::string("amk_prefill: ") + hipGetErrorString(e));
+  clear_error();
+  return AMK_OK;
+  AMK_API_END
 }
 
 extern "C" amk_status amk_sync(amk_model *m, void *stream) {

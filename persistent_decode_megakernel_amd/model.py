@@ -182,6 +182,19 @@ class Model:
         _lib.check(st, "amk_decode_steps")
         return out
 
+    def prefill(self, kv: KVCache, tokens: torch.Tensor, pos0: int = 0, seq: int = 0,
+                logits: Optional[torch.Tensor] = None, next_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Process a prompt (device int32 [n]) of KV sequence `seq` at positions pos0 .. pos0 + n - 1
+        (amk_prefill). Returns the device int32 [1] greedy next token; logits (if given): the last
+        prompt token's float32 [V]."""
+        if next_out is None:
+            next_out = torch.empty(1, dtype=torch.int32, device=self.device)
+        st = self.lib.amk_prefill(self.handle, kv.handle, seq, C.c_void_p(tokens.data_ptr()), pos0,
+                                  tokens.numel(), C.c_void_p(_ptr(logits)) if logits is not None else None,
+                                  C.c_void_p(next_out.data_ptr()), _stream_ptr())
+        _lib.check(st, "amk_prefill")
+        return next_out
+
     def sync(self):
         _lib.check(self.lib.amk_sync(self.handle, _stream_ptr()), "amk_sync")
 
