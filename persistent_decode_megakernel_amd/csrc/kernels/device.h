@@ -1248,10 +1248,14 @@ struct MfmaTile {
   int K, rb, n, t0, t1;
   const float *sc;  // int4: the tile's scale rows [n][ng]
   int ng, gs;
-  uint32_t xrow;   // byte offset of this lane's input row (past the range when inactive)
+  uint32_t xrow;   // byte offset of this lane's input row (kNoRow: loads nothing, reads zeros)
   int col, kq;     // B/C column (l % 16) and k quarter (l / 16)
   bool emb, gain, lo_half;
 };
+
+// An input offset no k step brings back inside the input resource (its loads return zeros and
+// touch no memory).
+constexpr uint32_t kNoRow = 0x80000000u;
 
 // one pass: groups [g0, g0 + gn) (gn <= GP) over this wave's k steps, the loads of U steps
 // issued before any of them is used; returns the partial tiles
@@ -1304,6 +1308,14 @@ __device__ __forceinline__ void mfma_pass(const MfmaTile &T, int g0, int gn, boo
     for (int u = 0; u < U; ++u) {
       if (t + u < T.t1) {
         const int k = 32 * (t + u) + 8 * T.kq;
+        if constexpr (!WIDE) {
+          // packed: the lo-half lanes (columns 8..15, banks 2 and 3 of each 16-lane row) loaded
+          // nothing; they take their sequence's inputs from the hi-half lane 8 columns away
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            xw[u][i] = (uint32_t)__builtin_amdgcn_update_dpp((int)xw[u][i], (int)xw[u][i], 0x128, 0xF,
+                                                             0xC, false);
+        }
         float xv[8];
         if (T.emb) {
 #pragma unroll
@@ -1420,8 +1432,10 @@ __device__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, c
                 : make_rsrc(in.x, (uint32_t)B * (uint32_t)in.stride * 4u);
   T.rg = make_rsrc(in.gain ? in.gain : m.final_norm, (uint32_t)K * 2u);
   const int b = wide ? T.col : (T.col & 7);
-  T.xrow = 0xffffffffu;
-  if (b < B) T.xrow = in.emb ? (uint32_t)token_of(m, s, b) * (uint32_t)K * 2u : (uint32_t)b * (uint32_t)in.stride * 4u;
+  // one load per sequence and k: packed lo-half lanes receive the inputs from their hi-half lane
+  T.xrow = kNoRow;
+  if (b < B && !T.lo_half)
+    T.xrow = in.emb ? (uint32_t)token_of(m, s, b) * (uint32_t)K * 2u : (uint32_t)b * (uint32_t)in.stride * 4u;
   float ss = 0.f;
   for (int g0 = 0; g0 < G; g0 += kMfmaGroups) {
     const int gn = min(kMfmaGroups, G - g0);
