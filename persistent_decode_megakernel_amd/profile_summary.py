@@ -102,5 +102,49 @@ def main():
     print(json.dumps(out))
 
 
+def lds_main(argv):
+    """LDS counters of one --pmc pass (SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE and others) summed
+    over the kernel's dispatches:
+
+        python -m persistent_decode_megakernel_amd.profile_summary lds PMC_DIR OUT_STEM \
+            --kernel amk_megakernel_w0_h128_q1 --cmd "..."
+
+    The bank-conflict share is SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (cycles the LDS spent
+    resolving conflicts per cycle it was active)."""
+    ap = argparse.ArgumentParser(prog="profile_summary lds")
+    ap.add_argument("pmc_dir")
+    ap.add_argument("out_stem")
+    ap.add_argument("--kernel", required=True)
+    ap.add_argument("--cmd", default="")
+    args = ap.parse_args(argv)
+    rows = list(csv.DictReader(open(_one(os.path.join(args.pmc_dir, "**", "*counter_collection.csv")))))
+    tot, disp = {}, set()
+    for r in rows:
+        if r["Kernel_Name"] != args.kernel:
+            continue
+        disp.add(r["Dispatch_Id"])
+        tot[r["Counter_Name"]] = tot.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    n = max(1, len(disp))
+    per = {k: v / n for k, v in sorted(tot.items())}
+    share = per.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(1.0, per.get("SQ_LDS_IDX_ACTIVE", 0.0))
+    out = {"kernel": args.kernel, "dispatches": n, "per_dispatch": per,
+           "bank_conflict_share": share, "source_hash": source_hash()}
+    with open(args.out_stem + ".json", "w") as fo:
+        json.dump(out, fo, indent=1)
+    lines = [f"# rocprofv3 LDS counters: {args.kernel}", "", "Command(s):", "", "```", args.cmd, "```",
+             "", f"Per dispatch, mean over {n} dispatches of {args.kernel}:", "",
+             "| counter | value |", "|---|---|"]
+    lines += [f"| {k} | {v:.4g} |" for k, v in per.items()]
+    lines += ["", f"- bank-conflict share (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE): {share:.4f}",
+              f"- kernel source hash: {out['source_hash']}"]
+    with open(args.out_stem + ".md", "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+    print(json.dumps(out))
+
+
 if __name__ == "__main__":
-    main()
+    import sys
+    if len(sys.argv) > 1 and sys.argv[1] == "lds":
+        lds_main(sys.argv[2:])
+    else:
+        main()

@@ -37,6 +37,11 @@ def test_argument_errors_without_gpu(libamk):
     assert libamk.amk_kv_free(None) == _lib.AMK_E_INVALID
     assert libamk.amk_destroy(None) == _lib.AMK_E_INVALID
     assert libamk.amk_sync(None, None) == _lib.AMK_E_INVALID
+    assert libamk.amk_decode_steps(None, None, None, 0, 1, 1, None, None, None) == _lib.AMK_E_INVALID
+    pos = (C.c_int32 * 2)(0, 0)
+    assert libamk.amk_decode_steps_ragged(None, None, None, pos, 1, 2, None, None, None) == _lib.AMK_E_INVALID
+    assert libamk.amk_prefill(None, None, 0, None, 0, 1, None, None, None) == _lib.AMK_E_INVALID
+    assert b"amk_prefill" in libamk.amk_last_error()
     # invalid config rejected before any device call
     cfg = _lib.make_config(synth.get_config("tiny"))
     cfg.n_heads = 3  # not a multiple of n_kv_heads, hidden != heads * head_dim
