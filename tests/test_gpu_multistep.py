@@ -29,10 +29,18 @@ def _fresh_kv(model, cfg, kv_host, max_seq):
 
 
 @pytest.mark.parametrize("name,path", [("smollm2_135m", "megakernel"), ("tiny_b3", "megakernel"),
-                                       ("tiny_b3", "unfused")])
+                                       ("tiny_b3", "unfused"), ("tiny_int8", "megakernel"),
+                                       ("tiny_int4", "megakernel"), ("tiny_int4_b3", "megakernel")])
 def test_multistep_equals_single_steps_and_oracle(name, path):
+    tiny = synth.get_config("tiny").replace(prompt=0, prefill=20, steps=8)
     if name == "tiny_b3":
-        cfg = synth.get_config("tiny").replace(batch=3, prompt=0, prefill=20, steps=8)
+        cfg = tiny.replace(batch=3)
+    elif name == "tiny_int8":
+        cfg = tiny.replace(wtype="int8")
+    elif name == "tiny_int4":
+        cfg = tiny.replace(wtype="int4", ffn=768, group=128)
+    elif name == "tiny_int4_b3":
+        cfg = tiny.replace(wtype="int4", ffn=768, group=128, batch=3)
     else:
         cfg = synth.get_config(name)
     # n is a multiple of 4: the single-step run's epochs then have the same two low bits as the

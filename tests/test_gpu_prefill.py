@@ -19,10 +19,13 @@ def _ulp_close(a_bits, e_bits):
     return np.all(np.abs(a - e) <= 2.0 ** -6 * np.abs(e) + 1e-3)
 
 
-@pytest.mark.parametrize("path,n_prompt", [("megakernel", 40), ("unfused", 40), ("megakernel", 1),
-                                           ("megakernel", 17)])
-def test_prefill_then_decode_matches_oracle(path, n_prompt):
-    cfg = synth.get_config("tiny").replace(prompt=0, prefill=0, steps=6)
+@pytest.mark.parametrize("path,n_prompt,wtype", [("megakernel", 40, "bf16"), ("unfused", 40, "bf16"),
+                                                 ("megakernel", 1, "bf16"), ("megakernel", 17, "bf16"),
+                                                 ("megakernel", 33, "int8"), ("megakernel", 33, "int4")])
+def test_prefill_then_decode_matches_oracle(path, n_prompt, wtype):
+    cfg = synth.get_config("tiny").replace(prompt=0, prefill=0, steps=6, wtype=wtype)
+    if wtype == "int4":
+        cfg = cfg.replace(ffn=768, group=128)
     n_dec = 6
     max_seq = n_prompt + n_dec + 1
     w = synth.make_weights(cfg, 21)

@@ -32,10 +32,13 @@ def _run(cfg, path, pos0, n, seed, wtype_cfg=None):
     return out
 
 
-@pytest.mark.parametrize("path,batch", [("megakernel", 4), ("unfused", 4), ("megakernel", 1),
-                                        ("megakernel", 11)])
-def test_ragged_positions_match_per_sequence_oracle(path, batch):
-    cfg = synth.get_config("tiny").replace(batch=batch, prompt=0, prefill=24, steps=6)
+@pytest.mark.parametrize("path,batch,wtype", [("megakernel", 4, "bf16"), ("unfused", 4, "bf16"),
+                                              ("megakernel", 1, "bf16"), ("megakernel", 11, "bf16"),
+                                              ("megakernel", 5, "int8"), ("megakernel", 3, "int4")])
+def test_ragged_positions_match_per_sequence_oracle(path, batch, wtype):
+    cfg = synth.get_config("tiny").replace(batch=batch, prompt=0, prefill=24, steps=6, wtype=wtype)
+    if wtype == "int4":
+        cfg = cfg.replace(ffn=768, group=128)
     pos0 = [24 - (7 * b) % 23 for b in range(batch)]  # 24, 17, 10, 3, 19, ...
     n = 6
     w, kv_host, first, toks, logits, kv_dev = _run(cfg, path, pos0, n, seed=11)
