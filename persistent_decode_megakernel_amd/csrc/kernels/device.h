@@ -25,6 +25,7 @@ struct DevModel {
   int32_t L, d, nq, nkv, hd, F, V, qkvr, qd, qpg;
   int32_t wtype, tied, max_batch, max_seq;
   int32_t gs;  // int4: inputs per scale group
+  int32_t tiled;  // layer matrices (and an untied LM head) are tile-major (weight_tiled_bytes)
   int32_t nblk, n_lm;
   uint32_t n_tasks;
   uint32_t argmax_id;  // the step's last task: every other task of the step precedes it
@@ -263,8 +264,17 @@ constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitVm8 = 0x0F78;
 constexpr int kWaitVm16 = 0x4F70;  // vmcnt 16: its bits 5:4 sit in bits 15:14
 #define AMK_LDS __attribute__((address_space(3)))
+// A buffer resource must sit in scalar registers: every caller passes wave-uniform values, and
+// taking them from the first lane lets the compiler see that (otherwise it may keep the resource in
+// vector registers and wrap every load in a loop over its distinct values).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+  // (the builtin returns a signed int: widen through uint32_t, never by sign extension)
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t u = ((uint64_t)hi << 32) | (uint64_t)lo;
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(u), 0,
+                                           __builtin_amdgcn_readfirstlane((int)bytes), kRsrcWord3);
 }
 __device__ __forceinline__ float4 cld4(__amdgpu_buffer_rsrc_t r, uint32_t off_bytes) {
   const f32x4_t v = __builtin_bit_cast(
@@ -1031,7 +1041,7 @@ __device__ void stage_norm(const DevModel &m, const StepArgs &s, int slot, const
 
 // ys[b][i] *= 1 / sqrt(mean(src_b^2) + eps) with the partial sums stage_norm left in red (read
 // after the workgroup barrier that follows the GEMV). Ends with a barrier.
-__device__ void norm_scale_ys(const DevModel &m, const StepArgs &s, int n, float *ys,
+__device__ __forceinline__ void norm_scale_ys(const DevModel &m, const StepArgs &s, int n, float *ys,
                               const float *red, int nw) {
   for (int b = 0; b < s.batch; ++b) {
     float tot = 0.f;
@@ -1088,7 +1098,7 @@ __device__ __forceinline__ uint32_t tag_word(float v, uint32_t epoch) {
 // (one round: n <= kDigitMaxK), then go to LDS as integer digits (see stage_digits) instead of
 // fp32; *sx receives the weight of one digit unit.
 template <bool DIGITS>
-__device__ bool stage_tagged(const DevModel &m, const uint32_t *src, int n, const uint16_t *gain,
+__device__ __forceinline__ bool stage_tagged(const DevModel &m, const uint32_t *src, int n, const uint16_t *gain,
                              uint32_t epoch, float *xs, float *red, uint32_t task,
                              float *sx = nullptr) {
   constexpr int V = 8;
@@ -1248,6 +1258,9 @@ struct MfmaTile {
   int K, rb, n, t0, t1;
   const float *sc;  // int4: the tile's scale rows [n][ng]
   int ng, gs;
+  // byte offset of this lane's weights for 16-row group g and k step t: wl + g wg + t wt
+  uint32_t wl, wg, wt;
+  int B;           // sequences
   uint32_t xrow;   // byte offset of this lane's input row (kNoRow: loads nothing, reads zeros)
   int col, kq;     // B/C column (l % 16) and k quarter (l / 16)
   bool emb, gain, lo_half;
@@ -1288,8 +1301,7 @@ __device__ __forceinline__ void mfma_pass(const MfmaTile &T, int g0, int gn, boo
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
           if (g < gn) {
-            const uint32_t off = (uint32_t)(16 * (g0 + g) + T.col) * (uint32_t)T.rb +
-                                 (WT == 2 ? (uint32_t)k / 2u : (uint32_t)k * (WT ? 1u : 2u));
+            const uint32_t off = T.wl + (uint32_t)(g0 + g) * T.wg + (uint32_t)(t + u) * T.wt;
             if constexpr (WT == 2) {
               wf[u][g][0] = __builtin_amdgcn_raw_buffer_load_b32(T.rw, (int)off, 0, kCachePolicyNt);
               wf[u][g][1] = wf[u][g][2] = wf[u][g][3] = 0;
@@ -1403,10 +1415,205 @@ __device__ __forceinline__ void mfma_dispatch(const MfmaTile &T, int g0, int gn,
   }
 }
 
-template <int WT>
-__device__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, const float *scale,
-                          int K, int r0, int r1, const BatchInput &in, float *ys, float *red,
-                          float *mred) {
+// ------------------------------------------------------------------------------------------
+// Batched GEMV over tile-major weights, streamed through a per-wave LDS ring (megakernel
+// instances). A round is one k step of a pass: the step's tile of each of the GP row groups (one
+// 64-lane copy of 16 bytes per lane; int8 and int4 tiles fill the first 32 or 16 lanes), the
+// step's inputs of every sequence, the norm gain and, for int4, the step's group scale of each
+// row, all copied from memory straight into the round's LDS slot. Every round issues the same
+// copies; lanes and rounds with nothing to fetch address past their buffer resource, which moves
+// no data. D rounds are issued ahead, so round r is in LDS once the vector-memory count is down to
+// D times the copies per round, and no registers wait on loads in flight. A copy writes 16 (or 4)
+// bytes of LDS for each active lane whether or not it fetched anything, so each copy's slot area
+// holds 64 lanes' worth, except the gain's, which only lanes 0..3 copy.
+// ------------------------------------------------------------------------------------------
+template <int WT, int GP, bool GAIN, bool WIDE>
+struct RingShape {
+  static constexpr int NX = WIDE ? 2 : 1;             // input copies (8 fp32 or 16 bf16 rows each)
+  static constexpr int XO = GP * 1024;                // inputs [b][32]: fp32, or bf16 embedding rows
+  static constexpr int GO = XO + NX * 1024;           // gain [32] bf16
+  static constexpr int SO = GO + (GAIN ? 64 : 0);     // int4: scales [16 GP] fp32
+  static constexpr int SB = (SO + (WT == 2 ? 256 : 0) + 63) / 64 * 64;  // slot bytes
+  static constexpr int NS = kRingBytes / SB;          // slots
+  static constexpr int D = NS - 1;                    // rounds in flight
+  static constexpr int NI = GP + NX + (GAIN ? 1 : 0) + (WT == 2 ? 1 : 0);  // copies per round
+  static_assert(D >= 1 && D * NI <= 63, "the vector-memory count has 6 bits");
+};
+
+// this lane's part of the ring copies
+struct RingLanes {
+  AMK_LDS uint8_t *ring;        // this wave's ring
+  __amdgpu_buffer_rsrc_t rs;    // int4: scale rows of the tile
+  uint32_t woff;                // lane's 16 bytes of a weight tile (kNoRow: none)
+  uint32_t xoff[2], xstep;      // input copies: bytes at k step 0, bytes per k step
+  uint32_t goff;                // gain: lanes 0..3
+  uint32_t soff;                // int4 scales: lane's row in the pass (kNoRow: none)
+};
+
+template <int WT, int GP, bool GAIN, bool WIDE>
+__device__ __forceinline__ void ring_issue(const MfmaTile &T, const RingLanes &L, int g0, int gn,
+                                           int r, int NR, int slot) {
+  using RS = RingShape<WT, GP, GAIN, WIDE>;
+  const bool live = r < NR;  // wave-uniform
+  const uint32_t t = (uint32_t)(T.t0 + r);
+  AMK_LDS uint8_t *p = L.ring + slot * RS::SB;
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    const uint32_t off = (live && g < gn) ? L.woff + (uint32_t)(g0 + g) * T.wg + t * T.wt : kNoRow;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(T.rw, (AMK_LDS void *)(p + g * 1024), 16, (int)off, 0, 0,
+                                             kCachePolicyNt);
+  }
+#pragma unroll
+  for (int j = 0; j < RS::NX; ++j) {
+    const uint32_t off = live ? L.xoff[j] + t * L.xstep : kNoRow;
+    if (T.emb)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(T.rx, (AMK_LDS void *)(p + RS::XO + j * 1024), 16,
+                                               (int)off, 0, 0, 0);
+    else  // produced this step by other CUs: device-coherent
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(T.rx, (AMK_LDS void *)(p + RS::XO + j * 1024), 16,
+                                               (int)off, 0, 0, kCachePolicySc1);
+  }
+  if constexpr (GAIN) {
+    // only lanes 0..3 run this copy: an LDS copy writes 16 bytes for every active lane, fetched
+    // or not, and the slot holds 64 bytes of gain
+    if (lane_id() < 4) {
+      const uint32_t off = live ? L.goff + t * 64u : kNoRow;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(T.rg, (AMK_LDS void *)(p + RS::GO), 16, (int)off, 0, 0, 0);
+    }
+  }
+  if constexpr (WT == 2) {
+    const uint32_t off = live ? L.soff + (uint32_t)((32 * (int)t) / T.gs) * 4u : kNoRow;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rs, (AMK_LDS void *)(p + RS::SO), 4, (int)off, 0, 0, 0);
+  }
+}
+
+template <int WT, int GP, bool GAIN, bool WIDE>
+__device__ __forceinline__ void mfma_ring_pass(const MfmaTile &T, RingLanes &L, int g0, int gn,
+                                               bool sumsq, float &ss, f32x4_t (&acc)[kMfmaGroups]) {
+  using RS = RingShape<WT, GP, GAIN, WIDE>;
+#pragma unroll
+  for (int g = 0; g < kMfmaGroups; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int NR = T.t1 - T.t0, lane = lane_id();
+  const int b = WIDE ? T.col : (T.col & 7);  // this lane's sequence (packed: hi or lo half of it)
+  const bool xlive = b < T.B;
+  if constexpr (WT == 2) L.soff = lane < 16 * gn ? (uint32_t)((16 * g0 + lane) * T.ng) * 4u : kNoRow;
+  int wslot = 0;
+#pragma unroll
+  for (int r = 0; r < RS::D; ++r) ring_issue<WT, GP, GAIN, WIDE>(T, L, g0, gn, r, NR, r);
+  wslot = RS::D;
+  int rslot = 0;
+  for (int r = 0; r < NR; ++r) {
+    // the slot refilled now was read in the previous round: let those reads finish first
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    ring_issue<WT, GP, GAIN, WIDE>(T, L, g0, gn, r + RS::D, NR, wslot);
+    wslot = wslot + 1 == RS::NS ? 0 : wslot + 1;
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RS::D * RS::NI) : "memory");
+    const AMK_LDS uint8_t *p = L.ring + rslot * RS::SB;
+    rslot = rslot + 1 == RS::NS ? 0 : rslot + 1;
+    const int k = 32 * (T.t0 + r) + 8 * T.kq;
+    float xv[8];
+    if (T.emb) {
+      const u32x4_t e = *(const AMK_LDS u32x4_t *)(p + RS::XO + (b * 32 + 8 * T.kq) * 2);
+      xv[0] = bf_lo(e.x); xv[1] = bf_hi(e.x); xv[2] = bf_lo(e.y); xv[3] = bf_hi(e.y);
+      xv[4] = bf_lo(e.z); xv[5] = bf_hi(e.z); xv[6] = bf_lo(e.w); xv[7] = bf_hi(e.w);
+    } else {
+      const AMK_LDS u32x4_t *xp = (const AMK_LDS u32x4_t *)(p + RS::XO + (b * 32 + 8 * T.kq) * 4);
+      const u32x4_t a = xp[0], c = xp[1];
+      xv[0] = __uint_as_float(a.x); xv[1] = __uint_as_float(a.y);
+      xv[2] = __uint_as_float(a.z); xv[3] = __uint_as_float(a.w);
+      xv[4] = __uint_as_float(c.x); xv[5] = __uint_as_float(c.y);
+      xv[6] = __uint_as_float(c.z); xv[7] = __uint_as_float(c.w);
+    }
+    u32x4_t gw = {0u, 0u, 0u, 0u};
+    if constexpr (GAIN) gw = *(const AMK_LDS u32x4_t *)(p + RS::GO + T.kq * 16);
+    uint32_t hx[4], lx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v0 = (xlive && k + 2 * i < T.K) ? xv[2 * i] : 0.f;
+      float v1 = (xlive && k + 2 * i + 1 < T.K) ? xv[2 * i + 1] : 0.f;
+      if (sumsq && (WIDE || !T.lo_half)) ss = fmaf(v0, v0, fmaf(v1, v1, ss));
+      if constexpr (GAIN) {
+        v0 *= bf_lo(gw[i]);
+        v1 *= bf_hi(gw[i]);
+      }
+      const uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
+      const uint16_t l0 = f32_to_bf16(v0 - bf16_to_f32(h0)), l1 = f32_to_bf16(v1 - bf16_to_f32(h1));
+      if (!WIDE && T.lo_half)
+        hx[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      else
+        hx[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      lx[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+    const bf16x8_t xb = bf16x8_of_bits(hx[0], hx[1], hx[2], hx[3]);
+    const bf16x8_t xl = bf16x8_of_bits(lx[0], lx[1], lx[2], lx[3]);  // wide only
+    if constexpr (WT == 2) {
+      const uint32_t c136 = 0x43084308u;  // bf16 136.0, twice
+      const bf16x8_t a136 = bf16x8_of_bits(c136, c136, c136, c136);
+      f32x4_t corr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a136, xb, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      if constexpr (WIDE) corr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a136, xl, corr, 0, 0, 0);
+      const f32x4_t ncorr = -corr;
+#pragma unroll
+      for (int g = 0; g < GP; ++g) {
+        if (g < gn) {
+          const uint32_t w = *(const AMK_LDS uint32_t *)(p + g * 1024 + lane * 4);
+          const f32x4_t sc = *(const AMK_LDS f32x4_t *)(p + RS::SO + (16 * g + 4 * T.kq) * 4);
+          const bf16x8_t a = bf16x8_of_i4_offset(w);
+          f32x4_t q = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb, ncorr, 0, 0, 0);
+          if constexpr (WIDE) q = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl, q, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[g][i] = fmaf(q[i], sc[i], acc[g][i]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < GP; ++g) {
+        if (g < gn) {
+          bf16x8_t a;
+          if constexpr (WT == 0) {
+            const u32x4_t w = *(const AMK_LDS u32x4_t *)(p + g * 1024 + lane * 16);
+            a = bf16x8_of_bits(w.x, w.y, w.z, w.w);
+          } else {
+            const u32x2_t w = *(const AMK_LDS u32x2_t *)(p + g * 1024 + lane * 8);
+            a = bf16x8_of_i8(w.x, w.y);
+          }
+          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb, acc[g], 0, 0, 0);
+          if constexpr (WIDE) acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl, acc[g], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // the rounds issued past the end land in the ring too: drain them before the LDS is reused
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int WT, bool WIDE>
+__device__ __forceinline__ void ring_dispatch(const MfmaTile &T, RingLanes &L, int g0, int gn, bool sq,
+                                              float &ss, f32x4_t (&acc)[kMfmaGroups]) {
+  if (T.gain) {
+    if (gn <= 1)
+      mfma_ring_pass<WT, 1, true, WIDE>(T, L, g0, gn, sq, ss, acc);
+    else if (gn == 2)
+      mfma_ring_pass<WT, 2, true, WIDE>(T, L, g0, gn, sq, ss, acc);
+    else
+      mfma_ring_pass<WT, 4, true, WIDE>(T, L, g0, gn, sq, ss, acc);
+  } else {
+    if (gn <= 1)
+      mfma_ring_pass<WT, 1, false, WIDE>(T, L, g0, gn, sq, ss, acc);
+    else if (gn == 2)
+      mfma_ring_pass<WT, 2, false, WIDE>(T, L, g0, gn, sq, ss, acc);
+    else
+      mfma_ring_pass<WT, 4, false, WIDE>(T, L, g0, gn, sq, ss, acc);
+  }
+}
+
+// `tiled`: W is in the tile-major layout (weight_tiled_bytes) and r0 a multiple of 16; else
+// row-major. RING (megakernel instances, whose LDS region `mred` holds kRingBytes per wave): a
+// tile-major matrix is streamed through the waves' LDS rings, and each wave's partial tiles sit at
+// the start of its own ring; otherwise the loads go to registers.
+template <int WT, bool RING = false>
+__device__ __forceinline__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, bool tiled,
+                          const float *scale, int K, int r0, int r1, const BatchInput &in, float *ys,
+                          float *red, float *mred) {
   constexpr int NW = kWaves;
   const int B = s.batch, n = r1 - r0, G = (n + 15) / 16;
   const int lane = lane_id(), wave = (int)uniform_u32((uint32_t)wave_id());
@@ -1427,7 +1634,19 @@ __device__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, c
   T.lo_half = !wide && T.col >= 8;
   T.emb = in.emb != nullptr;
   T.gain = in.gain != nullptr;
-  T.rw = make_rsrc(static_cast<const uint8_t *>(W) + (int64_t)r0 * T.rb, (uint32_t)n * (uint32_t)T.rb);
+  T.B = B;
+  const uint32_t lb = WT == 0 ? 16u : (WT == 1 ? 8u : 4u);  // one lane's 8 weights, bytes
+  if (tiled) {  // a k step of a 16-row group is one 64-lane run
+    T.wl = (uint32_t)lane * lb;
+    T.wt = 64u * lb;
+    T.wg = (uint32_t)steps * T.wt;
+    T.rw = make_rsrc(static_cast<const uint8_t *>(W) + (int64_t)(r0 / 16) * T.wg, (uint32_t)G * T.wg);
+  } else {
+    T.wl = (uint32_t)T.col * (uint32_t)T.rb + (uint32_t)T.kq * lb;
+    T.wt = 4u * lb;
+    T.wg = 16u * (uint32_t)T.rb;
+    T.rw = make_rsrc(static_cast<const uint8_t *>(W) + (int64_t)r0 * T.rb, (uint32_t)n * (uint32_t)T.rb);
+  }
   T.rx = in.emb ? make_rsrc(in.emb, (uint32_t)m.V * (uint32_t)K * 2u)
                 : make_rsrc(in.x, (uint32_t)B * (uint32_t)in.stride * 4u);
   T.rg = make_rsrc(in.gain ? in.gain : m.final_norm, (uint32_t)K * 2u);
@@ -1436,15 +1655,49 @@ __device__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, c
   T.xrow = kNoRow;
   if (b < B && !T.lo_half)
     T.xrow = in.emb ? (uint32_t)token_of(m, s, b) * (uint32_t)K * 2u : (uint32_t)b * (uint32_t)in.stride * 4u;
+  const bool ring = RING && tiled;
+  RingLanes L;
+  if (ring) {
+    L.ring = (AMK_LDS uint8_t *)(mred) + wave * kRingBytes;
+    L.rs = make_rsrc(WT == 2 ? T.sc : scale, WT == 2 ? (uint32_t)(n * T.ng) * 4u : 0u);
+    L.woff = (uint32_t)lane < T.wt / 16u ? (uint32_t)lane * 16u : kNoRow;  // a tile is T.wt bytes
+    L.goff = lane < 4 ? (uint32_t)lane * 16u : kNoRow;
+    L.soff = kNoRow;
+    if (in.emb) {  // bf16 rows: 4 lanes of 16 bytes per sequence and k step, 16 sequences
+      const int bx = lane >> 2;
+      L.xoff[0] = bx < B ? (uint32_t)token_of(m, s, bx) * (uint32_t)K * 2u + (uint32_t)(lane & 3) * 16u : kNoRow;
+      L.xoff[1] = kNoRow;
+      L.xstep = 64u;
+    } else {  // fp32 rows: 8 lanes per sequence and k step, 8 sequences per copy
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int bx = 8 * j + (lane >> 3);
+        L.xoff[j] = bx < B ? (uint32_t)bx * (uint32_t)in.stride * 4u + (uint32_t)(lane & 7) * 16u : kNoRow;
+      }
+      L.xstep = 128u;
+    }
+  }
+  // partial tiles: wave w's at mred + w * wstride, [group][16 rows][NC]
+  const int wstride = ring ? kRingBytes / 4 : kMfmaGroups * 16 * NC;
   float ss = 0.f;
   for (int g0 = 0; g0 < G; g0 += kMfmaGroups) {
     const int gn = min(kMfmaGroups, G - g0);
     const bool sq = in.sumsq && g0 == 0;
     f32x4_t acc[kMfmaGroups];
-    if (wide)
-      mfma_dispatch<WT, true>(T, g0, gn, sq, ss, acc);
-    else
-      mfma_dispatch<WT, false>(T, g0, gn, sq, ss, acc);
+    if constexpr (RING) {
+      if (ring) {
+        if (wide)
+          ring_dispatch<WT, true>(T, L, g0, gn, sq, ss, acc);
+        else
+          ring_dispatch<WT, false>(T, L, g0, gn, sq, ss, acc);
+      }
+    }
+    if (!ring) {
+      if (wide)
+        mfma_dispatch<WT, true>(T, g0, gn, sq, ss, acc);
+      else
+        mfma_dispatch<WT, false>(T, g0, gn, sq, ss, acc);
+    }
     // partial tiles of all waves (16 columns: hi and lo halves) -> ys
 #pragma unroll
     for (int g = 0; g < kMfmaGroups; ++g)
@@ -1455,7 +1708,7 @@ __device__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, c
           const int row = 4 * T.kq + i;
           float v = acc[g][i];
           if (!wide) v += __shfl_xor(v, 8, 64);  // lanes c and c ^ 8: the halves of sequence c & 7
-          if (T.col < NC) mred[((wave * kMfmaGroups + g) * 16 + row) * NC + T.col] = v;
+          if (T.col < NC) mred[wave * wstride + (g * 16 + row) * NC + T.col] = v;
         }
     __syncthreads();
     for (int e = threadIdx.x; e < gn * 16 * NC; e += NW * 64) {
@@ -1463,7 +1716,7 @@ __device__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, c
       const int r = 16 * (g0 + g) + row;
       if (bb < B && r < n) {
         float t = 0.f;
-        for (int w = 0; w < NW; ++w) t += mred[((w * kMfmaGroups + g) * 16 + row) * NC + bb];
+        for (int w = 0; w < NW; ++w) t += mred[w * wstride + (g * 16 + row) * NC + bb];
         if constexpr (WT == 1) t *= gld(&scale[r0 + r]);
         ys[bb * n + r] = t;
       }
@@ -1488,7 +1741,7 @@ __device__ __forceinline__ int64_t kv_index(const DevModel &m, const StepArgs &s
 }
 
 // QKV rows: RoPE on pairs of rotary rows, q -> q buffer (fp32), k/v -> KV cache slot pos (bf16).
-__device__ void epi_qkv(const DevModel &m, const StepArgs &s, int l, int r0, int r1,
+__device__ __forceinline__ void epi_qkv(const DevModel &m, const StepArgs &s, int l, int r0, int r1,
                         const float *ys, int nw) {
   const int n = r1 - r0, hd = m.hd, half = hd / 2;
   for (int b = 0; b < s.batch; ++b) {
@@ -1548,7 +1801,7 @@ __device__ void epi_qkv(const DevModel &m, const StepArgs &s, int l, int r0, int
 }
 
 // out[b][r] = res[b][r] + ys (res slot 0 = the embedding row of the token)
-__device__ void epi_residual(const DevModel &m, const StepArgs &s, int res_slot, int out_slot,
+__device__ __forceinline__ void epi_residual(const DevModel &m, const StepArgs &s, int res_slot, int out_slot,
                              int r0, int r1, const float *ys, int nw) {
   const int n = r1 - r0, d = m.d;
   for (int b = 0; b < s.batch; ++b) {
@@ -1563,7 +1816,7 @@ __device__ void epi_residual(const DevModel &m, const StepArgs &s, int res_slot,
   }
 }
 
-__device__ void epi_swiglu(const DevModel &m, const StepArgs &s, int l, int r0, int r1,
+__device__ __forceinline__ void epi_swiglu(const DevModel &m, const StepArgs &s, int l, int r0, int r1,
                            const float *ys, int nw) {
   const int n = r1 - r0;
   for (int b = 0; b < s.batch; ++b) {
@@ -1597,7 +1850,7 @@ __device__ void epi_swiglu_tagged(const DevModel &m, const StepArgs &s, int l, i
 }
 
 // logits rows + (max, lowest index of max) of this tile into amax[slot][b]
-__device__ void epi_logits(const DevModel &m, const StepArgs &s, int r0, int r1, int slot,
+__device__ __forceinline__ void epi_logits(const DevModel &m, const StepArgs &s, int r0, int r1, int slot,
                            const float *ys, float *red, int nw) {
   const int n = r1 - r0;
   float *lg = s.logits ? s.logits : m.logits;

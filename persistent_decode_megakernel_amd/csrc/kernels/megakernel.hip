@@ -198,7 +198,7 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
       return false;
     if (!wait_task(m, t, s.epoch, abort_slot)) return false;
     if (m.trace && threadIdx.x == 0) gst(&m.trace[(uint64_t)t.id * 4 + 2], (uint64_t)wall_clock64());
-    gemv_mfma<WT>(m, s, W, scale, K, r0, r1, in, ys, red, xs);
+    gemv_mfma<WT, true>(m, s, W, m.tiled && !(t.mat == M_LM && m.tied), scale, K, r0, r1, in, ys, red, xs);
   }
   __syncthreads();
   if (t.mat != M_O && t.mat != M_D) norm_scale_ys(m, s, r1 - r0, ys, red, NW);

@@ -48,11 +48,14 @@ __device__ void uf_gemv(const DevModel &m, const StepArgs &s, const void *W, con
   float *ys = red + 64 * 8;               // batch * kUfRowsPerBlock
   float *xs = ys + kMaxBatch * kUfRowsPerBlock;  // K (batch 1) or the matrix cores' partial tiles
   const int r0 = blockIdx.x * kUfRowsPerBlock, r1 = min(rows, r0 + kUfRowsPerBlock);
-  if (s.batch == 1) {
+  // tile-major weights (batched models; a tied LM head stays the row-major embedding) are read
+  // by the matrix-core GEMV at any batch
+  const bool tiled = m.tiled && !(MODE == 2 && m.tied);
+  if (s.batch == 1 && !tiled) {
     stage_plain(x, K, K, 1, xs, kUfWaves);
     gemv_rows<WT>(W, scale, K, r0, r1, xs, ys, 1, kUfWaves, m.gs);
   } else {
-    gemv_mfma<WT>(m, s, W, scale, K, r0, r1, BatchInput{x, K, nullptr, nullptr, false}, ys, red, xs);
+    gemv_mfma<WT>(m, s, W, tiled, scale, K, r0, r1, BatchInput{x, K, nullptr, nullptr, false}, ys, red, xs);
   }
   __syncthreads();
   const int n = r1 - r0;

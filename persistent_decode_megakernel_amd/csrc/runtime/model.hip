@@ -91,6 +91,22 @@ extern "C" __global__ void __launch_bounds__(256) amk_int4_reorder(uint32_t *w, 
   }
 }
 
+// tile-major copy of a row-major matrix [rows][K] for the batched matrix-core GEMV (layout in
+// weight_tiled_bytes): one thread per lane piece of lb bytes (8 inputs), zeros past the matrix
+extern "C" __global__ void __launch_bounds__(256)
+amk_tile_rows(uint8_t *dst, const uint8_t *src, int rows, int K, int lb) {
+  const int S = (K + 31) / 32;
+  const size_t row_bytes = (size_t)K * lb / 8, n = (size_t)((rows + 15) / 16) * S * 64;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const int l = (int)(i % 64), t = (int)((i / 64) % S), g = (int)(i / 64 / S);
+    const int r = 16 * g + (l & 15);
+    const size_t b0 = (size_t)(32 * t + 8 * (l >> 4)) * lb / 8;  // byte of input 32 t + 8 q
+    uint8_t *d = dst + i * lb;
+    for (int j = 0; j < lb; ++j)
+      d[j] = (r < rows && b0 + j < row_bytes) ? src[(size_t)r * row_bytes + b0 + j] : (uint8_t)0;
+  }
+}
+
 // zero n 32-bit words: used instead of a memset node where the caller may be capturing a graph
 extern "C" __global__ void __launch_bounds__(256) amk_zero_words(uint32_t *p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
@@ -221,6 +237,19 @@ void gather(amk_model *m, void *dst, const void *src, const std::vector<int2> &p
   hip_check(e, "repack");
   (void)m;
 }
+
+// device buffer for the duration of a scope (repack staging)
+struct DeviceTemp {
+  void *p = nullptr;
+  explicit DeviceTemp(size_t bytes) {
+    if (bytes) hip_check(hipMalloc(&p, bytes), "hipMalloc");
+  }
+  ~DeviceTemp() {
+    if (p) (void)hipFree(p);
+  }
+  DeviceTemp(const DeviceTemp &) = delete;
+  DeviceTemp &operator=(const DeviceTemp &) = delete;
+};
 
 void copy_d2d(void *dst, const void *src, size_t bytes, hipStream_t st) {
   hip_check(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st), "hipMemcpyAsync");
@@ -378,11 +407,37 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
                          dim3(256), 0, st, (uint32_t *)w, n);
       hip_check(hipGetLastError(), "amk_int4_reorder");
     };
+    // Batched models keep the layer matrices (and an untied LM head) tile-major: each matrix is
+    // assembled row-major in `stage`, then tiled into its own allocation.
+    const bool tiled = B > 1;
+    const int wbits = i4 ? 4 : (i8 ? 8 : 16);
+    size_t stage_bytes = 0;
+    if (tiled) {
+      const size_t mx = std::max(std::max((size_t)qkvr * row_b(d), (size_t)2 * F * row_b(d)),
+                                 std::max((size_t)d * row_b(qd), (size_t)d * row_b(F)));
+      stage_bytes = cfg->tied_lm_head ? mx : std::max(mx, (size_t)V * row_b(d));
+    }
+    DeviceTemp stage(stage_bytes);
+    // where a matrix of `rows` x K is assembled, and its final home
+    auto home = [&](int rows, int K) -> void * {
+      return m->dalloc<uint8_t>(tiled ? (size_t)weight_tiled_bytes(rows, K, wbits) : (size_t)rows * row_b(K));
+    };
+    auto build = [&](void *dst) -> void * { return tiled ? stage.p : dst; };
+    auto finish = [&](void *dst, int rows, int K) {
+      if (!tiled) return;
+      const size_t n = (size_t)((rows + 15) / 16) * ((K + 31) / 32) * 64;
+      hipLaunchKernelGGL(amk_tile_rows, dim3((unsigned)std::min<size_t>((n + 255) / 256, 65535)),
+                         dim3(256), 0, st, (uint8_t *)dst, (const uint8_t *)stage.p, rows, K,
+                         weight_lane_bytes(wbits));
+      hip_check(hipGetLastError(), "amk_tile_rows");
+      hip_check(hipStreamSynchronize(st), "hipStreamSynchronize");  // `stage` is reused
+    };
     DevModel &dm = m->dm;
     dm.L = L; dm.d = d; dm.nq = nq; dm.nkv = nkv; dm.hd = hd; dm.F = F; dm.V = V;
     dm.qkvr = qkvr; dm.qd = qd; dm.qpg = nq / nkv;
     dm.wtype = cfg->wtype; dm.tied = cfg->tied_lm_head; dm.max_batch = B; dm.max_seq = cfg->max_seq;
     dm.gs = cfg->group_size;
+    dm.tiled = tiled;
     dm.nblk = (int32_t)h.attn_blocks;
     dm.n_lm = (int32_t)h.n_lm_tiles;
     dm.n_tasks = h.n_tasks;
@@ -394,10 +449,7 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     for (int l = 0; l < L; ++l) {
       const amk_layer_weights &lw = w->layers[l];
       DevLayer &dl = m->layers[l];
-      void *qkv = m->dalloc<uint8_t>((size_t)qkvr * row_b(d));
-      void *gu = m->dalloc<uint8_t>((size_t)2 * F * row_b(d));
-      void *o = m->dalloc<uint8_t>((size_t)d * row_b(qd));
-      void *dn = m->dalloc<uint8_t>((size_t)d * row_b(F));
+      void *qkv = home(qkvr, d), *gu = home(2 * F, d), *o = home(d, qd), *dn = home(d, F);
       std::vector<int2> pq, pk, pv, pg, pu;
       for (int r = 0; r < qkvr; ++r) {
         QkvRow q = qkv_decode(r, nq, nkv, hd);
@@ -408,17 +460,25 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
         pg.push_back(make_int2(2 * i, i));
         pu.push_back(make_int2(2 * i + 1, i));
       }
-      gather(m, qkv, lw.wq, pq, row_b(d), st);
-      gather(m, qkv, lw.wk, pk, row_b(d), st);
-      gather(m, qkv, lw.wv, pv, row_b(d), st);
-      gather(m, gu, lw.wg, pg, row_b(d), st);
-      gather(m, gu, lw.wu, pu, row_b(d), st);
-      copy_d2d(o, lw.wo, (size_t)d * row_b(qd), st);
-      copy_d2d(dn, lw.wd, (size_t)d * row_b(F), st);
-      reorder(qkv, (size_t)qkvr * row_b(d));
-      reorder(gu, (size_t)2 * F * row_b(d));
-      reorder(o, (size_t)d * row_b(qd));
-      reorder(dn, (size_t)d * row_b(F));
+      void *w_ = build(qkv);
+      gather(m, w_, lw.wq, pq, row_b(d), st);
+      gather(m, w_, lw.wk, pk, row_b(d), st);
+      gather(m, w_, lw.wv, pv, row_b(d), st);
+      reorder(w_, (size_t)qkvr * row_b(d));
+      finish(qkv, qkvr, d);
+      w_ = build(gu);
+      gather(m, w_, lw.wg, pg, row_b(d), st);
+      gather(m, w_, lw.wu, pu, row_b(d), st);
+      reorder(w_, (size_t)2 * F * row_b(d));
+      finish(gu, 2 * F, d);
+      w_ = build(o);
+      copy_d2d(w_, lw.wo, (size_t)d * row_b(qd), st);
+      reorder(w_, (size_t)d * row_b(qd));
+      finish(o, d, qd);
+      w_ = build(dn);
+      copy_d2d(w_, lw.wd, (size_t)d * row_b(F), st);
+      reorder(w_, (size_t)d * row_b(F));
+      finish(dn, d, F);
       dl.qkv = qkv; dl.gu = gu; dl.o = o; dl.dn = dn;
       dl.s_qkv = dl.s_gu = dl.s_o = dl.s_dn = nullptr;
       if (i8 || i4) {
@@ -455,9 +515,11 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
       dm.lm_scale = nullptr;
       m->weight_bytes += 2ull * V * d;
     } else {
-      void *lm = m->dalloc<uint8_t>((size_t)V * row_b(d));
-      copy_d2d(lm, w->lm_head, (size_t)V * row_b(d), st);
-      reorder(lm, (size_t)V * row_b(d));
+      void *lm = home(V, d);
+      void *w_ = build(lm);
+      copy_d2d(w_, w->lm_head, (size_t)V * row_b(d), st);
+      reorder(w_, (size_t)V * row_b(d));
+      finish(lm, V, d);
       dm.lm = lm;
       m->weight_bytes += (uint64_t)V * row_b(d);
       if (i8 || i4) {
@@ -640,8 +702,11 @@ static void launch_unfused(amk_model *m, const DevModel &dm, const DevModel *g, 
                            hipStream_t st) {
   const int B = s.batch, L = dm.L, d = dm.d;
   const int wt = dm.wtype;
+  // LDS: the staged input of a batch-1 row-major GEMV and/or the matrix cores' partial tiles (a
+  // tile-major model runs those at batch 1 too, except for a tied LM head)
+  const int kmx = std::max(std::max(d, dm.qd), dm.F);
   const uint32_t gl = 4u * (64 * 8 + kMaxBatch * kUfRowsPerBlock +
-                            (uint32_t)(B == 1 ? std::max(std::max(d, dm.qd), dm.F) : kMfmaRedFloats));
+                            (uint32_t)(B > 1 ? kMfmaRedFloats : (dm.tiled ? std::max(kmx, kMfmaRedFloats) : kmx)));
   auto grid = [](int rows) { return dim3((rows + kUfRowsPerBlock - 1) / kUfRowsPerBlock); };
   float *h = dm.h;
   auto hslot = [&](int slot) { return h + (size_t)slot * dm.max_batch * d; };

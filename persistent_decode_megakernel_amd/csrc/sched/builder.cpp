@@ -75,15 +75,17 @@ struct Tiling {
   uint32_t n() const { return (uint32_t)bounds.size() - 1; }
 };
 
-// Cut `rows` rows (multiple of `align`) into at most `max_tiles` balanced tiles whose
-// boundaries are multiples of `align`, with at least `min_rows` rows per tile when possible.
+// Cut `rows` rows into at most `max_tiles` balanced tiles whose boundaries are multiples of
+// `align` (the last tile ends at `rows`, which need not be one), with at least `min_rows` rows per
+// tile when possible.
 Tiling cut_rows(uint32_t rows, uint32_t align, uint32_t max_tiles, uint32_t min_rows) {
-  uint32_t units = rows / align;
+  uint32_t units = (rows + align - 1) / align;
   uint32_t n = std::min<uint32_t>(max_tiles, units);
   if (min_rows > align) n = std::min<uint32_t>(n, std::max<uint32_t>(1, rows / min_rows));
   n = std::max<uint32_t>(n, 1);
   Tiling t;
-  for (uint32_t i = 0; i <= n; ++i) t.bounds.push_back(align * (uint32_t)(((uint64_t)i * units) / n));
+  for (uint32_t i = 0; i <= n; ++i)
+    t.bounds.push_back(std::min<uint32_t>(rows, align * (uint32_t)(((uint64_t)i * units) / n)));
   return t;
 }
 
@@ -116,9 +118,9 @@ struct Builder {
   }
 
   // Emit a GEMV phase; returns [first id, last id + 1) and the tiling.
-  std::pair<uint32_t, uint32_t> gemv(uint8_t mat, uint16_t layer, uint32_t rows, uint32_t align,
-                                     uint32_t K, uint32_t wbits, uint32_t w_lo, uint32_t w_hi,
-                                     Tiling *out_tiling) {
+  std::pair<uint32_t, uint32_t> gemv(uint8_t mat, uint16_t layer, uint32_t rows, uint32_t K,
+                                     uint32_t wbits, uint32_t w_lo, uint32_t w_hi, Tiling *out_tiling) {
+    const uint32_t align = gemv_row_align(mat, c.max_batch);
     const uint32_t min_bytes = (uint32_t)std::max(1, p.min_tile_kb) * 1024u;
     uint32_t row_bytes = std::max<uint32_t>(1, K * wbits / 8);
     uint32_t min_rows = (min_bytes + row_bytes - 1) / row_bytes;
@@ -130,7 +132,7 @@ struct Builder {
     while (true) {
       uint32_t mx = 0;
       for (uint32_t i = 0; i < t.n(); ++i) mx = std::max(mx, t.bounds[i + 1] - t.bounds[i]);
-      if (mx <= cap_rows || t.n() >= rows / align) break;
+      if (mx <= cap_rows || t.n() >= (rows + align - 1) / align) break;
       t = cut_rows(rows, align, t.n() * 2, align);
     }
     uint32_t first = next_id;
@@ -173,7 +175,7 @@ struct Builder {
     uint32_t d_lo = 0, d_hi = 0;  // tasks producing the residual entering the layer
     for (uint32_t l = 0; l < L; ++l) {
       Tiling qt;
-      auto qkv = gemv(M_QKV, (uint16_t)l, qkvr, 2, d, wb, d_lo, d_hi, &qt);
+      auto qkv = gemv(M_QKV, (uint16_t)l, qkvr, d, wb, d_lo, d_hi, &qt);
       // attention: one task per (kv group, KV block); waits on the QKV tiles of its group. The
       // group's last block also merges the group's partials and so waits on the other blocks too.
       // Mergers are numbered after all other blocks of the layer, so the O tiles wait on the id
@@ -211,15 +213,15 @@ struct Builder {
       }
       next_id = a_first + n_attn;
       ++phase;
-      auto o = gemv(M_O, (uint16_t)l, d, 1, nq * hd, wb, m_first, next_id, nullptr);
-      auto gu = gemv(M_GU, (uint16_t)l, 2 * F, 2, d, wb, o.first, o.second, nullptr);
-      auto dn = gemv(M_D, (uint16_t)l, d, 1, F, wb, gu.first, gu.second, nullptr);
+      auto o = gemv(M_O, (uint16_t)l, d, nq * hd, wb, m_first, next_id, nullptr);
+      auto gu = gemv(M_GU, (uint16_t)l, 2 * F, d, wb, o.first, o.second, nullptr);
+      auto dn = gemv(M_D, (uint16_t)l, d, F, wb, gu.first, gu.second, nullptr);
       d_lo = dn.first;
       d_hi = dn.second;
     }
     const uint32_t lmwb = c.tied_lm_head ? 16 : wb;
     Tiling lt;
-    auto lm = gemv(M_LM, 0, V, 1, d, lmwb, d_lo, d_hi, &lt);
+    auto lm = gemv(M_LM, 0, V, d, lmwb, d_lo, d_hi, &lt);
     Task k{};
     k.type = T_ARGMAX;
     k.id = next_id++;

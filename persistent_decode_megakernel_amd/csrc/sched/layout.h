@@ -103,6 +103,25 @@ struct BlobHeader {
   double predicted_us;
 };
 
+// Row alignment of GEMV tiles. A model of batch capacity above 1 runs the batched kernel
+// instance on tile-major weights (16-row groups, see weight_tiled_bytes), so its tile boundaries
+// are multiples of 16 rows (the last tile may end at the matrix's ragged row count); batch-1 tiles
+// only keep RoPE and SwiGLU row pairs whole.
+AMK_HD uint32_t gemv_row_align(int32_t mat, int32_t max_batch) {
+  return max_batch > 1 ? 16u : ((mat == M_QKV || mat == M_GU) ? 2u : 1u);
+}
+
+// Tile-major weight layout of the batched matrix-core GEMV: the matrix is cut into 16-row x
+// 32-input tiles, stored group-major (tile (g, t) of the rows' group g and input step t at
+// index g * ceil(K / 32) + t). Inside a tile, lane l = 16 q + c of the instruction's A operand
+// holds row 16 g + c, inputs 32 t + 8 q .. 32 t + 8 q + 7 (16 bytes bf16, 8 int8, 4 int4) at byte
+// l * lane_bytes, so one step of a 16-row group is one contiguous 64-lane load. Rows past the
+// matrix and inputs past K are zero.
+AMK_HD int32_t weight_lane_bytes(int32_t wbits) { return wbits; }  // 8 inputs of wbits bits
+AMK_HD uint64_t weight_tiled_bytes(int64_t rows, int64_t K, int32_t wbits) {
+  return (uint64_t)((rows + 15) / 16) * (uint64_t)((K + 31) / 32) * 64u * (uint64_t)weight_lane_bytes(wbits);
+}
+
 // Attention KV block b of nblk over a context of ctx positions: [lo, hi).
 AMK_HD void attn_block_range(int32_t ctx, int32_t nblk, int32_t b, int32_t *lo, int32_t *hi) {
   *lo = (int32_t)(((int64_t)b * ctx) / nblk);
@@ -139,10 +158,14 @@ constexpr int32_t kDigitMaxK = 16384;
 constexpr int32_t kMaxBatch = 16;  // sequences per step
 // partial 16-row tiles of the batched GEMV: waves x row groups x 16 rows x 16 columns
 constexpr int32_t kMfmaRedFloats = kWaves * 4 * 16 * 16;
+// Batched megakernel instances stream tile-major weights through a 16 KB LDS ring per wave, which
+// also holds that wave's partial tiles between passes.
+constexpr int32_t kRingBytes = 16384;
+constexpr int32_t kRingFloats = kWaves * kRingBytes / 4;
 AMK_HD int32_t lds_xs_floats(int32_t batch, int32_t hidden, int32_t qdim, int32_t ffn) {
   int32_t k = hidden > qdim ? hidden : qdim;
   k = k > ffn ? k : ffn;
-  return batch == 1 ? k : kMfmaRedFloats;
+  return batch == 1 ? k : kRingFloats;
 }
 AMK_HD int32_t lds_attn_floats(int32_t qpg, int32_t hd) {
   // one sequence and at most kAttnMaxHeads heads per pass:

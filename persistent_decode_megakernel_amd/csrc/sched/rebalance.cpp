@@ -28,23 +28,24 @@ namespace {
 
 constexpr double kTickUs = 0.01;  // task-trace stamps count a 100 MHz clock
 
-// Row boundaries (multiples of align, every tile >= align rows) closest to the real-valued
-// target sizes w[i] scaled to `rows` in total.
+// Row boundaries (multiples of align except the last, which is `rows`; every tile holds at least
+// one align unit) closest to the real-valued target sizes w[i] scaled to `rows` in total.
 std::vector<uint32_t> boundaries(const std::vector<double> &w, uint32_t rows, uint32_t align) {
   const size_t n = w.size();
+  const int64_t units = ((int64_t)rows + align - 1) / align;
   double tot = 0;
   for (double x : w) tot += x;
   std::vector<uint32_t> b(n + 1, 0);
   b[n] = rows;
   double cum = 0;
+  int64_t prev = 0;  // previous boundary in align units
   for (size_t i = 1; i < n; ++i) {
     cum += w[i - 1];
-    const double want = rows * (cum / tot);
-    int64_t v = (int64_t)std::llround(want / align) * align;
-    const int64_t lo = (int64_t)b[i - 1] + align;
-    const int64_t hi = (int64_t)rows - (int64_t)(n - i) * align;
-    v = std::min(std::max(v, lo), hi);
-    b[i] = (uint32_t)v;
+    const double want = (double)rows * (cum / tot);
+    int64_t u = (int64_t)std::llround(want / align);
+    u = std::min(std::max(u, prev + 1), units - (int64_t)(n - i));
+    b[i] = (uint32_t)(u * align);
+    prev = u;
   }
   return b;
 }
@@ -81,7 +82,7 @@ bool rebalance_schedule(Schedule *s, const uint64_t *traces, int n_traces, doubl
     std::sort(v.begin(), v.end(), [](const Task *a, const Task *b) { return a->a0 < b->a0; });
     const size_t k = v.size();
     const int mat = ph.first.first;
-    const uint32_t align = (mat == M_QKV || mat == M_GU) ? 2u : 1u;
+    const uint32_t align = gemv_row_align(mat, h.cfg.max_batch);
     const uint32_t rows = v.back()->a1;
     bool ok = k >= 2 && v.front()->a0 == 0;
     // staged and end times relative to the phase's first staged stamp, averaged over the traces

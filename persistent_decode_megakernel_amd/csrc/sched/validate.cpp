@@ -81,17 +81,20 @@ bool footprint(const BlobHeader &h, const Task &t, std::vector<Access> *acc, std
     if (t.a0 >= t.a1) return bad("empty or inverted row range");
     const int64_t l = t.layer;
     if (t.mat != M_LM && l >= L) return bad("layer out of range");
-    int64_t rows, K, align = 1;
+    int64_t rows, K;
     switch (t.mat) {
-      case M_QKV: rows = qkv_rows((int32_t)nq, (int32_t)nkv, (int32_t)hd); K = d; align = 2; break;
+      case M_QKV: rows = qkv_rows((int32_t)nq, (int32_t)nkv, (int32_t)hd); K = d; break;
       case M_O: rows = d; K = qd; break;
-      case M_GU: rows = 2 * F; K = d; align = 2; break;
+      case M_GU: rows = 2 * F; K = d; break;
       case M_D: rows = d; K = F; break;
       case M_LM: rows = V; K = d; break;
       default: return bad("unknown matrix");
     }
     if (t.a1 > rows) return bad("rows beyond the matrix");
-    if (t.a0 % align || t.a1 % align) return bad("tile splits a row pair");
+    // the kernel instance, and with it the weight layout, follows the model's batch capacity
+    const int64_t align = gemv_row_align(t.mat, c.max_batch);
+    if (t.a0 % align || (t.a1 % align && t.a1 != rows))
+      return bad(c.max_batch > 1 ? "tile boundary off the weights' 16-row groups" : "tile splits a row pair");
     if (t.aux1 != 0 || (int64_t)t.aux2 != K) return bad("K range must be the full row");
     if ((int64_t)t.a1 - t.a0 > 4096 / B) return bad("tile too tall for the output staging");
     const int64_t a0 = t.a0, a1 = t.a1;

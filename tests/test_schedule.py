@@ -326,3 +326,62 @@ def test_int4_weight_bytes_and_config_checks(libamk):
     c.group_size = 128
     with pytest.raises(_lib.AmkError):
         _lib.schedule_build(c, 1, 256)
+
+
+def _gemv_phases(b: B.Blob):
+    ph = {}
+    for v in b.per_cu:
+        for t in v:
+            if t["type"] == B.T_GEMV:
+                ph.setdefault((int(t["mat"]), int(t["layer"])), []).append(t)
+    for k in ph:
+        ph[k].sort(key=lambda t: int(t["a0"]))
+    return ph
+
+
+@pytest.mark.parametrize("name,max_batch", [("llama2_7b", 8), ("llama2_7b", 16), ("tiny", 3),
+                                            ("smollm2_135m", 4), ("llama2_7b_w4a16", 2)])
+def test_batched_tiles_follow_the_16_row_weight_groups(libamk, name, max_batch):
+    """A model of batch capacity above 1 stores its weights tile-major in 16-row groups, so each
+    GEMV tile of its schedules starts on a group boundary (the last ends at the matrix's rows) and
+    the validator rejects a boundary moved off one, even by a whole row pair."""
+    cfg = synth.get_config(name)
+    c = _lib.make_config(cfg, max_batch=max_batch)
+    for batch in sorted({1, max_batch}):
+        b = B.Blob(_lib.schedule_build(c, batch, 256))
+        assert _lib.schedule_validate(b.to_bytes())[0] == _lib.AMK_OK
+        for (mat, layer), v in _gemv_phases(b).items():
+            assert int(v[0]["a0"]) == 0
+            for t0, t1 in zip(v, v[1:]):
+                assert int(t0["a1"]) == int(t1["a0"]) and int(t1["a0"]) % 16 == 0, (mat, layer)
+    # shift one gate/up boundary by a row pair: pair-aligned, complete, but off the groups (the
+    # tile that grows stays within the tallest tile, which the LDS size covers; 13 CUs make the
+    # tiles uneven)
+    b = B.Blob(_lib.schedule_build(c, max_batch, 13))
+    assert _lib.schedule_validate(b.to_bytes())[0] == _lib.AMK_OK
+    ph = _gemv_phases(b)
+    tallest = max(int(t["a1"]) - int(t["a0"]) for v in ph.values() for t in v)
+    v = ph[(B.M_GU, 0)]
+    i = next(i for i in range(len(v) - 1) if int(v[i]["a1"]) - int(v[i]["a0"]) > 2
+             and int(v[i + 1]["a1"]) - int(v[i + 1]["a0"]) + 2 <= tallest)
+    v[i]["a1"] = int(v[i]["a1"]) - 2
+    v[i + 1]["a0"] = int(v[i + 1]["a0"]) - 2
+    st, rep = _lib.schedule_validate(b.to_bytes())
+    assert st == _lib.AMK_E_SCHEDULE_REJECTED and "16-row" in rep, rep
+
+
+def test_batch1_tiles_keep_row_pairs_only(libamk):
+    """Batch-1 models keep row-major weights: tiles need only whole RoPE / SwiGLU pairs, and a
+    boundary moved by a pair is still valid."""
+    cfg = synth.get_config("tiny")
+    b = B.Blob(_lib.schedule_build(_lib.make_config(cfg), 1, 8))
+    v = _gemv_phases(b)[(B.M_GU, 0)]
+    i = next(i for i in range(len(v) - 1) if int(v[i]["a1"]) - int(v[i]["a0"]) > 2)
+    v[i]["a1"] = int(v[i]["a1"]) - 2
+    v[i + 1]["a0"] = int(v[i + 1]["a0"]) - 2
+    st, rep = _lib.schedule_validate(b.to_bytes())
+    assert st == _lib.AMK_OK, rep
+    v[i]["a1"] = int(v[i]["a1"]) - 1
+    v[i + 1]["a0"] = int(v[i + 1]["a0"]) - 1
+    st, rep = _lib.schedule_validate(b.to_bytes())
+    assert st == _lib.AMK_E_SCHEDULE_REJECTED and "row pair" in rep, rep
