@@ -1450,11 +1450,11 @@ struct RingLanes {
   uint32_t soff;                // int4 scales: lane's row in the pass (kNoRow: none)
 };
 
+// the copies of round r that do not depend on the step's activations: weight tiles, gain, scales
 template <int WT, int GP, bool GAIN, bool WIDE>
-__device__ __forceinline__ void ring_issue(const MfmaTile &T, const RingLanes &L, int g0, int gn,
-                                           int r, int NR, int slot) {
+__device__ __forceinline__ void ring_issue_w(const MfmaTile &T, const RingLanes &L, int g0, int gn,
+                                             bool live, int r, int slot) {
   using RS = RingShape<WT, GP, GAIN, WIDE>;
-  const bool live = r < NR;  // wave-uniform
   const uint32_t t = (uint32_t)(T.t0 + r);
   AMK_LDS uint8_t *p = L.ring + slot * RS::SB;
 #pragma unroll
@@ -1462,16 +1462,6 @@ __device__ __forceinline__ void ring_issue(const MfmaTile &T, const RingLanes &L
     const uint32_t off = (live && g < gn) ? L.woff + (uint32_t)(g0 + g) * T.wg + t * T.wt : kNoRow;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(T.rw, (AMK_LDS void *)(p + g * 1024), 16, (int)off, 0, 0,
                                              kCachePolicyNt);
-  }
-#pragma unroll
-  for (int j = 0; j < RS::NX; ++j) {
-    const uint32_t off = live ? L.xoff[j] + t * L.xstep : kNoRow;
-    if (T.emb)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(T.rx, (AMK_LDS void *)(p + RS::XO + j * 1024), 16,
-                                               (int)off, 0, 0, 0);
-    else  // produced this step by other CUs: device-coherent
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(T.rx, (AMK_LDS void *)(p + RS::XO + j * 1024), 16,
-                                               (int)off, 0, 0, kCachePolicySc1);
   }
   if constexpr (GAIN) {
     // only lanes 0..3 run this copy: an LDS copy writes 16 bytes for every active lane, fetched
@@ -1487,27 +1477,79 @@ __device__ __forceinline__ void ring_issue(const MfmaTile &T, const RingLanes &L
   }
 }
 
+// the input copies of round r (written by other tasks of this step)
+template <int WT, int GP, bool GAIN, bool WIDE>
+__device__ __forceinline__ void ring_issue_x(const MfmaTile &T, const RingLanes &L, bool live, int r,
+                                             int slot) {
+  using RS = RingShape<WT, GP, GAIN, WIDE>;
+  const uint32_t t = (uint32_t)(T.t0 + r);
+  AMK_LDS uint8_t *p = L.ring + slot * RS::SB;
+#pragma unroll
+  for (int j = 0; j < RS::NX; ++j) {
+    const uint32_t off = live ? L.xoff[j] + t * L.xstep : kNoRow;
+    if (T.emb)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(T.rx, (AMK_LDS void *)(p + RS::XO + j * 1024), 16,
+                                               (int)off, 0, 0, 0);
+    else  // produced this step by other CUs: device-coherent
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(T.rx, (AMK_LDS void *)(p + RS::XO + j * 1024), 16,
+                                               (int)off, 0, 0, kCachePolicySc1);
+  }
+}
+
+// A pass's prologue, part one: the weight copies of its first D rounds. On a task's first pass
+// this is issued before the task's dependency wait.
+template <int WT, int GP, bool GAIN, bool WIDE>
+__device__ __forceinline__ void ring_prefetch(const MfmaTile &T, RingLanes &L, int g0, int gn) {
+  using RS = RingShape<WT, GP, GAIN, WIDE>;
+  const int NR = T.t1 - T.t0;
+  if constexpr (WT == 2) L.soff = lane_id() < 16 * gn ? (uint32_t)((16 * g0 + lane_id()) * T.ng) * 4u : kNoRow;
+#pragma unroll
+  for (int r = 0; r < RS::D; ++r) ring_issue_w<WT, GP, GAIN, WIDE>(T, L, g0, gn, r < NR, r, r);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Round r is in LDS. Issue order: the first D rounds' weight copies (ring_prefetch), their input
+// copies, then one whole round per iteration. For r < D the copies issued after round r are the
+// later prologue rounds' inputs plus r + 1 whole rounds; after that, D whole rounds.
+template <int D, int NX, int NI, int I = 0>
+__device__ __forceinline__ void wait_round(int r) {
+  if constexpr (I < D) {
+    if (r == I) {
+      wait_vm<(D - 1 - I) * NX + (I + 1) * NI>();
+      return;
+    }
+    wait_round<D, NX, NI, I + 1>(r);
+  } else {
+    wait_vm<D * NI>();
+  }
+}
+
+// One pass (groups [g0, g0 + gn)) of the ring stream; `prefetched`: ring_prefetch already ran.
 template <int WT, int GP, bool GAIN, bool WIDE>
 __device__ __forceinline__ void mfma_ring_pass(const MfmaTile &T, RingLanes &L, int g0, int gn,
-                                               bool sumsq, float &ss, f32x4_t (&acc)[kMfmaGroups]) {
+                                               bool sumsq, float &ss, f32x4_t (&acc)[kMfmaGroups],
+                                               bool prefetched) {
   using RS = RingShape<WT, GP, GAIN, WIDE>;
 #pragma unroll
   for (int g = 0; g < kMfmaGroups; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int NR = T.t1 - T.t0, lane = lane_id();
   const int b = WIDE ? T.col : (T.col & 7);  // this lane's sequence (packed: hi or lo half of it)
   const bool xlive = b < T.B;
-  if constexpr (WT == 2) L.soff = lane < 16 * gn ? (uint32_t)((16 * g0 + lane) * T.ng) * 4u : kNoRow;
-  int wslot = 0;
+  if (!prefetched) ring_prefetch<WT, GP, GAIN, WIDE>(T, L, g0, gn);
 #pragma unroll
-  for (int r = 0; r < RS::D; ++r) ring_issue<WT, GP, GAIN, WIDE>(T, L, g0, gn, r, NR, r);
-  wslot = RS::D;
-  int rslot = 0;
+  for (int r = 0; r < RS::D; ++r) ring_issue_x<WT, GP, GAIN, WIDE>(T, L, r < NR, r, r);
+  int wslot = RS::D, rslot = 0;
   for (int r = 0; r < NR; ++r) {
     // the slot refilled now was read in the previous round: let those reads finish first
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    ring_issue<WT, GP, GAIN, WIDE>(T, L, g0, gn, r + RS::D, NR, wslot);
+    const bool live = r + RS::D < NR;
+    ring_issue_w<WT, GP, GAIN, WIDE>(T, L, g0, gn, live, r + RS::D, wslot);
+    ring_issue_x<WT, GP, GAIN, WIDE>(T, L, live, r + RS::D, wslot);
     wslot = wslot + 1 == RS::NS ? 0 : wslot + 1;
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RS::D * RS::NI) : "memory");
+    wait_round<RS::D, RS::NX, RS::NI>(r);
     const AMK_LDS uint8_t *p = L.ring + rslot * RS::SB;
     rslot = rslot + 1 == RS::NS ? 0 : rslot + 1;
     const int k = 32 * (T.t0 + r) + 8 * T.kq;
@@ -1588,36 +1630,56 @@ __device__ __forceinline__ void mfma_ring_pass(const MfmaTile &T, RingLanes &L, 
 
 template <int WT, bool WIDE>
 __device__ __forceinline__ void ring_dispatch(const MfmaTile &T, RingLanes &L, int g0, int gn, bool sq,
-                                              float &ss, f32x4_t (&acc)[kMfmaGroups]) {
+                                              float &ss, f32x4_t (&acc)[kMfmaGroups], bool prefetched) {
   if (T.gain) {
-    if (gn <= 1)
-      mfma_ring_pass<WT, 1, true, WIDE>(T, L, g0, gn, sq, ss, acc);
-    else if (gn == 2)
-      mfma_ring_pass<WT, 2, true, WIDE>(T, L, g0, gn, sq, ss, acc);
-    else
-      mfma_ring_pass<WT, 4, true, WIDE>(T, L, g0, gn, sq, ss, acc);
+    if (gn <= 1) mfma_ring_pass<WT, 1, true, WIDE>(T, L, g0, gn, sq, ss, acc, prefetched);
+    else if (gn == 2) mfma_ring_pass<WT, 2, true, WIDE>(T, L, g0, gn, sq, ss, acc, prefetched);
+    else mfma_ring_pass<WT, 4, true, WIDE>(T, L, g0, gn, sq, ss, acc, prefetched);
   } else {
-    if (gn <= 1)
-      mfma_ring_pass<WT, 1, false, WIDE>(T, L, g0, gn, sq, ss, acc);
-    else if (gn == 2)
-      mfma_ring_pass<WT, 2, false, WIDE>(T, L, g0, gn, sq, ss, acc);
-    else
-      mfma_ring_pass<WT, 4, false, WIDE>(T, L, g0, gn, sq, ss, acc);
+    if (gn <= 1) mfma_ring_pass<WT, 1, false, WIDE>(T, L, g0, gn, sq, ss, acc, prefetched);
+    else if (gn == 2) mfma_ring_pass<WT, 2, false, WIDE>(T, L, g0, gn, sq, ss, acc, prefetched);
+    else mfma_ring_pass<WT, 4, false, WIDE>(T, L, g0, gn, sq, ss, acc, prefetched);
   }
 }
 
+template <int WT, bool WIDE>
+__device__ __forceinline__ void ring_prefetch_dispatch(const MfmaTile &T, RingLanes &L, int g0, int gn) {
+  if (T.gain) {
+    if (gn <= 1) ring_prefetch<WT, 1, true, WIDE>(T, L, g0, gn);
+    else if (gn == 2) ring_prefetch<WT, 2, true, WIDE>(T, L, g0, gn);
+    else ring_prefetch<WT, 4, true, WIDE>(T, L, g0, gn);
+  } else {
+    if (gn <= 1) ring_prefetch<WT, 1, false, WIDE>(T, L, g0, gn);
+    else if (gn == 2) ring_prefetch<WT, 2, false, WIDE>(T, L, g0, gn);
+    else ring_prefetch<WT, 4, false, WIDE>(T, L, g0, gn);
+  }
+}
+
+// A batched GEMV tile in two parts. gemv_mfma_begin sets the tile up and, on the ring path,
+// issues the first pass's weight copies; it reads nothing the step produces, so a task calls it
+// before its dependency wait and gemv_mfma_end (inputs, passes, reduction) after.
 // `tiled`: W is in the tile-major layout (weight_tiled_bytes) and r0 a multiple of 16; else
 // row-major. RING (megakernel instances, whose LDS region `mred` holds kRingBytes per wave): a
 // tile-major matrix is streamed through the waves' LDS rings, and each wave's partial tiles sit at
 // the start of its own ring; otherwise the loads go to registers.
-template <int WT, bool RING = false>
-__device__ __forceinline__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, bool tiled,
-                          const float *scale, int K, int r0, int r1, const BatchInput &in, float *ys,
-                          float *red, float *mred) {
+struct MfmaJob {
+  MfmaTile T;
+  RingLanes L;
+  int G, NC, wave, lane;
+  bool wide, ring;
+};
+
+template <int WT, bool RING>
+__device__ __forceinline__ void gemv_mfma_begin(MfmaJob &J, const DevModel &m, const StepArgs &s,
+                                                const void *W, bool tiled, const float *scale, int K,
+                                                int r0, int r1, const BatchInput &in, float *mred) {
   constexpr int NW = kWaves;
+  MfmaTile &T = J.T;
   const int B = s.batch, n = r1 - r0, G = (n + 15) / 16;
   const int lane = lane_id(), wave = (int)uniform_u32((uint32_t)wave_id());
-  MfmaTile T;
+  J.G = G;
+  J.lane = lane;
+  J.wave = wave;
   T.K = K;
   T.n = n;
   T.rb = WT == 2 ? K / 2 : K * (WT ? 1 : 2);
@@ -1629,9 +1691,9 @@ __device__ __forceinline__ void gemv_mfma(const DevModel &m, const StepArgs &s, 
   T.t1 = (int)((int64_t)steps * (wave + 1) / NW);
   T.col = lane & 15;
   T.kq = lane >> 4;
-  const bool wide = B > 8;  // one column per sequence, both halves by two instructions
-  const int NC = wide ? 16 : 8;  // columns of the partial tiles in LDS
-  T.lo_half = !wide && T.col >= 8;
+  J.wide = B > 8;  // one column per sequence, both halves by two instructions
+  J.NC = J.wide ? 16 : 8;  // columns of the partial tiles in LDS
+  T.lo_half = !J.wide && T.col >= 8;
   T.emb = in.emb != nullptr;
   T.gain = in.gain != nullptr;
   T.B = B;
@@ -1650,19 +1712,46 @@ __device__ __forceinline__ void gemv_mfma(const DevModel &m, const StepArgs &s, 
   T.rx = in.emb ? make_rsrc(in.emb, (uint32_t)m.V * (uint32_t)K * 2u)
                 : make_rsrc(in.x, (uint32_t)B * (uint32_t)in.stride * 4u);
   T.rg = make_rsrc(in.gain ? in.gain : m.final_norm, (uint32_t)K * 2u);
+  J.ring = RING && tiled;
+  if constexpr (RING) {
+    if (J.ring) {
+      RingLanes &L = J.L;
+      L.ring = (AMK_LDS uint8_t *)(mred) + wave * kRingBytes;
+      L.rs = make_rsrc(WT == 2 ? T.sc : scale, WT == 2 ? (uint32_t)(n * T.ng) * 4u : 0u);
+      L.woff = (uint32_t)lane < T.wt / 16u ? (uint32_t)lane * 16u : kNoRow;  // a tile is T.wt bytes
+      L.goff = lane < 4 ? (uint32_t)lane * 16u : kNoRow;
+      L.soff = kNoRow;
+      const int gn = min(kMfmaGroups, G);
+      if (J.wide)
+        ring_prefetch_dispatch<WT, true>(T, L, 0, gn);
+      else
+        ring_prefetch_dispatch<WT, false>(T, L, 0, gn);
+    }
+  }
+}
+
+// After gemv_mfma_begin with the ring prefetch in flight, a task that abandons the tile (its
+// dependency wait failed) lets the copies land before it leaves.
+__device__ __forceinline__ void gemv_mfma_abandon() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int WT, bool RING>
+__device__ __forceinline__ void gemv_mfma_end(MfmaJob &J, const DevModel &m, const StepArgs &s,
+                                              const float *scale, int r0, const BatchInput &in,
+                                              float *ys, float *red, float *mred) {
+  constexpr int NW = kWaves;
+  MfmaTile &T = J.T;
+  RingLanes &L = J.L;
+  const int B = s.batch, n = T.n, G = J.G, K = T.K, NC = J.NC, lane = J.lane, wave = J.wave;
+  const bool wide = J.wide, ring = J.ring;
+  // where the inputs come from (the tokens of a later step of a multi-step launch are written by
+  // the previous step, so only now)
   const int b = wide ? T.col : (T.col & 7);
-  // one load per sequence and k: packed lo-half lanes receive the inputs from their hi-half lane
+  // register path: one load per sequence and k; packed lo-half lanes receive the inputs from
+  // their hi-half lane
   T.xrow = kNoRow;
   if (b < B && !T.lo_half)
     T.xrow = in.emb ? (uint32_t)token_of(m, s, b) * (uint32_t)K * 2u : (uint32_t)b * (uint32_t)in.stride * 4u;
-  const bool ring = RING && tiled;
-  RingLanes L;
   if (ring) {
-    L.ring = (AMK_LDS uint8_t *)(mred) + wave * kRingBytes;
-    L.rs = make_rsrc(WT == 2 ? T.sc : scale, WT == 2 ? (uint32_t)(n * T.ng) * 4u : 0u);
-    L.woff = (uint32_t)lane < T.wt / 16u ? (uint32_t)lane * 16u : kNoRow;  // a tile is T.wt bytes
-    L.goff = lane < 4 ? (uint32_t)lane * 16u : kNoRow;
-    L.soff = kNoRow;
     if (in.emb) {  // bf16 rows: 4 lanes of 16 bytes per sequence and k step, 16 sequences
       const int bx = lane >> 2;
       L.xoff[0] = bx < B ? (uint32_t)token_of(m, s, bx) * (uint32_t)K * 2u + (uint32_t)(lane & 3) * 16u : kNoRow;
@@ -1687,9 +1776,9 @@ __device__ __forceinline__ void gemv_mfma(const DevModel &m, const StepArgs &s, 
     if constexpr (RING) {
       if (ring) {
         if (wide)
-          ring_dispatch<WT, true>(T, L, g0, gn, sq, ss, acc);
+          ring_dispatch<WT, true>(T, L, g0, gn, sq, ss, acc, g0 == 0);
         else
-          ring_dispatch<WT, false>(T, L, g0, gn, sq, ss, acc);
+          ring_dispatch<WT, false>(T, L, g0, gn, sq, ss, acc, g0 == 0);
       }
     }
     if (!ring) {
@@ -1728,6 +1817,15 @@ __device__ __forceinline__ void gemv_mfma(const DevModel &m, const StepArgs &s, 
     ss += __shfl_xor(ss, 32, 64);
     if (T.kq == 0 && T.col < B && (wide || T.col < 8)) red[T.col * NW + wave] = ss;
   }
+}
+
+template <int WT, bool RING = false>
+__device__ __forceinline__ void gemv_mfma(const DevModel &m, const StepArgs &s, const void *W, bool tiled,
+                                          const float *scale, int K, int r0, int r1, const BatchInput &in,
+                                          float *ys, float *red, float *mred) {
+  MfmaJob J;
+  gemv_mfma_begin<WT, RING>(J, m, s, W, tiled, scale, K, r0, r1, in, mred);
+  gemv_mfma_end<WT, RING>(J, m, s, scale, r0, in, ys, red, mred);
 }
 
 // ------------------------------------------------------------------------------------------

@@ -194,11 +194,16 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
       case M_D: in = BatchInput{m.a + (int64_t)l * m.max_batch * m.F, m.F, nullptr, nullptr, false}; break;
       default: in.x = m.h + 2 * (int64_t)m.L * hb; in.gain = m.final_norm; break;
     }
-    if (s.step > 0 && t.mat == M_QKV && l == 0 && !wait_task(m, prev_step(m, t), s.epoch - 1, abort_slot))
+    // the first weight copies go out before the dependency wait (weights do not depend on it)
+    MfmaJob job;
+    gemv_mfma_begin<WT, true>(job, m, s, W, m.tiled && !(t.mat == M_LM && m.tied), scale, K, r0, r1, in, xs);
+    if ((s.step > 0 && t.mat == M_QKV && l == 0 && !wait_task(m, prev_step(m, t), s.epoch - 1, abort_slot)) ||
+        !wait_task(m, t, s.epoch, abort_slot)) {
+      gemv_mfma_abandon();
       return false;
-    if (!wait_task(m, t, s.epoch, abort_slot)) return false;
+    }
     if (m.trace && threadIdx.x == 0) gst(&m.trace[(uint64_t)t.id * 4 + 2], (uint64_t)wall_clock64());
-    gemv_mfma<WT, true>(m, s, W, m.tiled && !(t.mat == M_LM && m.tied), scale, K, r0, r1, in, ys, red, xs);
+    gemv_mfma_end<WT, true>(job, m, s, scale, r0, in, ys, red, xs);
   }
   __syncthreads();
   if (t.mat != M_O && t.mat != M_D) norm_scale_ys(m, s, r1 - r0, ys, red, NW);
