@@ -120,8 +120,11 @@ typedef struct amk_model amk_model;
 typedef struct amk_kv amk_kv;
 
 /* Create a model on the current device. Weights are BORROWED for the duration of the call: the
- * library repacks them into its own buffers (tile-major row order) and synchronises `stream`
- * before returning, so the caller may free them afterwards. schedule_blob (host, may be NULL)
+ * library repacks them into its own buffers and synchronises `stream` before returning, so the
+ * caller may free them afterwards. The packed rows keep RoPE pairs and gate/up pairs adjacent.
+ * A model of max_batch 1 keeps those rows row-major. A larger max_batch stores each matrix
+ * tile-major (16 rows x 32 inputs per contiguous tile, the matrix cores' step), which is why its
+ * schedules cut GEMVs on 16-row boundaries. schedule_blob (host, may be NULL)
  * is a frozen schedule from amk_schedule_build; NULL builds one with default parameters. The
  * schedule is validated before anything is launched (AMK_E_SCHEDULE_REJECTED on failure). */
 amk_status amk_model_create(const amk_config *cfg, const amk_weights *weights, int32_t path,
