@@ -154,6 +154,17 @@ def test_tiny_batch3(path):
 
 
 @pytest.mark.parametrize("path", ["megakernel", "unfused"])
+def test_batch3_tiles_off_the_grid(path):
+    """A batched model's tile-major weights end in zero-padded tiles: 4100 vocabulary rows
+    leave the LM head a last 16-row group of 4 rows, and a 696-wide FFN gives the down projection
+    21.75 steps of 32 inputs."""
+    cfg = synth.get_config("tiny").replace(batch=3, ffn=696, vocab=4100)
+    rep = teacher_forced(cfg, path, seed=12, n_calls=8)
+    assert rep.tokens_checked > 0
+    assert_parity(rep)
+
+
+@pytest.mark.parametrize("path", ["megakernel", "unfused"])
 def test_tiny_batch16(path):
     """Sixteen sequences: the matrix cores take one column per sequence and multiply the two bf16
     halves of the input by two instructions."""
