@@ -76,6 +76,29 @@ def test_unequal_rates_are_equalised(libamk, n_cu):
     assert sorted((t[0], t[1]) for t in _gemv_tasks(out)) == sorted((t[0], t[1]) for t in _gemv_tasks(b))
 
 
+def test_batched_rebalance_keeps_the_16_row_groups(libamk):
+    """A model of batch capacity 4 reads tile-major weights in 16-row groups: re-tiling for
+    unequal rates moves boundaries in whole groups, stays valid, and still equalises the finish
+    times to within that coarser alignment."""
+    n_cu = 8
+    blob = _tiny_blob(n_cu, batch=4)
+    b = B.Blob(blob)
+    rate = np.where(np.arange(n_cu) % 2 == 0, 0.02, 0.04)
+    start = np.linspace(0.0, 1.0, n_cu)
+    spread0 = _finish_spread(b, rate, start)
+    out_blob = _lib.schedule_rebalance(blob, _trace(b, rate, start)[None], gain=1.0)
+    out = B.Blob(out_blob)
+    assert _lib.schedule_validate(out_blob)[0] == _lib.AMK_OK
+    assert _lib.schedule_simulate(out_blob)[0] == _lib.AMK_OK
+    moved = 0
+    for (t0, t1) in zip(sorted(_gemv_tasks(b)), sorted(_gemv_tasks(out))):
+        assert t1[4] % 16 == 0, t1
+        moved += t0[4] != t1[4]
+    assert moved > 0
+    spread1 = _finish_spread(out, rate, start)
+    assert spread1 < 0.5 * spread0 and spread1 <= 2 * 16 * 0.04 + 1e-9, (spread0, spread1)
+
+
 def test_partial_gain_moves_part_of_the_way(libamk):
     blob = _tiny_blob()
     b = B.Blob(blob)
