@@ -1422,8 +1422,9 @@ __device__ __forceinline__ void mfma_dispatch(const MfmaTile &T, int g0, int gn,
 // step's inputs of every sequence, the norm gain and, for int4, the step's group scale of each
 // row, all copied from memory straight into the round's LDS slot. Every round issues the same
 // copies; lanes and rounds with nothing to fetch address past their buffer resource, which moves
-// no data. D rounds are issued ahead, so round r is in LDS once the vector-memory count is down to
-// D times the copies per round, and no registers wait on loads in flight. A copy writes 16 (or 4)
+// no data. D rounds are issued ahead (in steady state round r is in LDS once the vector-memory
+// count is down to D times the copies per round; wait_round has the prologue's counts), and no
+// registers wait on loads in flight. A copy writes 16 (or 4)
 // bytes of LDS for each active lane whether or not it fetched anything, so each copy's slot area
 // holds 64 lanes' worth, except the gain's, which only lanes 0..3 copy.
 // ------------------------------------------------------------------------------------------
