@@ -37,3 +37,25 @@ def test_tuned_schedule_keeps_parity():
     rep = teacher_forced(cfg, "megakernel", seed=6, n_calls=2, weights=w, model=model)
     assert_parity(rep)
     model.close()
+
+
+def test_tuned_batched_schedule_keeps_the_weight_groups():
+    """Re-tiling a model of batch capacity 4, whose weights are tile-major: the tuned GEMV tiles
+    stay on the 16-row weight groups and the tuned model still matches the oracle."""
+    cfg = synth.get_config("tiny").replace(batch=4)
+    w = synth.make_weights(cfg, 9, threads=16)
+    model = Model(cfg, w, max_seq=cfg.max_seq)
+    kv = model.kv(cfg.batch, cfg.max_seq)
+    us = model.tune(kv, 8, rounds=2, steps=2, gain=0.6)
+    after = model.schedule()
+    log(f"tiny batch-4 tuned: {us:.1f} us/step")
+    assert us > 0
+    assert _lib.schedule_validate(after)[0] == _lib.AMK_OK
+    t = B.Blob(after).all_tasks()
+    g = t[t["type"] == B.T_GEMV]
+    assert (g["a0"] % 16 == 0).all()
+    kv.close()
+    rep = teacher_forced(cfg, "megakernel", seed=9, n_calls=10, weights=w, model=model)
+    assert rep.tokens_checked > 0
+    assert_parity(rep)
+    model.close()
