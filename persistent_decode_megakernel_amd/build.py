@@ -16,7 +16,10 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libamk.so")
 BUILD = os.path.join(ROOT, "_build")
 
-HIP_SOURCES = ["kernels/megakernel.hip", "kernels/unfused.hip", "runtime/model.hip"]
+HIP_SOURCES = ["kernels/unfused.hip", "runtime/model.hip"]
+# the megakernel source is compiled once per (weight type, head_dim) pair, in parallel
+MEGAKERNEL = "kernels/megakernel.hip"
+MK_PAIRS = [(wt, hd) for wt in (0, 1, 2) for hd in (64, 128)]
 CXX_SOURCES = ["runtime/errors.cpp", "sched/builder.cpp", "sched/validate.cpp", "sched/sched_api.cpp",
                "sched/rebalance.cpp"]
 ARCH = "gfx950"
@@ -36,20 +39,47 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
+def _headers():
+    out = []
+    for d in (CSRC, os.path.join(ROOT, "include")):
+        for dp, _, fs in os.walk(d):
+            out += [os.path.join(dp, f) for f in fs if f.endswith(".h")]
+    return out
+
+
+def _stale(obj: str, src: str, newest_header: float) -> bool:
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    return os.path.getmtime(src) > t or newest_header > t
+
+
+def build(verbose: bool = False, jobs: int = 8, incremental: bool = False) -> str:
+    """Compile every source and link libamk.so. incremental=True recompiles only objects older
+    than their source or any header (for development loops; the default rebuilds everything)."""
     os.makedirs(BUILD, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include")]
     common = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function"] + inc
+    hip = [hipcc(), f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops"]
+    newest_header = max((os.path.getmtime(h) for h in _headers()), default=0.0)
     objs, cmds = [], []
+
+    def add(cmd, src, obj):
+        objs.append(obj)
+        if not incremental or _stale(obj, src, newest_header):
+            cmds.append(cmd)
+
+    for wt, hd in MK_PAIRS:
+        src = os.path.join(CSRC, MEGAKERNEL)
+        obj = os.path.join(BUILD, f"kernels_megakernel_w{wt}_h{hd}.o")
+        add(hip + [f"-DAMK_MK_WT={wt}", f"-DAMK_MK_HD={hd}", "-c", src, "-o", obj] + common, src, obj)
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src.replace("/", "_") + ".o")
-        cmds.append([hipcc(), f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-                     "-packed-fp32-ops", "-c", os.path.join(CSRC, src), "-o", obj] + common)
-        objs.append(obj)
+        add(hip + ["-c", os.path.join(CSRC, src), "-o", obj] + common, os.path.join(CSRC, src), obj)
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src.replace("/", "_") + ".o")
-        cmds.append(["g++", "-c", os.path.join(CSRC, src), "-o", obj] + common)
-        objs.append(obj)
+        add(["g++", "-c", os.path.join(CSRC, src), "-o", obj] + common, os.path.join(CSRC, src), obj)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
@@ -61,4 +91,4 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv))

@@ -311,22 +311,13 @@ using namespace amk;
     megakernel_body<WT, HD, Q, true>(*mp, s);                                                 \
   }
 
-// batch-1 instances (weight stream with LDS prefetch) and batched ones (suffix _b: matrix cores)
-AMK_MK(0, 64, 1)
-AMK_MK(0, 64, 2)
-AMK_MK(0, 64, 4)
-AMK_MK(0, 128, 1)
-AMK_MK(0, 128, 2)
-AMK_MK(0, 128, 4)
-AMK_MK(1, 64, 1)
-AMK_MK(1, 64, 2)
-AMK_MK(1, 64, 4)
-AMK_MK(1, 128, 1)
-AMK_MK(1, 128, 2)
-AMK_MK(1, 128, 4)
-AMK_MK(2, 64, 1)
-AMK_MK(2, 64, 2)
-AMK_MK(2, 64, 4)
-AMK_MK(2, 128, 1)
-AMK_MK(2, 128, 2)
-AMK_MK(2, 128, 4)
+// batch-1 instances (weight stream with LDS prefetch) and batched ones (suffix _b: matrix cores).
+// The build compiles this file once per (weight type, head_dim) pair, selected by AMK_MK_WT and
+// AMK_MK_HD, so the instances compile in parallel; each object holds that pair's three instances.
+#if !defined(AMK_MK_WT) || !defined(AMK_MK_HD)
+#error "compile with -DAMK_MK_WT=<0|1|2> -DAMK_MK_HD=<64|128>"
+#endif
+#define AMK_MK_CAT(a, b, c) AMK_MK(a, b, c)
+AMK_MK_CAT(AMK_MK_WT, AMK_MK_HD, 1)
+AMK_MK_CAT(AMK_MK_WT, AMK_MK_HD, 2)
+AMK_MK_CAT(AMK_MK_WT, AMK_MK_HD, 4)

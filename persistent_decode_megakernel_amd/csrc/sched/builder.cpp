@@ -394,10 +394,13 @@ bool parse(const void *blob, size_t bytes, Schedule *out, std::string *err) {
   std::vector<uint32_t> off(h.n_cu + 1);
   std::memcpy(off.data(), b + h.offsets_off, 4u * (h.n_cu + 1));
   if (off[0] != 0 || off[h.n_cu] != h.n_tasks) return fail("blob: offsets do not span tasks");
+  // every offset is checked before any task is copied: a single monotone, bounded sequence
+  // keeps every CU's task range inside the task table
+  for (uint32_t c = 0; c < h.n_cu; ++c)
+    if (off[c + 1] < off[c] || off[c + 1] > h.n_tasks) return fail("blob: offsets not monotone");
   out->hdr = h;
   out->per_cu.assign(h.n_cu, {});
   for (uint32_t c = 0; c < h.n_cu; ++c) {
-    if (off[c + 1] < off[c]) return fail("blob: offsets not monotone");
     for (uint32_t i = off[c]; i < off[c + 1]; ++i) {
       Task t;
       std::memcpy(&t, b + h.tasks_off + sizeof(Task) * i, sizeof t);

@@ -1,5 +1,6 @@
 """Schedule layer (host only): real lowerings validate and simulate clean; adversarial mutants
 that the simulator finds unsafe are all rejected by the static validator (no false accepts)."""
+import ctypes as C
 import random
 
 import numpy as np
@@ -167,6 +168,26 @@ def test_truncated_and_corrupt_blobs_rejected(libamk):
     b = B.Blob(blob)
     b.hdr.lds_bytes = 200 * 1024
     assert _lib.schedule_validate(b.to_bytes())[0] == _lib.AMK_E_SCHEDULE_REJECTED
+
+
+@pytest.mark.parametrize("bad_offset", ["huge", "past_end", "non_monotone"])
+def test_intermediate_offsets_checked_before_any_task_is_read(libamk, bad_offset):
+    """Per-CU offsets of a blob whose first and last offsets are consistent but whose middle one
+    points far past the task table: every parser entry rejects it without reading beyond the
+    buffer (a parser that copied one CU's tasks before checking the next offset read past it)."""
+    cfg = synth.get_config("tiny")
+    blob = bytearray(_lib.schedule_build(_lib.make_config(cfg), 1, 8))
+    h = B.BlobHeader.from_buffer_copy(bytes(blob[:C.sizeof(B.BlobHeader)]))
+    off = np.frombuffer(bytes(blob), dtype="<u4", count=h.n_cu + 1, offset=h.offsets_off).copy()
+    assert off[-1] == h.n_tasks and h.n_cu == 8
+    off[1] = {"huge": 50_000_000, "past_end": h.n_tasks + 1000, "non_monotone": off[3] + 1}[bad_offset]
+    if bad_offset == "non_monotone":
+        off[2] = off[1] - 2
+    blob[h.offsets_off:h.offsets_off + 4 * (h.n_cu + 1)] = off.astype("<u4").tobytes()
+    data = bytes(blob)
+    st, rep = _lib.schedule_validate(data)
+    assert st == _lib.AMK_E_SCHEDULE_REJECTED and "offsets" in rep, rep
+    assert _lib.schedule_simulate(data)[0] == _lib.AMK_E_SCHEDULE_REJECTED
 
 
 def FOUR_BLOCKS():
