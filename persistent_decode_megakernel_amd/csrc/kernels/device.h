@@ -49,6 +49,10 @@ struct DevModel {
   float *logits;       // [B][V] used when the caller passes no logits buffer
   float2 *amax;        // [n_lm][B] (value, index bits)
   uint32_t *flags;     // [n_tasks]
+  // The epoch of the last completed step. A launch reads it once per workgroup at its start and
+  // runs step i at epoch + 1 + i; the last step's argmax stores epoch + n_steps. Kept on the
+  // device (not a launch argument) so that a captured and replayed launch still advances it.
+  uint32_t *ectr;
   uint32_t *err;       // [0] status, [1] abort, [2] task, [3] detail
   const Task *tasks;
   const uint32_t *offsets;
@@ -1089,6 +1093,10 @@ constexpr uint32_t kTagMask = 3u;
 __device__ __forceinline__ uint32_t tag_word(float v, uint32_t epoch) {
   return (__float_as_uint(v) & ~kTagMask) | (epoch & kTagMask);
 }
+// The value a tagged word carries, with its tag bits cleared: the value the producer computed
+// truncated to 21 mantissa bits, whatever the epoch. Results therefore do not depend on the step
+// count, and two runs of the same inputs agree bit for bit at any epochs.
+__device__ __forceinline__ float untag(uint32_t w) { return __uint_as_float(w & ~kTagMask); }
 
 // xs[i] = v_i * gain[i] (gain may be null) for the n tagged words at src (n % 4 == 0), once every
 // tag matches `epoch`; with a gain the per-wave sums of v^2 go to red[wave]. Each thread owns up
@@ -1142,8 +1150,7 @@ __device__ __forceinline__ bool stage_tagged(const DevModel &m, const uint32_t *
           if ((((w.x ^ tag) | (w.y ^ tag) | (w.z ^ tag) | (w.w ^ tag)) & kTagMask) == 0) {
             need &= ~(1u << j);
             const int u = base + (int)threadIdx.x + j * kThreads;
-            float a = __uint_as_float(w.x), b = __uint_as_float(w.y), c = __uint_as_float(w.z),
-                  d = __uint_as_float(w.w);
+            float a = untag(w.x), b = untag(w.y), c = untag(w.z), d = untag(w.w);
             if (gain) {
               ss = fmaf(a, a, fmaf(b, b, fmaf(c, c, fmaf(d, d, ss))));
               const uint2 g = gld_bf16x4(gain, u);
@@ -1936,7 +1943,7 @@ __device__ void epi_residual_tagged(const DevModel &m, const StepArgs &s, int re
   const uint16_t *e = (res_slot == 0) ? m.embed + (int64_t)token_of(m, s, 0) * d : nullptr;
   for (int i = threadIdx.x; i < n; i += nw * 64) {
     const int r = r0 + i;
-    const float base = e ? bf16_to_f32(gld(&e[r])) : __uint_as_float(cld(&res[r]));
+    const float base = e ? bf16_to_f32(gld(&e[r])) : untag(cld(&res[r]));
     cst(&out[r], tag_word(base + ys[i], s.epoch));
   }
 }
@@ -2062,7 +2069,7 @@ __device__ bool attn_stage_tagged(const DevModel &m, const StepArgs &s, int l, i
       if ((need & (1u << j)) && (w[j] & kTagMask) == tag) {
         need &= ~(1u << j);
         if (i < nqw)
-          qs[i] = __uint_as_float(w[j]) * m.attn_scale;
+          qs[i] = untag(w[j]) * m.attn_scale;
         else
           kvrow[i - nqw] = (uint16_t)(w[j] >> 16);
       }
@@ -2367,11 +2374,13 @@ __device__ __forceinline__ bool attn_merge(const DevModel &m, const StepArgs &s,
           wl[j] = cld(pk + hd + 1);
           wa[j] = cld(pk + e);
         }
+        // tagged partials are read with their tag bits cleared
+        auto val = [](uint32_t w) { return TAGGED ? untag(w) : __uint_as_float(w); };
         float Mb = M;
 #pragma unroll
         for (int j = 0; j < KB; ++j) {
           if (TAGGED) bad |= ((wm[j] ^ tag) | (wl[j] ^ tag) | (wa[j] ^ tag)) & kTagMask;
-          if (k0 + j < nblk) Mb = fmaxf(Mb, __uint_as_float(wm[j]));
+          if (k0 + j < nblk) Mb = fmaxf(Mb, val(wm[j]));
         }
         const float f = __expf(M - Mb);
         den *= f;
@@ -2379,9 +2388,9 @@ __device__ __forceinline__ bool attn_merge(const DevModel &m, const StepArgs &s,
 #pragma unroll
         for (int j = 0; j < KB; ++j) {
           if (k0 + j < nblk) {
-            const float w = __expf(__uint_as_float(wm[j]) - Mb);
-            den = fmaf(w, __uint_as_float(wl[j]), den);
-            num = fmaf(w, __uint_as_float(wa[j]), num);
+            const float w = __expf(val(wm[j]) - Mb);
+            den = fmaf(w, val(wl[j]), den);
+            num = fmaf(w, val(wa[j]), num);
           }
         }
         M = Mb;

@@ -255,10 +255,15 @@ __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArg
     const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20);
     gst(&trace[(uint64_t)m.n_tasks * 4 + blockIdx.x], (uint64_t)xcc);
   }
+  // Epoch of the last completed step, read once per workgroup. Every workgroup with tasks reads
+  // it before its first task, and the store below comes after the last step's argmax, which
+  // every task follows, so all of them see the same value. A workgroup without tasks may read
+  // either value and uses neither.
+  const uint32_t e0 = uniform_u32(flag_load(m.ectr));
   for (int step = 0; step < s0.n_steps; ++step) {
     StepArgs s = s0;
     s.step = step;
-    s.epoch = s0.epoch + (uint32_t)step;
+    s.epoch = e0 + 1u + (uint32_t)step;
     s.pos = s0.pos + step;
     s.posp = &s0.pos_in[0];
     if (step > 0) s.tokens = s0.next + (int64_t)(step - 1) * s0.batch;
@@ -277,6 +282,9 @@ __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArg
       } else {
         ok = wait_task(m, t, s.epoch, &abort_flag);
         if (ok) argmax_combine(m, s, (int)t.aux0);
+        // the launch's last step is complete: the next launch starts from its epoch
+        if (ok && step == s0.n_steps - 1 && threadIdx.x == 0)
+          __hip_atomic_store(gptr(m.ectr), s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       if (!ok) return;
       // Publish: every wave waits for its own (device-coherent) stores to complete, the workgroup

@@ -158,6 +158,78 @@ UgFn pick_uf_gemv(int wt, int mode) {
 
 int qmax_for(int qpg) { return qpg <= 1 ? 1 : (qpg <= 2 ? 2 : kAttnMaxHeads); }
 
+// The per-step scratch of a model as one block of device memory. It opens with the state region,
+// which must hold zeros before a model's first step (and again after a reset or a schedule
+// change): the epoch counter, the dependency flags and the tagged activation slots of batch-1
+// instances (whose tags must not match any epoch yet). Plain scratch follows, written before it
+// is read within every step. Offsets are 256-byte aligned; an absent buffer has kNone.
+constexpr size_t kNone = ~(size_t)0;
+struct ScratchPlan {
+  size_t ectr = kNone, flags = kNone, ht = kNone, at = kNone, aot = kNone, qt = kNone,
+         kvt = kNone, part = kNone;  // state region
+  size_t h = kNone, q = kNone, ao = kNone, a = kNone, logits = kNone, amax = kNone, xn = kNone,
+         y = kNone, o = kNone;
+  size_t state_bytes = 0, total = 0;
+};
+
+ScratchPlan plan_scratch(const amk_config &c, int nblk, uint32_t n_tasks, int n_amax) {
+  ScratchPlan p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    if (bytes == 0) return kNone;
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  const size_t L = c.n_layers, d = c.hidden, nq = c.n_heads, nkv = c.n_kv_heads, hd = c.head_dim,
+               F = c.ffn, V = c.vocab, B = c.max_batch, qd = nq * hd;
+  const size_t qkvr = (size_t)qkv_rows(c.n_heads, c.n_kv_heads, c.head_dim);
+  const bool tagged = B == 1;  // batch-1 instances hand activations over as tagged words
+  p.ectr = take(4);
+  p.flags = take(4 * (size_t)std::max<uint32_t>(1, n_tasks));
+  p.ht = take(tagged ? 4 * (2 * L + 1) * d : 0);
+  p.at = take(tagged ? 4 * L * F : 0);
+  p.aot = take(tagged ? 4 * L * qd : 0);
+  p.qt = take(tagged ? 4 * L * qd : 0);
+  p.kvt = take(tagged ? 4 * L * 2 * nkv * hd : 0);
+  p.part = take(4 * L * B * nq * (size_t)nblk * (hd + 2));
+  p.state_bytes = off;
+  const size_t kmax = std::max(std::max(d, qd), F);
+  p.h = take(4 * (2 * L + 1) * B * d);
+  p.q = take(4 * L * B * qd);
+  p.ao = take(4 * L * B * qd);
+  p.a = take(4 * L * B * F);
+  p.logits = take(4 * B * V);
+  p.amax = take(8 * (size_t)n_amax * B);
+  p.xn = take(4 * B * kmax);
+  p.y = take(4 * B * std::max(std::max(qkvr, 2 * F), std::max(V, d)));
+  p.o = take(4 * B * qd);
+  p.total = off;
+  return p;
+}
+
+// Point the scratch fields of dm into the block at base, laid out by p.
+void carve_scratch(DevModel &dm, uint8_t *base, const ScratchPlan &p) {
+  auto at = [&](size_t off) -> uint8_t * { return off == kNone ? nullptr : base + off; };
+  dm.ectr = reinterpret_cast<uint32_t *>(at(p.ectr));
+  dm.flags = reinterpret_cast<uint32_t *>(at(p.flags));
+  dm.ht = reinterpret_cast<uint32_t *>(at(p.ht));
+  dm.at = reinterpret_cast<uint32_t *>(at(p.at));
+  dm.aot = reinterpret_cast<uint32_t *>(at(p.aot));
+  dm.qt = reinterpret_cast<uint32_t *>(at(p.qt));
+  dm.kvt = reinterpret_cast<uint32_t *>(at(p.kvt));
+  dm.part = reinterpret_cast<float *>(at(p.part));
+  dm.h = reinterpret_cast<float *>(at(p.h));
+  dm.q = reinterpret_cast<float *>(at(p.q));
+  dm.ao = reinterpret_cast<float *>(at(p.ao));
+  dm.a = reinterpret_cast<float *>(at(p.a));
+  dm.logits = reinterpret_cast<float *>(at(p.logits));
+  dm.amax = reinterpret_cast<float2 *>(at(p.amax));
+  dm.xn = reinterpret_cast<float *>(at(p.xn));
+  dm.y = reinterpret_cast<float *>(at(p.y));
+  dm.o = reinterpret_cast<float *>(at(p.o));
+}
+
 }  // namespace
 
 struct amk_model {
@@ -176,7 +248,8 @@ struct amk_model {
   DevModel *d_dm_pf = nullptr;
   int32_t *pf_next = nullptr;  // device int32 [kMaxBatch]
   std::vector<DevLayer> layers;
-  uint32_t epoch = 0;
+  ScratchPlan plan;
+  uint8_t *scratch = nullptr;  // the model's own per-step scratch block (plan.total bytes)
   uint32_t lds_bytes = 0;
   uint32_t uf_attn_lds = 0;
   uint64_t weight_bytes = 0;
@@ -280,27 +353,20 @@ uint32_t argmax_of(const Schedule &s) {
   return 0;
 }
 
-// Tagged activations carry an epoch: whenever the epoch restarts they are cleared too, so no
-// word of an earlier run can pass for the new step's. A fill kernel, not a memset, since this runs
-// inside amk_decode_step, which a caller may capture into a graph.
-void clear_tags(amk_model *m, hipStream_t st) {
-  const size_t L = m->cfg.n_layers, d = m->cfg.hidden, F = m->cfg.ffn, hd = m->cfg.head_dim,
-               qd = (size_t)m->cfg.n_heads * hd, B = m->cfg.max_batch;
-  zero_async(m->dm.ht, sizeof(uint32_t) * (2 * L + 1) * d, st);
-  zero_async(m->dm.at, sizeof(uint32_t) * L * F, st);
-  zero_async(m->dm.aot, sizeof(uint32_t) * L * qd, st);
-  zero_async(m->dm.qt, sizeof(uint32_t) * L * qd, st);
-  zero_async(m->dm.kvt, sizeof(uint32_t) * L * 2 * m->cfg.n_kv_heads * hd, st);
-  zero_async(m->dm.part, sizeof(float) * L * B * m->cfg.n_heads * m->dm.nblk * (hd + 2), st);
+// Zero the state region of the model's scratch (epoch counter, flags, tagged slots): the step
+// after this starts at epoch 1 and no stale word can carry its tag.
+void zero_state(amk_model *m, hipStream_t st) { zero_async(m->scratch, m->plan.state_bytes, st); }
+
+// upload the host copy of the model's device descriptor
+void upload_dm(amk_model *m) {
+  hip_check(hipMemcpy(m->d_dm, &m->dm, sizeof(DevModel), hipMemcpyHostToDevice), "hipMemcpy");
 }
 
-// reset device error words, flags and the epoch after a device-side failure
+// reset device error words, flags, tagged slots and the epoch after a device-side failure
 void reset_device_state(amk_model *m, hipStream_t st) {
   (void)hipMemsetAsync(m->dm.err, 0, 4 * sizeof(uint32_t), st);
-  (void)hipMemsetAsync(m->dm.flags, 0, sizeof(uint32_t) * std::max<uint32_t>(1, m->sched.hdr.n_tasks), st);
-  clear_tags(m, st);
+  zero_state(m, st);
   (void)hipStreamSynchronize(st);
-  m->epoch = 0;
   m->err_pending = false;
 }
 
@@ -545,30 +611,14 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     hip_check(hipMemcpyAsync(d_rope, rope.data(), rope.size() * sizeof(float2),
                              hipMemcpyHostToDevice, st), "hipMemcpyAsync");
     dm.rope = d_rope;
-    const int nblk = dm.nblk;
-    dm.h = m->dalloc<float>((size_t)(2 * L + 1) * B * d);
-    dm.q = m->dalloc<float>((size_t)L * B * qd);
-    dm.part = m->dalloc<float>((size_t)L * B * nq * nblk * (hd + 2));
-    dm.ao = m->dalloc<float>((size_t)L * B * qd);
-    // batch-1 instances exchange these activations as tagged words instead
-    dm.ht = m->dalloc<uint32_t>((size_t)(2 * L + 1) * d);
-    dm.at = m->dalloc<uint32_t>((size_t)L * F);
-    dm.aot = m->dalloc<uint32_t>((size_t)L * qd);
-    dm.qt = m->dalloc<uint32_t>((size_t)L * qd);
-    dm.kvt = m->dalloc<uint32_t>((size_t)L * 2 * cfg->n_kv_heads * hd);
-    dm.a = m->dalloc<float>((size_t)L * B * F);
-    dm.logits = m->dalloc<float>((size_t)B * V);
     m->n_lm_uf = (V + kUfRowsPerBlock - 1) / kUfRowsPerBlock;
-    dm.amax = m->dalloc<float2>((size_t)std::max<int>(m->n_lm_uf, dm.n_lm) * B);
-    dm.flags = m->dalloc<uint32_t>(std::max<uint32_t>(1, h.n_tasks));
+    m->plan = plan_scratch(*cfg, dm.nblk, h.n_tasks, std::max<int>(m->n_lm_uf, dm.n_lm));
+    m->scratch = m->dalloc<uint8_t>(m->plan.total);
+    carve_scratch(dm, m->scratch, m->plan);
     dm.err = m->dalloc<uint32_t>(4);
     const int kmax = std::max(std::max(d, qd), F);
-    dm.xn = m->dalloc<float>((size_t)B * kmax);
-    dm.y = m->dalloc<float>((size_t)B * std::max(std::max(qkvr, 2 * F), std::max(V, d)));
-    dm.o = m->dalloc<float>((size_t)B * qd);
-    hip_check(hipMemsetAsync(dm.flags, 0, sizeof(uint32_t) * std::max<uint32_t>(1, h.n_tasks), st), "hipMemsetAsync");
     hip_check(hipMemsetAsync(dm.err, 0, 16, st), "hipMemsetAsync");
-    clear_tags(m, st);
+    zero_state(m, st);
     // task tables
     std::vector<uint32_t> offs(h.n_cu + 1);
     std::vector<Task> tasks;
@@ -747,11 +797,6 @@ amk_status decode(amk_model *m, amk_kv *kv, const int32_t *d_tokens, const int32
     if (pos[b] < 0 || (int64_t)pos[b] + n_steps > std::min(kv->max_seq, m->cfg.max_seq))
       return set_error(AMK_E_CAPACITY, f + ": positions beyond max_seq");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (m->epoch >= 0x7ffffff0u - (uint32_t)n_steps) {  // keep the signed flag comparison unambiguous
-    zero_async(m->dm.flags, sizeof(uint32_t) * std::max<uint32_t>(1, m->sched.hdr.n_tasks), st);
-    clear_tags(m, st);
-    m->epoch = 0;
-  }
   StepArgs s;
   s.tokens = d_tokens;
   s.logits = d_logits;
@@ -764,10 +809,9 @@ amk_status decode(amk_model *m, amk_kv *kv, const int32_t *d_tokens, const int32
   s.kv_seq = -1;
   s.posp = nullptr;  // set on the device
   s.batch = batch;
-  s.epoch = m->epoch + 1;
+  s.epoch = 0;  // the megakernel takes its epochs from the device counter
   s.step = 0;
   s.n_steps = n_steps;
-  m->epoch += (uint32_t)n_steps;
   if (m->path == AMK_PATH_MEGAKERNEL) {
     const DevModel *g = m->d_dm;
     void *args[] = {(void *)&g, (void *)&s};
@@ -781,7 +825,6 @@ amk_status decode(amk_model *m, amk_kv *kv, const int32_t *d_tokens, const int32
       si.n_steps = 1;
       si.pos = pos[0] + i;
       for (int32_t b = 0; b < batch; ++b) si.pos_in[b] = pos[b] + i;
-      si.epoch = s.epoch + (uint32_t)i;
       si.tokens = i ? d_out + (int64_t)(i - 1) * batch : d_tokens;
       si.next = d_out + (int64_t)i * batch;
       si.logits = d_logits ? d_logits + (int64_t)i * batch * m->cfg.vocab : nullptr;
@@ -1003,10 +1046,8 @@ amk_status install_schedule(amk_model *m, Schedule &&s, std::vector<uint8_t> &&b
                       hipMemcpyHostToDevice), "hipMemcpy");
   hip_check(hipMemcpy(const_cast<uint32_t *>(m->dm.offsets), offs.data(), offs.size() * 4,
                       hipMemcpyHostToDevice), "hipMemcpy");
-  zero_async(m->dm.flags, sizeof(uint32_t) * std::max<uint32_t>(1, h.n_tasks), st);
-  clear_tags(m, st);
+  zero_state(m, st);
   hip_check(hipStreamSynchronize(st), "hipStreamSynchronize");
-  m->epoch = 0;
   m->lds_bytes = h.lds_bytes;
   m->sched = std::move(s);
   m->blob = std::move(blob);
