@@ -149,7 +149,10 @@ amk_status amk_kv_data(const amk_kv *kv, void **d_ptr);
  * (device int32 [batch], greedy argmax, lowest index on ties) and, when d_logits != NULL,
  * d_logits (device float32 [batch, vocab]). d_next may alias the next call's d_tokens. Calls on
  * one model must be stream-ordered (scratch is reused). Device-side errors (dependency timeout,
- * token out of range) are recorded on the device and reported by amk_sync. */
+ * token out of range) are recorded on the device and reported by amk_sync. The call may be
+ * captured into a graph: the step counter that orders the megakernel's dependency flags lives on
+ * the device, so every replay advances it as an eager launch does, and results do not depend on
+ * it (a replay gives the eager launch's logits bit for bit). */
 amk_status amk_decode_step(amk_model *m, amk_kv *kv, const int32_t *d_tokens, int32_t pos,
                            int32_t batch, float *d_logits, int32_t *d_next, void *stream);
 
