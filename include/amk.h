@@ -114,6 +114,8 @@ typedef struct {
   int32_t path;              /* amk_path */
   uint64_t weight_bytes;     /* algorithmic weight bytes read per step (matrices, gains, scales) */
   double predicted_us;       /* cost-model makespan of the frozen schedule at ctx_hint */
+  uint64_t scratch_bytes;    /* device scratch of one decode step: flags, step counter, activation
+                              * slots, attention partials, logits (one block, owned by the model) */
 } amk_model_info;
 
 typedef struct amk_model amk_model;

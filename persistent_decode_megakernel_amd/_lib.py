@@ -65,7 +65,8 @@ class amk_cost_model(C.Structure):
 class amk_model_info(C.Structure):
     _fields_ = [("n_cu", C.c_int32), ("n_tasks", C.c_int32), ("launches_per_step", C.c_int32),
                 ("lds_bytes", C.c_int32), ("attn_blocks", C.c_int32), ("path", C.c_int32),
-                ("weight_bytes", C.c_uint64), ("predicted_us", C.c_double)]
+                ("weight_bytes", C.c_uint64), ("predicted_us", C.c_double),
+                ("scratch_bytes", C.c_uint64)]
 
 
 # name -> (restype, argtypes); every symbol include/amk.h declares

@@ -980,8 +980,7 @@ extern "C" amk_status amk_trace_enable(amk_model *m, uint64_t *d_trace, size_t b
     return set_error(AMK_E_CAPACITY, "amk_trace_enable: buffer needs " + std::to_string(need) + " bytes");
   (void)hipDeviceSynchronize();
   m->dm.trace = d_trace;
-  hipError_t e = hipMemcpy(m->d_dm, &m->dm, sizeof(DevModel), hipMemcpyHostToDevice);
-  if (e != hipSuccess) return set_error(AMK_E_HIP, std::string("amk_trace_enable: ") + hipGetErrorString(e));
+  upload_dm(m);
   clear_error();
   return AMK_OK;
   AMK_API_END
@@ -997,6 +996,7 @@ extern "C" amk_status amk_model_get_info(const amk_model *m, amk_model_info *out
   out->path = m->path;
   out->weight_bytes = m->weight_bytes;
   out->predicted_us = m->sched.hdr.predicted_us;
+  out->scratch_bytes = m->plan.total;
   return AMK_OK;
 }
 
@@ -1052,13 +1052,13 @@ amk_status install_schedule(amk_model *m, Schedule &&s, std::vector<uint8_t> &&b
   m->sched = std::move(s);
   m->blob = std::move(blob);
   m->dm.argmax_id = argmax_of(m->sched);
-  hip_check(hipMemcpy(m->d_dm, &m->dm, sizeof(DevModel), hipMemcpyHostToDevice), "hipMemcpy");
+  upload_dm(m);
   return AMK_OK;
 }
 
 void set_trace(amk_model *m, uint64_t *d_trace) {
   m->dm.trace = d_trace;
-  hip_check(hipMemcpy(m->d_dm, &m->dm, sizeof(DevModel), hipMemcpyHostToDevice), "hipMemcpy");
+  upload_dm(m);
 }
 
 }  // namespace
@@ -1159,7 +1159,10 @@ extern "C" amk_status amk_model_tune(amk_model *m, amk_kv *kv, int32_t pos, int3
   } catch (...) {
     (void)hipDeviceSynchronize();
     m->dm.trace = nullptr;
-    (void)hipMemcpy(m->d_dm, &m->dm, sizeof(DevModel), hipMemcpyHostToDevice);
+    try {
+      upload_dm(m);
+    } catch (...) {
+    }
     if (d_tok) (void)hipFree(d_tok);
     if (d_trace) (void)hipFree(d_trace);
     for (hipEvent_t e : ev)
@@ -1169,7 +1172,7 @@ extern "C" amk_status amk_model_tune(amk_model *m, amk_kv *kv, int32_t pos, int3
   (void)hipDeviceSynchronize();
   if (m->dm.trace) {
     m->dm.trace = nullptr;
-    (void)hipMemcpy(m->d_dm, &m->dm, sizeof(DevModel), hipMemcpyHostToDevice);
+    upload_dm(m);
   }
   (void)hipFree(d_tok);
   (void)hipFree(d_trace);
