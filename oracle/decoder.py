@@ -30,7 +30,7 @@ Data layout of the KV cache (shared with the library as an input/output conventi
 from __future__ import annotations
 
 import math
-from typing import Dict, List, Optional
+from typing import Dict, Optional
 
 import numpy as np
 
@@ -47,9 +47,12 @@ def bf16_to_float(bits: np.ndarray, dtype=np.float64) -> np.ndarray:
 def float_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round to the nearest bfloat16, ties to even, returning bit patterns (uint16).
 
-    The value is first rounded to float32 (the cache is fed from float32 arithmetic on the
-    device), then the low 16 bits are rounded away: add 0x7FFF plus the lowest kept bit and
-    truncate. NaN inputs are not expected and not handled.
+    Reading taken: the pages fix only that the KV cache is bf16 (they decode HuggingFace
+    Llama-family models in bf16, the AutoMegaKernel abstract). A value stored there is a matrix
+    product's result, which such a model accumulates in float32 before storing it in bf16. So the
+    value is first rounded to float32, then to bf16 with round-to-nearest-even (the rounding of
+    torch's and numpy's bf16 casts): add 0x7FFF plus the lowest kept bit and drop the low 16 bits.
+    NaN inputs are not expected and not handled.
     """
     u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
     rounded = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
@@ -235,20 +238,3 @@ class Decoder:
         x = rmsnorm(r, self._vec(w["final_norm"]), eps)
         lm = w["lm_head"] if w.get("lm_head") is not None else w["embed"]
         return self.matvec(("lm",), lm, w.get("lm_head_scale"), x)
-
-    def greedy(self, kv: np.ndarray, first_tokens: np.ndarray, pos0: int, n_steps: int,
-               forced: Optional[List[np.ndarray]] = None):
-        """Run n_steps decode steps from pos0. The token fed at step i is forced[i] when given
-        (prompt feeding / teacher forcing), else the previous step's argmax.
-        Returns (list of logits [B,V], list of argmax ids [B])."""
-        tok = np.asarray(first_tokens, dtype=np.int64).reshape(-1)
-        logits_all, ids_all = [], []
-        for i in range(n_steps):
-            if forced is not None and i < len(forced) and forced[i] is not None:
-                tok = np.asarray(forced[i], dtype=np.int64).reshape(-1)
-            lg = self.step(kv, tok, pos0 + i)
-            ids = argmax_lowest(lg)
-            logits_all.append(lg)
-            ids_all.append(ids)
-            tok = ids.astype(np.int64)
-        return logits_all, ids_all
