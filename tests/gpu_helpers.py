@@ -33,20 +33,33 @@ class Report:
     kv_max_rel: float = 0.0
 
 
-def bf16_close(gpu_bits: np.ndarray, ref_bits: np.ndarray) -> float:
-    """Largest |a - b| / (2 ulp_bf16(|b|) + 1e-3) over two bf16 arrays; <= 1 passes.
+# Appended K/V rows: the device rounds fp32 values, the oracle float64 values, to bf16 (RNE).
+#  * 2 ulps: each side's rounding moves its value by at most half an ulp of its own result, and
+#    across a binade boundary the device's ulp can be twice the oracle's (1/2 * 2 + 1/2 <= 2);
+#  * KV_TAU * max|row|: the two values differ before rounding by the device's fp32 accumulation
+#    error, which scales with the magnitude of the head's row (for elements near zero an ulp bound
+#    alone would demand an fp32 error below the element's own bf16 ulp).
+# KV_TAU was set from measurement: the largest excess beyond 2 ulps seen in every parity test
+# (logged as KVSTAT lines), times four, rounded up to a power of two.
+KV_TAU = 2.0 ** -10
 
-    Appended K/V rows are bf16 roundings of fp32 (device) and fp64 (oracle) values. Through a
-    deep random network fp32 rounding is amplified (the oracle's own fp32 mode differs from its
-    fp64 mode by one bf16 ulp on ~5% of appended elements), so the bound allows 2 ulps plus a
-    small absolute floor rather than bit equality."""
+
+def kv_row_error(gpu_bits: np.ndarray, ref_bits: np.ndarray, label: str = "") -> float:
+    """Largest (|a - b| - 2 ulp_bf16(b))+ / (KV_TAU * max|row of b|) over two bf16 arrays whose
+    last axis is one head's row; <= 1 passes. Logs the measured excess for the record."""
     a = oracle.bf16_to_float(gpu_bits, np.float64)
     b = oracle.bf16_to_float(ref_bits, np.float64)
     if not a.size:
         return 0.0
-    mag = np.maximum(np.abs(b), 1e-30)
-    ulp = np.exp2(np.floor(np.log2(mag)) - 7)
-    return float(np.max(np.abs(a - b) / (2 * ulp + 1e-3)))
+    mag = np.abs(b)
+    ulp = np.where(mag > 0, np.exp2(np.floor(np.log2(np.maximum(mag, 1e-38))) - 7), 0.0)
+    scale = np.maximum(np.max(mag, axis=-1, keepdims=True), 1e-30)
+    diff = np.abs(a - b)
+    excess = np.maximum(diff - 2 * ulp, 0.0) / scale
+    log(f"KVSTAT {label} elems {a.size} differ {np.mean(diff > 0):.4f} "
+        f"beyond1ulp {np.mean(diff > ulp):.5f} beyond2ulp {np.mean(diff > 2 * ulp):.6f} "
+        f"max_excess_over_rowmax {float(np.max(excess)):.3e}")
+    return float(np.max(excess) / KV_TAU)
 
 
 def teacher_forced(cfg: synth.Config, path: str = "megakernel", seed: int = 0,
@@ -102,7 +115,7 @@ def teacher_forced(cfg: synth.Config, path: str = "megakernel", seed: int = 0,
     if check_kv:
         g = synth.bf16_to_numpy_bits(kv.tensor.cpu())
         sl = (slice(None),) * 4 + (slice(p0, p0 + n),)
-        rep.kv_max_rel = bf16_close(g[sl], kv_np[sl])
+        rep.kv_max_rel = kv_row_error(g[sl], kv_np[sl], f"{cfg.name}/{path}")
         # history untouched
         assert np.array_equal(g[..., :p0, :], kv_np[..., :p0, :]), "KV history was modified"
     kv.close()
@@ -114,4 +127,4 @@ def teacher_forced(cfg: synth.Config, path: str = "megakernel", seed: int = 0,
 def assert_parity(rep: Report):
     assert rep.max_abs <= LOGIT_TOL, f"logits max-abs {rep.max_abs} > {LOGIT_TOL}"
     assert not rep.token_mismatch, f"greedy ids differ at confident steps: {rep.token_mismatch[:5]}"
-    assert rep.kv_max_rel <= 1.0, f"appended KV rows differ beyond 2 bf16 ulps: {rep.kv_max_rel}"
+    assert rep.kv_max_rel <= 1.0, f"appended KV rows differ beyond the bound: {rep.kv_max_rel}"

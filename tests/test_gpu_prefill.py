@@ -9,14 +9,9 @@ import oracle
 from persistent_decode_megakernel_amd import _lib, synth
 from persistent_decode_megakernel_amd.model import Model
 
-from gpu_helpers import LOGIT_TOL, MARGIN, log
+from gpu_helpers import LOGIT_TOL, MARGIN, kv_row_error, log
 
 pytestmark = pytest.mark.gpu
-
-
-def _ulp_close(a_bits, e_bits):
-    a, e = oracle.bf16_to_float(a_bits), oracle.bf16_to_float(e_bits)
-    return np.all(np.abs(a - e) <= 2.0 ** -6 * np.abs(e) + 1e-3)
 
 
 @pytest.mark.parametrize("path,n_prompt,wtype", [("megakernel", 40, "bf16"), ("unfused", 40, "bf16"),
@@ -50,7 +45,8 @@ def test_prefill_then_decode_matches_oracle(path, n_prompt, wtype):
     assert worst <= LOGIT_TOL, worst
     if oracle.top2_margin(lo[None])[0] > MARGIN:
         assert int(nxt.item()) == oracle.argmax_lowest(lo[None])[0]
-    assert _ulp_close(kv_dev[:, :, :, :, :n_prompt], kv_np[:, :, :, :, :n_prompt])
+    assert kv_row_error(kv_dev[:, :, :, :, :n_prompt], kv_np[:, :, :, :, :n_prompt],
+                        f"prefill/{path}/{wtype}/{n_prompt}") <= 1.0
     # decoding on from the prompt's cache, the oracle fed the device's tokens
     tok = int(nxt.item())
     g_toks, g_lo = toks.cpu().numpy(), dec_logits.cpu().numpy().astype(np.float64)
@@ -89,7 +85,7 @@ def test_prefill_into_one_sequence_of_a_batch():
     for i, t in enumerate(prompt.cpu().numpy()):
         lo = dec.step(kv1, np.array([int(t)]), 5 + i)[0]
     assert np.max(np.abs(logits.cpu().numpy() - lo)) <= LOGIT_TOL
-    assert _ulp_close(kv_dev[:, :, 1:2, :, 5:25], kv1[:, :, :, :, 5:25])
+    assert kv_row_error(kv_dev[:, :, 1:2, :, 5:25], kv1[:, :, :, :, 5:25], "prefill/seq1") <= 1.0
     assert np.array_equal(kv_dev[:, :, 1, :, :5], kv_np[:, :, 1, :, :5])
     kv.close()
     model.close()

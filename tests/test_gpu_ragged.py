@@ -9,7 +9,7 @@ import oracle
 from persistent_decode_megakernel_amd import _lib, synth
 from persistent_decode_megakernel_amd.model import Model
 
-from gpu_helpers import LOGIT_TOL, MARGIN, log
+from gpu_helpers import LOGIT_TOL, MARGIN, kv_row_error, log
 
 pytestmark = pytest.mark.gpu
 
@@ -56,11 +56,10 @@ def test_ragged_positions_match_per_sequence_oracle(path, batch, wtype):
                 checked += 1
                 assert toks[i, b] == oracle.argmax_lowest(lo[None])[0], (b, i)
             tok = int(toks[i, b])
-        # the rows this sequence appended, within two bf16 ulps of the oracle's
+        # the rows this sequence appended, within the KV-row bound of the oracle's
         rows = slice(pos0[b], pos0[b] + n)
-        a = oracle.bf16_to_float(kv_dev[:, :, b, :, rows, :])
-        e = oracle.bf16_to_float(kv_b[:, :, 0, :, rows, :])
-        assert np.all(np.abs(a - e) <= 2.0 ** -6 * np.abs(e) + 1e-3), b
+        assert kv_row_error(kv_dev[:, :, b, :, rows, :], kv_b[:, :, 0, :, rows, :],
+                            f"ragged/{path}/B{batch}/seq{b}") <= 1.0, b
         # nothing else of the sequence's cache changed
         other = np.ones(kv_dev.shape[4], bool)
         other[rows] = False
