@@ -127,8 +127,15 @@ def load(path: Optional[str] = None) -> C.CDLL:
         raise FileNotFoundError(
             f"{p} is missing: build it with persistent_decode_megakernel_amd.build (hipcc, gfx950)")
     lib = C.CDLL(p)
+    # AMK_LIB_HOST_ONLY=1: a build of the host schedule layer alone (e.g. the sanitizer build),
+    # which exports only the schedule entry points
+    host_only = os.environ.get("AMK_LIB_HOST_ONLY") == "1"
     for name, (res, args) in SIGNATURES.items():
-        fn = getattr(lib, name)
+        fn = getattr(lib, name, None)
+        if fn is None:
+            if host_only:
+                continue
+            raise AttributeError(f"{p} does not export {name}")
         fn.restype = res
         fn.argtypes = args
     if path is None:

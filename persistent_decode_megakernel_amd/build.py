@@ -90,5 +90,21 @@ def build(verbose: bool = False, jobs: int = 8, incremental: bool = False) -> st
     return OUT
 
 
+SANITIZED_OUT = os.path.join(BUILD, "sanitize", "libamk_sched_sanitized.so")
+
+
+def build_sched_sanitized() -> str:
+    """The host-only schedule layer (builder, validator, simulator, re-tiler and their C entry
+    points; no HIP code) as a shared library built with AddressSanitizer and UndefinedBehavior-
+    Sanitizer, for running the adversarial blob corpus under them. Load it with libasan preloaded
+    (the process must start with the ASan runtime) and AMK_LIB_HOST_ONLY=1."""
+    os.makedirs(os.path.dirname(SANITIZED_OUT), exist_ok=True)
+    srcs = [os.path.join(CSRC, s) for s in CXX_SOURCES]
+    _run(["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fPIC", "-shared",
+          "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+          "-I", os.path.join(ROOT, "include"), "-o", SANITIZED_OUT] + srcs)
+    return SANITIZED_OUT
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv))

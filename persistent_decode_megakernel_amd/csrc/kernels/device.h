@@ -272,11 +272,10 @@ constexpr int kWaitVm16 = 0x4F70;  // vmcnt 16: its bits 5:4 sit in bits 15:14
 // taking them from the first lane lets the compiler see that (otherwise it may keep the resource in
 // vector registers and wrap every load in a loop over its distinct values).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  // (the builtin returns a signed int: widen through uint32_t, never by sign extension)
+  // (the builtin returns a signed int: address_from_words widens each half without sign extension)
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  const uint64_t u = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint64_t u = address_from_words(__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)),
+                                        __builtin_amdgcn_readfirstlane((int)(uint32_t)a));
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(u), 0,
                                            __builtin_amdgcn_readfirstlane((int)bytes), kRsrcWord3);
 }

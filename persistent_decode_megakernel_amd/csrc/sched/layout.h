@@ -21,6 +21,13 @@
 
 namespace amk {
 
+// A 64-bit address from its two 32-bit halves as signed words (the form in which the device's
+// first-lane broadcast returns them). Each half is widened as unsigned: converting a signed word
+// with bit 31 set straight to 64 bits would sign-extend it into the upper half.
+AMK_HD uint64_t address_from_words(int32_t hi, int32_t lo) {
+  return ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo;
+}
+
 enum QkvKind : int32_t { KIND_Q = 0, KIND_K = 1, KIND_V = 2 };
 
 struct QkvRow {
