@@ -180,6 +180,24 @@ amk_status amk_decode_steps_ragged(amk_model *m, amk_kv *kv, const int32_t *d_to
                                    const int32_t *h_pos, int32_t n_steps, int32_t batch,
                                    float *d_logits, int32_t *d_out, void *stream);
 
+/* Capacity (bytes) of the static device array behind amk_decode_steps_noalloc, one per GPU. */
+#define AMK_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* amk_decode_steps for callers that cannot allocate device memory: code being captured into a
+ * graph, tight serving loops, harnesses that forbid hipMalloc. Same arguments, results and
+ * ordering rules as amk_decode_steps (bit for bit the same tokens and logits), but the step's
+ * scratch (dependency flags, step counter, activation slots, attention partials, logits when
+ * d_logits is NULL) lives in a static device array of AMK_STATIC_SCRATCH_BYTES per GPU, which
+ * the library holds until the process ends; the call allocates nothing (no hipMalloc/hipFree).
+ * The caller still passes the inputs and outputs. Every call on a GPU, of any model, shares that
+ * GPU's array and first clears its flags and step counter, so calls that overlap on one GPU
+ * (other streams, other threads) race: serialise them. Errors: AMK_E_CAPACITY when the model's
+ * step scratch (amk_model_info.scratch_bytes) exceeds the array; the argument errors of
+ * amk_decode_steps. Device-side errors are reported by amk_sync as for the other calls. */
+amk_status amk_decode_steps_noalloc(amk_model *m, amk_kv *kv, const int32_t *d_tokens,
+                                    int32_t pos, int32_t n_steps, int32_t batch,
+                                    float *d_logits, int32_t *d_out, void *stream);
+
 /* Prompt processing: the n_tokens prompt ids d_tokens (device int32 [n_tokens]) of KV sequence
  * `seq` at positions pos0 .. pos0 + n_tokens - 1, run as operator launches whose GEMVs take up to 16
  * tokens at once on the matrix cores (each token a column at its own position, all columns

@@ -20,6 +20,7 @@ AMK_E_HIP = 5
 AMK_E_CAPACITY = 6
 AMK_E_DEVICE_TIMEOUT = 7
 AMK_E_DEVICE_FAULT = 8
+AMK_STATIC_SCRATCH_BYTES = 64 << 20  # capacity of the array behind amk_decode_steps_noalloc
 
 AMK_WT_BF16 = 0
 AMK_WT_INT8 = 1
@@ -81,6 +82,9 @@ SIGNATURES = {
                                   C.c_void_p, C.c_void_p, C.c_void_p]),
     "amk_decode_steps": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                    C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "amk_decode_steps_noalloc": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                                           C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                                           C.c_void_p]),
     "amk_decode_steps_ragged": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(C.c_int32),
                                           C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
     "amk_prefill": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_int32,

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <stdexcept>
 #include <string>
@@ -230,6 +231,32 @@ void carve_scratch(DevModel &dm, uint8_t *base, const ScratchPlan &p) {
   dm.o = reinterpret_cast<float *>(at(p.o));
 }
 
+// ---- scratch of the entry point that allocates nothing (amk_decode_steps_noalloc) ----------
+// A file-scope device array, one copy per GPU the library runs on, held until the process ends.
+// In host code its name is only a stand-in: kernels and copies use the address that
+// hipGetSymbolAddress returns for the current device (static_scratch_base).
+constexpr size_t kStaticScratchBytes = (size_t)AMK_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t *g_scratch_base[kMaxDevices] = {};
+
+// Device address of `scratch` on device `dev`, which must be current. Looked up once per device
+// (at the first model creation there) and kept.
+uint8_t *static_scratch_base(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) throw std::runtime_error("device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_base[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      throw std::runtime_error(std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_base[dev] = static_cast<uint8_t *>(p);
+  }
+  return g_scratch_base[dev];
+}
+
 }  // namespace
 
 struct amk_model {
@@ -250,6 +277,11 @@ struct amk_model {
   std::vector<DevLayer> layers;
   ScratchPlan plan;
   uint8_t *scratch = nullptr;  // the model's own per-step scratch block (plan.total bytes)
+  // the same descriptor with its scratch in this device's static array (amk_decode_steps_noalloc);
+  // null when plan.total exceeds the array
+  DevModel dm_static{};
+  DevModel *d_dm_static = nullptr;
+  uint8_t *static_base = nullptr;
   uint32_t lds_bytes = 0;
   uint32_t uf_attn_lds = 0;
   uint64_t weight_bytes = 0;
@@ -357,9 +389,15 @@ uint32_t argmax_of(const Schedule &s) {
 // after this starts at epoch 1 and no stale word can carry its tag.
 void zero_state(amk_model *m, hipStream_t st) { zero_async(m->scratch, m->plan.state_bytes, st); }
 
-// upload the host copy of the model's device descriptor
+// upload the host copy of the model's device descriptor (and of its static-scratch twin)
 void upload_dm(amk_model *m) {
   hip_check(hipMemcpy(m->d_dm, &m->dm, sizeof(DevModel), hipMemcpyHostToDevice), "hipMemcpy");
+  if (m->d_dm_static) {
+    m->dm_static = m->dm;
+    carve_scratch(m->dm_static, m->static_base, m->plan);
+    hip_check(hipMemcpy(m->d_dm_static, &m->dm_static, sizeof(DevModel), hipMemcpyHostToDevice),
+              "hipMemcpy");
+  }
 }
 
 // reset device error words, flags, tagged slots and the epoch after a device-side failure
@@ -641,7 +679,11 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     if (const char *env = std::getenv("AMK_WATCHDOG_MS")) wd_ms = std::atof(env);
     dm.timeout_ticks = (uint64_t)(wd_ms * clock_khz);
     m->d_dm = m->dalloc<DevModel>(1);
-    hip_check(hipMemcpyAsync(m->d_dm, &dm, sizeof dm, hipMemcpyHostToDevice, st), "hipMemcpyAsync");
+    // the static scratch array of this device: looked up here, once per device
+    m->static_base = static_scratch_base(m->device);
+    if (m->plan.total <= kStaticScratchBytes) m->d_dm_static = m->dalloc<DevModel>(1);
+    hip_check(hipStreamSynchronize(st), "hipStreamSynchronize");
+    upload_dm(m);
 
     const int qmax = qmax_for(dm.qpg);
     m->mk = pick_megakernel(cfg->wtype, hd, qmax, B > 1);
@@ -783,20 +825,28 @@ static void launch_unfused(amk_model *m, const DevModel &dm, const DevModel *g, 
 namespace {
 
 // n_steps greedy steps of `batch` sequences, sequence b at position pos[b] in the first step
-amk_status decode(amk_model *m, amk_kv *kv, const int32_t *d_tokens, const int32_t *pos,
-                  int32_t n_steps, int32_t batch, float *d_logits, int32_t *d_out, void *stream,
-                  const char *fn) {
-  const std::string f(fn);
-  if (!m || !kv || !d_tokens || !d_out || !pos) return set_error(AMK_E_INVALID, f + ": null argument");
-  if (kv->m != m) return set_error(AMK_E_INVALID, f + ": KV cache belongs to another model");
-  if (n_steps < 1) return set_error(AMK_E_INVALID, f + ": n_steps must be >= 1");
-  if (n_steps > 0x100000) return set_error(AMK_E_INVALID, f + ": n_steps too large");
+// Argument checks of a decode call (no allocation unless an error is reported).
+amk_status check_decode(const amk_model *m, const amk_kv *kv, const int32_t *d_tokens,
+                        const int32_t *pos, int32_t n_steps, int32_t batch, const int32_t *d_out,
+                        const char *fn) {
+  auto fail = [&](amk_status st, const char *why) { return set_error(st, std::string(fn) + why); };
+  if (!m || !kv || !d_tokens || !d_out || !pos) return fail(AMK_E_INVALID, ": null argument");
+  if (kv->m != m) return fail(AMK_E_INVALID, ": KV cache belongs to another model");
+  if (n_steps < 1) return fail(AMK_E_INVALID, ": n_steps must be >= 1");
+  if (n_steps > 0x100000) return fail(AMK_E_INVALID, ": n_steps too large");
   if (batch < 1 || batch > m->cfg.max_batch || batch > kv->batch)
-    return set_error(AMK_E_CAPACITY, f + ": batch exceeds max_batch or the KV cache");
+    return fail(AMK_E_CAPACITY, ": batch exceeds max_batch or the KV cache");
   for (int32_t b = 0; b < batch; ++b)
     if (pos[b] < 0 || (int64_t)pos[b] + n_steps > std::min(kv->max_seq, m->cfg.max_seq))
-      return set_error(AMK_E_CAPACITY, f + ": positions beyond max_seq");
-  hipStream_t st = static_cast<hipStream_t>(stream);
+      return fail(AMK_E_CAPACITY, ": positions beyond max_seq");
+  return AMK_OK;
+}
+
+// n_steps greedy steps of `batch` sequences, sequence b at position pos[b] in the first step, on
+// the scratch that descriptor dm (device copy g) points at. Launches only: no allocation.
+amk_status decode_on(amk_model *m, const DevModel &dm, const DevModel *g, amk_kv *kv,
+                     const int32_t *d_tokens, const int32_t *pos, int32_t n_steps, int32_t batch,
+                     float *d_logits, int32_t *d_out, hipStream_t st) {
   StepArgs s;
   s.tokens = d_tokens;
   s.logits = d_logits;
@@ -813,7 +863,6 @@ amk_status decode(amk_model *m, amk_kv *kv, const int32_t *d_tokens, const int32
   s.step = 0;
   s.n_steps = n_steps;
   if (m->path == AMK_PATH_MEGAKERNEL) {
-    const DevModel *g = m->d_dm;
     void *args[] = {(void *)&g, (void *)&s};
     hipError_t e = hipLaunchCooperativeKernel((const void *)m->mk, dim3(m->n_cu), dim3(kThreads),
                                               args, m->lds_bytes, st);
@@ -828,13 +877,22 @@ amk_status decode(amk_model *m, amk_kv *kv, const int32_t *d_tokens, const int32
       si.tokens = i ? d_out + (int64_t)(i - 1) * batch : d_tokens;
       si.next = d_out + (int64_t)i * batch;
       si.logits = d_logits ? d_logits + (int64_t)i * batch * m->cfg.vocab : nullptr;
-      launch_unfused(m, m->dm, m->d_dm, si, st);
+      launch_unfused(m, dm, g, si, st);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return set_error(AMK_E_HIP, std::string("unfused launch: ") + hipGetErrorString(e));
   }
   clear_error();
   return AMK_OK;
+}
+
+amk_status decode(amk_model *m, amk_kv *kv, const int32_t *d_tokens, const int32_t *pos,
+                  int32_t n_steps, int32_t batch, float *d_logits, int32_t *d_out, void *stream,
+                  const char *fn) {
+  const amk_status c = check_decode(m, kv, d_tokens, pos, n_steps, batch, d_out, fn);
+  if (c != AMK_OK) return c;
+  return decode_on(m, m->dm, m->d_dm, kv, d_tokens, pos, n_steps, batch, d_logits, d_out,
+                   static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -856,6 +914,30 @@ extern "C" amk_status amk_decode_steps_ragged(amk_model *m, amk_kv *kv, const in
   AMK_API_BEGIN
   return decode(m, kv, d_tokens, h_pos, n_steps, batch, d_logits, d_out, stream,
                 "amk_decode_steps_ragged");
+  AMK_API_END
+}
+
+// The variant of amk_decode_steps that allocates nothing: the same kernels on this device's
+// static scratch array instead of the model's scratch block. Every call first clears the array's
+// state region (a fill kernel, so the call may be captured into a graph), since the array keeps
+// whatever the last call on this GPU, of any model, left there.
+extern "C" amk_status amk_decode_steps_noalloc(amk_model *m, amk_kv *kv, const int32_t *d_tokens,
+                                               int32_t pos, int32_t n_steps, int32_t batch,
+                                               float *d_logits, int32_t *d_out, void *stream) {
+  AMK_API_BEGIN
+  if (batch > kMaxBatch) return set_error(AMK_E_CAPACITY, "amk_decode_steps_noalloc: batch exceeds max_batch");
+  int32_t pv[kMaxBatch];
+  for (int32_t b = 0; b < kMaxBatch; ++b) pv[b] = pos;
+  const amk_status c = check_decode(m, kv, d_tokens, pv, n_steps, batch, d_out, "amk_decode_steps_noalloc");
+  if (c != AMK_OK) return c;
+  if (!m->d_dm_static)
+    return set_error(AMK_E_CAPACITY, "amk_decode_steps_noalloc: the model's step scratch (" +
+                                         std::to_string(m->plan.total) + " bytes) exceeds the static array (" +
+                                         std::to_string(kStaticScratchBytes) + " bytes)");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (m->path == AMK_PATH_MEGAKERNEL) zero_async(m->static_base, m->plan.state_bytes, st);
+  return decode_on(m, m->dm_static, m->d_dm_static, kv, d_tokens, pv, n_steps, batch, d_logits,
+                   d_out, st);
   AMK_API_END
 }
 

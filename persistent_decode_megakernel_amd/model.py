@@ -182,6 +182,22 @@ class Model:
         _lib.check(st, "amk_decode_steps")
         return out
 
+    def steps_noalloc(self, kv: KVCache, tokens: torch.Tensor, pos: int, n_steps: int,
+                      logits: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """amk_decode_steps_noalloc: as steps() with one position, on the library's static
+        per-GPU scratch array (the call allocates no device memory; `out` must then be given by
+        callers that cannot allocate). Returns the device int32 [n_steps, B] tokens."""
+        B = tokens.numel()
+        if out is None:
+            out = torch.empty((n_steps, B), dtype=torch.int32, device=self.device)
+        st = self.lib.amk_decode_steps_noalloc(
+            self.handle, kv.handle, C.c_void_p(tokens.data_ptr()), pos, n_steps, B,
+            C.c_void_p(_ptr(logits)) if logits is not None else None, C.c_void_p(out.data_ptr()),
+            _stream_ptr())
+        _lib.check(st, "amk_decode_steps_noalloc")
+        return out
+
     def prefill(self, kv: KVCache, tokens: torch.Tensor, pos0: int = 0, seq: int = 0,
                 logits: Optional[torch.Tensor] = None, next_out: Optional[torch.Tensor] = None) -> torch.Tensor:
         """Process a prompt (device int32 [n]) of KV sequence `seq` at positions pos0 .. pos0 + n - 1
