@@ -29,10 +29,13 @@ def kv_bytes_step(cfg, ctx):
     return cfg.batch * cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim * 2 * ctx
 
 
-def time_path(cfg, weights, kv_host, path, steps, warmup, graph=False):
+def time_path(cfg, weights, kv_host, path, steps, warmup, graph=False, cold_mib=0):
     """Returns (ms per step from events around the whole timed region, per-launch durations ms,
     model info, final token ids). graph=True: each timed step is one hipGraph replay of the step's
-    launches (captured beforehand, one graph per position, since the position is a launch argument)."""
+    launches (captured beforehand, one graph per position, since the position is a launch argument).
+    cold_mib > 0: before every step a kernel writes a scratch buffer of that size, evicting the
+    model from the GPU's caches; each step is then timed by its own pair of events and the
+    returned ms per step is their mean (the writes are not counted)."""
     import torch
     from persistent_decode_megakernel_amd import synth
     from persistent_decode_megakernel_amd.model import Model
@@ -67,10 +70,15 @@ def time_path(cfg, weights, kv_host, path, steps, warmup, graph=False):
     model.sync()
     torch.cuda.synchronize()
     tok.copy_(first)
+    flush = torch.empty((cold_mib << 20) // 4, dtype=torch.float32, device="cuda") if cold_mib else None
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev_begin = [torch.cuda.Event(enable_timing=True) for _ in range(steps)] if cold_mib else None
     torch.cuda.synchronize()
     ev[0].record(stream)
     for i in range(steps):
+        if flush is not None:
+            flush.fill_(float(i))
+            ev_begin[i].record(stream)
         if graph:
             graphs[i].replay()
         else:
@@ -78,8 +86,13 @@ def time_path(cfg, weights, kv_host, path, steps, warmup, graph=False):
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     model.sync()
-    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    total = ev[0].elapsed_time(ev[steps])
+    if flush is not None:
+        per = [ev_begin[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        total = sum(per)
+        del flush
+    else:
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        total = ev[0].elapsed_time(ev[steps])
     ids = tok.cpu().tolist()
     del graphs
     kv.close()
@@ -128,7 +141,7 @@ def time_prompt_scenario(cfg, weights, n_in=64, n_out=12, reps=3):
     "Experimental Results"), from an empty cache. Hybrid: the prompt through amk_prefill (up to 16
     tokens per matrix-core pass), then the 12 greedy steps as one megakernel launch. Decode only:
     the 64 prompt tokens fed as 64 single megakernel steps, then the same 12 steps. Returns ms of
-    each (best of `reps`) and whether both produced the same 12 tokens."""
+    each (best of `reps`) and how far the two runs' tokens agree."""
     import numpy as np
     import torch
     from persistent_decode_megakernel_amd.model import Model
@@ -140,12 +153,13 @@ def time_prompt_scenario(cfg, weights, n_in=64, n_out=12, reps=3):
         np.random.default_rng(64).integers(0, cfg.vocab, n_in).astype(np.int32)).cuda()
     stream = torch.cuda.current_stream()
     best = {"hybrid": 1e30, "decode_only": 1e30}
-    outs = {}
+    outs, lgs = {}, {}
     for _ in range(reps):
         for mode in ("hybrid", "decode_only"):
             kv = model.kv(1, max_seq)
             torch.cuda.synchronize()
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            lg = torch.empty((n_out, 1, cfg.vocab), dtype=torch.float32, device="cuda")
             ev[0].record(stream)
             if mode == "hybrid":
                 nxt = model.prefill(kv, prompt, 0)
@@ -153,26 +167,40 @@ def time_prompt_scenario(cfg, weights, n_in=64, n_out=12, reps=3):
                 nxt = torch.empty(1, dtype=torch.int32, device="cuda")
                 for i in range(n_in):
                     model.step(kv, prompt[i:i + 1], i, next_out=nxt)
-            out = model.steps(kv, nxt, n_in, n_out)
+            out = model.steps(kv, nxt, n_in, n_out, logits=lg)
             ev[1].record(stream)
             torch.cuda.synchronize()
             model.sync()
             best[mode] = min(best[mode], ev[0].elapsed_time(ev[1]))
             outs[mode] = out.cpu().numpy().ravel().tolist()
+            lgs[mode] = lg.cpu().numpy()[:, 0].astype(np.float64)
             kv.close()
     model.close()
     torch.cuda.empty_cache()
-    return {"input_tokens": n_in, "output_tokens": n_out,
-            "hybrid_ms": round(best["hybrid"], 3), "decode_only_ms": round(best["decode_only"], 3),
-            "hybrid_speedup": round(best["decode_only"] / best["hybrid"], 3),
-            "same_output_tokens": outs["hybrid"] == outs["decode_only"]}
+    # The two runs agree on their tokens until the first step whose top-2 logit margin is within
+    # their rounding difference (the prompt's KV rows are computed by different kernels); the
+    # oracle parity of both paths at this width is a GPU test. Reported: where they part, and
+    # how close the two runs' logits are at the first output step, which both reach from the
+    # same prompt.
+    a, b = outs["hybrid"], outs["decode_only"]
+    first = next((i for i in range(n_out) if a[i] != b[i]), None)
+    res = {"input_tokens": n_in, "output_tokens": n_out,
+           "hybrid_ms": round(best["hybrid"], 3), "decode_only_ms": round(best["decode_only"], 3),
+           "hybrid_speedup": round(best["decode_only"] / best["hybrid"], 3),
+           "output_tokens_equal_until": n_out if first is None else first,
+           "step0_max_abs_logit_diff": round(float(np.max(np.abs(lgs["hybrid"][0] - lgs["decode_only"][0]))), 6)}
+    if first is not None:
+        top2 = np.sort(lgs["hybrid"][first])[-2:]
+        res["hybrid_top2_margin_at_first_difference"] = round(float(top2[1] - top2[0]), 6)
+    return res
 
 
-def profiled_traffic(cfg, kernel_name):
+def profiled_traffic(key, kernel_name):
     """Per-launch HBM bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from the committed
-    rocprofv3 summary of this workload, or None when the kernel sources changed since."""
+    rocprofv3 summary of this workload (profiles/megakernel_<key>.json, key = name_b<batch>), or
+    None when the kernel sources changed since."""
     from persistent_decode_megakernel_amd import profile_summary
-    path = os.path.join(ROOT, "profiles", f"megakernel_{cfg.name}_b{cfg.batch}.json")
+    path = os.path.join(ROOT, "profiles", f"megakernel_{key}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -182,42 +210,113 @@ def profiled_traffic(cfg, kernel_name):
     return float(rec["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(cfg, weights, kv_host, sample_steps):
-    """The oracle (float64 numpy, as it stands) on a bounded sample of the same workload: the first
-    `sample_steps` decode steps of the full model from the same prefilled cache and first token."""
+def cpu_baseline(cfg, weights, kv_host, sample_steps, threads=16):
+    """The oracle as it stands, in its float32 mode (weights converted to float32 once, before
+    the timed region), on a bounded sample of the same workload: the first `sample_steps` greedy
+    decode steps of the full model from the same prefilled cache and first token, with the BLAS
+    thread pool limited to `threads` (the host cores a GPU's share of the box provides)."""
     import numpy as np
     import oracle
     from persistent_decode_megakernel_amd import synth
 
     params, wn = synth.oracle_inputs(weights)
     pos = cfg.prefill
-    kv = synth.bf16_to_numpy_bits(kv_host[..., :pos + sample_steps, :]).copy()
+    kv = synth.bf16_to_numpy_bits(kv_host[..., :pos + sample_steps + 1, :]).copy()
     tok = synth.make_tokens(cfg, 0)[:, 0].numpy()
-    dec = oracle.Decoder(params, wn, cache_bytes=0)
+    dec = oracle.Decoder(params, wn, dtype=np.float32, cache_bytes=64 << 30)
+    host_cores = len(os.sched_getaffinity(0))
+    used = min(threads, host_cores)
+    limiter = None
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=used, user_api="blas")
+    except Exception:  # threadpoolctl absent: BLAS keeps its own thread count
+        used = int(os.environ.get("OMP_NUM_THREADS", host_cores))
+    t = time.perf_counter()
+    dec.step(kv.copy(), tok, pos)  # converts every weight matrix once (not timed)
+    t_conv = time.perf_counter() - t
     t = time.perf_counter()
     for i in range(sample_steps):
         logits = dec.step(kv, tok, pos + i)
         tok = oracle.argmax_lowest(logits)
     t_step = (time.perf_counter() - t) / sample_steps
-    cores = len(os.sched_getaffinity(0))
-    threads = cores
-    try:
-        from threadpoolctl import threadpool_info
-        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-        if info:
-            threads = int(info[0].get("num_threads", cores))
-    except Exception:
-        pass
+    if limiter is not None:
+        limiter.restore_original_limits()
     return {
         "value": round(cfg.batch / t_step, 4),
         "unit": "tokens/s",
-        "cores": threads,
+        "cores": used,
         "kind": "oracle",
         "sample": (f"{sample_steps} greedy decode steps of the full {cfg.name} model at positions "
-                   f"{pos}..{pos + sample_steps - 1} ({t_step:.1f} s per step), float64 numpy "
-                   f"matrix-vector products, weights converted per matrix per step; host has "
-                   f"{cores} cores"),
+                   f"{pos}..{pos + sample_steps - 1}, {t_step:.2f} s per step: the oracle's "
+                   f"float32 numpy matrix-vector products on {used} BLAS threads (host has "
+                   f"{host_cores} cores), weights converted to float32 once beforehand "
+                   f"({t_conv:.1f} s, not timed)"),
     }
+
+
+def kernel_name(cfg):
+    qpg = cfg.n_heads // cfg.n_kv_heads
+    hd_q = 1 if qpg <= 1 else (2 if qpg <= 2 else 4)
+    wt = {"bf16": 0, "int8": 1, "int4": 2}[cfg.wtype]
+    return f"amk_megakernel_w{wt}_h{cfg.head_dim}_q{hd_q}" + ("_b" if cfg.batch > 1 else "")
+
+
+def measure(cfg, weights, kv_host, steps, warmup, ablation=True, graph_ablation=False,
+            cold_mib=0, profile_key=None):
+    """Megakernel steps of one workload with its roofline: algorithmic bytes per launch (weights,
+    norm gains, scales, embedding rows and the KV rows each step reads) over the mean launch time
+    from events on the launch stream; and, optionally, the unfused ablation on the same inputs."""
+    ms, per, info, ids = time_path(cfg, weights, kv_host, "megakernel", steps, warmup,
+                                   cold_mib=cold_mib)
+    kname = kernel_name(cfg)
+    traffic_bytes = profiled_traffic(profile_key or f"{cfg.name}_b{cfg.batch}", kname)
+    weight_bytes = info.weight_bytes + 2 * cfg.hidden * cfg.batch  # + embedding rows
+    ctxs = [cfg.prefill + i + 1 for i in range(steps)]
+    avg_bytes = sum(weight_bytes + kv_bytes_step(cfg, c) for c in ctxs) / steps
+    avg_launch_ms = sum(per) / steps  # one launch per step
+    achieved = avg_bytes / (avg_launch_ms * 1e-3) / 1e9
+    res = {
+        "ms_per_step": round(ms, 4),
+        "tokens_per_s": round(cfg.batch / (ms * 1e-3), 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": (None if traffic_bytes is None
+                        else round(traffic_bytes / (avg_launch_ms * 1e-3) / 1e9, 1)),
+        },
+        "kernel": kname,
+        "algorithmic_bytes_per_step": int(avg_bytes),
+        "traffic_bytes_per_launch": None if traffic_bytes is None else int(traffic_bytes),
+        "launches_per_step": info.launches_per_step,
+        "step_ms_p10_p50_p90": [round(sorted(per)[int(q * (steps - 1))], 4) for q in (0.1, 0.5, 0.9)],
+        "positions": f"{cfg.prefill}..{cfg.prefill + steps - 1}",
+        "batch": cfg.batch,
+        "_ids": ids,
+    }
+    if ablation:
+        variants = (("ablation_unfused", False),) + ((("ablation_unfused_hipgraph", True),)
+                                                     if graph_ablation else ())
+        for key, graph in variants:
+            ms_u, per_u, info_u, ids_u = time_path(cfg, weights, kv_host, "unfused", steps, warmup,
+                                                   graph=graph, cold_mib=cold_mib)
+            res[key] = {
+                "ms_per_step": round(ms_u, 4),
+                "tokens_per_s": round(cfg.batch / (ms_u * 1e-3), 2),
+                "launches_per_step": info_u.launches_per_step,
+                "hbm_gbs": round(avg_bytes / (ms_u * 1e-3) / 1e9, 1),
+                "same_final_ids": ids_u == ids,
+                "megakernel_speedup": round(ms_u / ms, 3),
+            }
+    return res
+
+
+# the other workloads measured in the same run (BASELINE configs and the batch-8 matrix-core step)
+EXTRA = [("smollm2_135m", {}), ("smollm2_135m_cold", {"cold_mib": 1024}), ("tinyllama_1b", {}),
+         ("llama2_7b_w8a16", {}), ("llama2_7b_b8", {})]
 
 
 def main():
@@ -230,9 +329,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-multistep", action="store_true")
     ap.add_argument("--no-scenario", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="measure only --workload, not the other configurations")
     ap.add_argument("--batch", type=int, default=0,
                     help="override the workload's batch (sequences per step, 1..16)")
-    ap.add_argument("--cpu-sample-steps", type=int, default=2)
+    ap.add_argument("--cpu-sample-steps", type=int, default=8)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (a kernel of "
                          "known traffic for scaling hardware byte counters)")
@@ -267,27 +368,17 @@ def main():
     kv_host = synth.make_kv(cfg, max_seq, 0, threads=16)
     log(f"[bench] synthetic {cfg.name} generated in {time.time() - t0:.1f}s")
 
-    ms, per, info, ids = time_path(cfg, weights, kv_host, "megakernel", steps, warmup)
-    hd_q = 1 if cfg.n_heads // cfg.n_kv_heads <= 1 else (2 if cfg.n_heads // cfg.n_kv_heads <= 2 else 4)
-    wt = {"bf16": 0, "int8": 1, "int4": 2}[cfg.wtype]
-    kname = (f"amk_megakernel_w{wt}_h{cfg.head_dim}_q{hd_q}"
-             + ("_b" if cfg.batch > 1 else ""))
-    traffic_bytes = profiled_traffic(cfg, kname)
-    weight_bytes = info.weight_bytes + 2 * cfg.hidden * cfg.batch  # + embedding rows
-    ctxs = [cfg.prefill + i + 1 for i in range(steps)]
-    step_bytes = [weight_bytes + kv_bytes_step(cfg, c) for c in ctxs]
-    avg_bytes = sum(step_bytes) / steps
-    avg_launch_ms = sum(per) / steps  # one launch per step
-    achieved = avg_bytes / (avg_launch_ms * 1e-3) / 1e9
-    value = cfg.batch * steps / (ms * steps * 1e-3)
+    head = measure(cfg, weights, kv_host, steps, warmup, ablation=not args.no_ablation,
+                   graph_ablation=True)
+    ids = head.pop("_ids")
     out = {
         "metric": "decode tokens/s at batch 1 + achieved HBM GB/s as % of 8 TB/s peak",
-        "value": round(value, 2),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -299,53 +390,61 @@ def main():
                         f"FFN {cfg.ffn}, vocab {cfg.vocab}, random-init {cfg.wtype} weights",
             "batch": cfg.batch,
             "kv_prefill": cfg.prefill,
-            "positions": f"{cfg.prefill}..{cfg.prefill + steps - 1}",
+            "positions": head["positions"],
             "path": "megakernel (1 persistent launch per step)",
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": (None if traffic_bytes is None
-                        else round(traffic_bytes / (avg_launch_ms * 1e-3) / 1e9, 1)),
-        },
-        "traffic_bytes_per_launch": None if traffic_bytes is None else int(traffic_bytes),
-        "kernel": kname,
-        "algorithmic_bytes_per_step": int(avg_bytes),
-        "launches_per_step": info.launches_per_step,
-        "step_ms_p10_p50_p90": [round(sorted(per)[int(q * (steps - 1))], 4) for q in (0.1, 0.5, 0.9)],
+        "roofline": head["roofline"],
     }
+    for k in ("traffic_bytes_per_launch", "kernel", "algorithmic_bytes_per_step",
+              "launches_per_step", "step_ms_p10_p50_p90", "ablation_unfused",
+              "ablation_unfused_hipgraph"):
+        if k in head:
+            out[k] = head[k]
     if not args.no_multistep:
         ms_m, ids_m = time_multistep(cfg, weights, kv_host, steps, warmup)
         out["multistep_one_launch"] = {
             "steps_per_launch": steps,
             "ms_per_step": round(ms_m, 4),
             "tokens_per_s": round(cfg.batch / (ms_m * 1e-3), 2),
-            "hbm_gbs": round(avg_bytes / (ms_m * 1e-3) / 1e9, 1),
+            "hbm_gbs": round(head["algorithmic_bytes_per_step"] / (ms_m * 1e-3) / 1e9, 1),
             "same_final_ids": ids_m == ids,
         }
         log(f"[bench] multistep: {ms_m:.4f} ms/step in one launch of {steps}")
     if not args.no_scenario and cfg.batch == 1:
         out["scenario_in64_out12"] = time_prompt_scenario(cfg, weights)
         log(f"[bench] in64/out12: {out['scenario_in64_out12']}")
-    if not args.no_ablation:
-        for key, graph in (("ablation_unfused", False), ("ablation_unfused_hipgraph", True)):
-            ms_u, per_u, info_u, ids_u = time_path(cfg, weights, kv_host, "unfused", steps, warmup,
-                                                   graph=graph)
-            out[key] = {
-                "ms_per_step": round(ms_u, 4),
-                "tokens_per_s": round(cfg.batch / (ms_u * 1e-3), 2),
-                "launches_per_step": info_u.launches_per_step,
-                "hbm_gbs": round(avg_bytes / (ms_u * 1e-3) / 1e9, 1),
-                "same_final_ids": ids_u == ids,
-                "megakernel_speedup": round(ms_u / ms, 3),
-            }
     if not args.no_cpu_baseline:
         t = time.time()
         out["cpu_baseline"] = cpu_baseline(cfg, weights, kv_host, args.cpu_sample_steps)
         log(f"[bench] cpu baseline took {time.time() - t:.1f}s")
+    if not args.no_extra and not args.batch and args.workload == "llama2_7b":
+        out["workloads"] = {}
+        cache = {}
+        for key, opt in EXTRA:
+            name = key.replace("_cold", "")
+            wcfg = synth.get_config(name)
+            t = time.time()
+            w_key = (wcfg.cfg_id, wcfg.wtype)
+            if w_key == (cfg.cfg_id, cfg.wtype):
+                wts = weights  # the batch-8 workload shares the headline model's weights
+            else:
+                if w_key not in cache:
+                    cache.clear()
+                    cache[w_key] = synth.make_weights(wcfg, 0, threads=16)
+                wts = cache[w_key]
+            kvh = synth.make_kv(wcfg, wcfg.prefill + max(steps, warmup) + 1, 0, threads=16)
+            res = measure(wcfg, wts, kvh, steps, warmup, profile_key=key + f"_b{wcfg.batch}",
+                          **opt)
+            res.pop("_ids")
+            res["workload"] = (f"{wcfg.name}: {wcfg.n_layers} layers, hidden {wcfg.hidden}, "
+                               f"{wcfg.n_heads}/{wcfg.n_kv_heads} heads, head_dim {wcfg.head_dim}, "
+                               f"FFN {wcfg.ffn}, vocab {wcfg.vocab}{', tied' if wcfg.tied else ''}, "
+                               f"{wcfg.wtype}, KV prefill {wcfg.prefill}"
+                               + (f", {opt['cold_mib']} MiB written between steps" if opt.get("cold_mib") else ""))
+            out["workloads"][key] = res
+            del kvh
+            log(f"[bench] {key}: {res['ms_per_step']} ms/step, frac {res['roofline']['frac']} "
+                f"({time.time() - t:.1f}s)")
     print(json.dumps(out), flush=True)
 
 
