@@ -39,9 +39,11 @@ class Report:
 #  * KV_TAU * max|row|: the two values differ before rounding by the device's fp32 accumulation
 #    error, which scales with the magnitude of the head's row (for elements near zero an ulp bound
 #    alone would demand an fp32 error below the element's own bf16 ulp).
-# KV_TAU was set from measurement: the largest excess beyond 2 ulps seen in every parity test
-# (logged as KVSTAT lines), times four, rounded up to a power of two.
-KV_TAU = 2.0 ** -10
+# KV_TAU was set from measurement: over every parity test (KVSTAT lines) the largest excess
+# beyond 2 ulps was 9.2e-4 of the row's max (prompt processing at 7B width, whose matrix-core
+# inputs keep 16 mantissa bits; batch-1 fp32 paths stay below 7.6e-4); the bound is about twice
+# that, rounded up to a power of two.
+KV_TAU = 2.0 ** -9
 
 
 def kv_row_error(gpu_bits: np.ndarray, ref_bits: np.ndarray, label: str = "") -> float:
