@@ -2082,9 +2082,10 @@ __device__ bool attn_stage_tagged(const DevModel &m, const StepArgs &s, int l, i
   }
 }
 
-// TAGGED (batch-1 megakernel): q and the appended row come from attn_stage_tagged, the partial is
-// stored as tagged words. Otherwise the QKV tiles' flags are waited on when wait_for is set
-// (batched megakernel) and q and the appended row are read from q and the KV cache.
+// One sequence's attention partial. TAGGED (batch-1 megakernel): q and the appended row come from
+// attn_stage_tagged, the partial is stored as tagged words. Otherwise the flags named by wait_for
+// are waited on and q and the appended row are read from q and the KV cache (batched steps and
+// the operator kernels use attn_block_seqs instead).
 template <int HD, int QMAX, bool TAGGED>
 __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, int blk,
                            int h0, int qn, float *lds, float *red, const Task *wait_for,
@@ -2305,6 +2306,283 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
   return true;
 }
 
+// Attention partials of a batched step (batch-2..16 megakernel instances and the operator
+// kernels): heads [h0, h0 + qn) of KV group g, KV block blk, for every sequence of the step.
+// Each wave streams its own rows, like a GEMV tile: sequence b's block is cut into chunks of
+// kWaves * U * RPW rows, wave w takes U * RPW consecutive rows of each chunk, and the wave walks
+// its chunks of all sequences in order with two register buffers, the next chunk's loads issued
+// before the current one is folded. The softmax is online per row slot of the wave (running
+// max, sum and weighted V), so nothing but the end of a sequence synchronises the waves: there
+// each wave folds its row slots together, writes (acc, m, l) to LDS, and after one barrier all
+// threads merge the waves' partials into the sequence's partial. q and the appended K/V row of
+// every sequence (written by this step's QKV tiles) are read once after the wait, into LDS; the
+// first chunk is issued before it. Partials stay in LDS until every sequence is done and then
+// go out in one burst (a store in the loop would hold up the next chunk's wait: vector loads and
+// stores complete under one counter). wait_for (batched megakernel): the QKV tiles' flags,
+// polled by wave 0. LDS: q [B][qn][HD] | appended rows [B][2][HD] bf16 | partials
+// [B][qn][HD + 2] | wave partials [2][NW][qn][HD + 2].
+template <int HD, int QMAX>
+__device__ __forceinline__ bool attn_block_seqs(const DevModel &m, const StepArgs &s, int l,
+                                                int g, int blk, int h0, int qn, float *lds,
+                                                float *red, const Task *wait_for,
+                                                int *abort_slot) {
+  (void)red;
+  constexpr int NW = kWaves;
+  constexpr int LPR = HD / 8;       // lanes per row (8 bf16 each)
+  constexpr int RPW = 64 / LPR;     // row slots of a wave
+  constexpr int U = kAttnSeqIters;  // loads of K (and of V) per chunk
+  constexpr int CR = U * RPW;       // rows of a wave's chunk
+  constexpr int WR = NW * CR;       // rows of a workgroup chunk
+  static_assert(WR == attn_seq_chunk_rows(HD), "chunk rows");
+  const int B = s.batch, nblk = m.nblk, nq = m.nq;
+  if (B <= 0) return true;
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());
+  const int sub = lane % LPR, rs = lane / LPR;
+  float *qall = lds;                                                   // [B][qn][HD]
+  uint16_t *rows = reinterpret_cast<uint16_t *>(qall + B * qn * HD);   // [B][2][HD]
+  float *parts = qall + B * qn * HD + B * HD;                          // [B][qn][HD + 2]
+  float *wpart = parts + B * qn * (HD + 2);                            // [2][NW][qn][HD + 2]
+
+  // a position in the stream of (sequence, chunk) pairs; sequences without rows in this block
+  // are skipped. Every field is wave-uniform.
+  struct Cur {
+    int b, c, lo, hi, nch, pos;
+  };
+  auto seq_at = [&](int b, Cur &cu) __attribute__((always_inline)) {
+    cu.b = b;
+    cu.c = 0;
+    cu.pos = pos_of(s, b);
+    attn_block_range(cu.pos + 1, nblk, blk, &cu.lo, &cu.hi);
+    cu.nch = cu.hi > cu.lo ? (cu.hi - cu.lo + WR - 1) / WR : 0;
+  };
+  auto from = [&](int b, Cur &cu) __attribute__((always_inline)) {
+    cu.nch = 0;
+    for (; b < B && cu.nch == 0; ++b) seq_at(b, cu);
+  };
+  auto advance = [&](Cur &cu) __attribute__((always_inline)) {
+    if (++cu.c == cu.nch) from(cu.b + 1, cu);
+  };
+  int S = 0;
+  for (int b = 0; b < B; ++b) {
+    int lo, hi;
+    attn_block_range(pos_of(s, b) + 1, nblk, blk, &lo, &hi);
+    if (hi > lo) S += (hi - lo + WR - 1) / WR;
+  }
+
+  // the wave's rows of a chunk. Loads are unconditional: rows past the block re-read its last
+  // row (skipped when folded); a per-lane branch or select here would make the compiler wait
+  // for every outstanding load at the first use, i.e. for the next chunk too.
+  auto load = [&](const Cur &cu, uint4 (&kr)[U], uint4 (&vr)[U]) __attribute__((always_inline)) {
+    const uint16_t *Kb = s.kv + kv_index(m, s, l, 0, cu.b, g, 0, 0);
+    const uint16_t *Vb = s.kv + kv_index(m, s, l, 1, cu.b, g, 0, 0);
+    const int j0 = cu.lo + cu.c * WR + wave * CR + rs;
+#pragma unroll
+    for (int it = 0; it < U; ++it) {
+      const int j = min(j0 + it * RPW, cu.hi - 1);
+      kr[it] = load_nt(reinterpret_cast<const uint4 *>(Kb + (int64_t)j * HD + sub * 8));
+      vr[it] = load_nt(reinterpret_cast<const uint4 *>(Vb + (int64_t)j * HD + sub * 8));
+    }
+  };
+
+  float acc[QMAX][8], lsum[QMAX], mrun[QMAX];
+  auto reset = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < QMAX; ++h) {
+      lsum[h] = 0.f;
+      mrun[h] = kEmptyBlockM;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    }
+  };
+  int ended = 0;  // sequences finished so far: picks the wave-partial buffer
+  // fold one chunk into the row slot's (acc, lsum, mrun); at the sequence's last chunk, merge
+  auto fold = [&](const Cur &cu, const uint4 (&kr)[U], const uint4 (&vr)[U]) __attribute__((always_inline)) {
+    const int b = cu.b, pos = cu.pos;
+    const float *qs = qall + b * qn * HD + sub * 8;
+    const uint16_t *row = rows + b * 2 * HD;
+    // the appended row as register values: the empty asm keeps the compiler from turning the
+    // choice below into a choice of addresses, which would move kr / vr to the stack
+    uint4 rk = *reinterpret_cast<const uint4 *>(row + sub * 8);
+    uint4 rv = *reinterpret_cast<const uint4 *>(row + HD + sub * 8);
+    asm("" : "+v"(rk.x), "+v"(rk.y), "+v"(rk.z), "+v"(rk.w), "+v"(rv.x), "+v"(rv.y), "+v"(rv.z), "+v"(rv.w));
+    const int j0 = cu.lo + cu.c * WR + wave * CR + rs;
+    float sc[U][QMAX];
+#pragma unroll
+    for (int it = 0; it < U; ++it) {
+      const int j = j0 + it * RPW;
+      const uint4 k = (j == pos) ? rk : kr[it];
+#pragma unroll
+      for (int h = 0; h < QMAX; ++h) {
+        float p = 0.f;
+        if (h < qn) {
+          p = dot8_bf16(k, qs + h * HD);
+#pragma unroll
+          for (int o = LPR / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o, 64);
+        }
+        sc[it][h] = p;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < QMAX; ++h) {
+      if (h < qn) {
+        float mc = mrun[h];
+#pragma unroll
+        for (int it = 0; it < U; ++it)
+          if (j0 + it * RPW < cu.hi) mc = fmaxf(mc, sc[it][h]);
+        const float f = __expf(mrun[h] - mc);
+        mrun[h] = mc;
+        lsum[h] *= f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= f;
+#pragma unroll
+        for (int it = 0; it < U; ++it) sc[it][h] = (j0 + it * RPW < cu.hi) ? __expf(sc[it][h] - mc) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < U; ++it) {
+      const int j = j0 + it * RPW;
+      const uint4 v = (j == pos) ? rv : vr[it];
+      const float vv[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
+                           bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
+#pragma unroll
+      for (int h = 0; h < QMAX; ++h) {
+        if (h < qn) {
+          lsum[h] += sc[it][h];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(sc[it][h], vv[e], acc[h][e]);
+        }
+      }
+    }
+    if (cu.c != cu.nch - 1) return;
+    // end of sequence b: fold the wave's row slots (lanes with equal sub), then the waves
+    float *wp = wpart + (ended & 1) * NW * qn * (HD + 2) + wave * qn * (HD + 2);
+#pragma unroll
+    for (int h = 0; h < QMAX; ++h) {
+      if (h < qn) {
+        float mx = mrun[h];
+#pragma unroll
+        for (int o = LPR; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        const float f = __expf(mrun[h] - mx);
+        float t = lsum[h] * f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= f;
+#pragma unroll
+        for (int o = LPR; o < 64; o <<= 1) {
+          t += __shfl_xor(t, o, 64);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, 64);
+        }
+        if (rs == 0) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) wp[h * (HD + 2) + sub * 8 + e] = acc[h][e];
+        }
+        if (lane == 0) {
+          wp[h * (HD + 2) + HD] = mx;
+          wp[h * (HD + 2) + HD + 1] = t;
+        }
+      }
+    }
+    reset();
+    __syncthreads();
+    const float *w0 = wpart + (ended & 1) * NW * qn * (HD + 2);
+    float *pl = parts + b * qn * (HD + 2);
+    for (int i = threadIdx.x; i < qn * (HD + 2); i += NW * 64) {
+      const int h = i / (HD + 2), e = i - h * (HD + 2);
+      float mx = kEmptyBlockM;
+      for (int w = 0; w < NW; ++w) mx = fmaxf(mx, w0[w * qn * (HD + 2) + h * (HD + 2) + HD]);
+      float t = 0.f;
+      if (e == HD) {
+        t = mx;
+      } else {
+        for (int w = 0; w < NW; ++w)
+          t += __expf(w0[w * qn * (HD + 2) + h * (HD + 2) + HD] - mx) * w0[w * qn * (HD + 2) + i];
+      }
+      pl[i] = t;
+    }
+    ++ended;
+  };
+
+  reset();
+  Cur lc, cc;
+  from(0, lc);
+  cc = lc;
+  uint4 P[2][U], A[2][U], Bf[2][U];
+  // wave 0 polls the flags and a wave's loads return in order, so it issues its first chunk
+  // after polling; the other waves issue theirs before the join
+  if (wait_for) wait_poll(m, *wait_for, s.epoch, abort_slot);
+  if (S > 0) load(lc, P[0], P[1]);
+  asm volatile("" ::: "memory");  // issue them before the join, not at their first use
+  if (wait_for && !wait_join(m, *wait_for, abort_slot)) return false;
+  // q (scaled by 1/sqrt(hd)) and the appended K/V rows of every sequence: one round of
+  // device-coherent 4-byte loads (this step's QKV tiles wrote them)
+  for (int i = threadIdx.x; i < B * qn * HD; i += NW * 64) {
+    const int b = i / (qn * HD), r = i - b * (qn * HD);
+    qall[i] = cldf(&m.q[((int64_t)l * m.max_batch + b) * m.qd + ((int64_t)g * m.qpg + h0) * HD + r]) *
+              m.attn_scale;
+  }
+  for (int i = threadIdx.x; i < B * HD; i += NW * 64) {  // 32-bit words: [B][2][HD / 2]
+    const int b = i / HD, r = i - b * HD, kvi = r / (HD / 2), w = r - kvi * (HD / 2);
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(
+        s.kv + kv_index(m, s, l, kvi, b, g, pos_of(s, b), 0));
+    reinterpret_cast<uint32_t *>(rows)[i] = cld(&src[w]);
+  }
+  // every thread's loads so far (chunk 0 too), also where a thread staged nothing: the wait
+  // counts of the stream below then start from no pending loads on every path
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  // the stream: P (chunk 0, complete by now) is folded before the steady loop, which starts and
+  // loops back with exactly one buffer of loads in flight, so the compiler's wait for a buffer
+  // leaves the other buffer's loads outstanding. The empty asm statements keep each chunk's
+  // loads issued ahead of the previous chunk's arithmetic.
+  if (S > 0) {
+    if (S > 1) {
+      advance(lc);
+      load(lc, A[0], A[1]);
+    }
+    asm volatile("" ::: "memory");
+    fold(cc, P[0], P[1]);
+    if (S > 1) {
+      advance(cc);
+      int t = 1;
+      for (; t + 2 < S; t += 2) {
+        advance(lc);
+        load(lc, Bf[0], Bf[1]);
+        asm volatile("" ::: "memory");
+        fold(cc, A[0], A[1]);
+        advance(cc);
+        advance(lc);
+        load(lc, A[0], A[1]);
+        asm volatile("" ::: "memory");
+        fold(cc, Bf[0], Bf[1]);
+        advance(cc);
+      }
+      if (t + 1 < S) {
+        advance(lc);
+        load(lc, Bf[0], Bf[1]);
+        asm volatile("" ::: "memory");
+        fold(cc, A[0], A[1]);
+        advance(cc);
+        fold(cc, Bf[0], Bf[1]);
+      } else {
+        fold(cc, A[0], A[1]);
+      }
+    }
+  }
+  __syncthreads();
+  // every sequence's partial of this block, [b][h][HD + 2]: device-coherent stores; a sequence
+  // without rows here gives the empty partial
+  const int per = qn * (HD + 2);
+  for (int i = threadIdx.x; i < B * per; i += NW * 64) {
+    const int b = i / per, r = i - b * per, h = r / (HD + 2), e = r - h * (HD + 2);
+    int lo, hi;
+    attn_block_range(pos_of(s, b) + 1, nblk, blk, &lo, &hi);
+    const float v = hi > lo ? parts[i] : (e == HD ? kEmptyBlockM : 0.f);
+    float *pout = m.part + ((((int64_t)l * m.max_batch + b) * nq + (int64_t)g * m.qpg + h0 + h) * nblk + blk) * (HD + 2);
+    cstf(&pout[e], v);
+  }
+  return true;
+}
+
 // Attention tasks always run with kWaves waves (kThreads threads). A group of more query heads than
 // QMAX is processed QMAX heads at a time (the KV block is re-read from cache for each pass).
 // wait_for (megakernel) is waited on inside the first pass, after the KV-history prefetch.
@@ -2319,11 +2597,18 @@ __device__ __forceinline__ bool attn_task(const DevModel &m, const StepArgs &s, 
     first = *wait_for;
     first.w1_lo = first.w1_hi = 0;
   }
-  for (int h0 = 0; h0 < m.qpg; h0 += QMAX)
-    if (!attn_block<HD, QMAX, TAGGED>(m, s, l, g, blk, h0, min(QMAX, m.qpg - h0), lds, red,
-                                      (wait_for && (TAGGED || h0 == 0)) ? &first : nullptr,
+  for (int h0 = 0; h0 < m.qpg; h0 += QMAX) {
+    const Task *w = (wait_for && (TAGGED || h0 == 0)) ? &first : nullptr;
+    if constexpr (TAGGED) {
+      if (!attn_block<HD, QMAX, true>(m, s, l, g, blk, h0, min(QMAX, m.qpg - h0), lds, red, w,
                                       abort_slot))
-      return false;
+        return false;
+    } else {
+      if (!attn_block_seqs<HD, QMAX>(m, s, l, g, blk, h0, min(QMAX, m.qpg - h0), lds, red, w,
+                                     abort_slot))
+        return false;
+    }
+  }
   return true;
 }
 

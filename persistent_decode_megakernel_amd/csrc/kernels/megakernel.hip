@@ -240,7 +240,7 @@ template <int WT, int HD, int QMAX, bool BATCHED>
 __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArgs &s0) {
   extern __shared__ __attribute__((aligned(16))) float lds[];  // 16-byte reads of xs need it
   const int32_t xa = lds_xs_floats(m.max_batch, m.d, m.qd, m.F);
-  const int32_t xb = lds_attn_floats(m.qpg, m.hd);
+  const int32_t xb = lds_attn_floats(m.max_batch, m.qpg, m.hd);
   float *xs = lds;
   float *red = lds + (xa > xb ? xa : xb);  // kRedFloats floats
   uint4 *pf = reinterpret_cast<uint4 *>(red + kRedFloats);  // lds_prefetch_floats(max_batch)

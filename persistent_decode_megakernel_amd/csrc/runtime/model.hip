@@ -157,7 +157,7 @@ UgFn pick_uf_gemv(int wt, int mode) {
   return t[wt][mode];
 }
 
-int qmax_for(int qpg) { return qpg <= 1 ? 1 : (qpg <= 2 ? 2 : kAttnMaxHeads); }
+int qmax_for(int qpg) { return attn_qmax(qpg); }
 
 // The per-step scratch of a model as one block of device memory. It opens with the state region,
 // which must hold zeros before a model's first step (and again after a reset or a schedule
@@ -689,7 +689,8 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     m->mk = pick_megakernel(cfg->wtype, hd, qmax, B > 1);
     m->uf_attn = pick_uf_attn(hd, qmax);
     if (!m->mk || !m->uf_attn) throw std::runtime_error("no kernel instance for this shape");
-    m->uf_attn_lds = 4u * (64 * 8 + (uint32_t)lds_attn_floats(qmax, hd));
+    // the operator kernels may run prompt chunks of kMaxBatch columns
+    m->uf_attn_lds = 4u * (64 * 8 + (uint32_t)lds_attn_floats(kMaxBatch, qmax, hd));
     if (path == AMK_PATH_MEGAKERNEL) {
       hip_check(hipFuncSetAttribute((const void *)m->mk, hipFuncAttributeMaxDynamicSharedMemorySize,
                                     (int)m->lds_bytes), "hipFuncSetAttribute");

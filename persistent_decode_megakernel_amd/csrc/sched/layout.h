@@ -155,6 +155,14 @@ constexpr int32_t kAttnMaxHeads = 4;  // query heads per attention pass (larger 
 AMK_HD constexpr int32_t attn_chunk_rows(int32_t hd, int32_t qmax) {
   return (hd <= 64 || qmax == 1) ? kAttnRowsPerChunk : 256;
 }
+// Query heads per attention pass of a KV group of qpg heads.
+AMK_HD constexpr int32_t attn_qmax(int32_t qpg) { return qpg <= 1 ? 1 : (qpg <= 2 ? 2 : kAttnMaxHeads); }
+// KV rows one loop iteration of the attention body covers: hd / 8 lanes per row, 8 waves.
+AMK_HD constexpr int32_t attn_rows_per_iter(int32_t hd) { return 8 * (64 / (hd / 8)); }
+// Batched steps stream each wave's own KV rows in chunks of kAttnSeqIters loads of K (and of V)
+// per lane, two chunks in flight per wave; a workgroup chunk is this many rows.
+constexpr int32_t kAttnSeqIters = 4;
+AMK_HD constexpr int32_t attn_seq_chunk_rows(int32_t hd) { return attn_rows_per_iter(hd) * kAttnSeqIters; }
 constexpr int32_t kRedFloats = 2048;        // reduction scratch; holds n_heads x blocks weights
 // Batch-1 int8 GEMV: the staged input is converted in place to integer digits, holding every
 // thread's share in registers; that bounds the input length of an int8 matrix.
@@ -174,11 +182,14 @@ AMK_HD int32_t lds_xs_floats(int32_t batch, int32_t hidden, int32_t qdim, int32_
   k = k > ffn ? k : ffn;
   return batch == 1 ? k : kRingFloats;
 }
-AMK_HD int32_t lds_attn_floats(int32_t qpg, int32_t hd) {
-  // one sequence and at most kAttnMaxHeads heads per pass:
-  // q [qn][hd] + scores [qn][chunk] + partial acc [waves][qn*hd] + appended K/V row [2][hd] bf16
+AMK_HD int32_t lds_attn_floats(int32_t batch, int32_t qpg, int32_t hd) {
+  // at most kAttnMaxHeads heads per pass. Batch 1: q [qn][hd] + scores [qn][chunk] + partial acc
+  // [waves][qn*hd] + appended K/V row [2][hd] bf16. Batched: q and the appended rows of every
+  // sequence, [batch][qn*hd] + [batch][2][hd] bf16, every sequence's partial until they are
+  // stored, [batch][qn][hd + 2], and the waves' partials of two sequences, [2][waves][qn][hd + 2].
   const int32_t qn = qpg < kAttnMaxHeads ? qpg : kAttnMaxHeads;
-  return qn * hd + qn * kAttnRowsPerChunk + kWaves * qn * hd + hd;
+  const int32_t one = qn * hd + qn * kAttnRowsPerChunk + kWaves * qn * hd + hd;
+  return batch == 1 ? one : batch * (qn * hd + hd + qn * (hd + 2)) + 2 * kWaves * qn * (hd + 2);
 }
 // Batch-1 GEMV tiles stage the first weight chunk of every wave in LDS (8 KB per wave).
 constexpr int32_t kPrefetchFloats = kWaves * 2048;
@@ -187,7 +198,7 @@ AMK_HD int32_t lds_prefetch_floats(int32_t batch) { return batch == 1 ? kPrefetc
 AMK_HD int32_t lds_bytes_for(int32_t batch, int32_t hidden, int32_t qdim, int32_t ffn,
                              int32_t qpg, int32_t hd, int32_t max_tile_rows) {
   int32_t a = lds_xs_floats(batch, hidden, qdim, ffn);
-  int32_t b = lds_attn_floats(qpg, hd);
+  int32_t b = lds_attn_floats(batch, qpg, hd);
   int32_t region = a > b ? a : b;
   return 4 * (region + kRedFloats + lds_prefetch_floats(batch) + batch * max_tile_rows);
 }

@@ -19,6 +19,11 @@ LOGIT_TOL = 3e-2
 MARGIN = 0.05
 
 
+def worst_of(a: float, b: float) -> float:
+    """The larger of two errors; NaN wins (Python's max would drop a NaN second argument)."""
+    return b if (b != b or b > a) else a
+
+
 def log(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()
@@ -97,7 +102,7 @@ def teacher_forced(cfg: synth.Config, path: str = "megakernel", seed: int = 0,
         model.sync()
         lg = d_logits.cpu().numpy().astype(np.float64)
         err = float(np.max(np.abs(lg - lo)))
-        rep.max_abs = max(rep.max_abs, err)
+        rep.max_abs = worst_of(rep.max_abs, err)
         ids_o = oracle.argmax_lowest(lo)
         marg = oracle.top2_margin(lo)
         ids_g = nxt.cpu().numpy()

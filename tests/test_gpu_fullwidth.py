@@ -16,7 +16,7 @@ import oracle
 from persistent_decode_megakernel_amd import synth
 from persistent_decode_megakernel_amd.model import Model
 
-from gpu_helpers import LOGIT_TOL, MARGIN, assert_parity, kv_row_error, log, teacher_forced
+from gpu_helpers import LOGIT_TOL, MARGIN, assert_parity, kv_row_error, log, teacher_forced, worst_of
 
 pytestmark = pytest.mark.gpu
 
@@ -68,7 +68,7 @@ def test_full_width_prompt_then_decode(name):
     g_toks, g_lo = toks.cpu().numpy(), dec_logits.cpu().numpy().astype(np.float64)
     for i in range(n_out):
         lo = dec.step(kv_np, np.array([tok]), n_in + i)[0]
-        worst = max(worst, float(np.max(np.abs(g_lo[i, 0] - lo))))
+        worst = worst_of(worst, float(np.max(np.abs(g_lo[i, 0] - lo))))
         if oracle.top2_margin(lo[None])[0] > MARGIN:
             checked += 1
             assert g_toks[i, 0] == oracle.argmax_lowest(lo[None])[0], i

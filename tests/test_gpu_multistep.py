@@ -9,7 +9,7 @@ import oracle
 from persistent_decode_megakernel_amd import _lib, synth
 from persistent_decode_megakernel_amd.model import Model
 
-from gpu_helpers import LOGIT_TOL, MARGIN, log
+from gpu_helpers import LOGIT_TOL, MARGIN, log, worst_of
 
 pytestmark = pytest.mark.gpu
 
@@ -83,7 +83,7 @@ def test_multistep_equals_single_steps_and_oracle(name, path):
     worst, checked = 0.0, 0
     for i in range(n):
         lo = dec.step(kv_np, tok_np, P + i)
-        worst = max(worst, float(np.max(np.abs(g_logits[i] - lo))))
+        worst = worst_of(worst, float(np.max(np.abs(g_logits[i] - lo))))
         ids, marg = oracle.argmax_lowest(lo), oracle.top2_margin(lo)
         for b in range(B):
             if marg[b] > MARGIN:

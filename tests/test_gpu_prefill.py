@@ -9,7 +9,7 @@ import oracle
 from persistent_decode_megakernel_amd import _lib, synth
 from persistent_decode_megakernel_amd.model import Model
 
-from gpu_helpers import LOGIT_TOL, MARGIN, kv_row_error, log
+from gpu_helpers import LOGIT_TOL, MARGIN, kv_row_error, log, worst_of
 
 pytestmark = pytest.mark.gpu
 
@@ -52,7 +52,7 @@ def test_prefill_then_decode_matches_oracle(path, n_prompt, wtype):
     g_toks, g_lo = toks.cpu().numpy(), dec_logits.cpu().numpy().astype(np.float64)
     for i in range(n_dec):
         lo = dec.step(kv_np, np.array([tok]), n_prompt + i)[0]
-        worst = max(worst, float(np.max(np.abs(g_lo[i, 0] - lo))))
+        worst = worst_of(worst, float(np.max(np.abs(g_lo[i, 0] - lo))))
         if oracle.top2_margin(lo[None])[0] > MARGIN:
             assert g_toks[i, 0] == oracle.argmax_lowest(lo[None])[0], i
         tok = int(g_toks[i, 0])

@@ -9,7 +9,7 @@ import oracle
 from persistent_decode_megakernel_amd import _lib, synth
 from persistent_decode_megakernel_amd.model import Model
 
-from gpu_helpers import LOGIT_TOL, MARGIN, kv_row_error, log
+from gpu_helpers import LOGIT_TOL, MARGIN, kv_row_error, log, worst_of
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +51,7 @@ def test_ragged_positions_match_per_sequence_oracle(path, batch, wtype):
         tok = int(first[b])
         for i in range(n):
             lo = dec.step(kv_b, np.array([tok]), pos0[b] + i)[0]
-            worst = max(worst, float(np.max(np.abs(logits[i, b] - lo))))
+            worst = worst_of(worst, float(np.max(np.abs(logits[i, b] - lo))))
             if oracle.top2_margin(lo[None])[0] > MARGIN:
                 checked += 1
                 assert toks[i, b] == oracle.argmax_lowest(lo[None])[0], (b, i)
