@@ -97,12 +97,17 @@ typedef struct {
   int32_t search;        /* 1: exhaustive search over the free fields above; 0: take them as is */
 } amk_sched_params;
 
-/* Cost model used by the schedule search (host only). Zero fields select defaults. */
+/* Cost model used by the schedule search (host only). Zero fields select defaults: the model
+ * amk_calibrate measured, stored as JSON in cost_model.json beside libamk.so (or the file named by
+ * the AMK_COST_MODEL environment variable; "off" skips it) when its CU count matches, else built-in
+ * values. */
 typedef struct {
   double cu_stream_gbs;  /* sustained HBM read rate of one CU when all CUs stream, GB/s */
-  double hop_us;         /* latency from a producer's flag release to a consumer's start, us */
-  double task_us;        /* fixed cost of one task (wait, staging, epilogue), us */
+  double hop_us;         /* latency from a producer's last store to a consumer's start, us */
+  double task_us;        /* fixed cost of one task beyond its hop and its bytes, us */
   double l2_gbs;         /* per-CU rate for re-read activation data (L2 / MALL), GB/s */
+  double prefetch_kb;    /* weight bytes a batch-1 GEMV tile streams before its wait, KiB */
+  double attn_us;        /* fixed cost of an attention block's partial beyond its hop and bytes, us */
 } amk_cost_model;
 
 typedef struct {
@@ -286,9 +291,52 @@ amk_status amk_schedule_rebalance(const void *blob, size_t bytes, const uint64_t
                                   int32_t n_traces, double gain, void **out_blob,
                                   size_t *out_bytes);
 
+/* Measure the cost model on the current device (the offline profiling behind the schedule
+ * search: Ada-MK technical summary, "Methodology", Phase I, and "Key Contributions" item 2).
+ * Microbenchmarks with the megakernel's own device code: the per-CU weight-stream rate with 8,
+ * 16, ... and all CUs streaming at once; the time of one dependency hop (wait, stage a vector of
+ * K fp32 words, write the next) from one workgroup to the next, for the tagged batch-1 protocol
+ * and the flag protocol, within one XCD and across XCDs, with the other CUs idle or streaming;
+ * and the all-to-all phase (every CU stages the vector all of them wrote a share of, then writes
+ * its share of the next). Fitted: cu_stream_gbs = the all-CU rate per CU; hop_us and l2_gbs from a
+ * line through the phases at K = 1024, 4096 and 11008 (time = hop_us + 4 K bytes / l2_gbs);
+ * task_us = attn_us = 0 (amk_cost_model_fit reads them off a traced step of the model). report
+ * (may be NULL) receives the measurements and the fit as JSON.
+ * Allocates about 8 MiB per CU of device memory for the duration of the call; synchronises
+ * `stream`; takes a few tenths of a second. */
+amk_status amk_calibrate(amk_cost_model *out, char *report, size_t report_cap, void *stream);
+
+/* The cost model the schedule search uses when given none, for n_cu compute units: the
+ * calibrated one (see amk_cost_model) or the built-in values. source (may be NULL) receives the
+ * path of the file it came from, or "built-in". Host only. */
+amk_status amk_cost_model_default(int32_t n_cu, amk_cost_model *out, char *source,
+                                  size_t source_cap);
+
 /* Cost-model makespan (us) of a schedule at context length ctx. */
 amk_status amk_schedule_predict(const void *blob, size_t bytes, const amk_cost_model *cost,
                                 int32_t ctx, double *makespan_us);
+
+/* The cost model's timeline of one step of a schedule at context length ctx, written as the task
+ * trace amk_trace_enable records (trace_words >= 4 * n_tasks + n_cu): per task, 100 MHz stamps
+ * of when its CU picks it up (twice), when its input is staged (an attention block: when its
+ * partial is done) and when it finishes; then n_cu zero words. A predicted step can so be
+ * exported and compared like a measured one. Host only; AMK_E_INVALID on a malformed blob or a
+ * short buffer. */
+amk_status amk_schedule_predict_trace(const void *blob, size_t bytes, const amk_cost_model *cost,
+                                      int32_t ctx, uint64_t *trace, size_t trace_words);
+
+/* Fit a cost model's fixed costs to measured task traces of one schedule (the per-model offline
+ * profiling of Ada-MK technical summary, "Methodology", Phase I): n_traces consecutive traces as
+ * amk_trace_enable writes them, of steps at context length ctx. Rates and prefetch come from
+ * `base` (zero fields: the default model, e.g. amk_calibrate's); hop_us, task_us and attn_us are
+ * the medians of what the traced tasks took beyond the simulation's other terms (hop: tiles that
+ * waited, staged time less staging and the last producer's end; task: GEMV tiles' end beyond
+ * their streaming; attn: attention partials' end beyond their staging and streaming). report
+ * (may be NULL) receives JSON with the sample counts, the measured and predicted step (us) and
+ * the fitted model in the "fit" object, in the format cost_model.json uses. Host only. */
+amk_status amk_cost_model_fit(const void *blob, size_t bytes, const uint64_t *traces,
+                              int32_t n_traces, int32_t ctx, const amk_cost_model *base,
+                              amk_cost_model *out, char *report, size_t report_cap);
 
 void amk_blob_free(void *blob);
 

@@ -60,7 +60,7 @@ class amk_sched_params(C.Structure):
 
 class amk_cost_model(C.Structure):
     _fields_ = [("cu_stream_gbs", C.c_double), ("hop_us", C.c_double), ("task_us", C.c_double),
-                ("l2_gbs", C.c_double)]
+                ("l2_gbs", C.c_double), ("prefetch_kb", C.c_double), ("attn_us", C.c_double)]
 
 
 class amk_model_info(C.Structure):
@@ -109,6 +109,14 @@ SIGNATURES = {
                                        C.c_int32, C.POINTER(C.c_double)]),
     "amk_schedule_rebalance": (C.c_int, [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int32, C.c_double,
                                          C.POINTER(C.c_void_p), C.POINTER(C.c_size_t)]),
+    "amk_calibrate": (C.c_int, [C.POINTER(amk_cost_model), C.c_char_p, C.c_size_t, C.c_void_p]),
+    "amk_cost_model_default": (C.c_int, [C.c_int32, C.POINTER(amk_cost_model), C.c_char_p,
+                                         C.c_size_t]),
+    "amk_schedule_predict_trace": (C.c_int, [C.c_void_p, C.c_size_t, C.POINTER(amk_cost_model),
+                                             C.c_int32, C.c_void_p, C.c_size_t]),
+    "amk_cost_model_fit": (C.c_int, [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int32, C.c_int32,
+                                     C.POINTER(amk_cost_model), C.POINTER(amk_cost_model),
+                                     C.c_char_p, C.c_size_t]),
     "amk_blob_free": (None, [C.c_void_p]),
 }
 
@@ -213,3 +221,46 @@ def schedule_rebalance(blob: bytes, traces, gain: float = 0.5) -> bytes:
         return C.string_at(out, n.value)
     finally:
         lib.amk_blob_free(out)
+
+
+def schedule_predict_trace(blob: bytes, ctx: int, cost: Optional[amk_cost_model] = None):
+    """The cost model's timeline of one step as a task trace (numpy uint64, 4 n_tasks + n_cu)."""
+    import numpy as np
+    from .blob import Blob
+    b = Blob(blob)
+    tr = np.zeros(4 * b.hdr.n_tasks + b.hdr.n_cu, dtype=np.uint64)
+    check(load().amk_schedule_predict_trace(blob, len(blob), C.byref(cost) if cost else None, ctx,
+                                            tr.ctypes.data_as(C.c_void_p), tr.size),
+          "amk_schedule_predict_trace")
+    return tr
+
+
+def cost_model_fit(blob: bytes, traces, ctx: int, base: Optional[amk_cost_model] = None):
+    """(amk_cost_model fitted to task traces of steps at context ctx, report as a dict)."""
+    import json
+    import numpy as np
+    tr = np.ascontiguousarray(traces, dtype=np.uint64)
+    n_traces = tr.shape[0] if tr.ndim == 2 else 1
+    out = amk_cost_model()
+    buf = C.create_string_buffer(1024)
+    check(load().amk_cost_model_fit(blob, len(blob), tr.ctypes.data_as(C.c_void_p), n_traces, ctx,
+                                    C.byref(base) if base else None, C.byref(out), buf, len(buf)),
+          "amk_cost_model_fit")
+    return out, json.loads(buf.value.decode())
+
+
+def calibrate(stream=None):
+    """amk_calibrate on the current device: (fitted amk_cost_model, measurements as a dict)."""
+    import json
+    cm = amk_cost_model()
+    buf = C.create_string_buffer(1 << 16)
+    check(load().amk_calibrate(C.byref(cm), buf, len(buf), stream), "amk_calibrate")
+    return cm, json.loads(buf.value.decode())
+
+
+def cost_model_default(n_cu: int):
+    """(amk_cost_model the search uses for n_cu CUs when given none, where it came from)."""
+    cm = amk_cost_model()
+    buf = C.create_string_buffer(4096)
+    check(load().amk_cost_model_default(n_cu, C.byref(cm), buf, len(buf)), "amk_cost_model_default")
+    return cm, buf.value.decode()

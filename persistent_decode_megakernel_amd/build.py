@@ -16,12 +16,12 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libamk.so")
 BUILD = os.path.join(ROOT, "_build")
 
-HIP_SOURCES = ["kernels/unfused.hip", "runtime/model.hip"]
+HIP_SOURCES = ["kernels/unfused.hip", "runtime/model.hip", "runtime/calibrate.hip"]
 # the megakernel source is compiled once per (weight type, head_dim) pair, in parallel
 MEGAKERNEL = "kernels/megakernel.hip"
 MK_PAIRS = [(wt, hd) for wt in (0, 1, 2) for hd in (64, 128)]
 CXX_SOURCES = ["runtime/errors.cpp", "sched/builder.cpp", "sched/validate.cpp", "sched/sched_api.cpp",
-               "sched/rebalance.cpp"]
+               "sched/rebalance.cpp", "sched/cost_model.cpp", "sched/cost_fit.cpp"]
 ARCH = "gfx950"
 
 
@@ -85,7 +85,7 @@ def build(verbose: bool = False, jobs: int = 8, incremental: bool = False) -> st
             if verbose and out.strip():
                 print(out)
     tmp = OUT + ".tmp"
-    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs)
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + ["-ldl"])
     os.replace(tmp, OUT)
     return OUT
 
@@ -102,7 +102,7 @@ def build_sched_sanitized() -> str:
     srcs = [os.path.join(CSRC, s) for s in CXX_SOURCES]
     _run(["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fPIC", "-shared",
           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
-          "-I", os.path.join(ROOT, "include"), "-o", SANITIZED_OUT] + srcs)
+          "-I", os.path.join(ROOT, "include"), "-o", SANITIZED_OUT] + srcs + ["-ldl"])
     return SANITIZED_OUT
 
 

@@ -2,10 +2,14 @@
 // tables), KV caches, and the per-step launch of the megakernel or the unfused ablation.
 #include <hip/hip_runtime.h>
 
+#include <unistd.h>
+
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <filesystem>
 #include <mutex>
 #include <new>
 #include <stdexcept>
@@ -229,6 +233,68 @@ void carve_scratch(DevModel &dm, uint8_t *base, const ScratchPlan &p) {
   dm.xn = reinterpret_cast<float *>(at(p.xn));
   dm.y = reinterpret_cast<float *>(at(p.y));
   dm.o = reinterpret_cast<float *>(at(p.o));
+}
+
+// ---- cache of built schedules ------------------------------------------------------------
+// Model creation without a caller's schedule keeps the schedule it builds on disk, keyed by all
+// the builder reads (config, batch, CU count, the device's architecture, the cost model the search
+// ranks with) and the build of the schedule layer; the next creation with the same key reads it
+// back instead of searching again. A cached blob is parsed and validated like a caller's; one that
+// fails, or was built for another configuration, is rebuilt and replaced. Directory:
+// $AMK_CACHE_DIR, else ~/.cache/amk; AMK_CACHE_DIR=off disables the cache.
+uint64_t fnv1a(const void *p, size_t n, uint64_t h = 1469598103934665603ull) {
+  const uint8_t *b = static_cast<const uint8_t *>(p);
+  for (size_t i = 0; i < n; ++i) h = (h ^ b[i]) * 1099511628211ull;
+  return h;
+}
+
+std::string cache_dir() {
+  const char *env = std::getenv("AMK_CACHE_DIR");
+  if (env && std::strcmp(env, "off") == 0) return "";
+  if (env && *env) return env;
+  const char *home = std::getenv("HOME");
+  return home && *home ? std::string(home) + "/.cache/amk" : "";
+}
+
+std::string cache_path(const amk_config &cfg, int n_cu, const char *arch) {
+  const std::string dir = cache_dir();
+  if (dir.empty()) return "";
+  BlobConfig bc;
+  std::memcpy(&bc, &cfg, sizeof bc);
+  const amk_cost_model cm = default_cost_model(n_cu);
+  uint64_t h = fnv1a(&bc, sizeof bc);
+  h = fnv1a(&n_cu, sizeof n_cu, h);
+  h = fnv1a(arch, std::strlen(arch), h);
+  h = fnv1a(&cm, sizeof cm, h);
+  const uint32_t version = kBlobVersion;
+  h = fnv1a(&version, sizeof version, h);
+  const char *stamp = schedule_build_stamp();
+  h = fnv1a(stamp, std::strlen(stamp), h);
+  char name[64];
+  std::snprintf(name, sizeof name, "/schedule-%016llx.amks", (unsigned long long)h);
+  return dir + name;
+}
+
+bool read_file(const std::string &path, std::vector<uint8_t> *out) {
+  FILE *f = std::fopen(path.c_str(), "rb");
+  if (!f) return false;
+  out->clear();
+  uint8_t buf[1 << 16];
+  size_t n;
+  while ((n = std::fread(buf, 1, sizeof buf, f)) > 0) out->insert(out->end(), buf, buf + n);
+  std::fclose(f);
+  return !out->empty();
+}
+
+// write by rename, so a reader never sees a partial file; failures leave no cache entry
+void write_file(const std::string &path, const std::vector<uint8_t> &data) {
+  std::error_code ec;
+  std::filesystem::create_directories(std::filesystem::path(path).parent_path(), ec);
+  const std::string tmp = path + ".tmp" + std::to_string((unsigned long)getpid());
+  FILE *f = std::fopen(tmp.c_str(), "wb");
+  if (!f) return;
+  const bool ok = std::fwrite(data.data(), 1, data.size(), f) == data.size();
+  if (std::fclose(f) != 0 || !ok || std::rename(tmp.c_str(), path.c_str()) != 0) std::remove(tmp.c_str());
 }
 
 // ---- scratch of the entry point that allocates nothing (amk_decode_steps_noalloc) ----------
@@ -460,16 +526,32 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
       }
       m->blob.assign((const uint8_t *)schedule_blob, (const uint8_t *)schedule_blob + blob_bytes);
     } else {
-      void *b = nullptr;
-      size_t n = 0;
-      amk_status s2 = amk_schedule_build(cfg, cfg->max_batch, m->n_cu, nullptr, nullptr, &b, &n);
-      if (s2 != AMK_OK) {
-        free_model(m);
-        return s2;
+      // a cached build of this configuration, if one validates; else build (and cache) it
+      const std::string cpath = cache_path(*cfg, m->n_cu, prop.gcnArchName);
+      bool cached = false;
+      if (!cpath.empty() && read_file(cpath, &m->blob)) {
+        Schedule cs;
+        std::string ce, crep;
+        if (parse(m->blob.data(), m->blob.size(), &cs, &ce) && validate_schedule(cs, &crep) &&
+            std::memcmp(&cs.hdr.cfg, cfg, sizeof(BlobConfig)) == 0 &&
+            (int32_t)cs.hdr.batch == cfg->max_batch && (int)cs.hdr.n_cu == m->n_cu) {
+          m->sched = std::move(cs);
+          cached = true;
+        }
       }
-      m->blob.assign((uint8_t *)b, (uint8_t *)b + n);
-      amk_blob_free(b);
-      parse(m->blob.data(), m->blob.size(), &m->sched, &e);
+      if (!cached) {
+        void *b = nullptr;
+        size_t n = 0;
+        amk_status s2 = amk_schedule_build(cfg, cfg->max_batch, m->n_cu, nullptr, nullptr, &b, &n);
+        if (s2 != AMK_OK) {
+          free_model(m);
+          return s2;
+        }
+        m->blob.assign((uint8_t *)b, (uint8_t *)b + n);
+        amk_blob_free(b);
+        parse(m->blob.data(), m->blob.size(), &m->sched, &e);
+        if (!cpath.empty()) write_file(cpath, m->blob);
+      }
     }
     std::string rep;
     if (!validate_schedule(m->sched, &rep)) {

@@ -15,6 +15,8 @@
 
 namespace amk {
 
+const char *builder_stamp() { return __DATE__ " " __TIME__; }
+
 uint32_t Schedule::n_tasks() const {
   uint32_t n = 0;
   for (auto &v : per_cu) n += (uint32_t)v.size();
@@ -249,12 +251,14 @@ struct Builder {
 
 }  // namespace
 
-amk_cost_model default_cost_model() {
+amk_cost_model builtin_cost_model() {
   amk_cost_model m{};
   m.cu_stream_gbs = 8000.0 * 0.8 / 256.0;  // 80% of 8 TB/s shared by 256 CUs
   m.hop_us = 2.0;
   m.task_us = 1.0;
+  m.attn_us = 1.0;
   m.l2_gbs = 100.0;
+  m.prefetch_kb = 128.0;  // two 8 KB chunks per wave, eight waves
   return m;
 }
 
@@ -284,13 +288,25 @@ void task_bytes(const BlobHeader &h, const Task &t, int32_t ctx, double *hbm, do
   }
 }
 
-double predict_makespan(const Schedule &s, const amk_cost_model &cm, int32_t ctx) {
+// List-schedule simulation of one step: every CU runs its tasks in order; a task's inputs are
+// seen hop_us after the last of its producers finished. Bytes stream at cu_stream_gbs per CU.
+// What a task can do before its inputs are there is overlapped with the wait, as the kernel does:
+// a GEMV tile streams its first prefetch_kb of weights (batch 1; the batched ring, its first
+// rounds) from the moment its CU is free; an attention block issues the KV history of its first
+// sequence. Staging an input costs its activation bytes at l2_gbs. Beyond hop and bytes, a task
+// takes task_us (an attention block's partial, attn_us).
+double predict_times(const Schedule &s, const amk_cost_model &cm, int32_t ctx,
+                     std::vector<TaskTimes> *times) {
   const uint32_t n = s.hdr.n_tasks;
   std::vector<double> finish(n, -1.0);
   std::vector<size_t> head(s.per_cu.size(), 0);
   std::vector<double> cu_free(s.per_cu.size(), 0.0);
   size_t done = 0, total = 0;
   for (auto &v : s.per_cu) total += v.size();
+  const double rate = cm.cu_stream_gbs * 1e3, l2 = cm.l2_gbs * 1e3;  // bytes per us
+  const double pf = cm.prefetch_kb * 1024.0;
+  const double B = std::max<uint32_t>(1, s.hdr.batch);
+  if (times) times->assign(n, TaskTimes{});
   // repeated sweeps; tasks become ready once all producers have finished
   bool progress = true;
   while (done < total && progress) {
@@ -298,8 +314,8 @@ double predict_makespan(const Schedule &s, const amk_cost_model &cm, int32_t ctx
     for (size_t c = 0; c < s.per_cu.size(); ++c) {
       while (head[c] < s.per_cu[c].size()) {
         const Task &t = s.per_cu[c][head[c]];
-        // ready[r]: when the producers of wait range r have finished and been seen
-        double ready[2] = {cu_free[c], 0.0};
+        // dep[r]: when the producers of wait range r have finished and been seen
+        double dep[2] = {0.0, 0.0};
         bool ok = true;
         for (int r = 0; r < 2 && ok; ++r) {
           uint32_t lo = r ? t.w1_lo : t.w0_lo, hi = r ? t.w1_hi : t.w0_hi;
@@ -308,21 +324,27 @@ double predict_makespan(const Schedule &s, const amk_cost_model &cm, int32_t ctx
               ok = false;
               break;
             }
-            ready[r] = std::max(ready[r], finish[i] + cm.hop_us);
+            dep[r] = std::max(dep[r], finish[i] + cm.hop_us);
           }
         }
         if (!ok) break;
+        const double free = cu_free[c];
         double hbm, act;
         task_bytes(s.hdr, t, ctx, &hbm, &act);
-        double dur = cm.task_us + hbm / (cm.cu_stream_gbs * 1e3) + act / (cm.l2_gbs * 1e3);
-        double end;
-        if (t.type == T_ATTN && t.aux1) {
-          // a merger computes its own partial after the QKV wait, then merges once its group's
-          // other blocks are done as well
-          end = std::max(ready[0] + dur, ready[1]) + cm.task_us;
+        const double staged = std::max(free, dep[0]) + act / l2;
+        double end, mid = staged;
+        if (t.type == T_GEMV) {
+          const double pre = std::min(hbm, pf);
+          end = std::max(free + pre / rate, staged) + (hbm - pre) / rate + cm.task_us;
+        } else if (t.type == T_ATTN) {
+          const double pre = hbm / B;  // the first sequence's rows, issued before the wait
+          end = mid = std::max(free + pre / rate, staged) + (hbm - pre) / rate + cm.attn_us;
+          // a merger then waits for its group's other blocks and merges their partials
+          if (t.aux1) end = std::max(end, dep[1]) + act / l2 + cm.task_us;
         } else {
-          end = std::max(ready[0], ready[1]) + dur;
+          end = staged + cm.task_us;
         }
+        if (times && t.id < n) (*times)[t.id] = TaskTimes{free, mid, end, (uint32_t)c};
         finish[t.id] = end;
         cu_free[c] = end;
         ++head[c];
@@ -335,6 +357,10 @@ double predict_makespan(const Schedule &s, const amk_cost_model &cm, int32_t ctx
   double m = 0;
   for (double f : cu_free) m = std::max(m, f);
   return m;
+}
+
+double predict_makespan(const Schedule &s, const amk_cost_model &cm, int32_t ctx) {
+  return predict_times(s, cm, ctx, nullptr);
 }
 
 Schedule build_schedule(const amk_config &cfg, int32_t batch, int32_t n_cu,

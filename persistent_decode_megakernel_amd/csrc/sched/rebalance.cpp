@@ -155,7 +155,7 @@ bool rebalance_schedule(Schedule *s, const uint64_t *traces, int n_traces, doubl
   s->hdr.lds_bytes = (uint32_t)lds_bytes_for((int32_t)h.batch, c.hidden, c.n_heads * c.head_dim,
                                              c.ffn, c.n_heads / c.n_kv_heads, c.head_dim,
                                              (int32_t)max_rows);
-  s->hdr.predicted_us = predict_makespan(*s, default_cost_model(), (int32_t)h.ctx_hint);
+  s->hdr.predicted_us = predict_makespan(*s, default_cost_model((int32_t)h.n_cu), (int32_t)h.ctx_hint);
   return true;
 }
 

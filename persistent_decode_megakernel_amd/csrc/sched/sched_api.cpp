@@ -4,6 +4,7 @@
 #include <cstring>
 #include <new>
 #include <stdexcept>
+#include <string>
 #include <vector>
 
 #include "../runtime/errors.h"
@@ -11,14 +12,17 @@
 
 namespace amk {
 
-static amk_cost_model fill_cost(const amk_cost_model *c) {
-  amk_cost_model d = default_cost_model();
+// the caller's model with its zero (or invalid) fields taken from the default model
+amk_cost_model fill_cost(const amk_cost_model *c, int32_t n_cu) {
+  amk_cost_model d = default_cost_model(n_cu);
   if (!c) return d;
   amk_cost_model m = *c;
   if (!(m.cu_stream_gbs > 0)) m.cu_stream_gbs = d.cu_stream_gbs;
-  if (!(m.hop_us >= 0)) m.hop_us = d.hop_us;
-  if (!(m.task_us >= 0)) m.task_us = d.task_us;
+  if (!(m.hop_us > 0)) m.hop_us = d.hop_us;
+  if (!(m.task_us > 0)) m.task_us = d.task_us;
   if (!(m.l2_gbs > 0)) m.l2_gbs = d.l2_gbs;
+  if (!(m.prefetch_kb > 0)) m.prefetch_kb = d.prefetch_kb;
+  if (!(m.attn_us > 0)) m.attn_us = d.attn_us;
   return m;
 }
 
@@ -70,6 +74,13 @@ Schedule search_schedule(const amk_config &cfg, int32_t batch, int32_t n_cu,
   return best;
 }
 
+// Build stamp of the schedule search (this file and the builder): part of the key under which
+// model creation caches built schedules, so a rebuilt library never reuses older builds' blobs.
+const char *schedule_build_stamp() {
+  static const std::string stamp = std::string(__DATE__ " " __TIME__) + "/" + builder_stamp();
+  return stamp.c_str();
+}
+
 }  // namespace amk
 
 using namespace amk;
@@ -90,7 +101,7 @@ extern "C" amk_status amk_schedule_build(const amk_config *cfg, int32_t batch, i
   if (p.attn_blocks < 0 || p.min_block < 0 || p.rotate < 0 || p.ctx_hint < 0 || p.min_tile_kb < 0 ||
       p.placement < 0 || p.placement > 1)
     return set_error(AMK_E_INVALID, "amk_schedule_build: negative or unknown parameter");
-  amk_cost_model cm = fill_cost(cost);
+  amk_cost_model cm = fill_cost(cost, n_cu);
   Schedule s = search_schedule(*cfg, batch, n_cu, p, cm);
   std::vector<uint8_t> out = serialize(s);
   void *mem = std::malloc(out.size());
@@ -144,7 +155,7 @@ extern "C" amk_status amk_schedule_predict(const void *blob, size_t bytes,
   std::string e;
   if (!parse(blob, bytes, &s, &e)) return set_error(AMK_E_INVALID, e);
   if (ctx < 1) return set_error(AMK_E_INVALID, "amk_schedule_predict: ctx must be >= 1");
-  *makespan_us = predict_makespan(s, fill_cost(cost), ctx);
+  *makespan_us = predict_makespan(s, fill_cost(cost, (int32_t)s.hdr.n_cu), ctx);
   clear_error();
   return AMK_OK;
   AMK_API_END

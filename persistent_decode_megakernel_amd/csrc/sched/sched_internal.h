@@ -65,11 +65,29 @@ bool footprint(const BlobHeader &h, const Task &t, std::vector<Access> *acc, std
 void task_bytes(const BlobHeader &h, const Task &t, int32_t ctx, double *hbm, double *act);
 
 double predict_makespan(const Schedule &s, const amk_cost_model &cost, int32_t ctx);
+// The same simulation, with each task's times (us): picked up by its CU, its input staged (an
+// attention block: its partial done), finished.
+struct TaskTimes {
+  double start, mid, end;
+  uint32_t cu;
+};
+double predict_times(const Schedule &s, const amk_cost_model &cost, int32_t ctx,
+                     std::vector<TaskTimes> *times);
 
-amk_cost_model default_cost_model();
+// Built-in cost model values, and the model the search uses when given none: the calibrated
+// one stored beside the library for this CU count, else the built-in one (*source says which).
+amk_cost_model builtin_cost_model();
+amk_cost_model default_cost_model(int32_t n_cu, std::string *source = nullptr);
+bool parse_cost_model(const std::string &text, int32_t n_cu, amk_cost_model *out);
+// The caller's model with its zero (or invalid) fields taken from default_cost_model(n_cu).
+amk_cost_model fill_cost(const amk_cost_model *c, int32_t n_cu);
 
 Schedule build_schedule(const amk_config &cfg, int32_t batch, int32_t n_cu,
                         const amk_sched_params &p);
+
+// Compile stamps of the builder and of the search (cache keys of built schedules).
+const char *builder_stamp();
+const char *schedule_build_stamp();
 
 bool validate_schedule(const Schedule &s, std::string *report);
 bool simulate_schedule(const Schedule &s, std::string *report, int32_t max_delay_runs);
