@@ -123,6 +123,30 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// a lane's value from another lane of its 16-lane row (DPP control CTRL, every lane active)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// sum over aligned groups of G lanes (G = 2, 4, 8 or 16, within a 16-lane row), every lane of a
+// group receiving it: lane ^ 1 and lane ^ 2 (quad_perm), then the mirrored half-row and row,
+// which pair groups already summed. No LDS round trip, unlike a shuffle.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(G == 2 || G == 4 || G == 8 || G == 16, "group of 2 to 16 lanes");
+  v += dpp_f<0xB1>(v);                    // quad_perm(1,0,3,2)
+  if constexpr (G >= 4) v += dpp_f<0x4E>(v);   // quad_perm(2,3,0,1)
+  if constexpr (G >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
+  if constexpr (G >= 16) v += dpp_f<0x140>(v); // row_mirror
+  return v;
+}
+
+// the value of lane ^ o (o a power of two below 64, known at compile time after unrolling): DPP
+// row_ror:8 for o = 8, a shuffle otherwise
+__device__ __forceinline__ float xor_lanes(float v, int o) {
+  return o == 8 ? dpp_f<0x128>(v) : __shfl_xor(v, o, 64);
+}
+
 // max over the 64 lanes of non-negative values, every lane receives it: DPP within rows of 16
 // lanes (float bits of non-negative values order as integers), then the four row maxima
 __device__ __forceinline__ float wave_max_nonneg(float v) {
@@ -2082,230 +2106,6 @@ __device__ bool attn_stage_tagged(const DevModel &m, const StepArgs &s, int l, i
   }
 }
 
-// One sequence's attention partial. TAGGED (batch-1 megakernel): q and the appended row come from
-// attn_stage_tagged, the partial is stored as tagged words. Otherwise the flags named by wait_for
-// are waited on and q and the appended row are read from q and the KV cache (batched steps and
-// the operator kernels use attn_block_seqs instead).
-template <int HD, int QMAX, bool TAGGED>
-__device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, int blk,
-                           int h0, int qn, float *lds, float *red, const Task *wait_for,
-                           int *abort_slot) {
-  // heads [h0, h0 + qn) of the group (qn <= QMAX), i.e. query heads g*qpg + h0 + i.
-  // The first chunk of KV history (rows written by earlier steps) is loaded before the
-  // dependency wait; only the row at `pos`, appended by this step's QKV tiles, is read after it.
-  constexpr int NW = kWaves;
-  constexpr int LPR = HD / 8;
-  constexpr int RPW = 64 / LPR;  // rows per wave per load
-  constexpr int ROWS_PER_ITER = NW * RPW;
-  constexpr int CH = attn_chunk_rows(HD, QMAX);
-  constexpr int NIT = CH / ROWS_PER_ITER;
-  static_assert(NIT * ROWS_PER_ITER == CH && CH <= kAttnRowsPerChunk, "chunk must be whole iterations");
-  const int qpg = qn, nq = m.nq, nblk = m.nblk;
-  const int lane = lane_id(), wave = wave_id();
-  const int sub = lane % LPR, rs = lane / LPR;
-  float *qs = lds;                             // [qpg][HD]
-  float *sc = qs + qpg * HD;                   // [qpg][chunk]
-  float *accw = sc + qpg * CH;                 // [NW][qpg*HD]
-  uint16_t *kvrow = reinterpret_cast<uint16_t *>(accw + NW * qpg * HD);  // [2][HD]
-  for (int b = 0; b < s.batch; ++b) {
-    // this sequence's position and its part of the KV block's range
-    const int pos = pos_of(s, b);
-    int lo, hi;
-    attn_block_range(pos + 1, nblk, blk, &lo, &hi);
-    const uint16_t *Kb = s.kv + kv_index(m, s, l, 0, b, g, 0, 0);
-    const uint16_t *Vb = s.kv + kv_index(m, s, l, 1, b, g, 0, 0);
-    uint4 kr[NIT], vr[NIT];
-    auto load_history = [&]() {
-      const int c1 = min(hi, lo + CH);
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int j = lo + it * ROWS_PER_ITER + wave * RPW + rs;
-        const bool ok = j < c1 && j != pos;
-        kr[it] = ok ? load_nt(reinterpret_cast<const uint4 *>(Kb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
-        vr[it] = ok ? load_nt(reinterpret_cast<const uint4 *>(Vb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
-      }
-    };
-    const int po = pos - lo;
-    const bool own_pos = po >= 0 && pos < hi && (po % ROWS_PER_ITER) == wave * RPW + rs;
-    uint4 kpos = make_uint4(0, 0, 0, 0), vpos = make_uint4(0, 0, 0, 0);
-    if constexpr (TAGGED) {
-      load_history();
-      // keep the history loads issued here, ahead of the staging loads (the compiler would
-      // otherwise sink them to their first use, after the wait)
-      asm volatile("" ::: "memory");
-      if (!attn_stage_tagged(m, s, l, g, h0, qn, qs, kvrow, wait_for ? wait_for->id : 0u)) {
-        __builtin_amdgcn_s_waitcnt(0);
-        return false;
-      }
-      if (m.trace && wait_for && h0 == 0 && threadIdx.x == 0)
-        gst(&m.trace[(uint64_t)wait_for->id * 4 + 1], (uint64_t)wall_clock64());
-      if (own_pos) {
-        kpos = *reinterpret_cast<const uint4 *>(kvrow + sub * 8);
-        vpos = *reinterpret_cast<const uint4 *>(kvrow + HD + sub * 8);
-      }
-    } else {
-      // wave 0 polls the flags and a wave's loads return in order, so it issues its history rows
-      // after polling; the other waves issue theirs before the join
-      const bool waits = wait_for && b == 0;
-      if (waits) wait_poll(m, *wait_for, s.epoch, abort_slot);
-      load_history();
-      asm volatile("" ::: "memory");  // issue them before the join, not at their first use
-      if (waits && !wait_join(m, *wait_for, abort_slot)) return false;
-      // The row at pos was appended by this step's QKV tiles: device-coherent loads, issued right
-      // after the wait together with q, for whichever chunk and lane holds it.
-      if (own_pos) {
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)pos * HD, HD * 2);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + (int64_t)pos * HD, HD * 2);
-        const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(rk, sub * 16, 0, kCachePolicySc1);
-        const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(rv, sub * 16, 0, kCachePolicySc1);
-        kpos = make_uint4(a.x, a.y, a.z, a.w);
-        vpos = make_uint4(c.x, c.y, c.z, c.w);
-      }
-      const float *qsrc = m.q + ((int64_t)l * m.max_batch + b) * m.qd + ((int64_t)g * m.qpg + h0) * HD;
-      for (int i = threadIdx.x; i < qpg * HD; i += NW * 64) qs[i] = cldf(&qsrc[i]) * m.attn_scale;
-    }
-    __syncthreads();
-    float *pout = m.part + ((((int64_t)l * m.max_batch + b) * nq + (int64_t)g * m.qpg + h0) * nblk + blk) * (HD + 2);
-    auto put = [&](float *p, float v) {
-      if constexpr (TAGGED)
-        cst(reinterpret_cast<uint32_t *>(p), tag_word(v, s.epoch));
-      else
-        cstf(p, v);
-    };
-    if (hi <= lo) {
-      for (int i = threadIdx.x; i < qpg * (HD + 2); i += NW * 64) {
-        const int h = i / (HD + 2), e = i - h * (HD + 2);
-        put(&pout[(int64_t)h * nblk * (HD + 2) + e], (e == HD) ? kEmptyBlockM : 0.f);
-      }
-      __syncthreads();
-      continue;
-    }
-    float acc[QMAX][8];
-    float lsum[QMAX];
-    float mrun[QMAX];
-#pragma unroll
-    for (int h = 0; h < QMAX; ++h) {
-      lsum[h] = 0.f;
-      mrun[h] = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-    }
-    for (int c0 = lo; c0 < hi; c0 += CH) {
-      const int c1 = min(hi, c0 + CH);
-      if (c0 != lo) {
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-          const int j = c0 + it * ROWS_PER_ITER + wave * RPW + rs;
-          const bool ok = j < c1 && j != pos;
-          kr[it] = ok ? load_nt(reinterpret_cast<const uint4 *>(Kb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
-          vr[it] = ok ? load_nt(reinterpret_cast<const uint4 *>(Vb + (int64_t)j * HD + sub * 8)) : make_uint4(0, 0, 0, 0);
-        }
-      }
-      // the appended row, wherever it falls (its history slot was left zero above)
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        if (c0 + it * ROWS_PER_ITER + wave * RPW + rs == pos) {
-          kr[it] = kpos;
-          vr[it] = vpos;
-        }
-      }
-      // scores of this lane's rows, reduced over the LPR lanes of a row
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int j = c0 + it * ROWS_PER_ITER + wave * RPW + rs;
-#pragma unroll
-        for (int h = 0; h < QMAX; ++h) {
-          if (h < qpg) {
-            float p = dot8_bf16(kr[it], qs + h * HD + sub * 8);
-#pragma unroll
-            for (int o = LPR / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o, 64);
-            if (j < c1 && sub == 0) sc[h * CH + (j - c0)] = p;
-          }
-        }
-      }
-      __syncthreads();
-      // chunk max per head (wave h), published in red[h]
-      const int n = c1 - c0;
-      if (wave < qpg) {
-        float mx = -INFINITY;
-        for (int i = lane; i < n; i += 64) mx = fmaxf(mx, sc[wave * CH + i]);
-        mx = wave_max(mx);
-        if (lane == 0) red[wave] = mx;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int h = 0; h < QMAX; ++h) {
-        if (h < qpg) {
-          const float mnew = fmaxf(mrun[h], red[h]);
-          const float f = __expf(mrun[h] - mnew);
-          lsum[h] *= f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] *= f;
-          mrun[h] = mnew;
-        }
-      }
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int j = c0 + it * ROWS_PER_ITER + wave * RPW + rs;
-        if (j < c1) {
-          const uint4 v = vr[it];
-          const float vv[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
-                               bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
-#pragma unroll
-          for (int h = 0; h < QMAX; ++h) {
-            if (h < qpg) {
-              const float p = __expf(sc[h * CH + (j - c0)] - mrun[h]);
-              if (sub == 0) lsum[h] += p;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vv[e], acc[h][e]);
-            }
-          }
-        }
-      }
-      __syncthreads();
-    }
-    // reduce acc over the row slots of the wave (lanes with equal sub), then over waves
-#pragma unroll
-    for (int h = 0; h < QMAX; ++h) {
-      if (h < qpg) {
-#pragma unroll
-        for (int o = LPR; o < 64; o <<= 1) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, 64);
-          lsum[h] += __shfl_xor(lsum[h], o, 64);
-        }
-#pragma unroll
-        for (int o = 1; o < LPR; o <<= 1) lsum[h] += __shfl_xor(lsum[h], o, 64);
-        if (rs == 0) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) accw[(int64_t)wave * qpg * HD + h * HD + sub * 8 + e] = acc[h][e];
-        }
-        if (lane == 0) red[16 + wave * 8 + h] = lsum[h];
-      }
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < qpg * HD; i += NW * 64) {
-      float t = 0.f;
-      for (int w = 0; w < NW; ++w) t += accw[(int64_t)w * qpg * HD + i];
-      const int h = i / HD, e = i - h * HD;
-      put(&pout[(int64_t)h * nblk * (HD + 2) + e], t);
-    }
-    if (threadIdx.x < qpg) {
-      const int h = threadIdx.x;
-      float t = 0.f;
-      for (int w = 0; w < NW; ++w) t += red[16 + w * 8 + h];
-      float mh = kEmptyBlockM;
-#pragma unroll
-      for (int k = 0; k < QMAX; ++k)
-        if (k == h) mh = mrun[k];
-      put(&pout[(int64_t)h * nblk * (HD + 2) + HD], mh);
-      put(&pout[(int64_t)h * nblk * (HD + 2) + HD + 1], t);
-    }
-    __syncthreads();
-  }
-  return true;
-}
-
 // Attention partials of a batched step (batch-2..16 megakernel instances and the operator
 // kernels): heads [h0, h0 + qn) of KV group g, KV block blk, for every sequence of the step.
 // Each wave streams its own rows, like a GEMV tile: sequence b's block is cut into chunks of
@@ -2321,7 +2121,7 @@ __device__ bool attn_block(const DevModel &m, const StepArgs &s, int l, int g, i
 // stores complete under one counter). wait_for (batched megakernel): the QKV tiles' flags,
 // polled by wave 0. LDS: q [B][qn][HD] | appended rows [B][2][HD] bf16 | partials
 // [B][qn][HD + 2] | wave partials [2][NW][qn][HD + 2].
-template <int HD, int QMAX>
+template <int HD, int QMAX, bool TAGGED>
 __device__ __forceinline__ bool attn_block_seqs(const DevModel &m, const StepArgs &s, int l,
                                                 int g, int blk, int h0, int qn, float *lds,
                                                 float *red, const Task *wait_for,
@@ -2415,9 +2215,7 @@ __device__ __forceinline__ bool attn_block_seqs(const DevModel &m, const StepArg
       for (int h = 0; h < QMAX; ++h) {
         float p = 0.f;
         if (h < qn) {
-          p = dot8_bf16(k, qs + h * HD);
-#pragma unroll
-          for (int o = LPR / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o, 64);
+          p = group_sum<LPR>(dot8_bf16(k, qs + h * HD));
         }
         sc[it][h] = p;
       }
@@ -2461,16 +2259,16 @@ __device__ __forceinline__ bool attn_block_seqs(const DevModel &m, const StepArg
       if (h < qn) {
         float mx = mrun[h];
 #pragma unroll
-        for (int o = LPR; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        for (int o = LPR; o < 64; o <<= 1) mx = fmaxf(mx, xor_lanes(mx, o));
         const float f = __expf(mrun[h] - mx);
         float t = lsum[h] * f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] *= f;
 #pragma unroll
         for (int o = LPR; o < 64; o <<= 1) {
-          t += __shfl_xor(t, o, 64);
+          t += xor_lanes(t, o);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, 64);
+          for (int e = 0; e < 8; ++e) acc[h][e] += xor_lanes(acc[h][e], o);
         }
         if (rs == 0) {
 #pragma unroll
@@ -2497,7 +2295,13 @@ __device__ __forceinline__ bool attn_block_seqs(const DevModel &m, const StepArg
         for (int w = 0; w < NW; ++w)
           t += __expf(w0[w * qn * (HD + 2) + h * (HD + 2) + HD] - mx) * w0[w * qn * (HD + 2) + i];
       }
-      pl[i] = t;
+      if constexpr (TAGGED) {
+        // batch 1: the only sequence's partial goes out at once, as tagged words
+        float *pout = m.part + ((((int64_t)l * m.max_batch + b) * nq + (int64_t)g * m.qpg + h0 + h) * nblk + blk) * (HD + 2);
+        cst(reinterpret_cast<uint32_t *>(&pout[e]), tag_word(t, s.epoch));
+      } else {
+        pl[i] = t;
+      }
     }
     ++ended;
   };
@@ -2507,39 +2311,60 @@ __device__ __forceinline__ bool attn_block_seqs(const DevModel &m, const StepArg
   from(0, lc);
   cc = lc;
   uint4 P[2][U], A[2][U], Bf[2][U];
-  // wave 0 polls the flags and a wave's loads return in order, so it issues its first chunk
-  // after polling; the other waves issue theirs before the join
-  if (wait_for) wait_poll(m, *wait_for, s.epoch, abort_slot);
-  if (S > 0) load(lc, P[0], P[1]);
-  asm volatile("" ::: "memory");  // issue them before the join, not at their first use
-  if (wait_for && !wait_join(m, *wait_for, abort_slot)) return false;
-  // q (scaled by 1/sqrt(hd)) and the appended K/V rows of every sequence: one round of
-  // device-coherent 4-byte loads (this step's QKV tiles wrote them)
-  for (int i = threadIdx.x; i < B * qn * HD; i += NW * 64) {
-    const int b = i / (qn * HD), r = i - b * (qn * HD);
-    qall[i] = cldf(&m.q[((int64_t)l * m.max_batch + b) * m.qd + ((int64_t)g * m.qpg + h0) * HD + r]) *
-              m.attn_scale;
-  }
-  for (int i = threadIdx.x; i < B * HD; i += NW * 64) {  // 32-bit words: [B][2][HD / 2]
-    const int b = i / HD, r = i - b * HD, kvi = r / (HD / 2), w = r - kvi * (HD / 2);
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(
-        s.kv + kv_index(m, s, l, kvi, b, g, pos_of(s, b), 0));
-    reinterpret_cast<uint32_t *>(rows)[i] = cld(&src[w]);
+  // the first two chunks go out before the wait (the KV history does not depend on it); chunk 1
+  // is then complete or nearly so when the stream starts
+  if constexpr (TAGGED) {
+    if (S > 0) load(lc, P[0], P[1]);
+    if (S > 1) {
+      advance(lc);
+      load(lc, A[0], A[1]);
+    }
+    asm volatile("" ::: "memory");  // issue them before the staging loads, not at their first use
+    // q (scaled) and the appended K/V row: epoch-tagged words, the staging loads are the wait
+    if (!attn_stage_tagged(m, s, l, g, h0, qn, qall, rows, wait_for ? wait_for->id : 0u)) {
+      __builtin_amdgcn_s_waitcnt(0);
+      return false;
+    }
+    if (m.trace && wait_for && h0 == 0 && threadIdx.x == 0)
+      gst(&m.trace[(uint64_t)wait_for->id * 4 + 1], (uint64_t)wall_clock64());
+  } else {
+    // wave 0 polls the flags and a wave's loads return in order, so it issues its first chunk
+    // after polling; the other waves issue theirs before the join. Chunk 1 goes out after the
+    // join: q is read behind whatever is in flight.
+    if (wait_for) wait_poll(m, *wait_for, s.epoch, abort_slot);
+    if (S > 0) load(lc, P[0], P[1]);
+    asm volatile("" ::: "memory");  // issue them before the join, not at their first use
+    if (wait_for && !wait_join(m, *wait_for, abort_slot)) return false;
+    // q (scaled by 1/sqrt(hd)) and the appended K/V rows of every sequence: one round of
+    // device-coherent 4-byte loads (this step's QKV tiles wrote them)
+    for (int i = threadIdx.x; i < B * qn * HD; i += NW * 64) {
+      const int b = i / (qn * HD), r = i - b * (qn * HD);
+      qall[i] = cldf(&m.q[((int64_t)l * m.max_batch + b) * m.qd + ((int64_t)g * m.qpg + h0) * HD + r]) *
+                m.attn_scale;
+    }
+    for (int i = threadIdx.x; i < B * HD; i += NW * 64) {  // 32-bit words: [B][2][HD / 2]
+      const int b = i / HD, r = i - b * HD, kvi = r / (HD / 2), w = r - kvi * (HD / 2);
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(
+          s.kv + kv_index(m, s, l, kvi, b, g, pos_of(s, b), 0));
+      reinterpret_cast<uint32_t *>(rows)[i] = cld(&src[w]);
+    }
   }
   // every thread's loads so far (chunk 0 too), also where a thread staged nothing: the wait
   // counts of the stream below then start from no pending loads on every path
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
-  // the stream: P (chunk 0, complete by now) is folded before the steady loop, which starts and
-  // loops back with exactly one buffer of loads in flight, so the compiler's wait for a buffer
-  // leaves the other buffer's loads outstanding. The empty asm statements keep each chunk's
-  // loads issued ahead of the previous chunk's arithmetic.
-  if (S > 0) {
+  if constexpr (!TAGGED) {
     if (S > 1) {
       advance(lc);
       load(lc, A[0], A[1]);
     }
     asm volatile("" ::: "memory");
+  }
+  // the stream: P and A (chunks 0 and 1, complete by now) are folded first and last-but-one;
+  // the steady loop loops back with exactly one buffer of loads in flight, so the compiler's wait
+  // for a buffer leaves the other buffer's loads outstanding. The empty asm statements keep each
+  // chunk's loads issued ahead of the previous chunk's arithmetic.
+  if (S > 0) {
     fold(cc, P[0], P[1]);
     if (S > 1) {
       advance(cc);
@@ -2568,6 +2393,8 @@ __device__ __forceinline__ bool attn_block_seqs(const DevModel &m, const StepArg
       }
     }
   }
+  // a batch-1 partial went out from the merge (the caller's barrier ends the task)
+  if (TAGGED && S > 0) return true;
   __syncthreads();
   // every sequence's partial of this block, [b][h][HD + 2]: device-coherent stores; a sequence
   // without rows here gives the empty partial
@@ -2578,7 +2405,10 @@ __device__ __forceinline__ bool attn_block_seqs(const DevModel &m, const StepArg
     attn_block_range(pos_of(s, b) + 1, nblk, blk, &lo, &hi);
     const float v = hi > lo ? parts[i] : (e == HD ? kEmptyBlockM : 0.f);
     float *pout = m.part + ((((int64_t)l * m.max_batch + b) * nq + (int64_t)g * m.qpg + h0 + h) * nblk + blk) * (HD + 2);
-    cstf(&pout[e], v);
+    if constexpr (TAGGED)
+      cst(reinterpret_cast<uint32_t *>(&pout[e]), tag_word(v, s.epoch));
+    else
+      cstf(&pout[e], v);
   }
   return true;
 }
@@ -2599,12 +2429,8 @@ __device__ __forceinline__ bool attn_task(const DevModel &m, const StepArgs &s, 
   }
   for (int h0 = 0; h0 < m.qpg; h0 += QMAX) {
     const Task *w = (wait_for && (TAGGED || h0 == 0)) ? &first : nullptr;
-    if constexpr (TAGGED) {
-      if (!attn_block<HD, QMAX, true>(m, s, l, g, blk, h0, min(QMAX, m.qpg - h0), lds, red, w,
-                                      abort_slot))
-        return false;
-    } else {
-      if (!attn_block_seqs<HD, QMAX>(m, s, l, g, blk, h0, min(QMAX, m.qpg - h0), lds, red, w,
+    {
+      if (!attn_block_seqs<HD, QMAX, TAGGED>(m, s, l, g, blk, h0, min(QMAX, m.qpg - h0), lds, red, w,
                                      abort_slot))
         return false;
     }

@@ -143,23 +143,15 @@ namespace amk {
 //   xs : batch x max(hidden, n_heads*head_dim, ffn) float  -- staged GEMV input vector(s)
 //   ys : batch x max_tile_rows float                        -- GEMV tile outputs before epilogue
 //   red: kRedFloats float                                   -- reductions, combine weights
-// Attention tasks reuse the xs region (q, scores, partial accumulators).
+// Attention tasks reuse the xs region (q, appended rows, partials).
 constexpr int32_t kWaves = 8;
 constexpr int32_t kThreads = kWaves * 64;
-// KV rows staged per attention chunk (a KV block of up to this many rows is one round of loads):
-// 320 rows (10 row iterations of the eight waves at head_dim 128, 5 at head_dim 64) where the
-// registers allow, 256 for head_dim 128 with several query heads per pass. LDS is sized for the
-// largest.
-constexpr int32_t kAttnRowsPerChunk = 320;
 constexpr int32_t kAttnMaxHeads = 4;  // query heads per attention pass (larger groups take several)
-AMK_HD constexpr int32_t attn_chunk_rows(int32_t hd, int32_t qmax) {
-  return (hd <= 64 || qmax == 1) ? kAttnRowsPerChunk : 256;
-}
 // Query heads per attention pass of a KV group of qpg heads.
 AMK_HD constexpr int32_t attn_qmax(int32_t qpg) { return qpg <= 1 ? 1 : (qpg <= 2 ? 2 : kAttnMaxHeads); }
 // KV rows one loop iteration of the attention body covers: hd / 8 lanes per row, 8 waves.
 AMK_HD constexpr int32_t attn_rows_per_iter(int32_t hd) { return 8 * (64 / (hd / 8)); }
-// Batched steps stream each wave's own KV rows in chunks of kAttnSeqIters loads of K (and of V)
+// Attention blocks stream each wave's own KV rows in chunks of kAttnSeqIters loads of K (and of V)
 // per lane, two chunks in flight per wave; a workgroup chunk is this many rows.
 constexpr int32_t kAttnSeqIters = 4;
 AMK_HD constexpr int32_t attn_seq_chunk_rows(int32_t hd) { return attn_rows_per_iter(hd) * kAttnSeqIters; }
@@ -180,16 +172,16 @@ constexpr int32_t kRingFloats = kWaves * kRingBytes / 4;
 AMK_HD int32_t lds_xs_floats(int32_t batch, int32_t hidden, int32_t qdim, int32_t ffn) {
   int32_t k = hidden > qdim ? hidden : qdim;
   k = k > ffn ? k : ffn;
-  return batch == 1 ? k : kRingFloats;
+  return batch == 1 ? (k + 63) / 64 * 64 : kRingFloats;
 }
 AMK_HD int32_t lds_attn_floats(int32_t batch, int32_t qpg, int32_t hd) {
-  // at most kAttnMaxHeads heads per pass. Batch 1: q [qn][hd] + scores [qn][chunk] + partial acc
-  // [waves][qn*hd] + appended K/V row [2][hd] bf16. Batched: q and the appended rows of every
-  // sequence, [batch][qn*hd] + [batch][2][hd] bf16, every sequence's partial until they are
-  // stored, [batch][qn][hd + 2], and the waves' partials of two sequences, [2][waves][qn][hd + 2].
+  // at most kAttnMaxHeads heads per pass: q and the appended K/V rows of every sequence,
+  // [batch][qn*hd] + [batch][2][hd] bf16, every sequence's partial until they are stored,
+  // [batch][qn][hd + 2], and the waves' partials of two sequences, [2][waves][qn][hd + 2]
+  // (rounded to 64 floats: the regions after it stay 256-byte aligned for 16-byte LDS copies)
   const int32_t qn = qpg < kAttnMaxHeads ? qpg : kAttnMaxHeads;
-  const int32_t one = qn * hd + qn * kAttnRowsPerChunk + kWaves * qn * hd + hd;
-  return batch == 1 ? one : batch * (qn * hd + hd + qn * (hd + 2)) + 2 * kWaves * qn * (hd + 2);
+  const int32_t n = batch * (qn * hd + hd + qn * (hd + 2)) + 2 * kWaves * qn * (hd + 2);
+  return (n + 63) / 64 * 64;
 }
 // Batch-1 GEMV tiles stage the first weight chunk of every wave in LDS (8 KB per wave).
 constexpr int32_t kPrefetchFloats = kWaves * 2048;
