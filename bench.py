@@ -433,8 +433,9 @@ def main():
                     cache[w_key] = synth.make_weights(wcfg, 0, threads=16)
                 wts = cache[w_key]
             kvh = synth.make_kv(wcfg, wcfg.prefill + max(steps, warmup) + 1, 0, threads=16)
-            res = measure(wcfg, wts, kvh, steps, warmup, profile_key=key + f"_b{wcfg.batch}",
-                          **opt)
+            # counters are taken on warm runs: the cold variant reports none of its own
+            pkey = f"{wcfg.name}_b{wcfg.batch}" + ("_cold" if opt.get("cold_mib") else "")
+            res = measure(wcfg, wts, kvh, steps, warmup, profile_key=pkey, **opt)
             res.pop("_ids")
             res["workload"] = (f"{wcfg.name}: {wcfg.n_layers} layers, hidden {wcfg.hidden}, "
                                f"{wcfg.n_heads}/{wcfg.n_kv_heads} heads, head_dim {wcfg.head_dim}, "
