@@ -126,7 +126,10 @@ typedef struct {
 typedef struct amk_model amk_model;
 typedef struct amk_kv amk_kv;
 
-/* Create a model on the current device. Weights are BORROWED for the duration of the call: the
+/* Create a model on the current device: the decoder compiled into one persistent kernel that runs
+ * a frozen, statically checked schedule (AutoMegaKernel abstract; Ada-MK technical summary,
+ * "Methodology", Phase I, the execution path solidified offline). Weights are BORROWED for the
+ * duration of the call: the
  * library repacks them into its own buffers and synchronises `stream` before returning, so the
  * caller may free them afterwards. The packed rows keep RoPE pairs and gate/up pairs adjacent.
  * A model of max_batch 1 keeps those rows row-major. A larger max_batch stores each matrix
@@ -138,20 +141,25 @@ amk_status amk_model_create(const amk_config *cfg, const amk_weights *weights, i
                             const void *schedule_blob, size_t blob_bytes, void *stream,
                             amk_model **out);
 
-/* Bytes of a KV cache for `batch` sequences of `max_seq` positions:
+/* Bytes of a KV cache for `batch` sequences of `max_seq` positions (the cache the decode step
+ * attends over; the pages fix no layout, this is the library's):
  * layout [n_layers][2 (K, V)][batch][n_kv_heads][max_seq][head_dim] bfloat16, K post-RoPE. */
 amk_status amk_kv_bytes(const amk_model *m, int32_t batch, int32_t max_seq, size_t *bytes);
 
-/* Attach a KV cache. d_buf == NULL: the library allocates (zeroed) and owns the memory;
+/* Attach a KV cache (library housekeeping; no passage of the pages defines it). d_buf == NULL:
+ * the library allocates (zeroed) and owns the memory;
  * otherwise d_buf is caller-owned device memory of at least amk_kv_bytes bytes, borrowed
  * until amk_kv_free. max_seq must not exceed the model's max_seq. */
 amk_status amk_kv_alloc(amk_model *m, int32_t batch, int32_t max_seq, void *d_buf,
                         size_t buf_bytes, amk_kv **out);
 
-/* Device pointer of the cache (for the caller to prefill or inspect). */
+/* Device pointer of the cache (for the caller to prefill or inspect; housekeeping). */
 amk_status amk_kv_data(const amk_kv *kv, void **d_ptr);
 
-/* One decode step, asynchronous on `stream`. d_tokens: device int32 [batch], the token of each
+/* One decode step, asynchronous on `stream`: the decode step of the pages' MegaKernel, all of a
+ * token's operators in one persistent launch (Ada-MK technical summary, "Problem Statement" and
+ * "Methodology"; greedy decoding as in the AutoMegaKernel abstract). d_tokens: device int32
+ * [batch], the token of each
  * sequence at position `pos`. Writes K/V at slot `pos`, attends over [0, pos], writes d_next
  * (device int32 [batch], greedy argmax, lowest index on ties) and, when d_logits != NULL,
  * d_logits (device float32 [batch, vocab]). d_next may alias the next call's d_tokens. Calls on
@@ -218,18 +226,24 @@ amk_status amk_prefill(amk_model *m, amk_kv *kv, int32_t seq, const int32_t *d_t
                        int32_t pos0, int32_t n_tokens, float *d_logits, int32_t *d_next,
                        void *stream);
 
-/* Synchronise `stream` and report a device-side error recorded by earlier steps (and clear it). */
+/* Synchronise `stream` and report a device-side error recorded by earlier steps (and clear it).
+ * Housekeeping: the bounded waits behind it make a dependency that never resolves an error
+ * instead of a hang. */
 amk_status amk_sync(amk_model *m, void *stream);
 
+/* Sizes and the cost-model prediction of the model's schedule (housekeeping). */
 amk_status amk_model_get_info(const amk_model *m, amk_model_info *out);
 
-/* Task trace of the megakernel (profiling). d_trace: device buffer of at least
+/* Task trace of the megakernel: the profiling behind the offline search (Ada-MK technical summary,
+ * "Methodology", Phase I; read by amk_cost_model_fit and amk_schedule_rebalance). d_trace:
+ * device buffer of at least
  * 8 * (4 * n_tasks + n_cu) bytes, caller-owned; NULL turns tracing off. While on, every step
  * writes, per task id, four 100 MHz wall-clock stamps (start of wait, wait done, input staged,
  * end) and, after them, the XCC id of each workgroup. Synchronises the device. */
 amk_status amk_trace_enable(amk_model *m, uint64_t *d_trace, size_t bytes);
 
-/* Copy of the model's frozen schedule blob (host memory, release with amk_blob_free). */
+/* Copy of the model's frozen schedule blob, the solidified execution path (Ada-MK technical
+ * summary, "Methodology", Phase I) (host memory, release with amk_blob_free). */
 amk_status amk_model_get_schedule(const amk_model *m, void **blob, size_t *bytes);
 
 /* Replace the frozen schedule of a megakernel model with another one of the same structure: same
@@ -254,6 +268,8 @@ amk_status amk_model_set_schedule(amk_model *m, const void *blob, size_t bytes, 
 amk_status amk_model_tune(amk_model *m, amk_kv *kv, int32_t pos, int32_t rounds, int32_t steps,
                           double gain, void *stream, double *best_us);
 
+/* Release a KV cache / a model and everything it owns (housekeeping). A caller-owned KV buffer is
+ * left alone. Not while a step using them is in flight. */
 amk_status amk_kv_free(amk_kv *kv);
 amk_status amk_destroy(amk_model *m);
 
