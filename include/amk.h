@@ -95,6 +95,9 @@ typedef struct {
   int32_t ctx_hint;      /* context length the cost model assumes (0 = max_seq) */
   int32_t min_tile_kb;   /* smallest weight tile (KiB) a GEMV is cut into; 0 = 4 */
   int32_t search;        /* 1: exhaustive search over the free fields above; 0: take them as is */
+  int32_t heads_per_task; /* query heads per attention task, a divisor of the heads sharing a KV
+                           * head: 0 = auto (models of batch capacity 1: a group's heads split so
+                           * that up to two attention tasks run per CU; otherwise whole groups) */
 } amk_sched_params;
 
 /* Cost model used by the schedule search (host only). Zero fields select defaults: the model

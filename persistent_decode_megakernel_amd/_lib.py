@@ -55,7 +55,7 @@ class amk_weights(C.Structure):
 class amk_sched_params(C.Structure):
     _fields_ = [("attn_blocks", C.c_int32), ("min_block", C.c_int32), ("placement", C.c_int32),
                 ("rotate", C.c_int32), ("ctx_hint", C.c_int32), ("min_tile_kb", C.c_int32),
-                ("search", C.c_int32)]
+                ("search", C.c_int32), ("heads_per_task", C.c_int32)]
 
 
 class amk_cost_model(C.Structure):

@@ -2049,61 +2049,68 @@ __device__ __forceinline__ void argmax_combine(const DevModel &m, const StepArgs
 // e^{m - M} is exactly 0.
 constexpr float kEmptyBlockM = -3.0e38f;
 
-// Batch 1: q of this pass's heads and the K/V row appended at pos, read from the QKV tiles'
-// tagged words and reloaded until every tag matches (this is the wait for those tiles): q, scaled
-// by 1/sqrt(hd), into qs [qn][hd]; the row's bf16 values into kvrow [2][hd]. Returns false after
-// a timeout (recorded) or when the abort word is set.
+// q of heads [h0, h0 + qn) of KV group g (scaled by 1/sqrt(hd)) into qs [qn][hd] and the appended
+// K/V row's bf16 values into kvrow [2][hd], from the QKV tiles' tagged words, reloaded until every
+// tag is current (this is the wait for those tiles). Every query head of the group is polled,
+// whichever heads this pass keeps: the task's declared wait is the QKV tiles of the whole group,
+// and reading all their words keeps that exact. The words go in rounds of V per thread
+// ((qpg + 2) * hd words: one round up to V * kThreads). Returns false after a timeout (recorded)
+// or when the abort word is set.
 __device__ bool attn_stage_tagged(const DevModel &m, const StepArgs &s, int l, int g, int h0,
                                   int qn, float *qs, uint16_t *kvrow, uint32_t task) {
-  constexpr int V = 4;  // words per thread per round: qn * hd + 2 * hd <= 6 * 256 < V * kThreads
-  const int hd = m.hd, nqw = qn * hd, n = nqw + 2 * hd;
+  constexpr int V = 4;
+  const int hd = m.hd, nqw = m.qpg * hd, n = nqw + 2 * hd, q0 = h0 * hd, q1 = (h0 + qn) * hd;
   const uint32_t tag = s.epoch & kTagMask;
-  const uint32_t *qsrc = m.qt + (int64_t)l * m.qd + (int64_t)(g * m.qpg + h0) * hd;
+  const uint32_t *qsrc = m.qt + (int64_t)l * m.qd + (int64_t)g * m.qpg * hd;
   const uint32_t *ksrc = m.kvt + ((int64_t)l * 2 * m.nkv + g) * hd;
   const uint32_t *vsrc = m.kvt + ((int64_t)(l * 2 + 1) * m.nkv + g) * hd;
   uint32_t *const err = m.err;
   const uint64_t tmo = m.timeout_ticks;
-  uint32_t need = 0;
-#pragma unroll
-  for (int j = 0; j < V; ++j)
-    if ((int)threadIdx.x + j * kThreads < n) need |= 1u << j;
   uint64_t t0 = 0;
   uint32_t spins = 0;
-  while (true) {
-    uint32_t w[V];
+  for (int base = 0; base < n; base += V * kThreads) {
+    uint32_t need = 0;
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const int i = (int)threadIdx.x + j * kThreads;
-      if (need & (1u << j))
-        w[j] = cld(i < nqw ? &qsrc[i] : (i < nqw + hd ? &ksrc[i - nqw] : &vsrc[i - nqw - hd]));
-    }
-    int ab = 0;
-    if (threadIdx.x == 0 && (spins == 0 || (spins & 7) == 7)) {
-      ab = flag_load(&err[1]) != 0;
-      if (!ab && spins && wall_clock64() - t0 > tmo) {
-        record_error(err, ERR_TIMEOUT, task, 0xfffffff1u);
-        __hip_atomic_store(gptr(&err[1]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ab = 1;
-      }
-    }
+    for (int j = 0; j < V; ++j)
+      if (base + (int)threadIdx.x + j * kThreads < n) need |= 1u << j;
+    while (true) {
+      uint32_t w[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const int i = (int)threadIdx.x + j * kThreads;
-      if ((need & (1u << j)) && (w[j] & kTagMask) == tag) {
-        need &= ~(1u << j);
-        if (i < nqw)
-          qs[i] = untag(w[j]) * m.attn_scale;
-        else
-          kvrow[i - nqw] = (uint16_t)(w[j] >> 16);
+      for (int j = 0; j < V; ++j) {
+        const int i = base + (int)threadIdx.x + j * kThreads;
+        if (need & (1u << j))
+          w[j] = cld(i < nqw ? &qsrc[i] : (i < nqw + hd ? &ksrc[i - nqw] : &vsrc[i - nqw - hd]));
       }
+      int ab = 0;
+      if (threadIdx.x == 0 && (spins == 0 || (spins & 7) == 7)) {
+        ab = flag_load(&err[1]) != 0;
+        if (!ab && spins && wall_clock64() - t0 > tmo) {
+          record_error(err, ERR_TIMEOUT, task, 0xfffffff1u);
+          __hip_atomic_store(gptr(&err[1]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ab = 1;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const int i = base + (int)threadIdx.x + j * kThreads;
+        if ((need & (1u << j)) && (w[j] & kTagMask) == tag) {
+          need &= ~(1u << j);
+          if (i < nqw) {
+            if (i >= q0 && i < q1) qs[i - q0] = untag(w[j]) * m.attn_scale;
+          } else {
+            kvrow[i - nqw] = (uint16_t)(w[j] >> 16);
+          }
+        }
+      }
+      const int pending = __syncthreads_or(need != 0);
+      if (__syncthreads_or(ab)) return false;
+      if (!pending) break;
+      if (spins == 0) t0 = wall_clock64();
+      ++spins;
+      __builtin_amdgcn_s_sleep(1);
     }
-    const int pending = __syncthreads_or(need != 0);
-    if (__syncthreads_or(ab)) return false;
-    if (!pending) return true;
-    if (spins == 0) t0 = wall_clock64();
-    ++spins;
-    __builtin_amdgcn_s_sleep(1);
   }
+  return true;
 }
 
 // Attention partials of a batched step (batch-2..16 megakernel instances and the operator
@@ -2410,13 +2417,17 @@ __device__ __forceinline__ bool attn_block_seqs(const DevModel &m, const StepArg
   return true;
 }
 
-// Attention tasks always run with kWaves waves (kThreads threads). A group of more query heads than
-// QMAX is processed QMAX heads at a time (the KV block is re-read from cache for each pass).
-// wait_for (megakernel) is waited on inside the first pass, after the KV-history prefetch.
+// Attention tasks always run with kWaves waves (kThreads threads). The task covers query heads
+// [hs, hs + hn) of KV group g (a megakernel task's aux2 / aux3; the whole group when aux3 is 0 and
+// for the operator kernels); more heads than QMAX are processed QMAX heads at a time (the KV block
+// is re-read from cache for each pass). wait_for (megakernel) is waited on inside the first pass,
+// after the KV-history prefetch.
 template <int HD, int QMAX, bool TAGGED>
 __device__ __forceinline__ bool attn_task(const DevModel &m, const StepArgs &s, int l, int g,
                                           int blk, float *lds, float *red, const Task *wait_for,
                                           int *abort_slot) {
+  const int hs = (wait_for && wait_for->aux3) ? (int)wait_for->aux2 : 0;
+  const int hn = (wait_for && wait_for->aux3) ? (int)wait_for->aux3 : m.qpg;
   // the partial waits for the QKV tiles only; a merger's wait for its group's other blocks (the
   // second range) comes in attn_merge
   Task first{};
@@ -2424,10 +2435,10 @@ __device__ __forceinline__ bool attn_task(const DevModel &m, const StepArgs &s, 
     first = *wait_for;
     first.w1_lo = first.w1_hi = 0;
   }
-  for (int h0 = 0; h0 < m.qpg; h0 += QMAX) {
-    const Task *w = (wait_for && (TAGGED || h0 == 0)) ? &first : nullptr;
+  for (int h0 = hs; h0 < hs + hn; h0 += QMAX) {
+    const Task *w = (wait_for && (TAGGED || h0 == hs)) ? &first : nullptr;
     {
-      if (!attn_block_seqs<HD, QMAX, TAGGED>(m, s, l, g, blk, h0, min(QMAX, m.qpg - h0), lds, red, w,
+      if (!attn_block_seqs<HD, QMAX, TAGGED>(m, s, l, g, blk, h0, min(QMAX, hs + hn - h0), lds, red, w,
                                      abort_slot))
         return false;
     }
@@ -2455,7 +2466,9 @@ __device__ __forceinline__ bool attn_merge(const DevModel &m, const StepArgs &s,
   __syncthreads();
   constexpr int KB = 8;
   const int hd = m.hd, nblk = m.nblk, qpg = m.qpg, nq = m.nq;
-  const int per_b = qpg * hd, total = s.batch * per_b;
+  // the task's query heads [hs, hs + hn) of the group (the whole group when aux3 is 0)
+  const int hs = t.aux3 ? (int)t.aux2 : 0, hn = t.aux3 ? (int)t.aux3 : qpg;
+  const int per_b = hn * hd, total = s.batch * per_b;
   const uint32_t tag = s.epoch & kTagMask;
   uint32_t *const err = m.err;
   const uint64_t tmo = m.timeout_ticks;
@@ -2467,7 +2480,7 @@ __device__ __forceinline__ bool attn_merge(const DevModel &m, const StepArgs &s,
     int it = 0;
     for (int i = threadIdx.x; i < total; i += kThreads, ++it) {
       if (TAGGED && (done & (1u << it))) continue;  // TAGGED: at most 8 elements per thread
-      const int b = i / per_b, r = i - b * per_b, h = g * qpg + r / hd, e = r % hd;
+      const int b = i / per_b, r = i - b * per_b, h = g * qpg + hs + r / hd, e = r % hd;
       const uint32_t *ph = reinterpret_cast<const uint32_t *>(m.part) +
                            (((int64_t)l * m.max_batch + b) * nq + h) * nblk * (hd + 2);
       float M = kEmptyBlockM, den = 0.f, num = 0.f;

@@ -767,8 +767,14 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     hip_check(hipStreamSynchronize(st), "hipStreamSynchronize");
     upload_dm(m);
 
+    // the megakernel instance fits the schedule's attention tasks (a task may cover only some of
+    // its group's query heads); the operator kernels take whole groups
     const int qmax = qmax_for(dm.qpg);
-    m->mk = pick_megakernel(cfg->wtype, hd, qmax, B > 1);
+    int task_heads = 1;
+    for (const auto &v : m->sched.per_cu)
+      for (const Task &t : v)
+        if (t.type == T_ATTN) task_heads = std::max(task_heads, t.aux3 ? (int)t.aux3 : dm.qpg);
+    m->mk = pick_megakernel(cfg->wtype, hd, qmax_for(task_heads), B > 1);
     m->uf_attn = pick_uf_attn(hd, qmax);
     if (!m->mk || !m->uf_attn) throw std::runtime_error("no kernel instance for this shape");
     // the operator kernels may run prompt chunks of kMaxBatch columns

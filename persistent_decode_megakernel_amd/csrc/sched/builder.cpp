@@ -173,18 +173,33 @@ struct Builder {
       uint32_t by_ctx = std::max<uint32_t>(1, ctx_hint / min_block);
       nblk = std::min(by_cu, by_ctx);
     }
+    // query heads per attention task: the group's heads split into `ranges` tasks per KV block
+    const uint32_t qpg = nq / nkv;
+    uint32_t hp = qpg;
+    if (p.heads_per_task > 0 && qpg % (uint32_t)p.heads_per_task == 0) {
+      hp = (uint32_t)p.heads_per_task;
+    } else if (p.heads_per_task == 0 && c.max_batch == 1) {
+      for (uint32_t r = qpg; r >= 1; --r)
+        if (qpg % r == 0 && nkv * r * nblk <= 2 * n_cu) {
+          hp = qpg / r;
+          break;
+        }
+    }
+    const uint32_t ranges = qpg / hp;
     s.per_cu.assign(n_cu, {});
     uint32_t d_lo = 0, d_hi = 0;  // tasks producing the residual entering the layer
     for (uint32_t l = 0; l < L; ++l) {
       Tiling qt;
       auto qkv = gemv(M_QKV, (uint16_t)l, qkvr, d, wb, d_lo, d_hi, &qt);
-      // attention: one task per (kv group, KV block); waits on the QKV tiles of its group. The
-      // group's last block also merges the group's partials and so waits on the other blocks too.
-      // Mergers are numbered after all other blocks of the layer, so the O tiles wait on the id
-      // range of the mergers and each merger on the id range of its group's other blocks.
+      // attention: one task per (kv group, range of its query heads, KV block); waits on the QKV
+      // tiles of its whole group (it reads every q word of the group). The range's last block
+      // also merges the range's partials and so waits on the range's other blocks too. Mergers
+      // are numbered after all other blocks of the layer, so the O tiles wait on the id range of
+      // the mergers and each merger on the id range of its head range's other blocks.
       const uint32_t a_first = next_id;
-      const uint32_t n_attn = nkv * nblk;
-      const uint32_t m_first = a_first + nkv * (nblk - 1);
+      const uint32_t n_rng = nkv * ranges;
+      const uint32_t n_attn = n_rng * nblk;
+      const uint32_t m_first = a_first + n_rng * (nblk - 1);
       for (uint32_t g = 0; g < nkv; ++g) {
         uint32_t r0 = g * grows, r1 = (g + 1) * grows;
         uint32_t lo = qkv.second, hi = qkv.first;
@@ -194,23 +209,28 @@ struct Builder {
             hi = std::max(hi, qkv.first + i + 1);
           }
         }
-        for (uint32_t b = 0; b < nblk; ++b) {
-          const bool merger = b + 1 == nblk;
-          Task k{};
-          k.type = T_ATTN;
-          k.layer = (uint16_t)l;
-          k.id = merger ? m_first + g : a_first + g * (nblk - 1) + b;
-          k.a0 = g;
-          k.a1 = b;
-          k.w0_lo = lo;
-          k.w0_hi = hi;
-          if (merger) {
-            k.w1_lo = a_first + g * (nblk - 1);
-            k.w1_hi = k.w1_lo + (nblk - 1);
+        for (uint32_t hr = 0; hr < ranges; ++hr) {
+          const uint32_t rg = g * ranges + hr;  // this head range's index in the layer
+          for (uint32_t b = 0; b < nblk; ++b) {
+            const bool merger = b + 1 == nblk;
+            Task k{};
+            k.type = T_ATTN;
+            k.layer = (uint16_t)l;
+            k.id = merger ? m_first + rg : a_first + rg * (nblk - 1) + b;
+            k.a0 = g;
+            k.a1 = b;
+            k.w0_lo = lo;
+            k.w0_hi = hi;
+            if (merger) {
+              k.w1_lo = a_first + rg * (nblk - 1);
+              k.w1_hi = k.w1_lo + (nblk - 1);
+            }
+            k.aux0 = nblk;
+            k.aux1 = merger ? 1u : 0u;
+            k.aux2 = hr * hp;  // first query head of the range within the group
+            k.aux3 = hp;       // heads in the range
+            s.per_cu[place(rg * nblk + b, n_attn)].push_back(k);
           }
-          k.aux0 = nblk;
-          k.aux1 = merger ? 1u : 0u;
-          s.per_cu[place(g * nblk + b, n_attn)].push_back(k);
         }
       }
       next_id = a_first + n_attn;
@@ -280,9 +300,10 @@ void task_bytes(const BlobHeader &h, const Task &t, int32_t ctx, double *hbm, do
     int32_t lo, hi;
     attn_block_range(ctx, (int32_t)h.attn_blocks, (int32_t)t.a1, &lo, &hi);
     *hbm = B * 2.0 * (double)(hi - lo) * c.head_dim * 2.0;
-    // q, plus (once per group, by the merger) the group's partials
+    // q of the group, plus (by the merger) the partials of its head range
     const double qpg = c.n_heads / c.n_kv_heads;
-    *act = B * qpg * c.head_dim * 4.0 + B * qpg * (c.head_dim + 2) * 4.0;
+    const double hn = t.aux3 ? (double)t.aux3 : qpg;
+    *act = B * qpg * c.head_dim * 4.0 + B * hn * (c.head_dim + 2) * 4.0;
   } else if (t.type == T_ARGMAX) {
     *act = (double)t.aux0 * B * 8.0;
   }

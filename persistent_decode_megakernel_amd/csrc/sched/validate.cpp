@@ -148,7 +148,10 @@ bool footprint(const BlobHeader &h, const Task &t, std::vector<Access> *acc, std
     if (l >= L) return bad("layer out of range");
     if (g >= nkv) return bad("kv group out of range");
     if (blk >= nblk || t.aux0 != h.attn_blocks) return bad("KV block out of range");
-    // the group's last block merges the group's partials (and only it)
+    // query heads [hs, hs + hn) of the group (aux3 = 0: the whole group)
+    const int64_t hs = t.aux3 ? (int64_t)t.aux2 : 0, hn = t.aux3 ? (int64_t)t.aux3 : qpg;
+    if (hn < 1 || hs < 0 || hs + hn > qpg) return bad("query head range outside the KV group");
+    // the range's last block merges the range's partials (and only it)
     const bool merger = blk == nblk - 1;
     if (t.aux1 != (merger ? 1u : 0u)) return bad("the merger must be the group's last KV block");
     for (int64_t b = 0; b < B; ++b) {
@@ -157,19 +160,20 @@ bool footprint(const BlobHeader &h, const Task &t, std::vector<Access> *acc, std
         int64_t base = ((kvi * B + b) * nkv + g) * hd;
         add_range(acc, BUF_KVNEW, (int)l, base, base + hd, false, true);
       }
-      for (int64_t hh = g * qpg; hh < (g + 1) * qpg; ++hh) {
+      for (int64_t hh = g * qpg + hs; hh < g * qpg + hs + hn; ++hh) {
         int64_t base = ((b * nq + hh) * nblk + blk) * (hd + 2);
         add_range(acc, BUF_PART, (int)l, base, base + hd + 2, true);
       }
     }
     if (merger) {
-      // every other block's partials in (its own it reads back after its stores), merged heads out
+      // every other block's partials of the range in (its own it reads back after its stores),
+      // the range's merged heads out
       for (int64_t b = 0; b < B; ++b) {
-        for (int64_t hh = g * qpg; hh < (g + 1) * qpg; ++hh) {
+        for (int64_t hh = g * qpg + hs; hh < g * qpg + hs + hn; ++hh) {
           int64_t base = (b * nq + hh) * nblk * (hd + 2);
           add_range(acc, BUF_PART, (int)l, base, base + blk * (hd + 2), false, true);
         }
-        add_range(acc, BUF_AO, (int)l, b * qd + g * qpg * hd, b * qd + (g + 1) * qpg * hd, true);
+        add_range(acc, BUF_AO, (int)l, b * qd + (g * qpg + hs) * hd, b * qd + (g * qpg + hs + hn) * hd, true);
       }
     }
     return true;

@@ -205,15 +205,22 @@ def _attn(b: B.Blob, layer: int):
     return o, mergers, others
 
 
+def _ranges(b: B.Blob, cfg):
+    """head ranges per KV group of a schedule's attention tasks"""
+    hp = {int(t["aux3"]) for v in b.per_cu for t in v if t["type"] == B.T_ATTN}
+    assert len(hp) == 1
+    return (cfg.n_heads // cfg.n_kv_heads) // hp.pop()
+
+
 @pytest.mark.parametrize("drop", ["first", "last"])
 def test_o_tile_must_wait_for_every_merger(libamk, drop):
-    """Each KV group's last block merges the group's partials into the attention output, so an
-    O-projection tile that skips any one merger may read an unmerged output: the validator
-    rejects it and the delayed-CU simulation shows the stale read."""
+    """The last block of each (KV group, query-head range) merges the range's partials into the
+    attention output, so an O-projection tile that skips any one merger may read an unmerged
+    output: the validator rejects it and the delayed-CU simulation shows the stale read."""
     cfg = synth.get_config("tiny")
     b = B.Blob(_lib.schedule_build(_lib.make_config(cfg), 1, 8, FOUR_BLOCKS()))
     o, mergers, others = _attn(b, 1)
-    assert len(mergers) == cfg.n_kv_heads and mergers[0] > max(others)
+    assert len(mergers) == cfg.n_kv_heads * _ranges(b, cfg) and mergers[0] > max(others)
     dropped = mergers[0] if drop == "first" else mergers[-1]
     cu_of = {int(t["id"]): c for c in range(len(b.per_cu)) for t in b.per_cu[c]}
     c, j = next((c, j) for c, j in o if c != cu_of[dropped])
@@ -229,17 +236,25 @@ def test_o_tile_must_wait_for_every_merger(libamk, drop):
     assert _lib.schedule_simulate(data)[0] != _lib.AMK_OK
 
 
-def test_merger_must_wait_for_every_block_of_its_group(libamk):
+@pytest.mark.parametrize("max_batch", [1, 2])
+def test_merger_must_wait_for_every_block_of_its_group(libamk, max_batch):
+    """A merger that skips its range's last sibling. Batched (flag waits): the race is real,
+    the validator reports it and the delayed-CU simulation shows the stale read. Batch 1: the
+    declared waits no longer equal the writers of the merger's tagged inputs, rejected."""
     cfg = synth.get_config("tiny")
-    b = B.Blob(_lib.schedule_build(_lib.make_config(cfg), 1, 8, FOUR_BLOCKS()))
+    b = B.Blob(_lib.schedule_build(_lib.make_config(cfg, max_batch=max_batch), 1, 8, FOUR_BLOCKS()))
     o, mergers, others = _attn(b, 0)
     t = next(t for v in b.per_cu for t in v if int(t["id"]) == mergers[0])
     assert int(t["w1_hi"]) - int(t["w1_lo"]) == b.hdr.attn_blocks - 1 > 0
     t["w1_hi"] = int(t["w1_hi"]) - 1
     data = b.to_bytes()
     st, rep = _lib.schedule_validate(data)
-    assert st == _lib.AMK_E_SCHEDULE_REJECTED and "race" in rep, rep
-    assert _lib.schedule_simulate(data)[0] != _lib.AMK_OK
+    assert st == _lib.AMK_E_SCHEDULE_REJECTED, rep
+    if max_batch == 1:
+        assert "writers" in rep or "race" in rep, rep
+    else:
+        assert "race" in rep, rep
+        assert _lib.schedule_simulate(data)[0] != _lib.AMK_OK
 
 
 def test_merger_must_be_the_groups_last_block(libamk):
@@ -406,3 +421,59 @@ def test_batch1_tiles_keep_row_pairs_only(libamk):
     v[i + 1]["a0"] = int(v[i + 1]["a0"]) - 1
     st, rep = _lib.schedule_validate(b.to_bytes())
     assert st == _lib.AMK_E_SCHEDULE_REJECTED and "row pair" in rep, rep
+
+
+@pytest.mark.parametrize("name,hp,ranges", [("tiny", 0, None), ("tiny", 2, 1), ("tiny", 1, 2),
+                                            ("tiny", 3, 1), ("smollm2_135m", 0, None),
+                                            ("tinyllama_1b", 0, None), ("tinyllama_1b", 2, 4),
+                                            ("tinyllama_1b", 8, 1), ("llama2_7b", 0, 1)])
+def test_query_head_ranges(libamk, name, hp, ranges):
+    """Attention tasks cover a range of their group's query heads (aux2 = first head, aux3 =
+    heads). Batch 1 splits a group so that up to two attention tasks run per CU unless told
+    otherwise; a heads_per_task that does not divide the group's heads keeps whole groups. Each
+    (group, range) has its own blocks and merger, every block waits on the QKV tiles of its whole
+    group, the O tiles wait on all mergers; the schedule validates and simulates clean."""
+    cfg = synth.get_config(name)
+    qpg = cfg.n_heads // cfg.n_kv_heads
+    p = _lib.amk_sched_params(search=0, heads_per_task=hp)
+    b = B.Blob(_lib.schedule_build(_lib.make_config(cfg, max_seq=cfg.prefill + 8), 1, 256, p))
+    data = b.to_bytes()
+    assert _lib.schedule_validate(data)[0] == _lib.AMK_OK
+    assert _lib.schedule_simulate(data)[0] == _lib.AMK_OK
+    nblk = int(b.hdr.attn_blocks)
+    if ranges is None:  # auto: the most ranges (a divisor of the group's heads) within 2 tasks per CU
+        ranges = max(r for r in range(1, qpg + 1) if qpg % r == 0 and cfg.n_kv_heads * r * nblk <= 512)
+    assert _ranges(b, cfg) == ranges
+    attn = [t for v in b.per_cu for t in v if t["type"] == B.T_ATTN and t["layer"] == 0]
+    assert len(attn) == cfg.n_kv_heads * ranges * nblk
+    heads = {}
+    for t in attn:
+        heads.setdefault((int(t["a0"]), int(t["a1"])), []).append((int(t["aux2"]), int(t["aux3"])))
+    for key, rs in heads.items():  # the ranges of a (group, block) tile the group's heads
+        covered = sorted(h for h0, n in rs for h in range(h0, h0 + n))
+        assert covered == list(range(qpg)), (key, rs)
+    mergers = [t for t in attn if t["aux1"]]
+    assert len(mergers) == cfg.n_kv_heads * ranges
+    assert all(int(t["a1"]) == nblk - 1 for t in mergers)
+
+
+def test_head_range_outside_the_group_is_rejected(libamk):
+    cfg = synth.get_config("tinyllama_1b")
+    b = B.Blob(_lib.schedule_build(_lib.make_config(cfg, max_seq=cfg.prefill + 8), 1, 256,
+                                   _lib.amk_sched_params(search=0)))
+    t = next(t for v in b.per_cu for t in v if t["type"] == B.T_ATTN)
+    t["aux2"] = 8 - int(t["aux3"]) + 1
+    st, rep = _lib.schedule_validate(b.to_bytes())
+    assert st == _lib.AMK_E_SCHEDULE_REJECTED and "head range" in rep, rep
+
+
+def test_overlapping_head_ranges_are_rejected(libamk):
+    """Two blocks writing the same head's partial: the single-writer rule catches it."""
+    cfg = synth.get_config("tinyllama_1b")
+    b = B.Blob(_lib.schedule_build(_lib.make_config(cfg, max_seq=cfg.prefill + 8), 1, 256,
+                                   _lib.amk_sched_params(search=0)))
+    t = next(t for v in b.per_cu for t in v if t["type"] == B.T_ATTN and int(t["aux2"]) > 0
+             and not t["aux1"])
+    t["aux2"] = int(t["aux2"]) - 1
+    st, rep = _lib.schedule_validate(b.to_bytes())
+    assert st == _lib.AMK_E_SCHEDULE_REJECTED, rep

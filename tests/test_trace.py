@@ -32,8 +32,10 @@ def test_summary_accounts_for_every_task(libamk, monkeypatch, name, batch):
     assert len(ph) == 5 * cfg.n_layers + 2
     assert sum(p["tasks"] for p in ph.values()) == b.hdr.n_tasks
     nblk = int(b.hdr.attn_blocks)
+    qpg = cfg.n_heads // cfg.n_kv_heads
+    ranges = {qpg // int(t["aux3"]) for v in b.per_cu for t in v if t["type"] == 2}.pop()
     for l in range(cfg.n_layers):
-        assert ph[f"{l}:attn"]["tasks"] == cfg.n_kv_heads * nblk
+        assert ph[f"{l}:attn"]["tasks"] == cfg.n_kv_heads * ranges * nblk
         # every phase of a layer starts no earlier than the previous phase's first task starts
         assert ph[f"{l}:o"]["last_end_us"] > ph[f"{l}:attn"]["first_start_us"]
     assert ph[f"{10 ** 6}:argmax"]["tasks"] == 1
