@@ -255,11 +255,11 @@ def cpu_baseline(cfg, weights, kv_host, sample_steps, threads=16):
     }
 
 
-def kernel_name(cfg):
-    qpg = cfg.n_heads // cfg.n_kv_heads
-    hd_q = 1 if qpg <= 1 else (2 if qpg <= 2 else 4)
+def kernel_name(cfg, info):
+    """the megakernel instance the model runs (query heads per attention pass from the library)"""
     wt = {"bf16": 0, "int8": 1, "int4": 2}[cfg.wtype]
-    return f"amk_megakernel_w{wt}_h{cfg.head_dim}_q{hd_q}" + ("_b" if cfg.batch > 1 else "")
+    return (f"amk_megakernel_w{wt}_h{cfg.head_dim}_q{info.heads_per_pass}"
+            + ("_b" if cfg.batch > 1 else ""))
 
 
 def measure(cfg, weights, kv_host, steps, warmup, ablation=True, graph_ablation=False,
@@ -269,7 +269,7 @@ def measure(cfg, weights, kv_host, steps, warmup, ablation=True, graph_ablation=
     from events on the launch stream; and, optionally, the unfused ablation on the same inputs."""
     ms, per, info, ids = time_path(cfg, weights, kv_host, "megakernel", steps, warmup,
                                    cold_mib=cold_mib)
-    kname = kernel_name(cfg)
+    kname = kernel_name(cfg, info)
     traffic_bytes = profiled_traffic(profile_key or f"{cfg.name}_b{cfg.batch}", kname)
     weight_bytes = info.weight_bytes + 2 * cfg.hidden * cfg.batch  # + embedding rows
     ctxs = [cfg.prefill + i + 1 for i in range(steps)]

@@ -124,6 +124,9 @@ typedef struct {
   double predicted_us;       /* cost-model makespan of the frozen schedule at ctx_hint */
   uint64_t scratch_bytes;    /* device scratch of one decode step: flags, step counter, activation
                               * slots, attention partials, logits (one block, owned by the model) */
+  int32_t heads_per_pass;    /* query heads one attention pass of the model's kernels processes:
+                              * the megakernel instance fitted to the schedule's head ranges, or
+                              * the operator kernels' whole-group passes */
 } amk_model_info;
 
 typedef struct amk_model amk_model;

@@ -67,7 +67,7 @@ class amk_model_info(C.Structure):
     _fields_ = [("n_cu", C.c_int32), ("n_tasks", C.c_int32), ("launches_per_step", C.c_int32),
                 ("lds_bytes", C.c_int32), ("attn_blocks", C.c_int32), ("path", C.c_int32),
                 ("weight_bytes", C.c_uint64), ("predicted_us", C.c_double),
-                ("scratch_bytes", C.c_uint64)]
+                ("scratch_bytes", C.c_uint64), ("heads_per_pass", C.c_int32)]
 
 
 # name -> (restype, argtypes); every symbol include/amk.h declares

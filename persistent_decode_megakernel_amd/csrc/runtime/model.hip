@@ -163,6 +163,16 @@ UgFn pick_uf_gemv(int wt, int mode) {
 
 int qmax_for(int qpg) { return attn_qmax(qpg); }
 
+// Query heads per pass of the megakernel instance that fits a schedule's attention tasks (a task
+// may cover only some of its group's query heads, aux2 / aux3).
+int mk_qmax_for(const Schedule &s, int qpg) {
+  int task_heads = 1;
+  for (const auto &v : s.per_cu)
+    for (const Task &t : v)
+      if (t.type == T_ATTN) task_heads = std::max(task_heads, t.aux3 ? (int)t.aux3 : qpg);
+  return qmax_for(task_heads);
+}
+
 // The per-step scratch of a model as one block of device memory. It opens with the state region,
 // which must hold zeros before a model's first step (and again after a reset or a schedule
 // change): the epoch counter, the dependency flags and the tagged activation slots of batch-1
@@ -353,6 +363,7 @@ struct amk_model {
   uint64_t weight_bytes = 0;
   int n_lm_uf = 0;
   MkFn mk = nullptr;
+  int mk_qmax = 0;  // query heads per attention pass of the megakernel instance
   UaFn uf_attn = nullptr;
   uint32_t *h_err = nullptr;  // pinned copy of the device error words
   hipEvent_t err_event = nullptr;
@@ -770,11 +781,8 @@ extern "C" amk_status amk_model_create(const amk_config *cfg, const amk_weights 
     // the megakernel instance fits the schedule's attention tasks (a task may cover only some of
     // its group's query heads); the operator kernels take whole groups
     const int qmax = qmax_for(dm.qpg);
-    int task_heads = 1;
-    for (const auto &v : m->sched.per_cu)
-      for (const Task &t : v)
-        if (t.type == T_ATTN) task_heads = std::max(task_heads, t.aux3 ? (int)t.aux3 : dm.qpg);
-    m->mk = pick_megakernel(cfg->wtype, hd, qmax_for(task_heads), B > 1);
+    m->mk_qmax = mk_qmax_for(m->sched, dm.qpg);
+    m->mk = pick_megakernel(cfg->wtype, hd, m->mk_qmax, B > 1);
     m->uf_attn = pick_uf_attn(hd, qmax);
     if (!m->mk || !m->uf_attn) throw std::runtime_error("no kernel instance for this shape");
     // the operator kernels may run prompt chunks of kMaxBatch columns
@@ -1168,6 +1176,7 @@ extern "C" amk_status amk_model_get_info(const amk_model *m, amk_model_info *out
   out->weight_bytes = m->weight_bytes;
   out->predicted_us = m->sched.hdr.predicted_us;
   out->scratch_bytes = m->plan.total;
+  out->heads_per_pass = m->path == AMK_PATH_MEGAKERNEL ? m->mk_qmax : qmax_for(m->dm.qpg);
   return AMK_OK;
 }
 
@@ -1205,11 +1214,14 @@ amk_status install_schedule(amk_model *m, Schedule &&s, std::vector<uint8_t> &&b
     for (const Task &t : s.per_cu[cu]) tasks.push_back(t);
   }
   offs[h.n_cu] = (uint32_t)tasks.size();
-  if (h.lds_bytes != m->lds_bytes) {
-    hip_check(hipFuncSetAttribute((const void *)m->mk, hipFuncAttributeMaxDynamicSharedMemorySize,
+  const int qmax = mk_qmax_for(s, m->dm.qpg);
+  const MkFn mk = pick_megakernel(m->cfg.wtype, m->dm.hd, qmax, m->cfg.max_batch > 1);
+  if (!mk) return set_error(AMK_E_UNSUPPORTED, "no megakernel instance for this schedule");
+  if (h.lds_bytes != m->lds_bytes || mk != m->mk) {
+    hip_check(hipFuncSetAttribute((const void *)mk, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)h.lds_bytes), "hipFuncSetAttribute");
     int per_cu = 0;
-    hip_check(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)m->mk, kThreads,
+    hip_check(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)mk, kThreads,
                                                            h.lds_bytes), "occupancy");
     if (per_cu < 1) return set_error(AMK_E_SCHEDULE_REJECTED, "schedule LDS does not fit on a CU");
   }
@@ -1220,6 +1232,8 @@ amk_status install_schedule(amk_model *m, Schedule &&s, std::vector<uint8_t> &&b
   zero_state(m, st);
   hip_check(hipStreamSynchronize(st), "hipStreamSynchronize");
   m->lds_bytes = h.lds_bytes;
+  m->mk = mk;
+  m->mk_qmax = qmax;
   m->sched = std::move(s);
   m->blob = std::move(blob);
   m->dm.argmax_id = argmax_of(m->sched);
