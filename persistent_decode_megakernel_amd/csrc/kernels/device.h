@@ -2113,7 +2113,7 @@ __device__ bool attn_stage_tagged(const DevModel &m, const StepArgs &s, int l, i
   return true;
 }
 
-// Attention partials of a batched step (batch-2..16 megakernel instances and the operator
+// Attention partials, on every path (batch-1 and batched megakernel instances, the operator
 // kernels): heads [h0, h0 + qn) of KV group g, KV block blk, for every sequence of the step.
 // Each wave streams its own rows, like a GEMV tile: sequence b's block is cut into chunks of
 // kWaves * U * RPW rows, wave w takes U * RPW consecutive rows of each chunk, and the wave walks
@@ -2126,7 +2126,10 @@ __device__ bool attn_stage_tagged(const DevModel &m, const StepArgs &s, int l, i
 // first chunk is issued before it. Partials stay in LDS until every sequence is done and then
 // go out in one burst (a store in the loop would hold up the next chunk's wait: vector loads and
 // stores complete under one counter). wait_for (batched megakernel): the QKV tiles' flags,
-// polled by wave 0. LDS: q [B][qn][HD] | appended rows [B][2][HD] bf16 | partials
+// polled by wave 0. TAGGED (batch 1, one sequence): q and the appended row are read from the QKV
+// tiles' tagged words (attn_stage_tagged, which is also the wait), the first chunk is issued
+// before and the second after that staging, and the partial goes out as tagged words straight
+// from the merge over waves. LDS: q [B][qn][HD] | appended rows [B][2][HD] bf16 | partials
 // [B][qn][HD + 2] | wave partials [2][NW][qn][HD + 2].
 template <int HD, int QMAX, bool TAGGED>
 __device__ __forceinline__ bool attn_block_seqs(const DevModel &m, const StepArgs &s, int l,
@@ -2137,10 +2140,12 @@ __device__ __forceinline__ bool attn_block_seqs(const DevModel &m, const StepArg
   constexpr int NW = kWaves;
   constexpr int LPR = HD / 8;       // lanes per row (8 bf16 each)
   constexpr int RPW = 64 / LPR;     // row slots of a wave
-  constexpr int U = kAttnSeqIters;  // loads of K (and of V) per chunk
+  // loads of K (and of V) per chunk: more for one-head batch-1 passes (their registers allow it)
+  constexpr bool LONG = TAGGED && QMAX == 1;
+  constexpr int U = LONG ? kAttnSeqItersB1 : kAttnSeqIters;
   constexpr int CR = U * RPW;       // rows of a wave's chunk
   constexpr int WR = NW * CR;       // rows of a workgroup chunk
-  static_assert(WR == attn_seq_chunk_rows(HD), "chunk rows");
+  static_assert(WR == attn_seq_chunk_rows(HD, LONG), "chunk rows");
   const int B = s.batch, nblk = m.nblk, nq = m.nq;
   if (B <= 0) return true;
   const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(wave_id());

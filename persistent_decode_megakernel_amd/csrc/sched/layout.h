@@ -154,7 +154,11 @@ AMK_HD constexpr int32_t attn_rows_per_iter(int32_t hd) { return 8 * (64 / (hd /
 // Attention blocks stream each wave's own KV rows in chunks of kAttnSeqIters loads of K (and of V)
 // per lane, two chunks in flight per wave; a workgroup chunk is this many rows.
 constexpr int32_t kAttnSeqIters = 4;
-AMK_HD constexpr int32_t attn_seq_chunk_rows(int32_t hd) { return attn_rows_per_iter(hd) * kAttnSeqIters; }
+// one-head batch-1 passes: longer chunks (the first is issued before the staging wait)
+constexpr int32_t kAttnSeqItersB1 = 6;
+AMK_HD constexpr int32_t attn_seq_chunk_rows(int32_t hd, bool b1_one_head = false) {
+  return attn_rows_per_iter(hd) * (b1_one_head ? kAttnSeqItersB1 : kAttnSeqIters);
+}
 constexpr int32_t kRedFloats = 2048;        // reduction scratch; holds n_heads x blocks weights
 // Batch-1 int8 GEMV: the staged input is converted in place to integer digits, holding every
 // thread's share in registers; that bounds the input length of an int8 matrix.
