@@ -103,10 +103,12 @@ __device__ __forceinline__ bool gemv_b1_q(const DevModel &m, const StepArgs &s, 
 // words, which is also the dependency wait (int8, int4: gemv_b1_q). Batched: a flag wait (wave 0 polls), then the matrix-core GEMV reads its inputs
 // straight from memory. The RMSNorm scale is applied to the outputs and the epilogue writes them
 // (tagged for batch 1).
+// pre0 (batch-1 bf16): the previous task on this CU already issued chunk 0 of every wave into
+// its LDS slot (gemv_issue_chunk0).
 template <int WT, bool BATCHED>
 __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, const Task &t,
                                           float *xs, float *ys, float *red, uint4 *pf,
-                                          int *abort_slot) {
+                                          int *abort_slot, bool pre0 = false) {
   constexpr int NW = kWaves;
   const int l = t.layer;
   const void *W;
@@ -130,7 +132,7 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
       // the first layer's QKV tiles read the token: in a later step of a multi-step launch they
       // wait for the previous step's argmax (which every task of that step precedes)
       if (!tagged) wait_poll(m, s.step > 0 ? prev_step(m, t) : t, s.epoch - (s.step > 0), abort_slot);
-      if (st.S > 0) st.load_lds(0, slot);
+      if (st.S > 0 && !pre0) st.load_lds(0, slot);
       if (st.S > 1) st.load(P, 1);
       // keep the register prefetch issued here, ahead of the staging loads, not at its first use
       asm volatile("" ::: "memory");
@@ -226,6 +228,27 @@ __device__ __forceinline__ bool gemv_task(const DevModel &m, const StepArgs &s, 
   return true;
 }
 
+// Chunk 0 of every wave of batch-1 bf16 GEMV task t into its LDS slot, issued by the task before
+// it on this CU once that task has no loads left to wait for (an attention block after its
+// partial, a merger after its merge): the copy then overlaps the end of that task instead of
+// following it, and gemv_task (pre0) issues the rest. Returns whether it issued.
+template <int WT, bool BATCHED>
+__device__ __forceinline__ bool gemv_issue_chunk0(const DevModel &m, const Task &t, uint4 *pf) {
+  if constexpr (WT != 0 || BATCHED) {
+    return false;
+  } else {
+    if (t.type != T_GEMV) return false;
+    const void *W;
+    const float *scale;
+    int K, wtype;
+    gemv_matrix(m, t.mat, t.layer, &W, &scale, &K, &wtype);
+    GemvStream<0> st;
+    st.init(W, K, (int)t.a0, (int)t.a1, kWaves);
+    if (st.S > 0) st.load_lds(0, pf + st.wave * (64 * kChunkUnits));
+    return true;
+  }
+}
+
 // Whether a finished task's consumers learn of it from its flag. In batch-1 instances only the LM
 // tiles (for the argmax) and the argmax do: every other task publishes tagged data (QKV: q and the
 // appended K/V row; attention blocks: partials and the merged output; O, gate/up, down: their
@@ -269,16 +292,20 @@ __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArg
     if (step > 0) s.tokens = s0.next + (int64_t)(step - 1) * s0.batch;
     s.next = s0.next + (int64_t)step * s0.batch;
     if (s0.logits) s.logits = s0.logits + (int64_t)step * s0.batch * m.V;
+    bool pre0 = false;  // the current task's chunk 0 was issued by the task before it
     for (uint32_t ti = t0; ti < t1; ++ti) {
       const Task t = load_task(&m.tasks[ti]);
       if (trace && threadIdx.x == 0) gst(&trace[(uint64_t)t.id * 4 + 0], (uint64_t)wall_clock64());
       bool ok;
       if (t.type == T_GEMV) {
-        ok = gemv_task<WT, BATCHED>(m, s, t, xs, ys, red, pf, &abort_flag);
+        ok = gemv_task<WT, BATCHED>(m, s, t, xs, ys, red, pf, &abort_flag, pre0);
+        pre0 = false;
       } else if (t.type == T_ATTN) {
         ok = attn_task<HD, QMAX, !BATCHED>(m, s, t.layer, (int)t.a0, (int)t.a1, xs, red, &t, &abort_flag);
         if (trace && threadIdx.x == 0) gst(&trace[(uint64_t)t.id * 4 + 2], (uint64_t)wall_clock64());
         if (ok && t.aux1) ok = attn_merge<!BATCHED>(m, s, t, &abort_flag);
+        // the next task's first weight chunk, into the GEMV prefetch slots (unused by attention)
+        if (ok && ti + 1 < t1) pre0 = gemv_issue_chunk0<WT, BATCHED>(m, load_task(&m.tasks[ti + 1]), pf);
       } else {
         ok = wait_task(m, t, s.epoch, &abort_flag);
         if (ok) argmax_combine(m, s, (int)t.aux0);
