@@ -313,7 +313,11 @@ __device__ __forceinline__ void megakernel_body(const DevModel &m, const StepArg
         if (ok && step == s0.n_steps - 1 && threadIdx.x == 0)
           __hip_atomic_store(gptr(m.ectr), s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      if (!ok) return;
+      // a failed task leaves no copy into LDS in flight when the workgroup ends
+      if (!ok) {
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+      }
       // Publish: every wave waits for its own (device-coherent) stores to complete, the workgroup
       // meets, then one thread stores the flag. Data that crosses CUs is written with device-scope
       // stores, so no L2 writeback is needed before the flag.
