@@ -1665,10 +1665,12 @@ __device__ __forceinline__ void ring_dispatch(const MfmaTile &T, RingLanes &L, i
   if (T.gain) {
     if (gn <= 1) mfma_ring_pass<WT, 1, true, WIDE>(T, L, g0, gn, sq, ss, acc, prefetched);
     else if (gn == 2) mfma_ring_pass<WT, 2, true, WIDE>(T, L, g0, gn, sq, ss, acc, prefetched);
+    else if (gn == 3) mfma_ring_pass<WT, 3, true, WIDE>(T, L, g0, gn, sq, ss, acc, prefetched);
     else mfma_ring_pass<WT, 4, true, WIDE>(T, L, g0, gn, sq, ss, acc, prefetched);
   } else {
     if (gn <= 1) mfma_ring_pass<WT, 1, false, WIDE>(T, L, g0, gn, sq, ss, acc, prefetched);
     else if (gn == 2) mfma_ring_pass<WT, 2, false, WIDE>(T, L, g0, gn, sq, ss, acc, prefetched);
+    else if (gn == 3) mfma_ring_pass<WT, 3, false, WIDE>(T, L, g0, gn, sq, ss, acc, prefetched);
     else mfma_ring_pass<WT, 4, false, WIDE>(T, L, g0, gn, sq, ss, acc, prefetched);
   }
 }
@@ -1678,12 +1680,23 @@ __device__ __forceinline__ void ring_prefetch_dispatch(const MfmaTile &T, RingLa
   if (T.gain) {
     if (gn <= 1) ring_prefetch<WT, 1, true, WIDE>(T, L, g0, gn);
     else if (gn == 2) ring_prefetch<WT, 2, true, WIDE>(T, L, g0, gn);
+    else if (gn == 3) ring_prefetch<WT, 3, true, WIDE>(T, L, g0, gn);
     else ring_prefetch<WT, 4, true, WIDE>(T, L, g0, gn);
   } else {
     if (gn <= 1) ring_prefetch<WT, 1, false, WIDE>(T, L, g0, gn);
     else if (gn == 2) ring_prefetch<WT, 2, false, WIDE>(T, L, g0, gn);
+    else if (gn == 3) ring_prefetch<WT, 3, false, WIDE>(T, L, g0, gn);
     else ring_prefetch<WT, 4, false, WIDE>(T, L, g0, gn);
   }
+}
+
+// Row groups of the pass that starts at group g0: the tile's G groups in ceil(G / kMfmaGroups)
+// passes of nearly equal size, the larger first (5 groups: 3 + 2; 6: 3 + 3; 7: 4 + 3). A pass of
+// three keeps three rounds in flight in the ring against two for a pass of four.
+__device__ __forceinline__ int pass_groups(int G, int g0) {
+  const int np = (G + kMfmaGroups - 1) / kMfmaGroups;
+  const int base = G / np, big = (G % np) * (base + 1);  // the first G % np passes have base + 1
+  return g0 < big ? base + 1 : base;
 }
 
 // A batched GEMV tile in two parts. gemv_mfma_begin sets the tile up and, on the ring path,
@@ -1752,7 +1765,7 @@ __device__ __forceinline__ void gemv_mfma_begin(MfmaJob &J, const DevModel &m, c
       L.woff = (uint32_t)lane < T.wt / 16u ? (uint32_t)lane * 16u : kNoRow;  // a tile is T.wt bytes
       L.goff = lane < 4 ? (uint32_t)lane * 16u : kNoRow;
       L.soff = kNoRow;
-      const int gn = min(kMfmaGroups, G);
+      const int gn = pass_groups(G, 0);
       if (J.wide)
         ring_prefetch_dispatch<WT, true>(T, L, 0, gn);
       else
@@ -1800,8 +1813,8 @@ __device__ __forceinline__ void gemv_mfma_end(MfmaJob &J, const DevModel &m, con
   // partial tiles: wave w's at mred + w * wstride, [group][16 rows][NC]
   const int wstride = ring ? kRingBytes / 4 : kMfmaGroups * 16 * NC;
   float ss = 0.f;
-  for (int g0 = 0; g0 < G; g0 += kMfmaGroups) {
-    const int gn = min(kMfmaGroups, G - g0);
+  for (int g0 = 0, gn = 0; g0 < G; g0 += gn) {
+    gn = pass_groups(G, g0);
     const bool sq = in.sumsq && g0 == 0;
     f32x4_t acc[kMfmaGroups];
     if constexpr (RING) {

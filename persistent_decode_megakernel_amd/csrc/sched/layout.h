@@ -169,9 +169,10 @@ constexpr int32_t kDigitMaxK = 16384;
 constexpr int32_t kMaxBatch = 16;  // sequences per step
 // partial 16-row tiles of the batched GEMV: waves x row groups x 16 rows x 16 columns
 constexpr int32_t kMfmaRedFloats = kWaves * 4 * 16 * 16;
-// Batched megakernel instances stream tile-major weights through a 16 KB LDS ring per wave, which
-// also holds that wave's partial tiles between passes.
-constexpr int32_t kRingBytes = 16384;
+// Batched megakernel instances stream tile-major weights through an LDS ring per wave, which also
+// holds that wave's partial tiles between passes: 16.25 KB, four slots of a three-group round
+// (three 1 KB weight copies, 1 KB of inputs, 64 bytes of gain).
+constexpr int32_t kRingBytes = 16640;
 constexpr int32_t kRingFloats = kWaves * kRingBytes / 4;
 AMK_HD int32_t lds_xs_floats(int32_t batch, int32_t hidden, int32_t qdim, int32_t ffn) {
   int32_t k = hidden > qdim ? hidden : qdim;
